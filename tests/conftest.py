@@ -1,0 +1,23 @@
+"""Shared pytest configuration.
+
+Marker ``gpu``: the test needs an MI355X (gfx950) and the built HIP library.
+CPU-only runs use ``-m "not gpu"``.
+"""
+
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X GPU and the built HIP library")
+
+
+@pytest.fixture(scope="session")
+def golden_dir():
+    return os.path.join(ROOT, "tests", "golden")
