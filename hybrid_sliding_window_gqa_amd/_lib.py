@@ -1,0 +1,120 @@
+"""ctypes declarations of the C ABI in include/hybrid_attn.h.
+
+Loading fails loudly when libhybridattn.so has not been built: there is no
+fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhybridattn.so")
+
+HA_OK = 0
+HA_ERR_NULL = 1
+HA_ERR_SHAPE = 2
+HA_ERR_RANGE = 3
+HA_ERR_WORKSPACE = 4
+HA_ERR_UNSUPPORTED = 5
+HA_ERR_HIP = 6
+
+HA_BF16 = 0
+HA_F32 = 1
+HA_SWA = 0
+HA_FULL = 1
+
+ABI_VERSION = 1
+
+# Every symbol include/hybrid_attn.h declares.
+EXPORTS = (
+    "swa_ring_append",
+    "full_pool_append",
+    "window_safe_match",
+    "hybrid_attn_prefill",
+    "hybrid_attn_decode",
+    "hybrid_attn_workspace_size",
+    "hybrid_attn_decode_splits",
+    "ha_status_str",
+    "ha_last_error",
+    "ha_abi_version",
+)
+
+
+class HaShape(ctypes.Structure):
+    _fields_ = [
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+
+class HaKvView(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("num_blocks", ctypes.c_int32),
+        ("table", ctypes.c_void_p),
+        ("table_stride", ctypes.c_int32),
+    ]
+
+
+class HybridAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_str(status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libhybridattn.so (once) and declare the ABI."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -m hybrid_sliding_window_gqa_amd.build)"
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    shp, view = ctypes.POINTER(HaShape), ctypes.POINTER(HaKvView)
+    append_args = [shp, view, p, p, i32, i32, p, p, i32, p]
+    lib.swa_ring_append.argtypes = append_args
+    lib.full_pool_append.argtypes = append_args
+    lib.window_safe_match.argtypes = [p, i64, p, i64, p, i32, ctypes.POINTER(i64)]
+    lib.hybrid_attn_prefill.argtypes = [shp, view, p, p, i32, i32, i32, p, p, p, i32, p, p, p, sz, p]
+    lib.hybrid_attn_decode.argtypes = [shp, view, p, i32, i32, p, i32, p, p, i32, p, sz, p]
+    lib.hybrid_attn_workspace_size.argtypes = [shp, i32, i32, i32, i32, i32]
+    lib.hybrid_attn_workspace_size.restype = sz
+    lib.hybrid_attn_decode_splits.argtypes = [shp, i32, i32, i32, i32]
+    lib.hybrid_attn_decode_splits.restype = i32
+    for fn in ("swa_ring_append", "full_pool_append", "window_safe_match", "hybrid_attn_prefill",
+               "hybrid_attn_decode"):
+        getattr(lib, fn).restype = i32
+    lib.ha_status_str.argtypes = [i32]
+    lib.ha_status_str.restype = ctypes.c_char_p
+    lib.ha_last_error.argtypes = []
+    lib.ha_last_error.restype = ctypes.c_char_p
+    lib.ha_abi_version.argtypes = []
+    lib.ha_abi_version.restype = i32
+    if lib.ha_abi_version() != ABI_VERSION:
+        raise ImportError(f"libhybridattn.so ABI {lib.ha_abi_version()} != binding ABI {ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().ha_status_str(int(status)).decode()
+
+
+def check(status: int) -> None:
+    if status != HA_OK:
+        raise HybridAttnError(status, load().ha_last_error().decode())

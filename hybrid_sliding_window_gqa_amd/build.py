@@ -1,0 +1,74 @@
+"""Build the HIP library libhybridattn.so in-tree for gfx950.
+
+Every source is compiled with hipcc for gfx950 only, with packed-FP32
+instruction generation disabled, into position-independent objects that are
+linked into one shared library next to this file.
+
+    python -m hybrid_sliding_window_gqa_amd.build
+"""
+
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+ROOT = os.path.dirname(HERE)
+LIB_NAME = "libhybridattn.so"
+LIB_PATH = os.path.join(HERE, LIB_NAME)
+BUILD_DIR = os.path.join(ROOT, "_build")
+SOURCES = ["api.cpp", "append.hip", "decode.hip", "prefill.hip"]
+ARCH = "gfx950"
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libhybridattn.so)")
+
+
+def common_flags() -> list[str]:
+    return [
+        "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"),
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link the library. Returns the library path."""
+    hipcc = _hipcc()
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs = []
+    cmds = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        cmds.append([hipcc, *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj])
+
+    def run(cmd):
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+        # hipcc's host pass does not know the packed-fp32 feature flag: harmless noise
+        noise = "'-packed-fp32-ops' is not a recognized feature"
+        err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
+        return err
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(cmds)) as pool:
+        list(pool.map(run, cmds))
+    tmp = LIB_PATH + ".tmp"
+    run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

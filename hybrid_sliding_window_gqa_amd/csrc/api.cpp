@@ -1,0 +1,287 @@
+// C ABI of the hybrid attention library: argument validation, error
+// reporting, the host-side window-safe prefix matcher, and dispatch to the
+// kernel launchers. Every check runs on the host before any HIP call, so a
+// rejected call never touches the device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/hybrid_attn.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ha_status fail(ha_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+ha_status ok() {
+  g_last_error.clear();
+  return HA_OK;
+}
+
+ha_status check_shape(const ha_shape* s, ha::Geometry* geo) {
+  if (!s) return fail(HA_ERR_NULL, "shape is NULL");
+  if (s->num_q_heads <= 0 || s->num_kv_heads <= 0)
+    return fail(HA_ERR_SHAPE, "head counts must be positive (got %d q, %d kv)", s->num_q_heads, s->num_kv_heads);
+  if (s->num_q_heads % s->num_kv_heads != 0)
+    return fail(HA_ERR_SHAPE, "num_q_heads %d is not a multiple of num_kv_heads %d", s->num_q_heads,
+                s->num_kv_heads);
+  const int group = s->num_q_heads / s->num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16)
+    return fail(HA_ERR_SHAPE, "query heads per kv head must be 1, 2, 4, 8 or 16 (got %d)", group);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(HA_ERR_SHAPE, "head_dim must be 64 or 128 (got %d)", s->head_dim);
+  if (s->window < 16 || s->window % 16 != 0)
+    return fail(HA_ERR_SHAPE, "window must be a positive multiple of 16 (got %d)", s->window);
+  if (s->page_size != 16) return fail(HA_ERR_SHAPE, "page_size must be 16 (got %d)", s->page_size);
+  if (!(std::isfinite(s->softmax_scale))) return fail(HA_ERR_SHAPE, "softmax_scale is not finite");
+  geo->hq = s->num_q_heads;
+  geo->hkv = s->num_kv_heads;
+  geo->d = s->head_dim;
+  geo->window = s->window;
+  geo->group = group;
+  geo->scale = s->softmax_scale > 0.0f ? s->softmax_scale : 1.0f / std::sqrt(static_cast<float>(s->head_dim));
+  return HA_OK;
+}
+
+ha_status check_view(const ha_kv_view* kv, int batch) {
+  if (!kv) return fail(HA_ERR_NULL, "kv view is NULL");
+  if (kv->kind != HA_SWA && kv->kind != HA_FULL) return fail(HA_ERR_UNSUPPORTED, "unknown layer kind %d", kv->kind);
+  if (kv->num_blocks < 0) return fail(HA_ERR_RANGE, "num_blocks is negative");
+  if (batch > 0) {
+    if (!kv->k || !kv->v) return fail(HA_ERR_NULL, "pool K or V pointer is NULL");
+    if (!kv->table) return fail(HA_ERR_NULL, "%s is NULL", kv->kind == HA_SWA ? "ring id table" : "page table");
+    if (kv->kind == HA_FULL && kv->table_stride <= 0)
+      return fail(HA_ERR_RANGE, "page table stride must be positive (got %d)", kv->table_stride);
+  }
+  return HA_OK;
+}
+
+ha_status check_dtype(int32_t dt) {
+  if (dt != HA_BF16 && dt != HA_F32) return fail(HA_ERR_UNSUPPORTED, "unsupported dtype %d", dt);
+  return HA_OK;
+}
+
+ha_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(HA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+ha_status append_common(const ha_shape* shape, const ha_kv_view* view, int32_t want_kind, const int32_t* pos0,
+                        const int32_t* cu_new, int32_t batch, int32_t num_tokens, const void* k_new,
+                        const void* v_new, int32_t src_dtype, void* stream) {
+  ha::Geometry geo;
+  ha_status st = check_shape(shape, &geo);
+  if (st != HA_OK) return st;
+  if (batch < 0 || num_tokens < 0) return fail(HA_ERR_RANGE, "batch and num_tokens must be >= 0");
+  st = check_view(view, batch);
+  if (st != HA_OK) return st;
+  if (view->kind != want_kind)
+    return fail(HA_ERR_UNSUPPORTED, "%s needs a %s view", want_kind == HA_SWA ? "swa_ring_append" : "full_pool_append",
+                want_kind == HA_SWA ? "HA_SWA" : "HA_FULL");
+  if ((st = check_dtype(src_dtype)) != HA_OK) return st;
+  if (batch == 0 || num_tokens == 0) return ok();
+  if (!pos0 || !cu_new) return fail(HA_ERR_NULL, "pos0 or cu_new is NULL");
+  if (!k_new || !v_new) return fail(HA_ERR_NULL, "k_new or v_new is NULL");
+  ha::AppendArgs a{};
+  a.geo = geo;
+  a.full = want_kind == HA_FULL;
+  a.k_pool = static_cast<uint16_t*>(view->k);
+  a.v_pool = static_cast<uint16_t*>(view->v);
+  a.num_blocks = view->num_blocks;
+  a.table = view->table;
+  a.table_stride = view->table_stride;
+  a.pos0 = pos0;
+  a.cu_new = cu_new;
+  a.batch = batch;
+  a.num_tokens = num_tokens;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.src_f32 = src_dtype == HA_F32;
+  return hip_status(ha::launch_append(a, static_cast<hipStream_t>(stream)), "append launch");
+}
+
+size_t decode_workspace(const ha::Geometry& geo, bool full, int batch, int max_kv_len, int num_splits) {
+  if (!full) return 0;
+  const int sb = ha::decode_split_blocks(true, geo.window, max_kv_len, batch, geo.hkv, num_splits);
+  const int ns = ha::decode_num_splits(true, geo.window, max_kv_len, sb);
+  if (ns <= 1) return 0;
+  return static_cast<size_t>(batch) * geo.hq * ns * (geo.d + 1) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+ha_status swa_ring_append(const ha_shape* shape, const ha_kv_view* ring, const int32_t* pos0, const int32_t* cu_new,
+                          int32_t batch, int32_t num_tokens, const void* k_new, const void* v_new,
+                          int32_t src_dtype, void* stream) {
+  return append_common(shape, ring, HA_SWA, pos0, cu_new, batch, num_tokens, k_new, v_new, src_dtype, stream);
+}
+
+ha_status full_pool_append(const ha_shape* shape, const ha_kv_view* pages, const int32_t* pos0,
+                           const int32_t* cu_new, int32_t batch, int32_t num_tokens, const void* k_new,
+                           const void* v_new, int32_t src_dtype, void* stream) {
+  return append_common(shape, pages, HA_FULL, pos0, cu_new, batch, num_tokens, k_new, v_new, src_dtype, stream);
+}
+
+ha_status window_safe_match(const int32_t* req_tokens, int64_t req_len, const int32_t* cached_tokens,
+                            int64_t cached_len, const uint8_t* swa_valid, int32_t window, int64_t* out_len) {
+  if (!out_len) return fail(HA_ERR_NULL, "out_len is NULL");
+  if (req_len < 0 || cached_len < 0) return fail(HA_ERR_RANGE, "lengths must be >= 0");
+  if (window < 1) return fail(HA_ERR_SHAPE, "window must be >= 1 (got %d)", window);
+  if ((req_len > 0 && !req_tokens) || (cached_len > 0 && (!cached_tokens || !swa_valid)))
+    return fail(HA_ERR_NULL, "token or validity array is NULL");
+  const int64_t n = req_len < cached_len ? req_len : cached_len;
+  int64_t m = 0;
+  while (m < n && req_tokens[m] == cached_tokens[m]) ++m;
+  // Walk back from m: if an invalid slot x lies in the candidate's last window
+  // [L - W, L), no length in (x, L] can be safe, so the next candidate is x.
+  int64_t len = m;
+  for (;;) {
+    const int64_t lo = len - window > 0 ? len - window : 0;
+    int64_t bad = -1;
+    for (int64_t p = len - 1; p >= lo; --p) {
+      if (!swa_valid[p]) {
+        bad = p;
+        break;
+      }
+    }
+    if (bad < 0) break;
+    len = bad;
+  }
+  *out_len = len;
+  return ok();
+}
+
+ha_status hybrid_attn_prefill(const ha_shape* shape, const ha_kv_view* kv, const int32_t* hist_len,
+                              const int32_t* cu_new, int32_t batch, int32_t num_tokens, int32_t max_new,
+                              const void* q, const void* k_new, const void* v_new, int32_t in_dtype, float* out,
+                              float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  ha::Geometry geo;
+  ha_status st = check_shape(shape, &geo);
+  if (st != HA_OK) return st;
+  if (batch < 0 || num_tokens < 0 || max_new < 0)
+    return fail(HA_ERR_RANGE, "batch, num_tokens and max_new must be >= 0");
+  if ((st = check_view(kv, batch)) != HA_OK) return st;
+  if ((st = check_dtype(in_dtype)) != HA_OK) return st;
+  if (batch == 0 || num_tokens == 0 || max_new == 0) return ok();
+  if (max_new > num_tokens) return fail(HA_ERR_RANGE, "max_new %d exceeds num_tokens %d", max_new, num_tokens);
+  if (!hist_len || !cu_new) return fail(HA_ERR_NULL, "hist_len or cu_new is NULL");
+  if (!q || !k_new || !v_new) return fail(HA_ERR_NULL, "q, k_new or v_new is NULL");
+  if (!out || !lse) return fail(HA_ERR_NULL, "out or lse is NULL");
+  ha::PrefillArgs a{};
+  a.geo = geo;
+  a.full = kv->kind == HA_FULL;
+  a.k_pool = static_cast<const uint16_t*>(kv->k);
+  a.v_pool = static_cast<const uint16_t*>(kv->v);
+  a.num_blocks = kv->num_blocks;
+  a.table = kv->table;
+  a.table_stride = kv->table_stride;
+  a.hist_len = hist_len;
+  a.cu_new = cu_new;
+  a.batch = batch;
+  a.num_tokens = num_tokens;
+  a.max_new = max_new;
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.in_f32 = in_dtype == HA_F32;
+  a.out = out;
+  a.lse = lse;
+  return hip_status(ha::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
+}
+
+ha_status hybrid_attn_decode(const ha_shape* shape, const ha_kv_view* kv, const int32_t* kv_len, int32_t batch,
+                             int32_t max_kv_len, const void* q, int32_t in_dtype, float* out, float* lse,
+                             int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  ha::Geometry geo;
+  ha_status st = check_shape(shape, &geo);
+  if (st != HA_OK) return st;
+  if (batch < 0 || max_kv_len < 0 || num_splits < 0)
+    return fail(HA_ERR_RANGE, "batch, max_kv_len and num_splits must be >= 0");
+  if ((st = check_view(kv, batch)) != HA_OK) return st;
+  if ((st = check_dtype(in_dtype)) != HA_OK) return st;
+  if (batch == 0) return ok();
+  if (batch > 65535) return fail(HA_ERR_RANGE, "decode batch %d exceeds 65535", batch);
+  if (!kv_len || !q || !out || !lse) return fail(HA_ERR_NULL, "kv_len, q, out or lse is NULL");
+  const bool full = kv->kind == HA_FULL;
+  const size_t need = decode_workspace(geo, full, batch, max_kv_len, num_splits);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(HA_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need, workspace ? workspace_bytes : 0);
+  ha::DecodeArgs a{};
+  a.geo = geo;
+  a.full = full;
+  a.k_pool = static_cast<const uint16_t*>(kv->k);
+  a.v_pool = static_cast<const uint16_t*>(kv->v);
+  a.num_blocks = kv->num_blocks;
+  a.table = kv->table;
+  a.table_stride = kv->table_stride;
+  a.kv_len = kv_len;
+  a.batch = batch;
+  a.q = q;
+  a.q_f32 = in_dtype == HA_F32;
+  a.out = out;
+  a.lse = lse;
+  a.split_blocks = ha::decode_split_blocks(full, geo.window, max_kv_len, batch, geo.hkv, num_splits);
+  a.splits = ha::decode_num_splits(full, geo.window, max_kv_len, a.split_blocks);
+  if (a.splits > 65535) return fail(HA_ERR_RANGE, "too many key splits (%d); pass a smaller num_splits", a.splits);
+  if (need > 0) {
+    float* ws = static_cast<float*>(workspace);
+    a.part_o = ws;
+    a.part_lse = ws + static_cast<size_t>(batch) * geo.hq * a.splits * geo.d;
+  }
+  return hip_status(ha::launch_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
+size_t hybrid_attn_workspace_size(const ha_shape* shape, int32_t kind, int32_t decode, int32_t batch,
+                                  int32_t max_kv_len, int32_t num_splits) {
+  ha::Geometry geo;
+  if (check_shape(shape, &geo) != HA_OK) return 0;
+  if ((kind != HA_SWA && kind != HA_FULL) || batch < 0 || max_kv_len < 0 || num_splits < 0) return 0;
+  if (!decode) return 0;
+  return decode_workspace(geo, kind == HA_FULL, batch, max_kv_len, num_splits);
+}
+
+int32_t hybrid_attn_decode_splits(const ha_shape* shape, int32_t kind, int32_t batch, int32_t max_kv_len,
+                                  int32_t num_splits) {
+  ha::Geometry geo;
+  if (check_shape(shape, &geo) != HA_OK) return 0;
+  if ((kind != HA_SWA && kind != HA_FULL) || batch < 0 || max_kv_len < 0 || num_splits < 0) return 0;
+  const bool full = kind == HA_FULL;
+  const int sb = ha::decode_split_blocks(full, geo.window, max_kv_len, batch, geo.hkv, num_splits);
+  return ha::decode_num_splits(full, geo.window, max_kv_len, sb);
+}
+
+const char* ha_status_str(int32_t status) {
+  switch (status) {
+    case HA_OK: return "HA_OK";
+    case HA_ERR_NULL: return "HA_ERR_NULL";
+    case HA_ERR_SHAPE: return "HA_ERR_SHAPE";
+    case HA_ERR_RANGE: return "HA_ERR_RANGE";
+    case HA_ERR_WORKSPACE: return "HA_ERR_WORKSPACE";
+    case HA_ERR_UNSUPPORTED: return "HA_ERR_UNSUPPORTED";
+    case HA_ERR_HIP: return "HA_ERR_HIP";
+    default: return "HA_ERR_UNKNOWN";
+  }
+}
+
+const char* ha_last_error(void) { return g_last_error.c_str(); }
+
+int32_t ha_abi_version(void) { return HA_ABI_VERSION; }
+
+}  // extern "C"

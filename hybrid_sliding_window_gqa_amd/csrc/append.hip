@@ -1,0 +1,92 @@
+// a1 / a2: scatter new K/V rows into the SWA ring pool or the Full page pool.
+//
+// The SWA pool is a per-sequence ring of W slots whose storage never grows
+// beyond the window, and the Full pool is a paged store that grows as the
+// caller hands out pages; both are physically separate (youleyou.com
+// "小米MiMo首次公开模型推理系统全链路优化降价99%", section
+// "KVCache系统重构：让缓存真正省下来"; blog.hotdry.top 2026-06-12,
+// section "双池分治与三级缓存的工程实现").
+//
+// One thread moves 8 channels (16 bytes of bfloat16) of one token row of one
+// kv head: the K row is written token-major with one 16-byte store, the V
+// row dim-major inside its 16-token block (8 two-byte stores, 32 bytes apart).
+// Appends are a few KiB per decode step and a few hundred MiB per prefill
+// chunk, far below the attention traffic, so they favour simplicity.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ha {
+
+template <bool kF32>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  const int d = a.geo.d;
+  const int hkv = a.geo.hkv;
+  const int chunks = d >> 3;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(a.num_tokens) * hkv * chunks;
+  if (gid >= total) return;
+  const int c = static_cast<int>(gid % chunks);
+  const int64_t rest = gid / chunks;
+  const int g = static_cast<int>(rest % hkv);
+  const int tok = static_cast<int>(rest / hkv);
+
+  // Sequence owning this row: the largest b with cu_new[b] <= tok.
+  int lo = 0, hi = a.batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.cu_new[mid] <= tok) lo = mid; else hi = mid - 1;
+  }
+  const int b = lo;
+  const int i = tok - a.cu_new[b];
+  const int n = a.cu_new[b + 1] - a.cu_new[b];
+  if (i < 0 || i >= n) return;
+  const int64_t p = static_cast<int64_t>(a.pos0[b]) + i;
+  if (p < 0) return;
+
+  int64_t block_base;  // element offset of the token's 16-token block for head g
+  int in_blk;
+  if (!a.full) {
+    const int w = a.geo.window;
+    if (i < n - w) return;  // overwritten later in this same call
+    const int r = a.table[b];
+    if (r < 0 || r >= a.num_blocks) return;
+    const int s = static_cast<int>(p % w);
+    block_base = ((static_cast<int64_t>(r) * hkv + g) * w + (s & ~(kBlock - 1))) * d;
+    in_blk = s & (kBlock - 1);
+  } else {
+    const int64_t lp = p >> 4;
+    if (lp >= a.table_stride) return;
+    const int pg = a.table[static_cast<int64_t>(b) * a.table_stride + lp];
+    if (pg < 0 || pg >= a.num_blocks) return;
+    block_base = (static_cast<int64_t>(pg) * hkv + g) * kBlock * d;
+    in_blk = static_cast<int>(p & (kBlock - 1));
+  }
+
+  const int64_t src = (static_cast<int64_t>(tok) * hkv + g) * d + c * 8;
+  const u32x4 kv = load8_as_bf16<kF32>(a.k_new, src);
+  *reinterpret_cast<u32x4*>(a.k_pool + block_base + static_cast<int64_t>(in_blk) * d + c * 8) = kv;
+
+  const u32x4 vv = load8_as_bf16<kF32>(a.v_new, src);
+  uint16_t* vdst = a.v_pool + block_base + static_cast<int64_t>(c * 8) * kBlock + in_blk;
+  const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    vdst[(2 * j) * kBlock] = static_cast<uint16_t>(w4[j] & 0xffffu);
+    vdst[(2 * j + 1) * kBlock] = static_cast<uint16_t>(w4[j] >> 16);
+  }
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
+  const int64_t total = static_cast<int64_t>(a.num_tokens) * a.geo.hkv * (a.geo.d >> 3);
+  if (total == 0 || a.batch == 0) return hipSuccess;
+  const int threads = 256;
+  const int64_t blocks = (total + threads - 1) / threads;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (a.src_f32)
+    hipLaunchKernelGGL(append_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(append_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace ha

@@ -1,0 +1,86 @@
+// Device-side helpers shared by the hybrid attention kernels (gfx950 / CDNA4).
+//
+// Matrix-core conventions used throughout (64-lane wavefront, lane l,
+// q = l / 16 "lane group", c = l % 16):
+//   v_mfma_f32_16x16x32_bf16  A[16 x 32]: lane holds A[c][8q .. 8q+7]
+//                             B[32 x 16]: lane holds B[8q .. 8q+7][c]
+//   v_mfma_f32_16x16x16_bf16  A[16 x 16]: lane holds A[c][4q .. 4q+3]
+//                             B[16 x 16]: lane holds B[4q .. 4q+3][c]
+//   accumulator C[16 x 16]:   lane holds C[4q + r][c], r = 0..3
+// Any relabelling of the reduction index applied to A and B alike leaves the
+// product unchanged, which the kernels use to load operands with long
+// contiguous runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ha {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = 16;         // tokens per page / ring block
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x16(const u32x2& a, const u32x2& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round-to-nearest-even float -> bfloat16 (hardware conversion on gfx950).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  __bf16 b = static_cast<__bf16>(f);
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// 16 bytes holding 8 bfloat16 values loaded from `src` (bf16 or f32 storage).
+template <bool kF32>
+__device__ __forceinline__ u32x4 load8_as_bf16(const void* src, int64_t elem_off) {
+  if constexpr (kF32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(src) + elem_off);
+    float4 a = p[0], b = p[1];
+    u32x4 r;
+    r.x = pack_bf16x2(a.x, a.y);
+    r.y = pack_bf16x2(a.z, a.w);
+    r.z = pack_bf16x2(b.x, b.y);
+    r.w = pack_bf16x2(b.z, b.w);
+    return r;
+  } else {
+    return *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + elem_off);
+  }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Cross-lane max / sum over the four lane groups (lanes c, c+16, c+32, c+48).
+__device__ __forceinline__ float group4_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float group4_sum(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+}  // namespace ha

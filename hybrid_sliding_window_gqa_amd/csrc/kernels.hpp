@@ -1,0 +1,82 @@
+// Launch parameters and host-side launchers of the hybrid attention kernels.
+// Validation happens in api.cpp; launchers assume valid arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ha {
+
+// Geometry after validation.
+struct Geometry {
+  int hq, hkv, d, window, group;  // group = hq / hkv
+  float scale;                    // softmax scale (natural units)
+};
+
+struct AppendArgs {
+  Geometry geo;
+  bool full;              // false: SWA ring, true: Full pages
+  uint16_t* k_pool;
+  uint16_t* v_pool;
+  int32_t num_blocks;     // rings or pages in the pool
+  const int32_t* table;   // ring ids [B] or page table [B][stride]
+  int32_t table_stride;
+  const int32_t* pos0;
+  const int32_t* cu_new;
+  int32_t batch;
+  int32_t num_tokens;
+  const void* k_new;
+  const void* v_new;
+  bool src_f32;
+};
+
+struct DecodeArgs {
+  Geometry geo;
+  bool full;
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  int32_t num_blocks;
+  const int32_t* table;
+  int32_t table_stride;
+  const int32_t* kv_len;
+  int32_t batch;
+  const void* q;
+  bool q_f32;
+  float* out;
+  float* lse;
+  int32_t splits;         // max splits per sequence (grid x)
+  int32_t split_blocks;   // 16-token blocks per split
+  float* part_o;          // [batch][hq][splits][d]
+  float* part_lse;        // [batch][hq][splits]  (log2 domain)
+};
+
+struct PrefillArgs {
+  Geometry geo;
+  bool full;
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  int32_t num_blocks;
+  const int32_t* table;
+  int32_t table_stride;
+  const int32_t* hist_len;
+  const int32_t* cu_new;
+  int32_t batch;
+  int32_t num_tokens;
+  int32_t max_new;
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  bool in_f32;
+  float* out;
+  float* lse;
+};
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// Decode split policy shared by the workspace query and the launcher.
+int decode_split_blocks(bool full, int window, int max_kv_len, int batch, int hkv, int requested_splits);
+int decode_num_splits(bool full, int window, int max_kv_len, int split_blocks);
+
+}  // namespace ha

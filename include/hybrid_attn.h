@@ -1,0 +1,200 @@
+/*
+ * hybrid_attn.h -- C ABI of the hybrid sliding-window / full GQA attention
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * The method (web pages cited by title and section):
+ *   [HTX]  htx.com news "Xiaomi MiMo's 99% price cut is not marketing -- Luo Fuli
+ *          posts ...", sections 工程一 (60 of 70 layers use a 128-token window,
+ *          10 attend to everything), 工程二 (two separate KV pools), 工程三
+ *          (window-safe prefix reuse).
+ *   [YLY]  youleyou.com "小米MiMo首次公开模型推理系统全链路优化降价99%",
+ *          section 1 "为什么选择 Hybrid SWA 架构" and section 2 sub-section
+ *          "KVCache系统重构：让缓存真正省下来" (Full pool grows on demand and is
+ *          long-lived; SWA pool is a ring buffer sized by the window, O(W);
+ *          the Full index is authoritative; window-safe length rule).
+ *   [HD9]  blog.hotdry.top 2026-06-09 "MiMo-V2.5 ultra-speed inference
+ *          architecture", sections "Hybrid SWA：用 1/7 计算量捕获长程依赖"
+ *          (6:1 interleave, match clipped to the window boundary) and
+ *          "PD 分离与长度分桶" (chunked prefill, 64K/256K/1M buckets).
+ *   [HD12] blog.hotdry.top 2026-06-12 "MiMo inference optimization / edge
+ *          deployment", section "双池分治与三级缓存的工程实现".
+ *
+ * Semantics. For query position t, query head h, kv head g = h / (Hq/Hkv):
+ *   visible keys j: lo(t) <= j <= t, lo = max(0, t-W+1) for SWA layers,
+ *   lo = 0 for full layers (W keys including the query itself);
+ *   o = softmax_j(scale * q.k_j) v_j, lse = ln sum_j exp(scale * q.k_j).
+ *
+ * Ownership and threading. The caller owns every buffer (pools, tables, Q/K/V,
+ * outputs, workspace). The library allocates no device memory, keeps no state
+ * between calls apart from a thread-local error message, and is thread-safe.
+ * Device work is enqueued on the caller's HIP stream (passed as void*, NULL =
+ * default stream) and the calls return without synchronising; only
+ * window_safe_match runs synchronously on the host.
+ *
+ * Errors. Every call returns ha_status. Arguments are validated on the host
+ * before any HIP call, so a rejected call never touches the device.
+ * ha_last_error() returns a message for the last failure on the calling
+ * thread. Out-of-range ring or page ids found inside a kernel are not
+ * reported: their keys are skipped (reads) or their writes dropped, and the
+ * results for that sequence are undefined, but no memory outside the pools
+ * is touched.
+ *
+ * Pool layouts (bfloat16, per layer; B = 16-token block, D = head_dim):
+ *   SWA ring pool, W slots per (ring, kv head), W a multiple of 16:
+ *     K  [num_rings][Hkv][W][D]                 slot s at row s
+ *     V  [num_rings][Hkv][W/16][D][16]          slot s, dim c at [s/16][c][s%16]
+ *   Full page pool, 16-token pages:
+ *     K  [num_pages][Hkv][16][D]
+ *     V  [num_pages][Hkv][D][16]                (dim-major inside the page)
+ *   Position p of a sequence lives in ring slot p mod W, or in page
+ *   page_table[b][p / 16] at offset p mod 16.
+ *   V is stored dim-major within each 16-token block so that the P.V
+ *   contraction reads matrix-core operands directly; K is token-major.
+ */
+#ifndef HYBRID_ATTN_H
+#define HYBRID_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HA_ABI_VERSION 1
+
+typedef enum ha_status {
+  HA_OK = 0,
+  HA_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  HA_ERR_SHAPE = 2,       /* unsupported head counts, head_dim, window, page   */
+  HA_ERR_RANGE = 3,       /* negative or inconsistent sizes                    */
+  HA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required        */
+  HA_ERR_UNSUPPORTED = 5, /* dtype or layer kind not supported                 */
+  HA_ERR_HIP = 6          /* a HIP launch failed (message has the HIP error)   */
+} ha_status;
+
+typedef enum ha_dtype { HA_BF16 = 0, HA_F32 = 1 } ha_dtype;
+
+typedef enum ha_layer_kind { HA_SWA = 0, HA_FULL = 1 } ha_layer_kind;
+
+/* Head geometry shared by every call of one layer stack, so the window used by
+ * the kernels and by window_safe_match cannot drift apart ([HD12] notes that
+ * changing W must change the window-safe rule with it).
+ *   num_q_heads % num_kv_heads == 0, group = num_q_heads / num_kv_heads in
+ *   {1, 2, 4, 8, 16}; head_dim in {64, 128}; window >= 16 and a multiple of
+ *   16; page_size == 16; softmax_scale <= 0 selects 1/sqrt(head_dim). */
+typedef struct ha_shape {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t window;
+  int32_t page_size;
+  float softmax_scale;
+} ha_shape;
+
+/* One layer's pool. kind selects the interpretation of table:
+ *   HA_SWA : table = ring id per sequence, int32 [batch] (device);
+ *            num_blocks = rings in the pool; table_stride ignored.
+ *   HA_FULL: table = page table, int32 [batch][table_stride] (device);
+ *            num_blocks = pages in the pool. The page table is the
+ *            authoritative logical->physical index of the sequence ([YLY]). */
+typedef struct ha_kv_view {
+  int32_t kind;
+  void* k;
+  void* v;
+  int32_t num_blocks;
+  const int32_t* table;
+  int32_t table_stride;
+} ha_kv_view;
+
+/* ---- a1: SWA ring append ([YLY] KVCache系统重构; [HD12] 双池分治) ----------
+ * Writes the new tokens of each sequence into its ring: token i of sequence b
+ * (row cu_new[b] + i of k_new/v_new, absolute position pos0[b] + i) goes to
+ * slot (pos0[b] + i) mod W of ring ring->table[b]. Only the last min(n_b, W)
+ * tokens are written; the result equals appending all of them in order.
+ *   ring      HA_SWA view
+ *   pos0      int32 [batch] device, >= 0
+ *   cu_new    int32 [batch+1] device, non-decreasing, cu_new[0] = 0,
+ *             cu_new[batch] = num_tokens
+ *   k_new, v_new  [num_tokens][Hkv][D] device, src_dtype (HA_F32 is rounded
+ *             to bfloat16 to nearest-even) */
+ha_status swa_ring_append(const ha_shape* shape, const ha_kv_view* ring, const int32_t* pos0,
+                          const int32_t* cu_new, int32_t batch, int32_t num_tokens,
+                          const void* k_new, const void* v_new, int32_t src_dtype, void* stream);
+
+/* ---- a2: Full pool append ([YLY] KVCache系统重构: grows on demand) --------
+ * Writes token i of sequence b (position p = pos0[b] + i) to page
+ * pages->table[b][p / 16], offset p mod 16. The caller allocates the pages
+ * (the pool grows by the caller handing out more page ids). Arguments as for
+ * swa_ring_append; every page id used must be < pages->num_blocks and
+ * p / 16 < table_stride. */
+ha_status full_pool_append(const ha_shape* shape, const ha_kv_view* pages, const int32_t* pos0,
+                           const int32_t* cu_new, int32_t batch, int32_t num_tokens,
+                           const void* k_new, const void* v_new, int32_t src_dtype, void* stream);
+
+/* ---- a3: window-safe prefix match ([HTX] 工程三; [YLY] KVCache系统重构;
+ *          [HD9] Hybrid SWA 节; [HD12] 双池分治) ------------------------------
+ * Host-only, synchronous. m = longest common prefix of the request and the
+ * cached tokens; *out_len = the largest L <= m such that every position in
+ * [max(0, L - window), L) has swa_valid[pos] != 0. L = 0 is always safe.
+ *   req_tokens [req_len], cached_tokens [cached_len], swa_valid [cached_len]
+ *   (all host memory); window >= 1. */
+ha_status window_safe_match(const int32_t* req_tokens, int64_t req_len, const int32_t* cached_tokens,
+                            int64_t cached_len, const uint8_t* swa_valid, int32_t window,
+                            int64_t* out_len);
+
+/* ---- a4/a5: prefill attention ([YLY] 为什么选择 Hybrid SWA 架构; [HD9]
+ *          PD 分离与长度分桶: chunked prefill) ---------------------------------
+ * Causal attention of a chunk of new tokens per sequence. Sequence b already
+ * holds positions [0, hist_len[b]) in the pool; its n_b = cu_new[b+1] -
+ * cu_new[b] new tokens are at positions [hist_len[b], hist_len[b] + n_b) and
+ * their K/V are read from k_new/v_new (not from the pool). Attention is a pure
+ * read: append the chunk afterwards (for SWA with n_b > 1 this order is
+ * required, as the chunk would overwrite ring slots its first queries read).
+ * For SWA layers the ring must hold positions [max(0, hist-W+1), hist).
+ *   hist_len  int32 [batch] device;  cu_new int32 [batch+1] device
+ *   num_tokens = cu_new[batch] (host);  max_new >= every n_b (host, sizes the grid)
+ *   q [num_tokens][Hq][D], k_new/v_new [num_tokens][Hkv][D], in_dtype
+ *   out float32 [num_tokens][Hq][D], lse float32 [num_tokens][Hq] (natural log)
+ *   workspace: hybrid_attn_workspace_size(..., decode = 0) bytes (0 today). */
+ha_status hybrid_attn_prefill(const ha_shape* shape, const ha_kv_view* kv, const int32_t* hist_len,
+                              const int32_t* cu_new, int32_t batch, int32_t num_tokens, int32_t max_new,
+                              const void* q, const void* k_new, const void* v_new, int32_t in_dtype,
+                              float* out, float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* ---- a6/a7/a8: decode attention with split-K ([YLY] 为什么选择 Hybrid SWA
+ *          架构 and Decode加速与多模态优化: decode cost follows KV bytes read) --
+ * One query per sequence at position t = kv_len[b] - 1, whose own K/V must
+ * already be appended. Keys are read from the pool only. Full layers split
+ * the key range over workgroups (split-K) and merge the partial results with
+ * lse = ln sum_s exp(lse_s), o = sum_s exp(lse_s - lse) o_s.
+ *   kv_len int32 [batch] device (0 = empty row: out = 0, lse = -inf)
+ *   max_kv_len >= every kv_len[b] (host; sizes the split grid)
+ *   q [batch][Hq][D] in_dtype; out float32 [batch][Hq][D]; lse float32 [batch][Hq]
+ *   num_splits: maximum key splits per sequence, 0 = automatic
+ *   workspace: hybrid_attn_workspace_size(..., decode = 1) bytes. */
+ha_status hybrid_attn_decode(const ha_shape* shape, const ha_kv_view* kv, const int32_t* kv_len,
+                             int32_t batch, int32_t max_kv_len, const void* q, int32_t in_dtype,
+                             float* out, float* lse, int32_t num_splits, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Workspace bytes needed by hybrid_attn_decode (decode = 1) or
+ * hybrid_attn_prefill (decode = 0) for the given sizes; 0 on invalid input. */
+size_t hybrid_attn_workspace_size(const ha_shape* shape, int32_t kind, int32_t decode, int32_t batch,
+                                  int32_t max_kv_len, int32_t num_splits);
+
+/* Key splits per sequence hybrid_attn_decode uses for these sizes (after
+ * resolving num_splits = 0), or 0 on invalid input. */
+int32_t hybrid_attn_decode_splits(const ha_shape* shape, int32_t kind, int32_t batch, int32_t max_kv_len,
+                                  int32_t num_splits);
+
+const char* ha_status_str(int32_t status);
+const char* ha_last_error(void);
+int32_t ha_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYBRID_ATTN_H */

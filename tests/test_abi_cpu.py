@@ -1,0 +1,146 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+and rejects invalid arguments on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from hybrid_sliding_window_gqa_amd import _lib
+from hybrid_sliding_window_gqa_amd._lib import HaKvView, HaShape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "hybrid_attn.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.ha_abi_version() == _lib.ABI_VERSION
+    assert _lib.status_str(0) == "HA_OK"
+    assert _lib.status_str(4) == "HA_ERR_WORKSPACE"
+    assert _lib.status_str(99) == "HA_ERR_UNKNOWN"
+
+
+def good_shape(**kw):
+    base = dict(num_q_heads=64, num_kv_heads=8, head_dim=128, window=128, page_size=16, softmax_scale=0.0)
+    base.update(kw)
+    return HaShape(**base)
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def view(kind=_lib.HA_FULL, k=FAKE, v=FAKE, table=FAKE, stride=4, blocks=8):
+    return HaKvView(kind, k, v, blocks, table, stride)
+
+
+def decode_call(lib, shape, kv, batch=2, max_len=100, q=FAKE, dtype=0, splits=0, ws=None, ws_bytes=0):
+    return lib.hybrid_attn_decode(ctypes.byref(shape) if shape is not None else None,
+                                  ctypes.byref(kv) if kv is not None else None, FAKE, batch, max_len, q, dtype,
+                                  FAKE, FAKE, splits, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize(
+    "shape_kw,status",
+    [
+        (dict(num_q_heads=60), _lib.HA_ERR_SHAPE),          # not a multiple of Hkv
+        (dict(num_q_heads=8 * 32), _lib.HA_ERR_SHAPE),      # group 32 unsupported
+        (dict(num_q_heads=24), _lib.HA_ERR_SHAPE),          # group 3 unsupported
+        (dict(head_dim=96), _lib.HA_ERR_SHAPE),
+        (dict(window=100), _lib.HA_ERR_SHAPE),
+        (dict(window=0), _lib.HA_ERR_SHAPE),
+        (dict(page_size=32), _lib.HA_ERR_SHAPE),
+        (dict(num_kv_heads=0), _lib.HA_ERR_SHAPE),
+        (dict(softmax_scale=float("nan")), _lib.HA_ERR_SHAPE),
+    ],
+)
+def test_shape_errors(lib, shape_kw, status):
+    assert decode_call(lib, good_shape(**shape_kw), view()) == status
+    assert "" != lib.ha_last_error().decode()
+
+
+def test_null_and_range_errors(lib):
+    s = good_shape()
+    assert decode_call(lib, None, view()) == _lib.HA_ERR_NULL
+    assert decode_call(lib, s, None) == _lib.HA_ERR_NULL
+    assert decode_call(lib, s, view(k=None)) == _lib.HA_ERR_NULL
+    assert decode_call(lib, s, view(table=None)) == _lib.HA_ERR_NULL
+    assert decode_call(lib, s, view(stride=0)) == _lib.HA_ERR_RANGE
+    assert decode_call(lib, s, view(), batch=-1) == _lib.HA_ERR_RANGE
+    assert decode_call(lib, s, view(), q=None) == _lib.HA_ERR_NULL
+    assert decode_call(lib, s, view(), dtype=7) == _lib.HA_ERR_UNSUPPORTED
+    assert decode_call(lib, s, view(kind=3)) == _lib.HA_ERR_UNSUPPORTED
+    assert decode_call(lib, s, view(), batch=70000) == _lib.HA_ERR_RANGE
+
+
+def test_decode_workspace_checked(lib):
+    s = good_shape()
+    need = lib.hybrid_attn_workspace_size(ctypes.byref(s), _lib.HA_FULL, 1, 64, 8193, 0)
+    splits = lib.hybrid_attn_decode_splits(ctypes.byref(s), _lib.HA_FULL, 64, 8193, 0)
+    assert splits > 1
+    assert need == 64 * 64 * splits * (128 + 1) * 4
+    assert decode_call(lib, s, view(), batch=64, max_len=8193) == _lib.HA_ERR_WORKSPACE
+    assert decode_call(lib, s, view(), batch=64, max_len=8193, ws=FAKE, ws_bytes=need - 1) == _lib.HA_ERR_WORKSPACE
+    # SWA decode and prefill need none
+    assert lib.hybrid_attn_workspace_size(ctypes.byref(s), _lib.HA_SWA, 1, 64, 8193, 0) == 0
+    assert lib.hybrid_attn_workspace_size(ctypes.byref(s), _lib.HA_FULL, 0, 64, 8193, 0) == 0
+    assert lib.hybrid_attn_decode_splits(ctypes.byref(s), _lib.HA_SWA, 64, 8193, 0) == 1
+    # explicit split count is honoured
+    assert lib.hybrid_attn_decode_splits(ctypes.byref(s), _lib.HA_FULL, 64, 8193, 4) == 4
+
+
+def test_append_and_prefill_errors(lib):
+    s = good_shape()
+    ring = view(kind=_lib.HA_SWA)
+    pages = view(kind=_lib.HA_FULL)
+    # wrong view kind
+    assert lib.swa_ring_append(ctypes.byref(s), ctypes.byref(pages), FAKE, FAKE, 2, 10, FAKE, FAKE, 0,
+                               None) == _lib.HA_ERR_UNSUPPORTED
+    assert lib.full_pool_append(ctypes.byref(s), ctypes.byref(ring), FAKE, FAKE, 2, 10, FAKE, FAKE, 0,
+                                None) == _lib.HA_ERR_UNSUPPORTED
+    assert lib.swa_ring_append(ctypes.byref(s), ctypes.byref(ring), None, FAKE, 2, 10, FAKE, FAKE, 0,
+                               None) == _lib.HA_ERR_NULL
+    assert lib.swa_ring_append(ctypes.byref(s), ctypes.byref(ring), FAKE, FAKE, 2, -1, FAKE, FAKE, 0,
+                               None) == _lib.HA_ERR_RANGE
+    assert lib.swa_ring_append(ctypes.byref(s), ctypes.byref(ring), FAKE, FAKE, 2, 10, FAKE, FAKE, 2,
+                               None) == _lib.HA_ERR_UNSUPPORTED
+    # empty work is a successful no-op that touches nothing
+    assert lib.swa_ring_append(ctypes.byref(s), ctypes.byref(ring), FAKE, FAKE, 0, 0, FAKE, FAKE, 0, None) == 0
+    args = [FAKE, FAKE, 2, 10, 5, FAKE, FAKE, FAKE, 0, FAKE, FAKE, None, 0, None]
+    assert lib.hybrid_attn_prefill(ctypes.byref(s), ctypes.byref(pages), *args[:2], 2, 10, 11,
+                                   *args[5:]) == _lib.HA_ERR_RANGE          # max_new > num_tokens
+    bad = list(args)
+    bad[5] = None
+    assert lib.hybrid_attn_prefill(ctypes.byref(s), ctypes.byref(pages), *bad) == _lib.HA_ERR_NULL
+    assert lib.hybrid_attn_prefill(ctypes.byref(s), ctypes.byref(pages), FAKE, FAKE, 0, 0, 0,
+                                   *args[5:]) == 0
+
+
+def test_errors_do_not_leak_between_calls(lib):
+    s = good_shape()
+    assert decode_call(lib, good_shape(head_dim=3), view()) == _lib.HA_ERR_SHAPE
+    assert b"head_dim" in lib.ha_last_error()
+    out = ctypes.c_int64()
+    assert lib.window_safe_match(None, 0, None, 0, None, 4, ctypes.byref(out)) == 0
+    assert out.value == 0
+    assert lib.ha_last_error() == b""
+    assert s.window == 128

@@ -1,0 +1,173 @@
+"""a4 / a5 on the GPU: causal prefill over pool history plus the chunk matches
+the oracle for one-shot, chunked and ragged batches, histories that do not
+start on a page edge, float32 inputs, and windows of several sizes; chunked
+prefill agrees with one-shot prefill and decode row t with prefill row t."""
+
+import numpy as np
+import pytest
+import torch
+
+import hybrid_sliding_window_gqa_amd as ha
+from gpu_util import (
+    append_history,
+    assert_close,
+    cu_from_counts,
+    host,
+    i32,
+    make_generator,
+    oracle_rows,
+    randn_bf16,
+)
+
+pytestmark = pytest.mark.gpu
+
+
+class Seqs:
+    """Logical Q/K/V per sequence (device bf16) for positions [0, total_b)."""
+
+    def __init__(self, shape, totals, seed):
+        gen = make_generator(seed)
+        hq, hkv, d = shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+        self.q = [randn_bf16(gen, t, hq, d) for t in totals]
+        self.k = [randn_bf16(gen, t, hkv, d) for t in totals]
+        self.v = [randn_bf16(gen, t, hkv, d) for t in totals]
+        self.totals = totals
+
+
+def make_pool(shape, kind, totals, perm_seed=0):
+    b = len(totals)
+    if kind == ha.HA_SWA:
+        pool = ha.SwaRingPool(shape, b + 1, "cuda", fill=float("nan"))
+        return pool, pool.view(i32(list(range(b))[::-1]))
+    per = [-(-t // 16) for t in totals]
+    num_pages = sum(per) + 3
+    perm = np.random.default_rng(perm_seed).permutation(num_pages)
+    table = np.full((b, max(per) + 1), -1, np.int32)
+    off = 0
+    for i, c in enumerate(per):
+        table[i, :c] = perm[off:off + c]
+        off += c
+    pool = ha.FullPagePool(shape, num_pages, "cuda", fill=float("nan"))
+    return pool, pool.view(i32(table))
+
+
+def run_chunks(shape, kind, seqs, boundaries, src=None):
+    """Prefill every sequence chunk by chunk: boundaries[b] = [0, c1, ..., total].
+    Returns per-sequence (out [total, Hq, D], lse [total, Hq]) as host arrays."""
+    pool, view = make_pool(shape, kind, seqs.totals)
+    nb = len(seqs.totals)
+    outs = [[] for _ in range(nb)]
+    lses = [[] for _ in range(nb)]
+    steps = max(len(x) for x in boundaries) - 1
+    for s in range(steps):
+        lo = [bd[s] if s < len(bd) - 1 else bd[-1] for bd in boundaries]
+        hi = [bd[s + 1] if s < len(bd) - 1 else bd[-1] for bd in boundaries]
+        counts = [h - l for l, h in zip(lo, hi)]
+        if sum(counts) == 0:
+            continue
+        cat = lambda xs: torch.cat([x[l:h] for x, l, h in zip(xs, lo, hi)]).contiguous()
+        q, k, v = cat(seqs.q), cat(seqs.k), cat(seqs.v)
+        if src is not None:
+            q, k, v = q.to(src), k.to(src), v.to(src)
+        out, lse = ha.hybrid_attn_prefill(shape, view, i32(lo), i32(cu_from_counts(counts)), q, k, v,
+                                          max_new=max(counts))
+        # attend first, then append the chunk
+        append_history(shape, view, [(a, b) for a, b in zip(seqs.k, seqs.v)], lo, hi)
+        o, l = host(out), host(lse)
+        cu = cu_from_counts(counts)
+        for b in range(nb):
+            outs[b].append(o[cu[b]:cu[b + 1]])
+            lses[b].append(l[cu[b]:cu[b + 1]])
+    torch.cuda.synchronize()
+    return [np.concatenate(x) for x in outs], [np.concatenate(x) for x in lses]
+
+
+def check_against_oracle(shape, kind, seqs, outs, lses, rows=None):
+    kname = "swa" if kind == ha.HA_SWA else "full"
+    for b, total in enumerate(seqs.totals):
+        sel = np.arange(total) if rows is None else np.array(sorted(set(r for r in rows(total) if 0 <= r < total)))
+        ref_o, ref_l = oracle_rows(host(seqs.q[b])[sel], host(seqs.k[b]), host(seqs.v[b]), sel, kname,
+                                   shape.window, shape.softmax_scale or None)
+        assert_close(outs[b][sel], lses[b][sel], ref_o, ref_l, f"kind={kname} seq={b}")
+
+
+@pytest.mark.parametrize("kind", [ha.HA_SWA, ha.HA_FULL])
+@pytest.mark.parametrize("hq,hkv,d,window", [(4, 1, 64, 128), (64, 8, 128, 128), (32, 2, 64, 48), (16, 16, 128, 64)])
+def test_one_shot_ragged_batch(kind, hq, hkv, d, window):
+    shape = ha.HeadShape(hq, hkv, d, window=window)
+    totals = [1, 15, 33, 130, 257, 700]
+    seqs = Seqs(shape, totals, seed=hq + d + window)
+    outs, lses = run_chunks(shape, kind, seqs, [[0, t] for t in totals])
+    check_against_oracle(shape, kind, seqs, outs, lses)
+
+
+@pytest.mark.parametrize("kind", [ha.HA_SWA, ha.HA_FULL])
+def test_chunked_matches_oracle_and_one_shot(kind):
+    shape = ha.HeadShape(64, 8, 128)
+    totals = [600, 517, 300]
+    seqs = Seqs(shape, totals, seed=77)
+    bounds = [[0, 128, 256, 384, 600], [0, 1, 100, 117, 300, 517], [0, 50, 51, 52, 300]]
+    outs, lses = run_chunks(shape, kind, seqs, bounds)
+    check_against_oracle(shape, kind, seqs, outs, lses)
+    one_o, one_l = run_chunks(shape, kind, seqs, [[0, t] for t in totals])
+    for b in range(len(totals)):
+        assert np.abs(outs[b] - one_o[b]).max() <= 1e-2
+        assert np.abs(lses[b] - one_l[b]).max() <= 1e-3
+
+
+def test_swa_with_window_covering_sequence_equals_full():
+    shape = ha.HeadShape(16, 2, 128, window=256)
+    totals = [256, 200, 31]
+    seqs = Seqs(shape, totals, seed=12)
+    o_s, l_s = run_chunks(shape, ha.HA_SWA, seqs, [[0, 100, t] for t in totals])
+    o_f, l_f = run_chunks(shape, ha.HA_FULL, seqs, [[0, 100, t] for t in totals])
+    for b in range(len(totals)):
+        assert np.abs(o_s[b] - o_f[b]).max() <= 1e-2
+        assert np.abs(l_s[b] - l_f[b]).max() <= 1e-3
+    check_against_oracle(shape, ha.HA_FULL, seqs, o_s, l_s)
+    check_against_oracle(shape, ha.HA_FULL, seqs, o_f, l_f)
+
+
+def test_float32_inputs_small_workload_shape():
+    # 4 query heads / 1 kv head, head_dim 64, scale 1/8, float32 inputs rounded to bf16.
+    shape = ha.HeadShape(4, 1, 64, softmax_scale=1.0 / 8.0)
+    totals = [512]
+    seqs = Seqs(shape, totals, seed=1)
+    for kind in (ha.HA_SWA, ha.HA_FULL):
+        outs, lses = run_chunks(shape, kind, seqs, [[0, 512]], src=torch.float32)
+        check_against_oracle(shape, kind, seqs, outs, lses)
+        outs, lses = run_chunks(shape, kind, seqs, [[0, 128, 256, 384, 512]], src=torch.float32)
+        check_against_oracle(shape, kind, seqs, outs, lses)
+
+
+@pytest.mark.parametrize("kind", [ha.HA_SWA, ha.HA_FULL])
+def test_decode_row_equals_prefill_row(kind):
+    shape = ha.HeadShape(64, 8, 128)
+    totals = [140, 333]
+    seqs = Seqs(shape, totals, seed=21)
+    outs, lses = run_chunks(shape, kind, seqs, [[0, t] for t in totals])
+    pool, view = make_pool(shape, kind, totals)
+    append_history(shape, view, list(zip(seqs.k, seqs.v)), [0, 0], totals)
+    q = torch.stack([seqs.q[b][t - 1] for b, t in enumerate(totals)]).contiguous()
+    out, lse = ha.hybrid_attn_decode(shape, view, i32(totals), q, max(totals))
+    torch.cuda.synchronize()
+    for b, t in enumerate(totals):
+        assert np.abs(host(out)[b] - outs[b][t - 1]).max() <= 1e-2
+        assert np.abs(host(lse)[b] - lses[b][t - 1]).max() <= 1e-3
+
+
+def test_prefill_is_deterministic_and_pure_read():
+    shape = ha.HeadShape(64, 8, 128)
+    totals = [400, 250]
+    seqs = Seqs(shape, totals, seed=31)
+    pool, view = make_pool(shape, ha.HA_FULL, totals)
+    append_history(shape, view, list(zip(seqs.k, seqs.v)), [0, 0], [100, 100])
+    counts = [t - 100 for t in totals]
+    cat = lambda xs: torch.cat([x[100:] for x in xs]).contiguous()
+    args = (shape, view, i32([100, 100]), i32(cu_from_counts(counts)), cat(seqs.q), cat(seqs.k), cat(seqs.v))
+    k_before = pool.k.clone()
+    o1, l1 = ha.hybrid_attn_prefill(*args, max_new=max(counts))
+    o2, l2 = ha.hybrid_attn_prefill(*args, max_new=max(counts))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(k_before.view(torch.int16), pool.k.view(torch.int16))
