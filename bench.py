@@ -1,0 +1,415 @@
+#!/usr/bin/env python3
+"""Benchmark of the hybrid SWA/full attention hot path on one MI355X.
+
+Default run (prints ONE JSON line on stdout):
+  step     one decode step of a 6:1 layer group (6 SWA layers on W=128 ring
+           pools + 1 full layer on a 16-token paged pool) for 64 sequences with
+           8192 cached tokens each, Hq/Hkv/D = 64/8/128, bf16 K/V ~ N(0,1):
+           per layer, append the new token then attend.
+  value    decode HBM GB/s = algorithmic bytes per step / step time, where
+           algorithmic bytes = K/V rows the queries see + Q read + O (fp32)
+           and LSE written.
+  prefill  chunked causal prefill of 4 x 32768 tokens in 8192-token chunks
+           through the same group (attend, then append): TFLOP/s with
+           4*D flops per visible (query head, key) pair.
+  roofline achieved/peak of the dominant kernel (the full-layer decode
+           call), timed with HIP events on the launch stream.
+  cpu_baseline  the fp64 oracle on a bounded sample of the decode step.
+
+Inputs are synthetic and resident in HBM before timing starts. Options select
+other workloads (--workload reuse|ragged) for extra JSON lines.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+METRIC = "decode attn HBM GB/s (% peak) + prefill TFLOP/s (% MFMA peak), SWA:full 6:1"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", choices=["decode", "reuse", "ragged", "chunked"], default="decode")
+    p.add_argument("--prefill-passes", type=int, default=3)
+    p.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill part")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU sample")
+    p.add_argument("--eager", action="store_true", help="launch calls directly instead of replaying a HIP graph")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (closed forms of the visibility rule)
+
+def visible_keys(t, kind, window):
+    t = np.asarray(t, dtype=np.int64)
+    return np.minimum(t + 1, window) if kind == "swa" else t + 1
+
+
+def visible_pairs_range(hist, n, kind, window):
+    """Sum over query positions hist..hist+n-1 of the visible key count."""
+    t = np.arange(hist, hist + n, dtype=np.int64)
+    return int(visible_keys(t, kind, window).sum())
+
+
+def kv_bytes_per_token(shape):
+    return shape.num_kv_heads * shape.head_dim * 2 * 2      # K and V, bf16
+
+
+def decode_layer_bytes(shape, kind, kv_len):
+    keys = visible_keys(np.asarray(kv_len) - 1, kind, shape.window).sum()
+    b = len(kv_len)
+    q = b * shape.num_q_heads * shape.head_dim * 2
+    o = b * shape.num_q_heads * shape.head_dim * 4
+    l = b * shape.num_q_heads * 4
+    return int(keys) * kv_bytes_per_token(shape) + q + o + l
+
+
+# ---------------------------------------------------------------------------
+
+def timed_events(torch, n):
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+
+def build_decode(torch, ha, grp, synth, struct, device, workload):
+    """Pools filled with each sequence's history; per-layer new-token tensors."""
+    shape = ha.HeadShape(struct.shape.num_q_heads, struct.shape.num_kv_heads, struct.shape.head_dim,
+                         struct.shape.window)
+    b = struct.batch
+    hist = struct.hist.astype(np.int64)
+    ring_id = torch.as_tensor(struct.ring_id, device=device)
+    table = torch.as_tensor(struct.page_table, device=device)
+    group = grp.HybridGroup(shape, ring_id, struct.num_rings, table, struct.num_pages)
+    hkv, hq, d, w = shape.num_kv_heads, shape.num_q_heads, shape.head_dim, shape.window
+    logical = []   # per layer: (k_hist, v_hist, first_position) host-side recipe for the oracle
+    q_l, k_l, v_l, out_l, lse_l = [], [], [], [], []
+    for li, layer in enumerate(group.layers):
+        if layer.kind == "swa":
+            start = np.maximum(hist - (w - 1), 0)
+        else:
+            start = np.zeros(b, np.int64)
+        counts = (hist - start).astype(np.int64)
+        total = int(counts.sum())
+        k_hist = synth.normal_bf16((total, hkv, d), workload, li, synth.K_VALUES, device)
+        v_hist = synth.normal_bf16((total, hkv, d), workload, li, synth.V_VALUES, device)
+        cu = torch.as_tensor(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32), device=device)
+        pos0 = torch.as_tensor(start.astype(np.int32), device=device)
+        fn = ha.swa_ring_append if layer.kind == "swa" else ha.full_pool_append
+        fn(shape, layer.view, pos0, cu, k_hist, v_hist)
+        logical.append((k_hist, v_hist, start, cu.cpu().numpy()))
+        q_l.append(synth.normal_bf16((b, hq, d), workload, li, synth.Q_VALUES, device))
+        k_l.append(synth.normal_bf16((b, hkv, d), workload, li, synth.K_VALUES + 3, device))
+        v_l.append(synth.normal_bf16((b, hkv, d), workload, li, synth.V_VALUES + 3, device))
+        out_l.append(torch.empty(b, hq, d, dtype=torch.float32, device=device))
+        lse_l.append(torch.empty(b, hq, dtype=torch.float32, device=device))
+    pos = torch.as_tensor(hist.astype(np.int32), device=device)
+    kv_len = torch.as_tensor((hist + 1).astype(np.int32), device=device)
+    plan = grp.plan_decode(group, q_l, k_l, v_l, pos, kv_len, int(hist.max()) + 1, out_l, lse_l)
+    torch.cuda.synchronize()
+    return shape, group, plan, dict(q=q_l, k=k_l, v=v_l, out=out_l, lse=lse_l, logical=logical,
+                                    hist=hist)
+
+
+def run_decode(torch, ha, grp, synth, struct, args, device):
+    shape, group, plan, data = build_decode(torch, ha, grp, synth, struct, device, struct.workload)
+    kv_len = data["hist"] + 1
+    per_layer_bytes = [decode_layer_bytes(shape, layer.kind, kv_len) for layer in group.layers]
+    step_bytes = sum(per_layer_bytes)
+    append_bytes = len(group.layers) * struct.batch * kv_bytes_per_token(shape) * 2
+
+    stream = torch.cuda.current_stream()
+    graph = None
+    if not args.eager:
+        plan.run()                              # eager warm call before capture
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            plan.run()
+        torch.cuda.synchronize()
+
+    def step():
+        if graph is not None:
+            graph.replay()
+        else:
+            plan.run()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+
+    # Per-call durations with HIP events on the launch stream (eager launches).
+    evs = timed_events(torch, len(plan.calls))
+    sums = np.zeros(len(plan.calls))
+    reps = max(5, min(args.steps, 20))
+    for _ in range(reps):
+        plan.run_timed(evs, stream)
+        torch.cuda.synchronize()
+        sums += np.array([a.elapsed_time(b) for a, b in evs])
+    call_ms = sums / reps
+    by_label = dict(zip(plan.labels, call_ms.tolist()))
+    full_idx = [i for i, lab in enumerate(plan.labels) if lab.startswith("decode") and "full" in lab]
+    swa_idx = [i for i, lab in enumerate(plan.labels) if lab.startswith("decode") and "swa" in lab]
+    app_idx = [i for i, lab in enumerate(plan.labels) if lab.startswith("append")]
+    full_ms = float(np.mean(call_ms[full_idx]))
+    swa_ms = float(np.mean(call_ms[swa_idx]))
+    full_layer = [i for i, layer in enumerate(group.layers) if layer.kind == "full"][0]
+    swa_layer = [i for i, layer in enumerate(group.layers) if layer.kind == "swa"][0]
+    full_bytes = per_layer_bytes[full_layer]
+    swa_bytes = per_layer_bytes[swa_layer]
+    info = {
+        "step_bytes": step_bytes,
+        "append_bytes": append_bytes,
+        "full_decode_ms": full_ms,
+        "full_decode_gbs": full_bytes / full_ms / 1e6,
+        "swa_decode_ms": swa_ms,
+        "swa_decode_gbs": swa_bytes / swa_ms / 1e6,
+        "append_ms_avg": float(np.mean(call_ms[app_idx])),
+        "calls_ms": by_label,
+        "graph": graph is not None,
+        "splits_full": ha.hybrid_attn_decode_splits(shape, ha.HA_FULL, struct.batch, int(kv_len.max())),
+    }
+    return shape, group, data, dt, step_bytes, full_bytes, info
+
+
+def prefill_pass_flops(shape, kinds, batch, total, chunk):
+    """Algorithmic flops of one chunked prefill pass through the group."""
+    flops = {"swa": 0, "full": 0}
+    for c in range(total // chunk):
+        for kind in set(kinds):
+            pairs = visible_pairs_range(c * chunk, chunk, kind, shape.window) * batch * shape.num_q_heads
+            flops[kind] += pairs * 4 * shape.head_dim * kinds.count(kind)
+    return flops
+
+
+def run_chunked(torch, ha, grp, synth, args, device):
+    struct = synth.chunked_structure()
+    shape = ha.HeadShape(struct.shape.num_q_heads, struct.shape.num_kv_heads, struct.shape.head_dim,
+                         struct.shape.window)
+    b, total, chunk = struct.batch, int(struct.new[0]), struct.extra["chunk"]
+    nchunks = total // chunk
+    hq, hkv, d = shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    group = grp.HybridGroup(shape, torch.as_tensor(struct.ring_id, device=device), struct.num_rings,
+                            torch.as_tensor(struct.page_table, device=device), struct.num_pages)
+    t_chunk = b * chunk
+    # per layer, per chunk: rows of the chunk for all sequences, contiguous
+    qs, ks, vs = [], [], []
+    for li in range(len(group.layers)):
+        q = synth.normal_bf16((nchunks, t_chunk, hq, d), "chunked", li, synth.Q_VALUES, device)
+        k = synth.normal_bf16((nchunks, t_chunk, hkv, d), "chunked", li, synth.K_VALUES, device)
+        v = synth.normal_bf16((nchunks, t_chunk, hkv, d), "chunked", li, synth.V_VALUES, device)
+        qs.append(q)
+        ks.append(k)
+        vs.append(v)
+    outs = [torch.empty(t_chunk, hq, d, dtype=torch.float32, device=device) for _ in group.layers]
+    lses = [torch.empty(t_chunk, hq, dtype=torch.float32, device=device) for _ in group.layers]
+    cu = torch.as_tensor(np.arange(b + 1, dtype=np.int32) * chunk, device=device)
+    plans = []
+    for c in range(nchunks):
+        hist = torch.full((b,), c * chunk, dtype=torch.int32, device=device)
+        plans.append(grp.plan_prefill(group, [q[c] for q in qs], [k[c] for k in ks], [v[c] for v in vs],
+                                      hist, cu, chunk, outs, lses))
+    flops = prefill_pass_flops(shape, list(group.kinds), b, total, chunk)
+    total_flops = flops["swa"] + flops["full"]
+
+    def one_pass():
+        for pl in plans:
+            pl.run()
+
+    one_pass()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.prefill_passes):
+        one_pass()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.prefill_passes
+
+    stream = torch.cuda.current_stream()
+    call_ms = {}
+    for pl in plans:
+        evs = timed_events(torch, len(pl.calls))
+        pl.run_timed(evs, stream)
+        torch.cuda.synchronize()
+        for lab, (a, e) in zip(pl.labels, evs):
+            call_ms.setdefault(lab, []).append(a.elapsed_time(e))
+    full_ms = sum(v for lab, vals in call_ms.items() if lab.startswith("prefill") and "full" in lab for v in vals)
+    swa_ms = sum(v for lab, vals in call_ms.items() if lab.startswith("prefill") and "swa" in lab for v in vals)
+    n_swa = list(group.kinds).count("swa")
+    swa_bytes_per_layer = 0
+    for c in range(nchunks):
+        rows = t_chunk
+        swa_bytes_per_layer += rows * hq * d * 2 + rows * hq * d * 4 + rows * hq * 4 + rows * kv_bytes_per_token(shape)
+    res = {
+        "workload": f"chunked causal prefill: {b} sequences x {total} tokens in {chunk}-token chunks, "
+                    f"one 6:1 group (6 SWA W={shape.window} + 1 full), Hq/Hkv/D {hq}/{hkv}/{d}, bf16",
+        "pass_ms": dt * 1e3,
+        "tflops": total_flops / dt / 1e12,
+        "pct_mfma_peak": 100.0 * total_flops / dt / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "flops_per_pass": total_flops,
+        "full_layer_ms": full_ms,
+        "full_layer_tflops": flops["full"] / (full_ms * 1e-3) / 1e12,
+        "swa_layers_ms": swa_ms,
+        "swa_layer_gbs": swa_bytes_per_layer * n_swa / (swa_ms * 1e-3) / 1e9,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": flops["full"] / (full_ms * 1e-3) / 1e12,
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": flops["full"] / (full_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": None,
+        },
+    }
+    del qs, ks, vs, outs, lses, group
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(torch, shape, group, data, target_s):
+    """Time the fp64 oracle on whole sequences of the decode step (all 7
+    layers each) until about target_s seconds of CPU work, and express it in
+    the metric's unit (algorithmic bytes per second)."""
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from oracle.attention import attend
+
+    try:
+        import threadpoolctl
+        blas_threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    w = shape.window
+    hist = data["hist"]
+    b_total = len(hist)
+    done_bytes, done_s, seqs = 0, 0.0, 0
+    for b in range(b_total):
+        # host copies of this sequence's logical K/V (generator tensors, not pools)
+        per_layer = []
+        for li, layer in enumerate(group.layers):
+            k_hist, v_hist, start, cu = data["logical"][li]
+            k = torch.cat([k_hist[cu[b]:cu[b + 1]], data["k"][li][b:b + 1]]).float().cpu().numpy()
+            v = torch.cat([v_hist[cu[b]:cu[b + 1]], data["v"][li][b:b + 1]]).float().cpu().numpy()
+            q = data["q"][li][b:b + 1].float().cpu().numpy()
+            per_layer.append((layer.kind, k, v, q, int(hist[b] - start[b])))
+        t0 = time.perf_counter()
+        for kind, k, v, q, t in per_layer:
+            attend(q, k, v, [t], kind, w)
+        done_s += time.perf_counter() - t0
+        seqs += 1
+        for li, layer in enumerate(group.layers):
+            done_bytes += decode_layer_bytes(shape, layer.kind, [hist[b] + 1])
+        if done_s >= target_s:
+            break
+    return {
+        "value": done_bytes / done_s / 1e9,
+        "unit": "GB/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"{seqs} of {b_total} sequences of the decode step, all 7 layers "
+                  f"({done_s:.1f} s of fp64 NumPy, one row per sequence and layer)",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this library has no "
+              "multi-GPU path", file=sys.stderr)
+        return 2
+    import torch
+
+    import hybrid_sliding_window_gqa_amd as ha
+    import synth
+    from hybrid_sliding_window_gqa_amd import group as grp
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+
+    if args.workload == "chunked":
+        res = run_chunked(torch, ha, grp, synth, args, device)
+        print(json.dumps(res))
+        return 0
+
+    struct = {"decode": synth.decode_structure, "reuse": None, "ragged": synth.ragged_structure}[args.workload]
+    if struct is None:
+        print("reuse workload runs in the tests; bench covers decode / ragged / chunked", file=sys.stderr)
+        return 2
+    struct = struct()
+    log(f"[bench] workload={args.workload} building inputs")
+    shape, group, data, dt, step_bytes, full_bytes, info = run_decode(torch, ha, grp, synth, struct, args, device)
+    value = step_bytes / dt / 1e9
+    log(f"[bench] step {dt * 1e3:.3f} ms, {value:.1f} GB/s; full decode {info['full_decode_ms'] * 1e3:.1f} us "
+        f"({info['full_decode_gbs']:.0f} GB/s), swa decode {info['swa_decode_ms'] * 1e3:.1f} us "
+        f"({info['swa_decode_gbs']:.0f} GB/s)")
+    if args.workload == "decode":
+        wl = (f"decode: {struct.batch} sequences x {int(struct.hist[0])} cached tokens, one 6:1 group "
+              f"(6 SWA layers W={shape.window} ring + 1 full layer, 16-token pages, seeded page permutation), "
+              f"Hq/Hkv/D {shape.num_q_heads}/{shape.num_kv_heads}/{shape.head_dim}, 1 new token per sequence")
+    else:
+        wl = (f"ragged decode: {struct.batch} sequences, cached lengths 12xU[1K,64K] 8xU[64K,256K] "
+              f"4xU[256K,1M] (total {int(struct.hist.sum())}), one 6:1 group, split-K over full pages")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dt * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl, "global_batch": struct.batch, "seq_len": int(struct.hist.max()) + 1,
+                   "parallelism": "none (1 GPU)"},
+        "pct_peak_hbm": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "decode_detail": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in info.items()
+                          if k != "calls_ms"},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(info["full_decode_gbs"], 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(info["full_decode_gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "hybrid_attn_decode, full layer (decode_kernel<128,full> + split-K reduce)",
+            "bytes_per_launch": full_bytes,
+        },
+    }
+    if args.workload == "decode" and not args.no_prefill:
+        log("[bench] chunked prefill")
+        line["prefill"] = run_chunked(torch, ha, grp, synth, args, device)
+        log(f"[bench] prefill {line['prefill']['tflops']:.1f} TFLOP/s, full layer "
+            f"{line['prefill']['full_layer_tflops']:.1f} TFLOP/s")
+    if args.workload == "decode" and not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(torch, shape, group, data, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -64,14 +64,15 @@ class KvView:
 class SwaRingPool:
     """SWA pool of one layer: W slots per (ring, kv head), bfloat16.
 
-    K [rings, Hkv, W, D]; V [rings, Hkv, W/16, D, 16] (dim-major per 16-slot block)."""
+    K and V are [rings, Hkv, W/16, 16*D]: 16-slot blocks stored in the
+    library's matrix-core operand order (include/hybrid_attn.h)."""
 
     def __init__(self, shape: HeadShape, num_rings: int, device, fill: float | None = None):
         w, d, h = shape.window, shape.head_dim, shape.num_kv_heads
         self.shape = shape
         self.num_rings = num_rings
-        self.k = torch.empty(num_rings, h, w, d, dtype=torch.bfloat16, device=device)
-        self.v = torch.empty(num_rings, h, w // BLOCK, d, BLOCK, dtype=torch.bfloat16, device=device)
+        self.k = torch.empty(num_rings, h, w // BLOCK, BLOCK * d, dtype=torch.bfloat16, device=device)
+        self.v = torch.empty(num_rings, h, w // BLOCK, BLOCK * d, dtype=torch.bfloat16, device=device)
         if fill is not None:
             self.k.fill_(fill)
             self.v.fill_(fill)
@@ -88,14 +89,15 @@ class SwaRingPool:
 class FullPagePool:
     """Full pool of one layer: 16-token pages, bfloat16.
 
-    K [pages, Hkv, 16, D]; V [pages, Hkv, D, 16] (dim-major per page)."""
+    K and V are [pages, Hkv, 16*D]: each page is one 16-token block per kv
+    head in the library's matrix-core operand order (include/hybrid_attn.h)."""
 
     def __init__(self, shape: HeadShape, num_pages: int, device, fill: float | None = None):
         d, h = shape.head_dim, shape.num_kv_heads
         self.shape = shape
         self.num_pages = num_pages
-        self.k = torch.empty(num_pages, h, BLOCK, d, dtype=torch.bfloat16, device=device)
-        self.v = torch.empty(num_pages, h, d, BLOCK, dtype=torch.bfloat16, device=device)
+        self.k = torch.empty(num_pages, h, BLOCK * d, dtype=torch.bfloat16, device=device)
+        self.v = torch.empty(num_pages, h, BLOCK * d, dtype=torch.bfloat16, device=device)
         if fill is not None:
             self.k.fill_(fill)
             self.v.fill_(fill)
@@ -221,7 +223,7 @@ def hybrid_attn_decode_splits(shape: HeadShape, kind: int, batch: int, max_kv_le
 def hybrid_attn_prefill(shape: HeadShape, kv: KvView, hist_len: torch.Tensor, cu_new: torch.Tensor,
                         q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, max_new: int,
                         out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
-                        stream=None):
+                        workspace: torch.Tensor | None = None, stream=None):
     """Causal prefill of a chunk per sequence over pool history + the chunk itself.
 
     Returns (out float32 [T, Hq, D], lse float32 [T, Hq])."""
@@ -241,11 +243,15 @@ def hybrid_attn_prefill(shape: HeadShape, kv: KvView, hist_len: torch.Tensor, cu
         lse = torch.empty(t, hq, dtype=torch.float32, device=dev)
     _check(out, "out", (t, hq, d), torch.float32, dev)
     _check(lse, "lse", (t, hq), torch.float32, dev)
+    need = hybrid_attn_workspace_size(shape, kv.kind, False, b, t)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
     c_shape, c_view = shape.c(), kv.c()
     check(load().hybrid_attn_prefill(ctypes.byref(c_shape), ctypes.byref(c_view), hist_len.data_ptr(),
                                      cu_new.data_ptr(), b, t, int(max_new), q.data_ptr(), k_new.data_ptr(),
-                                     v_new.data_ptr(), dt, out.data_ptr(), lse.data_ptr(), None, 0,
-                                     _stream_ptr(stream)))
+                                     v_new.data_ptr(), dt, out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+                                     ws_bytes, _stream_ptr(stream)))
     return out, lse
 
 

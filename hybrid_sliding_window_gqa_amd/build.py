@@ -36,6 +36,8 @@ def common_flags() -> list[str]:
     return [
         "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # keep MFMA accumulators in VGPRs: no AGPR copies around the softmax rescale
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"),
     ]
 

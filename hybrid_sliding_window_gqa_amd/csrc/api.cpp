@@ -113,6 +113,12 @@ ha_status append_common(const ha_shape* shape, const ha_kv_view* view, int32_t w
   return hip_status(ha::launch_append(a, static_cast<hipStream_t>(stream)), "append launch");
 }
 
+size_t prefill_workspace(const ha::Geometry& geo, int batch, int num_tokens) {
+  if (batch <= 0 || num_tokens <= 0) return 0;
+  // K and V of every staged 16-token block, bf16
+  return static_cast<size_t>(ha::prefill_stage_blocks(num_tokens, batch)) * geo.hkv * 16 * geo.d * 2 * 2;
+}
+
 size_t decode_workspace(const ha::Geometry& geo, bool full, int batch, int max_kv_len, int num_splits) {
   if (!full) return 0;
   const int sb = ha::decode_split_blocks(true, geo.window, max_kv_len, batch, geo.hkv, num_splits);
@@ -170,8 +176,6 @@ ha_status hybrid_attn_prefill(const ha_shape* shape, const ha_kv_view* kv, const
                               const int32_t* cu_new, int32_t batch, int32_t num_tokens, int32_t max_new,
                               const void* q, const void* k_new, const void* v_new, int32_t in_dtype, float* out,
                               float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   ha::Geometry geo;
   ha_status st = check_shape(shape, &geo);
   if (st != HA_OK) return st;
@@ -184,6 +188,9 @@ ha_status hybrid_attn_prefill(const ha_shape* shape, const ha_kv_view* kv, const
   if (!hist_len || !cu_new) return fail(HA_ERR_NULL, "hist_len or cu_new is NULL");
   if (!q || !k_new || !v_new) return fail(HA_ERR_NULL, "q, k_new or v_new is NULL");
   if (!out || !lse) return fail(HA_ERR_NULL, "out or lse is NULL");
+  const size_t need = prefill_workspace(geo, batch, num_tokens);
+  if (!workspace || workspace_bytes < need)
+    return fail(HA_ERR_WORKSPACE, "prefill needs %zu workspace bytes, got %zu", need, workspace ? workspace_bytes : 0);
   ha::PrefillArgs a{};
   a.geo = geo;
   a.full = kv->kind == HA_FULL;
@@ -203,6 +210,8 @@ ha_status hybrid_attn_prefill(const ha_shape* shape, const ha_kv_view* kv, const
   a.in_f32 = in_dtype == HA_F32;
   a.out = out;
   a.lse = lse;
+  a.stage = static_cast<uint16_t*>(workspace);
+  a.stage_blocks = ha::prefill_stage_blocks(num_tokens, batch);
   return hip_status(ha::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
 }
 
@@ -253,7 +262,7 @@ size_t hybrid_attn_workspace_size(const ha_shape* shape, int32_t kind, int32_t d
   ha::Geometry geo;
   if (check_shape(shape, &geo) != HA_OK) return 0;
   if ((kind != HA_SWA && kind != HA_FULL) || batch < 0 || max_kv_len < 0 || num_splits < 0) return 0;
-  if (!decode) return 0;
+  if (!decode) return prefill_workspace(geo, batch, max_kv_len);
   return decode_workspace(geo, kind == HA_FULL, batch, max_kv_len, num_splits);
 }
 

@@ -8,8 +8,9 @@
 // section "双池分治与三级缓存的工程实现").
 //
 // One thread moves 8 channels (16 bytes of bfloat16) of one token row of one
-// kv head: the K row is written token-major with one 16-byte store, the V
-// row dim-major inside its 16-token block (8 two-byte stores, 32 bytes apart).
+// kv head into its 16-token block, in the blocks' matrix-core operand order
+// (common.hpp): the K channels form one 16-byte unit (one store), the V
+// channels land in 8 different units (8 two-byte stores).
 // Appends are a few KiB per decode step and a few hundred MiB per prefill
 // chunk, far below the attention traffic, so they favour simplicity.
 #include "common.hpp"
@@ -64,15 +65,15 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 
   const int64_t src = (static_cast<int64_t>(tok) * hkv + g) * d + c * 8;
   const u32x4 kv = load8_as_bf16<kF32>(a.k_new, src);
-  *reinterpret_cast<u32x4*>(a.k_pool + block_base + static_cast<int64_t>(in_blk) * d + c * 8) = kv;
+  *reinterpret_cast<u32x4*>(a.k_pool + block_base + k_elem(in_blk, c * 8)) = kv;
 
   const u32x4 vv = load8_as_bf16<kF32>(a.v_new, src);
-  uint16_t* vdst = a.v_pool + block_base + static_cast<int64_t>(c * 8) * kBlock + in_blk;
+  uint16_t* vblk = a.v_pool + block_base;
   const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    vdst[(2 * j) * kBlock] = static_cast<uint16_t>(w4[j] & 0xffffu);
-    vdst[(2 * j + 1) * kBlock] = static_cast<uint16_t>(w4[j] >> 16);
+    vblk[v_elem(in_blk, c * 8 + 2 * j)] = static_cast<uint16_t>(w4[j] & 0xffffu);
+    vblk[v_elem(in_blk, c * 8 + 2 * j + 1)] = static_cast<uint16_t>(w4[j] >> 16);
   }
 }
 

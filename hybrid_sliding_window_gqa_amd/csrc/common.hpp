@@ -24,6 +24,23 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = 16;         // tokens per page / ring block
+
+// In-block layout of the pools (and of the prefill staging blocks): a block
+// of 16 tokens x D channels of one kv head is 16*D bfloat16 stored as 16-byte
+// units in matrix-core operand order, so a wavefront loads an operand set
+// with one fully contiguous 1 KiB read per instruction.
+//   K unit (m, q, c) = m*64 + q*16 + c  holds K[token c][32m + 8q .. +7]
+//   V unit (p, q, c) = p*64 + q*16 + c  holds V[tokens 4q..4q+3][32p + c]
+//                                         then V[tokens 4q..4q+3][32p + 16 + c]
+// Lane l = 16q + c of a wave reads unit (., q, c): for K that is the
+// v_mfma_f32_16x16x32_bf16 A operand of S^T = K Q^T, for V the two
+// v_mfma_f32_16x16x16_bf16 A operands (dim tiles 2p, 2p+1) of O^T = V^T P^T.
+__host__ __device__ constexpr int64_t k_elem(int token, int dim) {
+  return (static_cast<int64_t>(dim / 32) * 64 + ((dim % 32) / 8) * 16 + token) * 8 + dim % 8;
+}
+__host__ __device__ constexpr int64_t v_elem(int token, int dim) {
+  return (static_cast<int64_t>(dim / 32) * 64 + (token / 4) * 16 + dim % 16) * 8 + ((dim % 32) / 16) * 4 + token % 4;
+}
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -66,6 +83,20 @@ __device__ __forceinline__ u32x4 load8_as_bf16(const void* src, int64_t elem_off
   } else {
     return *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + elem_off);
   }
+}
+
+// Raw buffer access (gfx9 descriptor word 3 = 0x00020000). A descriptor with
+// num_records = 0 makes every lane out of range: the load returns zeros and
+// issues no memory traffic, so invalid blocks need no branch around the load
+// and the count of outstanding loads stays the same on every path.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

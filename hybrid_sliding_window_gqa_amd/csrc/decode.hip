@@ -6,21 +6,27 @@
 // ring; full layers read all pages of the sequence, split over workgroups
 // (split-K) when sequences are long, then merged by decode_reduce_kernel.
 //
-// Workgroup = 4 wavefronts = one (split, kv head, sequence). Each wave takes
-// every fourth 16-token block of the split; for each block it
-//   * loads K (16 keys x D, token-major) straight into v_mfma_f32_16x16x32_bf16
-//     A operands: lane (q, c) reads key c, channels 32m + 8q .. +7 -- 64
-//     contiguous bytes per key row per instruction;
+// Workgroup = one (split, kv head, sequence): 4 wavefronts for full layers,
+// 8 for SWA layers (one ring block per wave, so a W = 128 ring is fetched in
+// a single round trip). Wave w takes blocks w, w+NW, w+2NW, ... of the split
+// and keeps two of them in flight in ping-pong register buffers (no register
+// copies, so a block's loads are only waited for right before it is
+// consumed). For each 16-token block it
+//   * loads K straight into v_mfma_f32_16x16x32_bf16 A operands (lane (q, c):
+//     key c, channels 32m + 8q .. +7); the pools keep blocks in operand
+//     order, so each load instruction reads 1 KiB contiguous;
 //   * computes S^T = K Q^T (16 keys x 16 query heads of the GQA group; heads
 //     beyond the group are zero padding);
 //   * runs an exp2-domain online softmax per head: the 4 keys a lane holds
 //     plus two cross-lane steps;
-//   * loads V^T (dim-major block) straight into v_mfma_f32_16x16x16_bf16 A
-//     operands (8 contiguous bytes per lane) and accumulates O^T += V^T P^T,
-//     where P^T is the softmax tile in exactly the accumulator layout.
-// The next block's operands are loaded before the current one is consumed.
-// The four waves merge through LDS; a workgroup writes either the final
-// row (one split) or a partial (o, lse) for the reduce kernel.
+//   * loads V^T straight into v_mfma_f32_16x16x16_bf16 A operands (16 bytes
+//     per lane = two dim tiles, again 1 KiB contiguous per instruction) and
+//     accumulates O^T += V^T P^T, where P^T is the softmax tile in exactly the
+//     accumulator layout.
+// Page ids are scalar loads issued two blocks ahead of their use. The four
+// waves merge through LDS; a workgroup writes either the final row (one
+// split) or a partial (o, lse) for the reduce kernel.
+#include <climits>
 #include <cmath>
 
 #include "common.hpp"
@@ -30,7 +36,8 @@ namespace ha {
 
 namespace {
 
-constexpr int kWaves = 4;
+template <bool kFull>
+constexpr int waves_per_wg() { return kFull ? 4 : 8; }
 
 template <int D>
 struct BlockOps {
@@ -38,24 +45,77 @@ struct BlockOps {
   u32x2 v[D / 16];
 };
 
+// Loads one block's K and V^T operands; base < 0 loads zeros without traffic.
 template <int D>
 __device__ __forceinline__ void load_block(BlockOps<D>& ops, const uint16_t* kp, const uint16_t* vp,
                                            int64_t base, int q4, int c16) {
+  const bool ok = base >= 0;
+  const int64_t b0 = ok ? base : 0;
+  const uint32_t bytes = ok ? kBlock * D * 2 : 0;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + b0, bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + b0, bytes);
+  const int lane = 16 * q4 + c16;
 #pragma unroll
-  for (int m = 0; m < D / 32; ++m)
-    ops.k[m] = *reinterpret_cast<const u32x4*>(kp + base + c16 * D + 32 * m + 8 * q4);
+  for (int m = 0; m < D / 32; ++m) ops.k[m] = buf_load16(rk, 16 * (64 * m + lane));
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t)
-    ops.v[t] = *reinterpret_cast<const u32x2*>(vp + base + (16 * t + c16) * kBlock + 4 * q4);
+  for (int p = 0; p < D / 32; ++p) {
+    const u32x4 w = buf_load16(rv, 16 * (64 * p + lane));
+    ops.v[2 * p] = u32x2{w.x, w.y};
+    ops.v[2 * p + 1] = u32x2{w.z, w.w};
+  }
+}
+
+// One 16-token block: scores, masking of keys past `t` (when `partial`),
+// online-softmax update and the P.V accumulation.
+template <int D>
+__device__ __forceinline__ void consume_block(BlockOps<D>& ops, const u32x4* qop, int first_key, int t,
+                                              bool partial, float sl2, float& m_run, float& l_run, f32x4* o,
+                                              int q4) {
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < KS; ++m) s = mfma_16x16x32(ops.k[m], qop[m], s);
+  if (partial) {
+    uint32_t keep[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool ok = first_key + 4 * q4 + r <= t;
+      keep[r] = ok ? 0xffffu : 0u;
+      s[r] = ok ? s[r] : -INFINITY;
+    }
+    const uint32_t mlo = keep[0] | (keep[1] << 16);
+    const uint32_t mhi = keep[2] | (keep[3] << 16);
+#pragma unroll
+    for (int d = 0; d < DT; ++d) {
+      ops.v[d].x &= mlo;
+      ops.v[d].y &= mhi;
+    }
+  }
+  const float tmax = group4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))) * sl2;
+  const float m_new = fmaxf(m_run, tmax);
+  const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+  const float alpha = fast_exp2(m_run - m_use);
+  float p[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s[r] * sl2 - m_use);
+  l_run = l_run * alpha + (p[0] + p[1]) + (p[2] + p[3]);
+  m_run = m_new;
+#pragma unroll
+  for (int d = 0; d < DT; ++d) o[d] *= alpha;
+  const u32x2 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+#pragma unroll
+  for (int d = 0; d < DT; ++d) o[d] = mfma_16x16x16(ops.v[d], pb, o[d]);
 }
 
 }  // namespace
 
 template <int D, bool kFull, bool kQF32>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   constexpr int kPad = 4;
+  constexpr int kWaves = waves_per_wg<kFull>();
   __shared__ float sm_o[kWaves][16][D + kPad];
   __shared__ float sm_m[kWaves][16];
   __shared__ float sm_l[kWaves][16];
@@ -107,14 +167,20 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
   const int32_t* page_row = a.table + static_cast<int64_t>(b) * a.table_stride;
 
-  auto block_base = [&](int i) -> int64_t {
+  // Page id of block `i` and element offset of its K/V (-1: nothing to read).
+  auto page_of = [&](int i) -> int { return (i < last) ? page_row[i] : -1; };
+  auto base_of = [&](int i, int pg) -> int64_t {
     if constexpr (kFull) {
-      const int pg = page_row[i];
-      if (pg < 0 || pg >= a.num_blocks) return -1;
+      if (i >= last || pg < 0 || pg >= a.num_blocks) return -1;
       return (static_cast<int64_t>(pg) * hkv + g) * kBlock * D;
     } else {
+      if (i >= last) return -1;
       return ((static_cast<int64_t>(ring) * hkv + g) * W + kBlock * i) * D;
     }
+  };
+  auto is_partial = [&](int i) -> bool {
+    if constexpr (kFull) return kBlock * i + kBlock - 1 > t;
+    else return (t < W - 1) && (kBlock * i + kBlock - 1 > t);
   };
 
   // Q^T as the B operand: column c16 = query head g*G + c16 (zero past the group).
@@ -136,62 +202,42 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < DT; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  int i = first + wave;
-  int64_t base_cur = (i < last) ? block_base(i) : -1;
-  int64_t base_nxt = (i + kWaves < last) ? block_base(i + kWaves) : -1;
-  BlockOps<D> cur, nxt;
-  if (base_cur >= 0) load_block<D>(cur, a.k_pool, a.v_pool, base_cur, q4, c16);
-
-  for (; i < last; i += kWaves) {
-    if (base_nxt >= 0) load_block<D>(nxt, a.k_pool, a.v_pool, base_nxt, q4, c16);
-    const int64_t base_nn = (i + 2 * kWaves < last) ? block_base(i + 2 * kWaves) : -1;
-
-    if (base_cur >= 0) {
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int m = 0; m < KS; ++m) s = mfma_16x16x32(cur.k[m], qop[m], s);
-
-      // Keys this lane holds: 4*q4 + r of block i.
-      bool partial;
-      if constexpr (kFull) partial = (kBlock * i + kBlock - 1 > t);
-      else partial = (t < W - 1) && (kBlock * i + kBlock - 1 > t);
-      if (partial) {
-        uint32_t keep[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = kBlock * i + 4 * q4 + r;  // position (full) or slot (ring, t < W-1)
-          const bool ok = key <= t;
-          keep[r] = ok ? 0xffffu : 0u;
-          if (!ok) s[r] = -INFINITY;
-        }
-        const uint32_t mlo = keep[0] | (keep[1] << 16);
-        const uint32_t mhi = keep[2] | (keep[3] << 16);
-#pragma unroll
-        for (int d = 0; d < DT; ++d) {
-          cur.v[d].x &= mlo;
-          cur.v[d].y &= mhi;
-        }
-      }
-
-      const float tmax = group4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))) * sl2;
-      const float m_new = fmaxf(m_run, tmax);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s[r] * sl2 - m_use);
-      l_run = l_run * alpha + (p[0] + p[1]) + (p[2] + p[3]);
-      m_run = m_new;
-#pragma unroll
-      for (int d = 0; d < DT; ++d) o[d] *= alpha;
-      const u32x2 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-#pragma unroll
-      for (int d = 0; d < DT; ++d) o[d] = mfma_16x16x16(cur.v[d], pb, o[d]);
-    }
-    cur = nxt;
-    base_cur = base_nxt;
-    base_nxt = base_nn;
+  // Blocks of this wave: first + wave + 4k. Buffer A holds even k, B odd k.
+  constexpr int kStep = kWaves;
+  int ia = first + wave;
+  int ib = ia + kStep;
+  int pg_a = 0, pg_b = 0, pg_a2 = 0, pg_b2 = 0;
+  if constexpr (kFull) {
+    pg_a = page_of(ia);
+    pg_b = page_of(ib);
   }
+  int64_t base_a = base_of(ia, pg_a);
+  int64_t base_b = base_of(ib, pg_b);
+  BlockOps<D> A, B;
+  load_block<D>(A, a.k_pool, a.v_pool, base_a, q4, c16);
+  load_block<D>(B, a.k_pool, a.v_pool, base_b, q4, c16);
+  if constexpr (kFull) {
+    pg_a2 = page_of(ia + 2 * kStep);
+    pg_b2 = page_of(ib + 2 * kStep);
+  }
+  // Pairs (A, B) in a loop with a fixed trip count and no early exit, so the
+  // loads in flight at the loop head are the same on every path; an odd last
+  // block is consumed from A after the loop. Loads past `last` read nothing.
+  const int nmine = (last > ia) ? (last - ia + kStep - 1) / kStep : 0;
+  for (int k = 0; k + 1 < nmine; k += 2) {
+    if (base_a >= 0) consume_block<D>(A, qop, kBlock * ia, t, is_partial(ia), sl2, m_run, l_run, o, q4);
+    ia += 2 * kStep;
+    base_a = base_of(ia, pg_a2);
+    load_block<D>(A, a.k_pool, a.v_pool, base_a, q4, c16);
+    if constexpr (kFull) pg_a2 = page_of(ia + 2 * kStep);
+    if (base_b >= 0) consume_block<D>(B, qop, kBlock * ib, t, is_partial(ib), sl2, m_run, l_run, o, q4);
+    ib += 2 * kStep;
+    base_b = base_of(ib, pg_b2);
+    load_block<D>(B, a.k_pool, a.v_pool, base_b, q4, c16);
+    if constexpr (kFull) pg_b2 = page_of(ib + 2 * kStep);
+  }
+  if ((nmine & 1) && base_a >= 0)
+    consume_block<D>(A, qop, kBlock * ia, t, is_partial(ia), sl2, m_run, l_run, o, q4);
 
   // Merge the four waves.
   l_run = group4_sum(l_run);
@@ -232,42 +278,66 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 }
 
 // a8: lse = log2 sum_s 2^lse_s; o = sum_s 2^(lse_s - lse) o_s (log2 domain),
-// written back in natural-log units. One workgroup per (query head, sequence).
+// written back in natural-log units. One workgroup per (kv head, sequence):
+// thread e handles output element e of the G*D outputs of the group.
 template <int D>
-__global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a) {
-  const int h = blockIdx.x;
+__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
+  const int g = blockIdx.x;
   const int b = blockIdx.y;
   const int len = a.kv_len[b];
   if (len <= 0) return;
   const int nblk = min((len + kBlock - 1) / kBlock, a.table_stride);
   const int nsplit = min((nblk + a.split_blocks - 1) / a.split_blocks, a.splits);
   if (nsplit <= 1) return;
-  const int64_t row = static_cast<int64_t>(b) * a.geo.hq + h;
-  const float* pl = a.part_lse + row * a.splits;
-  float mx = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, pl[s]);
-  const float mu = (mx == -INFINITY) ? 0.0f : mx;
-  float l = 0.0f;
-  for (int s = 0; s < nsplit; ++s) l += fast_exp2(pl[s] - mu);
-  const float inv = 1.0f / l;
-  const float* po = a.part_o + row * a.splits * D;
-  for (int dd = threadIdx.x; dd < D; dd += 64) {
-    float acc = 0.0f;
-    for (int s = 0; s < nsplit; ++s) acc += fast_exp2(pl[s] - mu) * po[static_cast<int64_t>(s) * D + dd];
-    a.out[row * D + dd] = acc * inv;
+  const int G = a.geo.group;
+  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
+    const int h = e / D;
+    const int dd = e - h * D;
+    const int64_t row = static_cast<int64_t>(b) * a.geo.hq + g * G + h;
+    const float* pl = a.part_lse + row * a.splits;
+    const float* po = a.part_o + row * a.splits * D + dd;
+    float mx = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, pl[s]);
+    const float mu = (mx == -INFINITY) ? 0.0f : mx;
+    float l = 0.0f, acc = 0.0f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float w = fast_exp2(pl[s] - mu);
+      l += w;
+      acc += w * po[static_cast<int64_t>(s) * D];
+    }
+    a.out[row * D + dd] = acc / l;
+    if (dd == 0) a.lse[row] = (mu + fast_log2(l)) * kLn2;
   }
-  if (threadIdx.x == 0) a.lse[row] = (mu + fast_log2(l)) * kLn2;
 }
 
+// Split policy. Every split of the longest sequence is equally long, and the
+// split count is chosen to minimise (workgroup rounds) x (blocks per
+// workgroup + a fixed cost), where a round is what the chip runs at once
+// (256 CUs x 3 resident decode workgroups on MI355X). Equal workgroups and
+// whole rounds avoid a long tail of partly idle CUs. Workgroups are capped at
+// 256 blocks (2 MiB of K/V) so ragged batches still spread over the chip.
 int decode_split_blocks(bool full, int window, int max_kv_len, int batch, int hkv, int requested_splits) {
   if (!full) return window / kBlock;
   const int nblk = (max(max_kv_len, 1) + kBlock - 1) / kBlock;
   if (requested_splits > 0) return max(1, (nblk + requested_splits - 1) / requested_splits);
-  // Aim for a few thousand workgroups overall, 4..16 blocks per wave.
-  const int64_t total = static_cast<int64_t>(nblk) * max(batch, 1) * max(hkv, 1);
-  int64_t sb = (total + 4095) / 4096;
-  sb = sb < 16 ? 16 : (sb > 64 ? 64 : sb);
-  return static_cast<int>(sb);
+  constexpr int64_t kResident = 256 * 3;
+  constexpr int kMaxBlocks = 256, kMinBlocks = 4, kFixedCost = 4;
+  const int64_t pairs = static_cast<int64_t>(max(batch, 1)) * max(hkv, 1);
+  const int s_lo = max(1, (nblk + kMaxBlocks - 1) / kMaxBlocks);
+  const int s_hi = min(max(1, nblk / kMinBlocks), s_lo + 512);
+  int best_sb = (nblk + s_lo - 1) / s_lo;
+  int64_t best_cost = INT64_MAX;
+  for (int s = s_lo; s <= s_hi; ++s) {
+    const int sb = (nblk + s - 1) / s;
+    const int64_t s_eff = (nblk + sb - 1) / sb;
+    const int64_t rounds = (pairs * s_eff + kResident - 1) / kResident;
+    const int64_t cost = rounds * (sb + kFixedCost);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best_sb = sb;
+    }
+  }
+  return best_sb;
 }
 
 int decode_num_splits(bool full, int window, int max_kv_len, int split_blocks) {
@@ -279,18 +349,19 @@ int decode_num_splits(bool full, int window, int max_kv_len, int split_blocks) {
 template <int D>
 static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.full ? a.splits : 1, a.geo.hkv, a.batch);
-  const dim3 block(256);
   if (a.full) {
+    const dim3 block(64 * waves_per_wg<true>());
     if (a.q_f32) hipLaunchKernelGGL((decode_kernel<D, true, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((decode_kernel<D, true, false>), grid, block, 0, stream, a);
   } else {
+    const dim3 block(64 * waves_per_wg<false>());
     if (a.q_f32) hipLaunchKernelGGL((decode_kernel<D, false, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((decode_kernel<D, false, false>), grid, block, 0, stream, a);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (a.full && a.splits > 1) {
-    hipLaunchKernelGGL(decode_reduce_kernel<D>, dim3(a.geo.hq, a.batch), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(decode_reduce_kernel<D>, dim3(a.geo.hkv, a.batch), dim3(256), 0, stream, a);
     err = hipGetLastError();
   }
   return err;

@@ -69,7 +69,14 @@ struct PrefillArgs {
   bool in_f32;
   float* out;
   float* lse;
+  uint16_t* stage;        // workspace: chunk K/V re-laid as 16-token blocks
+  int64_t stage_blocks;   // blocks the workspace holds
 };
+
+// Workspace of hybrid_attn_prefill: the chunk's K and V in 16-token blocks
+// (same layout as a pool page), sequence b's blocks starting at
+// ceil(cu_new[b] / 16) + b.
+int64_t prefill_stage_blocks(int num_tokens, int batch);
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -2,28 +2,32 @@
 //
 // A chunk of new tokens per sequence attends to the sequence's history in the
 // pool (the SWA ring's last W-1 positions, or every page of the Full pool)
-// and causally to the chunk itself, read from k_new / v_new. SWA layers cut
-// the attended range from the whole sequence to the window (youleyou.com
+// and causally to the chunk itself. SWA layers cut the attended range from
+// the whole sequence to the window (youleyou.com
 // "小米MiMo首次公开模型推理系统全链路优化降价99%", section 1
 // "为什么选择 Hybrid SWA 架构"); chunked prefill is what the serving stack runs
 // for long requests (blog.hotdry.top 2026-06-09, section "PD 分离与长度分桶").
 //
-// Workgroup = 4 wavefronts = 128 rows of one (sequence, kv head), where a row
-// is a (query position, query head of the GQA group) pair: the whole group
-// shares every K/V tile, so K/V are read once per group instead of once per
-// query head. Each wave owns 32 rows (two 16-row MFMA column groups).
-// Keys stream in 64-key tiles (four 16-token blocks) staged in LDS with two
-// buffers: the next tile's global loads are in flight while the current tile
-// is consumed.
-//   K tile   [64 keys][D]   padded rows -> conflict-free 16-byte A-operand reads
-//   V^T tile [4][D][16]     dim-major blocks, rows padded to 40 bytes ->
-//                           conflict-free 8-byte A-operand reads
-// Per tile and wave: S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (Q^T held in
-// registers), exp2-domain online softmax per row (in-lane over 16 scores plus
-// two cross-lane steps), P^T cast to bf16 in the accumulator layout, then
-// O^T += V^T P^T with v_mfma_f32_16x16x16_bf16. Tiles that every row of a
-// wave sees completely skip the masking; tiles no row of the wave sees are
-// skipped.
+// Two kernels per call:
+//  1. stage_chunk_kernel re-lays the chunk's K/V (bf16 or f32) into 16-token
+//     blocks in the workspace, in exactly the pools' block format (matrix-core
+//     operand order, common.hpp), zero-padded past the chunk's end. Every key
+//     source then looks the same to the attention kernel: a K block and a V
+//     block of 16*D bf16 each.
+//  2. prefill_kernel. Workgroup = 4 wavefronts = 128 rows of one (sequence,
+//     kv head); a row is a (query position, query head of the GQA group) pair,
+//     so the whole group shares every K/V tile. Each wave owns 32 rows (two
+//     16-row MFMA column groups). Keys stream in 64-key tiles of four blocks;
+//     wave w stages block w of the next tile (global -> registers -> LDS)
+//     while the current tile is consumed, so one barrier per tile suffices.
+//     The LDS tiles are plain copies of the four blocks; since blocks are in
+//     operand order, every operand read is one ds_read_b128 at 16 * lane:
+//     consecutive lanes, consecutive 16 bytes, no bank conflicts.
+//     Per tile and wave: S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (Q^T held in
+//     registers), exp2-domain online softmax per row (16 scores in-lane plus
+//     two cross-lane steps), P^T cast to bf16 in the accumulator layout, then
+//     O^T += V^T P^T on v_mfma_f32_16x16x16_bf16. Tiles a wave sees completely
+//     skip masking; tiles no row of the wave sees are skipped.
 //
 // Grid order: workgroup i runs on XCD i % 8 (round-robin dispatch). All query
 // blocks of one (sequence, kv head) pair are placed on the same XCD, so the
@@ -43,47 +47,97 @@ constexpr int kRowGroups = kRowsPerWave / 16;
 constexpr int kWaves = 4;
 constexpr int kRowsPerWg = kRowsPerWave * kWaves;  // 128
 constexpr int kTileKeys = 64;
-constexpr int kTileBlocks = kTileKeys / kBlock;   // 4
-constexpr int kVRow = 20;                          // bf16 per padded V^T row (40 bytes)
+constexpr int kTileBlocks = kTileKeys / kBlock;   // 4 == kWaves: one block per wave
 constexpr int kXcds = 8;
+static_assert(kTileBlocks == kWaves, "each wave stages one block of a tile");
 
 template <int D>
 struct Smem {
-  static constexpr int kKRow = D + 8;  // bf16 per padded K row
-  uint16_t k[2][kTileKeys * kKRow];
-  uint16_t v[2][kTileBlocks * D * kVRow];
+  uint16_t k[2][kTileBlocks * kBlock * D];
+  uint16_t v[2][kTileBlocks * kBlock * D];
   int32_t pos[2][kTileKeys];
 };
 
-// Per-thread staging registers for one tile: D/32 16-byte chunks of K and of V.
-template <int D>
-struct Stage {
-  u32x4 k[D / 32];
-  u32x4 v[D / 32];
-};
-
-// Zero all but the first `nv` of the 8 bfloat16 values in `v` (nv may be <0 or >8).
-__device__ __forceinline__ u32x4 keep_first_bf16(u32x4 v, int nv) {
-  if (nv >= 8) return v;
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t lo = (2 * j < nv) ? 0x0000ffffu : 0u;
-    const uint32_t hi = (2 * j + 1 < nv) ? 0xffff0000u : 0u;
-    w[j] &= lo | hi;
-  }
-  return u32x4{w[0], w[1], w[2], w[3]};
+// V unit of lane group q holds tokens 4q..4q+3 (for two channels): zero the
+// tokens at index >= nv.
+__device__ __forceinline__ u32x4 keep_tokens_v(u32x4 v, int q, int nv) {
+  const int first = 4 * q;
+  if (first + 4 <= nv) return v;
+  const uint32_t m0 = (first + 0 < nv ? 0x0000ffffu : 0u) | (first + 1 < nv ? 0xffff0000u : 0u);
+  const uint32_t m1 = (first + 2 < nv ? 0x0000ffffu : 0u) | (first + 3 < nv ? 0xffff0000u : 0u);
+  return u32x4{v.x & m0, v.y & m1, v.z & m0, v.w & m1};
 }
 
 }  // namespace
 
+int64_t prefill_stage_blocks(int num_tokens, int batch) {
+  return (static_cast<int64_t>(num_tokens) + kBlock - 1) / kBlock + batch;
+}
+
+// ---- 1. stage the chunk's K/V as 16-token blocks ----
+// Grid (ceil(max_new/16), batch); one workgroup per (sequence, block), all kv heads.
+template <int D, bool kF32>
+__global__ __launch_bounds__(256) void stage_chunk_kernel(PrefillArgs a) {
+  constexpr int CPR = D / 8;                   // 16-byte chunks per row
+  __shared__ uint16_t tile[kBlock][D + 2];     // one head's 16 V rows
+  const int b = blockIdx.y;
+  const int i = blockIdx.x;
+  const int tok0 = a.cu_new[b];
+  const int n = min(a.cu_new[b + 1], a.num_tokens) - tok0;
+  if (tok0 < 0 || kBlock * i >= n) return;
+  const int64_t blk = (tok0 + kBlock - 1) / kBlock + b + i;
+  if (blk >= a.stage_blocks) return;
+  const int hkv = a.geo.hkv;
+  const int64_t blk_elems = static_cast<int64_t>(kBlock) * D;
+  uint16_t* ws_k = a.stage + blk * hkv * blk_elems;
+  uint16_t* ws_v = a.stage + (a.stage_blocks + blk) * hkv * blk_elems;
+  const int tid = threadIdx.x;
+  for (int g = 0; g < hkv; ++g) {
+    // K rows (and V rows into LDS): thread -> (key, chunk)
+    for (int e = tid; e < kBlock * CPR; e += blockDim.x) {
+      const int key = e / CPR;
+      const int col = e - key * CPR;
+      const int ci = kBlock * i + key;
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (ci < n) {
+        const int64_t off = (static_cast<int64_t>(tok0 + ci) * hkv + g) * D + col * 8;
+        kv = load8_as_bf16<kF32>(a.k_new, off);
+        vv = load8_as_bf16<kF32>(a.v_new, off);
+      }
+      *reinterpret_cast<u32x4*>(ws_k + g * blk_elems + k_elem(key, col * 8)) = kv;
+      const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        tile[key][col * 8 + 2 * j] = static_cast<uint16_t>(w4[j] & 0xffffu);
+        tile[key][col * 8 + 2 * j + 1] = static_cast<uint16_t>(w4[j] >> 16);
+      }
+    }
+    __syncthreads();
+    // V units: thread e -> unit (p, q, c): tokens 4q..4q+3 of channels 32p+c, 32p+16+c
+    for (int e = tid; e < 2 * D; e += blockDim.x) {
+      const int p = e / 64;
+      const int q = (e / 16) & 3;
+      const int c = e & 15;
+      uint32_t w4[4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int ch = 32 * p + 16 * h + c;
+        w4[2 * h] = static_cast<uint32_t>(tile[4 * q][ch]) | (static_cast<uint32_t>(tile[4 * q + 1][ch]) << 16);
+        w4[2 * h + 1] = static_cast<uint32_t>(tile[4 * q + 2][ch]) | (static_cast<uint32_t>(tile[4 * q + 3][ch]) << 16);
+      }
+      *reinterpret_cast<u32x4*>(ws_v + g * blk_elems + 8 * e) = u32x4{w4[0], w4[1], w4[2], w4[3]};
+    }
+    __syncthreads();
+  }
+}
+
+// ---- 2. attention ----
 template <int D, bool kFull, bool kF32>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int KS = D / 32;            // QK^T reduction steps
   constexpr int DT = D / 16;            // output dim tiles
-  constexpr int CPR = D / 8;            // 16-byte chunks per key row
-  constexpr int CPT = D / 32;           // chunks per thread per tile (K and V each)
-  constexpr int KROW = Smem<D>::kKRow;
+  constexpr int CPL = D / 32;           // 16-byte units per lane of one block
+  constexpr int kBlk = kBlock * D;      // bf16 per block
   __shared__ Smem<D> sm;
 
   const int tid = threadIdx.x;
@@ -104,9 +158,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int qb_max = (a.max_new + QB - 1) / QB;
   const int lin = blockIdx.x;
   const int xcd = lin % kXcds;
-  const int j = lin / kXcds;
-  const int pair = (j % ppx) * kXcds + xcd;
-  const int qblk = qb_max - 1 - j / ppx;
+  const int jj = lin / kXcds;
+  const int pair = (jj % ppx) * kXcds + xcd;
+  const int qblk = qb_max - 1 - jj / ppx;
   if (pair >= npairs || qblk < 0) return;
   const int b = pair / hkv;
   const int g = pair - b * hkv;
@@ -118,19 +172,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int hist = max(a.hist_len[b], 0);
   const int i_end = min(n, i0 + QB);      // one past the last chunk index
   const int t_first = hist + i0;
+  const int64_t stage_blk0 = (tok0 + kBlock - 1) / kBlock + b;
 
   // ---- tile list: history tiles, then chunk tiles ----
   int n_hist_tiles = 0;
   int ring = -1;
   const int32_t* page_row = a.table + static_cast<int64_t>(b) * a.table_stride;
+  int hist_blocks = 0;
   if constexpr (kFull) {
-    const int nblk = (hist + kBlock - 1) / kBlock;
-    n_hist_tiles = (nblk + kTileBlocks - 1) / kTileBlocks;
-    // loads below also require the logical block to lie inside the page-table row
+    hist_blocks = min((hist + kBlock - 1) / kBlock, a.table_stride);
+    n_hist_tiles = (hist_blocks + kTileBlocks - 1) / kTileBlocks;
   } else {
     ring = a.table[b];
     const bool ring_ok = ring >= 0 && ring < a.num_blocks;
-    if (ring_ok && hist > 0 && t_first - W + 1 < hist) n_hist_tiles = (W + kTileKeys - 1) / kTileKeys;
+    hist_blocks = W / kBlock;
+    if (ring_ok && hist > 0 && t_first - W + 1 < hist) n_hist_tiles = (hist_blocks + kTileBlocks - 1) / kTileBlocks;
   }
   int c_lo = 0;
   if constexpr (!kFull) c_lo = max(0, i0 - W + 1);
@@ -159,13 +215,50 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     const int64_t off = (static_cast<int64_t>(tok0 + (ok ? ci : 0)) * hq + hh) * D + 8 * q4;
 #pragma unroll
     for (int m = 0; m < KS; ++m) {
-      qop[rg][m] = ok ? load8_as_bf16<kF32>(a.q, off + 32 * m) : u32x4{0u, 0u, 0u, 0u};
+      qop[rg][m] = load8_as_bf16<kF32>(a.q, off + 32 * m);
+      if (!ok) qop[rg][m] = u32x4{0u, 0u, 0u, 0u};
     }
   }
 
-  // ---- tile loading ----
-  // Global -> registers for tile `tile`, and the key positions (threads < 64).
-  auto key_position = [&](int tile, int kk) -> int {
+  // ---- staging: wave w moves block w of a tile ----
+  // Page ids of this wave's history blocks, 64 tiles at a time: lane j holds
+  // the page of tile (batch_base + j). One vector load per 64 tiles; the
+  // per-tile id is a readlane (scalar), so the tile loop never waits on it.
+  int pg_vec = -1;
+  auto fetch_pages = [&](int batch_base) {
+    if constexpr (kFull) {
+      const int t = batch_base + lane;
+      const int lb = t * kTileBlocks + wave;
+      pg_vec = (t < n_hist_tiles && lb < hist_blocks) ? page_row[lb] : -1;
+    }
+  };
+  auto page_for = [&](int tile) -> int {
+    if constexpr (kFull) return __builtin_amdgcn_readlane(pg_vec, tile & 63);
+    else return -1;
+  };
+  // Element offset of this wave's block of tile `tile` (-1: nothing to load),
+  // plus the number of leading valid keys of that block.
+  auto block_of = [&](int tile, int pg, int& valid) -> int64_t {
+    if (tile < n_hist_tiles) {
+      const int lb = tile * kTileBlocks + wave;
+      if (lb >= hist_blocks) { valid = 0; return -1; }
+      if constexpr (kFull) {
+        valid = min(kBlock, hist - lb * kBlock);
+        if (pg < 0 || pg >= a.num_blocks) { valid = 0; return -1; }
+        return (static_cast<int64_t>(pg) * hkv + g) * kBlock * D;
+      } else {
+        valid = hist >= W ? kBlock : min(kBlock, max(0, hist - lb * kBlock));  // unwritten slots
+        return ((static_cast<int64_t>(ring) * hkv + g) * W + kBlock * lb) * D;
+      }
+    } else {
+      const int cb = (first_ctile + tile - n_hist_tiles) * kTileBlocks + wave;  // chunk block
+      if (kBlock * cb >= i_end) { valid = 0; return -1; }
+      valid = min(kBlock, i_end - kBlock * cb);
+      return ((stage_blk0 + cb) * hkv + g) * kBlock * D;  // K part; V part is offset by stage_blocks
+    }
+  };
+
+  auto key_position = [&](int tile, int kk) -> int {   // kk = key within the tile
     if (tile < n_hist_tiles) {
       if constexpr (kFull) {
         const int p = tile * kTileKeys + kk;
@@ -185,132 +278,59 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  auto load_tile = [&](int tile, Stage<D>& st, int& mypos) {
-    if (tile < n_hist_tiles) {
-      // K: chunk e -> key e / CPR, column e % CPR; V^T: chunk e -> block, dim row, half.
-#pragma unroll
-      for (int u = 0; u < CPT; ++u) {
-        const int e = tid + 256 * u;
-        {
-          const int key = e / CPR;
-          const int col = e - key * CPR;
-          const int blk = key >> 4;
-          const int kin = key & 15;
-          int64_t base = -1;
-          if constexpr (kFull) {
-            const int lb = tile * kTileBlocks + blk;
-            if (lb * kBlock + kin < hist && lb < a.table_stride) {
-              const int pg = page_row[lb];
-              if (pg >= 0 && pg < a.num_blocks) base = (static_cast<int64_t>(pg) * hkv + g) * kBlock * D;
-            }
-          } else {
-            const int rb = tile * kTileBlocks + blk;
-            if (rb * kBlock < W) base = ((static_cast<int64_t>(ring) * hkv + g) * W + kBlock * rb) * D;
-          }
-          st.k[u] = base >= 0 ? *reinterpret_cast<const u32x4*>(a.k_pool + base + kin * D + col * 8)
-                              : u32x4{0u, 0u, 0u, 0u};
-        }
-        {
-          const int blk = e / (2 * D);
-          const int rem = e - blk * 2 * D;
-          const int row = rem >> 1;
-          const int half = rem & 1;
-          int64_t base = -1;
-          int first_key, limit;  // the chunk's 8 keys are valid while first_key + j < limit
-          if constexpr (kFull) {
-            const int lb = tile * kTileBlocks + blk;
-            first_key = lb * kBlock + half * 8;
-            limit = hist;
-            if (lb * kBlock < hist && lb < a.table_stride) {
-              const int pg = page_row[lb];
-              if (pg >= 0 && pg < a.num_blocks) base = (static_cast<int64_t>(pg) * hkv + g) * kBlock * D;
-            }
-          } else {
-            const int rb = tile * kTileBlocks + blk;
-            first_key = rb * kBlock + half * 8;          // ring slot; slots >= hist unwritten while hist < W
-            limit = hist >= W ? W : hist;
-            if (rb * kBlock < W) base = ((static_cast<int64_t>(ring) * hkv + g) * W + kBlock * rb) * D;
-          }
-          st.v[u] = base >= 0 ? *reinterpret_cast<const u32x4*>(a.v_pool + base + row * kBlock + half * 8)
-                              : u32x4{0u, 0u, 0u, 0u};
-          st.v[u] = keep_first_bf16(st.v[u], limit - first_key);
-        }
-      }
-    } else {
-      const int cbase = (first_ctile + tile - n_hist_tiles) * kTileKeys;
-#pragma unroll
-      for (int u = 0; u < CPT; ++u) {
-        const int e = tid + 256 * u;
-        const int key = e / CPR;
-        const int col = e - key * CPR;
-        const int ci = cbase + key;
-        if (ci < i_end) {
-          const int64_t off = (static_cast<int64_t>(tok0 + ci) * hkv + g) * D + col * 8;
-          st.k[u] = load8_as_bf16<kF32>(a.k_new, off);
-          st.v[u] = load8_as_bf16<kF32>(a.v_new, off);
-        } else {
-          st.k[u] = u32x4{0u, 0u, 0u, 0u};
-          st.v[u] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-    }
-    if (tid < kTileKeys) mypos = key_position(tile, tid);
-  };
-
-  // Registers -> LDS buffer `buf`. History V is already dim-major; chunk V is
-  // transposed here. Keys with an invalid position hold zeros in K and V, so
-  // masked probabilities never multiply stale data.
-  auto store_tile = [&](int tile, const Stage<D>& st, int mypos, int buf) {
+  u32x4 stk[CPL], stv[CPL];
+  int st_pos = -1;
+  auto load_tile = [&](int tile, int pg) {
+    int valid;
+    const int64_t base = block_of(tile, pg, valid);
+    const int64_t b0 = base >= 0 ? base : 0;
+    const uint32_t bytes = base >= 0 ? kBlock * D * 2 : 0;   // 0: loads return zeros, no traffic
     const bool hist_tile = tile < n_hist_tiles;
+    const uint16_t* kp = hist_tile ? a.k_pool + b0 : a.stage + b0;
+    const uint16_t* vp = hist_tile ? a.v_pool + b0 : a.stage + a.stage_blocks * hkv * kBlock * D + b0;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp, bytes);
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int e = tid + 256 * u;
-      const int key = e / CPR;
-      const int col = e - key * CPR;
-      *reinterpret_cast<u32x4*>(&sm.k[buf][key * KROW + col * 8]) = st.k[u];
-      if (hist_tile) {
-        const int blk = e / (2 * D);
-        const int rem = e - blk * 2 * D;
-        const int row = rem >> 1;
-        const int half = rem & 1;
-        uint16_t* dst = &sm.v[buf][(blk * D + row) * kVRow + half * 8];
-        reinterpret_cast<u32x2*>(dst)[0] = u32x2{st.v[u].x, st.v[u].y};
-        reinterpret_cast<u32x2*>(dst)[1] = u32x2{st.v[u].z, st.v[u].w};
-      } else {
-        const int blk = key >> 4;
-        const int kin = key & 15;
-        uint16_t* dst = &sm.v[buf][(blk * D + col * 8) * kVRow + kin];
-        const uint32_t w4[4] = {st.v[u].x, st.v[u].y, st.v[u].z, st.v[u].w};
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          dst[(2 * jj) * kVRow] = static_cast<uint16_t>(w4[jj] & 0xffffu);
-          dst[(2 * jj + 1) * kVRow] = static_cast<uint16_t>(w4[jj] >> 16);
-        }
-      }
+    for (int u = 0; u < CPL; ++u) {
+      const int e = lane + 64 * u;      // 16-byte chunk of the block
+      stk[u] = buf_load16(rk, 16 * e);
+      stv[u] = buf_load16(rv, 16 * e);
     }
-    if (tid < kTileKeys) sm.pos[buf][tid] = mypos;
+    if (tile < n_hist_tiles && valid < kBlock) {
+      // unwritten or stale slots of a partial history block: zero their V
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) stv[u] = keep_tokens_v(stv[u], lane >> 4, valid);
+    }
+    if (lane < kBlock) st_pos = key_position(tile, wave * kBlock + lane);
   };
 
-  // Key-position bounds of a tile (uniform): [kmin, kmax], all_valid.
-  auto tile_bounds = [&](int tile, int& kmin, int& kmax, bool& all_valid, bool& contiguous) {
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      const int e = lane + 64 * u;   // unit e of the block, copied as is
+      *reinterpret_cast<u32x4*>(&sm.k[buf][wave * kBlk + 8 * e]) = stk[u];
+      *reinterpret_cast<u32x4*>(&sm.v[buf][wave * kBlk + 8 * e]) = stv[u];
+    }
+    if (lane < kBlock) sm.pos[buf][wave * kBlock + lane] = st_pos;
+  };
+
+  // Key-position bounds of a tile (uniform): [kmin, kmax]; exact = every key valid.
+  auto tile_bounds = [&](int tile, int& kmin, int& kmax, bool& exact) {
     if (tile < n_hist_tiles) {
       if constexpr (kFull) {
         kmin = tile * kTileKeys;
         kmax = min(kmin + kTileKeys, hist) - 1;
-        all_valid = kmin + kTileKeys <= hist;
-        contiguous = true;
+        exact = kmin + kTileKeys <= hist;
       } else {
         kmin = max(0, hist - W);
         kmax = hist - 1;
-        all_valid = false;
-        contiguous = false;
+        exact = false;
       }
     } else {
       const int c0 = (first_ctile + tile - n_hist_tiles) * kTileKeys;
       kmin = hist + c0;
       kmax = hist + min(c0 + kTileKeys, i_end) - 1;
-      all_valid = c0 + kTileKeys <= i_end;
-      contiguous = true;
+      exact = c0 + kTileKeys <= i_end;
     }
   };
 
@@ -326,25 +346,28 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     for (int d = 0; d < DT; ++d) o[rg][d] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  Stage<D> stage;
-  int mypos = -1;
+  fetch_pages(0);
   if (n_tiles > 0) {
-    load_tile(0, stage, mypos);
-    store_tile(0, stage, mypos, 0);
+    load_tile(0, page_for(0));
+    store_tile(0);
   }
+  // Everything loaded so far (Q, first tile) is complete before the loop, so
+  // the loop's only outstanding global loads are the next tile's staging.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int buf = tile & 1;
     const bool has_next = tile + 1 < n_tiles;
-    if (has_next) load_tile(tile + 1, stage, mypos);
+    if (((tile + 1) & 63) == 0 && tile + 1 < n_hist_tiles) fetch_pages(tile + 1);
+    if (has_next) load_tile(tile + 1, page_for(tile + 1));
 
     int kmin, kmax;
-    bool all_valid, contiguous;
-    tile_bounds(tile, kmin, kmax, all_valid, contiguous);
+    bool exact;
+    tile_bounds(tile, kmin, kmax, exact);
     bool visible_any = wave_live && kmin <= qhi;
     if constexpr (!kFull) visible_any = visible_any && kmax >= qlo - W + 1;
-    bool need_mask = !(all_valid && contiguous && kmax <= qlo);
+    bool need_mask = !(exact && kmax <= qlo);
     if constexpr (!kFull) need_mask = need_mask || kmin < qhi - W + 1;
 
     if (visible_any) {
@@ -357,7 +380,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         for (int rg = 0; rg < kRowGroups; ++rg) s[kb][rg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < KS; ++m) {
-          const u32x4 kop = *reinterpret_cast<const u32x4*>(&sk[(16 * kb + c16) * KROW + 32 * m + 8 * q4]);
+          const u32x4 kop = *reinterpret_cast<const u32x4*>(&sk[kb * kBlk + 8 * (64 * m + lane)]);
 #pragma unroll
           for (int rg = 0; rg < kRowGroups; ++rg) s[kb][rg] = mfma_16x16x32(kop, qop[rg][m], s[kb][rg]);
         }
@@ -374,7 +397,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
             for (int r = 0; r < 4; ++r) {
               bool ok = kps[r] >= 0 && kps[r] <= qpos[rg];
               if constexpr (!kFull) ok = ok && kps[r] > qpos[rg] - W;
-              if (!ok) s[kb][rg][r] = -INFINITY;
+              s[kb][rg][r] = ok ? s[kb][rg][r] : -INFINITY;
             }
           }
         }
@@ -407,17 +430,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       }
 
 #pragma unroll
-      for (int d = 0; d < DT; ++d) {
+      for (int p = 0; p < DT / 2; ++p) {
 #pragma unroll
         for (int kb = 0; kb < kTileBlocks; ++kb) {
-          const u32x2 vop = *reinterpret_cast<const u32x2*>(&sv[(kb * D + 16 * d + c16) * kVRow + 4 * q4]);
+          const u32x4 vv = *reinterpret_cast<const u32x4*>(&sv[kb * kBlk + 8 * (64 * p + lane)]);
+          const u32x2 v0 = {vv.x, vv.y}, v1 = {vv.z, vv.w};   // dim tiles 2p, 2p+1
 #pragma unroll
-          for (int rg = 0; rg < kRowGroups; ++rg) o[rg][d] = mfma_16x16x16(vop, pb[kb][rg], o[rg][d]);
+          for (int rg = 0; rg < kRowGroups; ++rg) {
+            o[rg][2 * p] = mfma_16x16x16(v0, pb[kb][rg], o[rg][2 * p]);
+            o[rg][2 * p + 1] = mfma_16x16x16(v1, pb[kb][rg], o[rg][2 * p + 1]);
+          }
         }
       }
     }
 
-    if (has_next) store_tile(tile + 1, stage, mypos, buf ^ 1);
+    if (has_next) store_tile(buf ^ 1);
     __syncthreads();
   }
 
@@ -441,12 +468,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-template <int D, bool kFull>
-static void launch_prefill_dk(const PrefillArgs& a, dim3 grid, hipStream_t stream) {
-  if (a.in_f32)
-    hipLaunchKernelGGL((prefill_kernel<D, kFull, true>), grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((prefill_kernel<D, kFull, false>), grid, dim3(256), 0, stream, a);
+template <int D>
+static void launch_prefill_d(const PrefillArgs& a, dim3 grid, hipStream_t stream) {
+  const dim3 sgrid((a.max_new + kBlock - 1) / kBlock, a.batch);
+  if (a.in_f32) {
+    hipLaunchKernelGGL((stage_chunk_kernel<D, true>), sgrid, dim3(256), 0, stream, a);
+    if (a.full) hipLaunchKernelGGL((prefill_kernel<D, true, true>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((prefill_kernel<D, false, true>), grid, dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((stage_chunk_kernel<D, false>), sgrid, dim3(256), 0, stream, a);
+    if (a.full) hipLaunchKernelGGL((prefill_kernel<D, true, false>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((prefill_kernel<D, false, false>), grid, dim3(256), 0, stream, a);
+  }
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
@@ -456,15 +489,10 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int64_t npairs = static_cast<int64_t>(a.batch) * a.geo.hkv;
   const int64_t ppx = (npairs + kXcds - 1) / kXcds;
   const int64_t blocks = qb_max * ppx * kXcds;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (blocks > 0x7fffffff || a.batch > 65535) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks));
-  if (a.geo.d == 64) {
-    if (a.full) launch_prefill_dk<64, true>(a, grid, stream);
-    else launch_prefill_dk<64, false>(a, grid, stream);
-  } else {
-    if (a.full) launch_prefill_dk<128, true>(a, grid, stream);
-    else launch_prefill_dk<128, false>(a, grid, stream);
-  }
+  if (a.geo.d == 64) launch_prefill_d<64>(a, grid, stream);
+  else launch_prefill_d<128>(a, grid, stream);
   return hipGetLastError();
 }
 

@@ -39,17 +39,22 @@
  * results for that sequence are undefined, but no memory outside the pools
  * is touched.
  *
- * Pool layouts (bfloat16, per layer; B = 16-token block, D = head_dim):
+ * Pool layouts (bfloat16, per layer). Both pools are made of blocks of 16
+ * tokens x D channels (D = head_dim) of one kv head, 16*D values each:
  *   SWA ring pool, W slots per (ring, kv head), W a multiple of 16:
- *     K  [num_rings][Hkv][W][D]                 slot s at row s
- *     V  [num_rings][Hkv][W/16][D][16]          slot s, dim c at [s/16][c][s%16]
- *   Full page pool, 16-token pages:
- *     K  [num_pages][Hkv][16][D]
- *     V  [num_pages][Hkv][D][16]                (dim-major inside the page)
+ *     K, V  [num_rings][Hkv][W/16][16*D]        ring slot s in block s/16, token s%16
+ *   Full page pool, one block per (page, kv head):
+ *     K, V  [num_pages][Hkv][16*D]
  *   Position p of a sequence lives in ring slot p mod W, or in page
- *   page_table[b][p / 16] at offset p mod 16.
- *   V is stored dim-major within each 16-token block so that the P.V
- *   contraction reads matrix-core operands directly; K is token-major.
+ *   page_table[b][p / 16] at token p mod 16.
+ *   Inside a block, values sit in matrix-core operand order: 16-byte units,
+ *   unit u = 64a + 16q + c (a < D/32, q < 4, c < 16):
+ *     K unit u = K[token c][channels 32a + 8q .. 32a + 8q + 7]
+ *     V unit u = V[tokens 4q..4q+3][channel 32a + c],
+ *                then V[tokens 4q..4q+3][channel 32a + 16 + c]
+ *   i.e. K(t, ch) is value ((ch/32)*64 + ((ch%32)/8)*16 + t)*8 + ch%8 and
+ *   V(t, ch) is value ((ch/32)*64 + (t/4)*16 + ch%16)*8 + ((ch%32)/16)*4 + t%4.
+ *   A wavefront then loads each operand set with fully contiguous 1 KiB reads.
  */
 #ifndef HYBRID_ATTN_H
 #define HYBRID_ATTN_H
@@ -156,7 +161,9 @@ ha_status window_safe_match(const int32_t* req_tokens, int64_t req_len, const in
  *   num_tokens = cu_new[batch] (host);  max_new >= every n_b (host, sizes the grid)
  *   q [num_tokens][Hq][D], k_new/v_new [num_tokens][Hkv][D], in_dtype
  *   out float32 [num_tokens][Hq][D], lse float32 [num_tokens][Hq] (natural log)
- *   workspace: hybrid_attn_workspace_size(..., decode = 0) bytes (0 today). */
+ *   workspace: hybrid_attn_workspace_size(shape, kind, 0, batch, num_tokens, 0)
+ *   bytes of device memory (the chunk's K/V re-laid as 16-token blocks);
+ *   it is scratch for this call only. */
 ha_status hybrid_attn_prefill(const ha_shape* shape, const ha_kv_view* kv, const int32_t* hist_len,
                               const int32_t* cu_new, int32_t batch, int32_t num_tokens, int32_t max_new,
                               const void* q, const void* k_new, const void* v_new, int32_t in_dtype,
@@ -179,8 +186,9 @@ ha_status hybrid_attn_decode(const ha_shape* shape, const ha_kv_view* kv, const 
                              float* out, float* lse, int32_t num_splits, void* workspace,
                              size_t workspace_bytes, void* stream);
 
-/* Workspace bytes needed by hybrid_attn_decode (decode = 1) or
- * hybrid_attn_prefill (decode = 0) for the given sizes; 0 on invalid input. */
+/* Workspace bytes needed by hybrid_attn_decode (decode = 1: max_kv_len and
+ * num_splits as passed to the call) or hybrid_attn_prefill (decode = 0: pass
+ * num_tokens as max_kv_len; num_splits ignored); 0 on invalid input. */
 size_t hybrid_attn_workspace_size(const ha_shape* shape, int32_t kind, int32_t decode, int32_t batch,
                                   int32_t max_kv_len, int32_t num_splits);
 

@@ -57,21 +57,32 @@ def append_history(shape, view, seq_kv, starts, ends, src=None):
     fn(shape, view, i32(starts), i32(cu_from_counts(counts)), k_new.contiguous(), v_new.contiguous())
 
 
+def block_k(blocks, d):
+    """Decode K blocks [..., 16*d] (the documented operand-order layout: value
+    ((ch/32)*64 + ((ch%32)/8)*16 + t)*8 + ch%8) into [..., 16 tokens, d]."""
+    a = np.asarray(blocks).reshape(*blocks.shape[:-1], d // 32, 4, 16, 8)   # a, q, token, j
+    return np.moveaxis(a, -2, -4).reshape(*blocks.shape[:-1], 16, d)
+
+
+def block_v(blocks, d):
+    """Decode V blocks [..., 16*d] (value ((ch/32)*64 + (t/4)*16 + ch%16)*8 +
+    ((ch%32)/16)*4 + t%4) into [..., 16 tokens, d]."""
+    a = np.asarray(blocks).reshape(*blocks.shape[:-1], d // 32, 4, 16, 2, 4)   # a, q, c, h, r
+    n = a.ndim
+    order = list(range(n - 5)) + [n - 4, n - 1, n - 5, n - 2, n - 3]       # q, r, a, h, c
+    return a.transpose(order).reshape(*blocks.shape[:-1], 16, d)
+
+
 def ring_slots(pool: ha.SwaRingPool, ring, g):
     """Host copies of ring `ring`, kv head g: K [W, D], V [W, D] by slot."""
-    k = host(pool.k[ring, g])
-    v = host(pool.v[ring, g])                      # [W/16, D, 16]
-    v = v.transpose(0, 2, 1).reshape(-1, v.shape[1])
-    return k, v
+    d = pool.shape.head_dim
+    return block_k(host(pool.k[ring, g]), d).reshape(-1, d), block_v(host(pool.v[ring, g]), d).reshape(-1, d)
 
 
-def page_rows(pool: ha.FullPagePool, pages, g):
-    """Host copies of the given physical pages, kv head g, in the order given:
-    K [len(pages)*16, D], V [len(pages)*16, D] by (page, offset)."""
-    idx = torch.as_tensor(np.asarray(pages, dtype=np.int64), device=pool.k.device)
-    k = host(pool.k[idx, g]).reshape(-1, pool.k.shape[-1])
-    v = host(pool.v[idx, g]).transpose(0, 2, 1).reshape(-1, pool.v.shape[2])
-    return k, v
+def page_blocks(pool: ha.FullPagePool, g):
+    """Host copies of every page of kv head g: K, V each [num_pages, 16, D]."""
+    d = pool.shape.head_dim
+    return block_k(host(pool.k[:, g]), d), block_v(host(pool.v[:, g]), d)
 
 
 def check_ring(pool, ring, seq_k, seq_v, appended_positions, window):
@@ -92,10 +103,9 @@ def check_pages(pool, table_row, seq_k, seq_v, length, page_size=16):
     pos = np.arange(length)
     pages, offs = page_location(table_row, pos, page_size)
     for g in range(seq_k.shape[1]):
-        k = host(pool.k[:, g])                       # [P, 16, D]
-        v = host(pool.v[:, g])                       # [P, D, 16]
+        k, v = page_blocks(pool, g)                  # [P, 16, D] each
         np.testing.assert_array_equal(k[pages, offs], seq_k[:length, g])
-        np.testing.assert_array_equal(v[pages, :, offs], seq_v[:length, g])
+        np.testing.assert_array_equal(v[pages, offs], seq_v[:length, g])
 
 
 def oracle_rows(q_rows, k_seq, v_seq, positions, kind, window, scale=None):

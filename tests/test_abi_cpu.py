@@ -102,7 +102,8 @@ def test_decode_workspace_checked(lib):
     assert decode_call(lib, s, view(), batch=64, max_len=8193, ws=FAKE, ws_bytes=need - 1) == _lib.HA_ERR_WORKSPACE
     # SWA decode and prefill need none
     assert lib.hybrid_attn_workspace_size(ctypes.byref(s), _lib.HA_SWA, 1, 64, 8193, 0) == 0
-    assert lib.hybrid_attn_workspace_size(ctypes.byref(s), _lib.HA_FULL, 0, 64, 8193, 0) == 0
+    assert lib.hybrid_attn_workspace_size(ctypes.byref(s), _lib.HA_FULL, 0, 64, 8193, 0) == \
+        ((8193 + 15) // 16 + 64) * 8 * 16 * 128 * 2 * 2
     assert lib.hybrid_attn_decode_splits(ctypes.byref(s), _lib.HA_SWA, 64, 8193, 0) == 1
     # explicit split count is honoured
     assert lib.hybrid_attn_decode_splits(ctypes.byref(s), _lib.HA_FULL, 64, 8193, 4) == 4
@@ -125,7 +126,7 @@ def test_append_and_prefill_errors(lib):
                                None) == _lib.HA_ERR_UNSUPPORTED
     # empty work is a successful no-op that touches nothing
     assert lib.swa_ring_append(ctypes.byref(s), ctypes.byref(ring), FAKE, FAKE, 0, 0, FAKE, FAKE, 0, None) == 0
-    args = [FAKE, FAKE, 2, 10, 5, FAKE, FAKE, FAKE, 0, FAKE, FAKE, None, 0, None]
+    args = [FAKE, FAKE, 2, 10, 5, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, 1 << 30, None]
     assert lib.hybrid_attn_prefill(ctypes.byref(s), ctypes.byref(pages), *args[:2], 2, 10, 11,
                                    *args[5:]) == _lib.HA_ERR_RANGE          # max_new > num_tokens
     bad = list(args)
@@ -133,6 +134,9 @@ def test_append_and_prefill_errors(lib):
     assert lib.hybrid_attn_prefill(ctypes.byref(s), ctypes.byref(pages), *bad) == _lib.HA_ERR_NULL
     assert lib.hybrid_attn_prefill(ctypes.byref(s), ctypes.byref(pages), FAKE, FAKE, 0, 0, 0,
                                    *args[5:]) == 0
+    small_ws = list(args)
+    small_ws[12] = 100
+    assert lib.hybrid_attn_prefill(ctypes.byref(s), ctypes.byref(pages), *small_ws) == _lib.HA_ERR_WORKSPACE
 
 
 def test_errors_do_not_leak_between_calls(lib):

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import hybrid_sliding_window_gqa_amd as ha
-from gpu_util import append_history, check_pages, check_ring, host, i32, make_generator, randn_bf16
+from gpu_util import append_history, check_pages, check_ring, host, i32, make_generator, page_blocks, randn_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -77,8 +77,9 @@ def test_page_append_permuted_table(hkv, d):
         # tail of the last page is untouched
         last = table[b, pages_per[b] - 1]
         tail = n - 16 * (pages_per[b] - 1)
-        assert torch.isnan(pool.k[last, :, tail:].float()).all()
-        assert torch.isnan(pool.v[last, :, :, tail:].float()).all()
+        for g in range(hkv):
+            kb, vb = page_blocks(pool, g)
+            assert np.isnan(kb[last, tail:]).all() and np.isnan(vb[last, tail:]).all()
     for p in set(range(num_pages)) - used:
         assert torch.isnan(pool.k[p].float()).all() and torch.isnan(pool.v[p].float()).all()
 
@@ -94,7 +95,8 @@ def test_out_of_range_ids_are_dropped():
     append_history(shape, ring.view(i32([7])), seq, [0], [20])
     torch.cuda.synchronize()
     k = host(seq[0][0])
-    np.testing.assert_array_equal(host(pool.k[2, 0]), k[0:16, 0])
-    np.testing.assert_array_equal(host(pool.k[1, 0]), k[48:64, 0])
+    kb, _ = page_blocks(pool, 0)
+    np.testing.assert_array_equal(kb[2], k[0:16, 0])
+    np.testing.assert_array_equal(kb[1], k[48:64, 0])
     assert torch.isnan(pool.k[0].float()).all() and torch.isnan(pool.k[3].float()).all()
     assert torch.isnan(ring.k.float()).all()
