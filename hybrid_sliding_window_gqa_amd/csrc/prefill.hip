@@ -26,13 +26,15 @@
 //     Per tile and wave: S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (Q^T held in
 //     registers), exp2-domain online softmax per row (16 scores in-lane plus
 //     two cross-lane steps), P^T cast to bf16 in the accumulator layout, then
-//     O^T += V^T P^T on v_mfma_f32_16x16x16_bf16. Tiles a wave sees completely
-//     skip masking; tiles no row of the wave sees are skipped.
+//     O^T += V^T P^T, also on v_mfma_f32_16x16x32_bf16 (two key blocks per
+//     product; the older 16x16x16 form runs at half the rate on gfx950).
+//     Tiles a wave sees completely skip masking; tiles no row of the wave
+//     sees are skipped.
 //
 // Grid order: workgroup i runs on XCD i % 8 (round-robin dispatch). All query
-// blocks of one (sequence, kv head) pair are placed on the same XCD, so the
-// pair's K/V stream is shared through that XCD's L2, and the heaviest
-// (latest) query blocks are dispatched first.
+// blocks of one (sequence, kv head) pair are placed on the same XCD and
+// dispatched back to back (heaviest, i.e. latest, first), so the workgroups
+// resident on an XCD stream one pair's K/V in near lockstep through its L2.
 #include <cmath>
 
 #include "common.hpp"
@@ -51,12 +53,25 @@ constexpr int kTileBlocks = kTileKeys / kBlock;   // 4 == kWaves: one block per 
 constexpr int kXcds = 8;
 static_assert(kTileBlocks == kWaves, "each wave stages one block of a tile");
 
+// LDS tiles as 16-byte units (alignment known to the compiler, so stores and
+// loads are single ds_write_b128 / ds_read_b128 instructions).
+//   k: the four K blocks as they are (operand order).
+//   v: the V blocks interleaved by pairs: unit [pair][a][h][lane] holds the
+//      8 bytes of half h (dim tile 2a + h) of V unit (a, lane) from block
+//      2*pair, then the same 8 bytes from block 2*pair + 1 -- exactly the
+//      v_mfma_f32_16x16x32_bf16 A operand of a 32-key product.
 template <int D>
 struct Smem {
-  uint16_t k[2][kTileBlocks * kBlock * D];
-  uint16_t v[2][kTileBlocks * kBlock * D];
-  int32_t pos[2][kTileKeys];
+  static constexpr int kUnits = kTileBlocks * kBlock * D / 8;   // 16-byte units per tile
+  u32x4 k[2][kUnits];
+  u32x4 v[2][kUnits];
+  int4 pos[2][kTileKeys / 4];
 };
+
+// Softmax reference slack (log2 units): the running max used as the exp2
+// reference is only raised when a tile's max exceeds it by more than this,
+// so probabilities stay <= 2^8 and the O/l rescale is rarely needed.
+constexpr float kRescaleSlack = 8.0f;
 
 // V unit of lane group q holds tokens 4q..4q+3 (for two channels): zero the
 // tokens at index >= nv.
@@ -154,13 +169,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 
   // ---- workgroup -> (sequence, kv head, query block), XCD-aware ----
   const int npairs = a.batch * hkv;
-  const int ppx = (npairs + kXcds - 1) / kXcds;   // pairs per XCD
   const int qb_max = (a.max_new + QB - 1) / QB;
   const int lin = blockIdx.x;
   const int xcd = lin % kXcds;
   const int jj = lin / kXcds;
-  const int pair = (jj % ppx) * kXcds + xcd;
-  const int qblk = qb_max - 1 - jj / ppx;
+  // Pair-major within an XCD: the workgroups resident on one XCD at a time
+  // are consecutive query blocks of ONE pair, so they stream the same K/V
+  // tiles at nearly the same time and the XCD's L2 serves most of them.
+  const int pair = (jj / qb_max) * kXcds + xcd;
+  const int qblk = qb_max - 1 - jj % qb_max;
   if (pair >= npairs || qblk < 0) return;
   const int b = pair / hkv;
   const int g = pair - b * hkv;
@@ -305,13 +322,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   };
 
   auto store_tile = [&](int buf) {
+    u32x2* vpair = reinterpret_cast<u32x2*>(sm.v[buf]);
+    const int pair = wave >> 1;
+    const int slot = wave & 1;
 #pragma unroll
     for (int u = 0; u < CPL; ++u) {
-      const int e = lane + 64 * u;   // unit e of the block, copied as is
-      *reinterpret_cast<u32x4*>(&sm.k[buf][wave * kBlk + 8 * e]) = stk[u];
-      *reinterpret_cast<u32x4*>(&sm.v[buf][wave * kBlk + 8 * e]) = stv[u];
+      const int e = lane + 64 * u;   // unit e of the block
+      sm.k[buf][wave * (kBlk / 8) + e] = stk[u];
+      // V unit (a = u, lane): half 0 -> dim tile 2u, half 1 -> dim tile 2u + 1
+      const int base = ((pair * CPL + u) * 2) * 64 + lane;        // [pair][a][h=0][lane]
+      vpair[2 * base + slot] = u32x2{stv[u].x, stv[u].y};
+      vpair[2 * (base + 64) + slot] = u32x2{stv[u].z, stv[u].w};
     }
-    if (lane < kBlock) sm.pos[buf][wave * kBlock + lane] = st_pos;
+    if (lane < kBlock) reinterpret_cast<int32_t*>(sm.pos[buf])[wave * kBlock + lane] = st_pos;
   };
 
   // Key-position bounds of a tile (uniform): [kmin, kmax]; exact = every key valid.
@@ -371,8 +394,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     if constexpr (!kFull) need_mask = need_mask || kmin < qhi - W + 1;
 
     if (visible_any) {
-      const uint16_t* sk = sm.k[buf];
-      const uint16_t* sv = sm.v[buf];
+      const u32x4* sk = sm.k[buf];
+      const u32x4* sv = sm.v[buf];
       f32x4 s[kTileBlocks][kRowGroups];
 #pragma unroll
       for (int kb = 0; kb < kTileBlocks; ++kb) {
@@ -380,7 +403,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         for (int rg = 0; rg < kRowGroups; ++rg) s[kb][rg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < KS; ++m) {
-          const u32x4 kop = *reinterpret_cast<const u32x4*>(&sk[kb * kBlk + 8 * (64 * m + lane)]);
+          const u32x4 kop = sk[kb * (kBlk / 8) + 64 * m + lane];
 #pragma unroll
           for (int rg = 0; rg < kRowGroups; ++rg) s[kb][rg] = mfma_16x16x32(kop, qop[rg][m], s[kb][rg]);
         }
@@ -389,7 +412,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < kTileBlocks; ++kb) {
-          const int4 kp = *reinterpret_cast<const int4*>(&sm.pos[buf][16 * kb + 4 * q4]);
+          const int4 kp = sm.pos[buf][4 * kb + q4];
           const int kps[4] = {kp.x, kp.y, kp.z, kp.w};
 #pragma unroll
           for (int rg = 0; rg < kRowGroups; ++rg) {
@@ -403,17 +426,34 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         }
       }
 
-      u32x2 pb[kTileBlocks][kRowGroups];
+      // Row max of this tile; raise the exp2 reference (and rescale O, l)
+      // only when some row of the wave outgrows it by more than the slack.
+      float tmax[kRowGroups];
+      bool grow = false;
 #pragma unroll
       for (int rg = 0; rg < kRowGroups; ++rg) {
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < kTileBlocks; ++kb)
           mx = fmaxf(mx, fmaxf(fmaxf(s[kb][rg][0], s[kb][rg][1]), fmaxf(s[kb][rg][2], s[kb][rg][3])));
-        const float tmax = group4_max(mx) * sl2;
-        const float m_new = fmaxf(m_run[rg], tmax);
-        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = fast_exp2(m_run[rg] - m_use);
+        tmax[rg] = group4_max(mx) * sl2;
+        grow = grow || (tmax[rg] > m_run[rg] + kRescaleSlack);
+      }
+      if (__any(grow)) {
+#pragma unroll
+        for (int rg = 0; rg < kRowGroups; ++rg) {
+          const float m_new = fmaxf(m_run[rg], tmax[rg]);
+          const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run[rg] - m_new);
+          l_run[rg] *= alpha;
+#pragma unroll
+          for (int d = 0; d < DT; ++d) o[rg][d] *= alpha;
+          m_run[rg] = m_new;
+        }
+      }
+      u32x4 pb[kTileBlocks / 2][kRowGroups];   // P^T for block pairs: B operands of P.V
+#pragma unroll
+      for (int rg = 0; rg < kRowGroups; ++rg) {
+        const float m_use = (m_run[rg] == -INFINITY) ? 0.0f : m_run[rg];
         float lsum = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < kTileBlocks; ++kb) {
@@ -421,24 +461,31 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s[kb][rg][r] * sl2 - m_use);
           lsum += (p[0] + p[1]) + (p[2] + p[3]);
-          pb[kb][rg] = u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+          const uint32_t lo = pack_bf16x2(p[0], p[1]), hi = pack_bf16x2(p[2], p[3]);
+          if (kb & 1) {
+            pb[kb / 2][rg].z = lo;
+            pb[kb / 2][rg].w = hi;
+          } else {
+            pb[kb / 2][rg].x = lo;
+            pb[kb / 2][rg].y = hi;
+          }
         }
-        l_run[rg] = l_run[rg] * alpha + lsum;
-        m_run[rg] = m_new;
-#pragma unroll
-        for (int d = 0; d < DT; ++d) o[rg][d] *= alpha;
+        l_run[rg] += lsum;
       }
 
+      // P.V on v_mfma_f32_16x16x32_bf16, two 16-key blocks per product: the
+      // reduction slots 8q..8q+3 of a lane are keys 4q..4q+3 of block kb,
+      // slots 8q+4..8q+7 the same keys of block kb+1, in both operands.
 #pragma unroll
       for (int p = 0; p < DT / 2; ++p) {
 #pragma unroll
-        for (int kb = 0; kb < kTileBlocks; ++kb) {
-          const u32x4 vv = *reinterpret_cast<const u32x4*>(&sv[kb * kBlk + 8 * (64 * p + lane)]);
-          const u32x2 v0 = {vv.x, vv.y}, v1 = {vv.z, vv.w};   // dim tiles 2p, 2p+1
+        for (int pair = 0; pair < kTileBlocks / 2; ++pair) {
+          const u32x4 v0 = sv[((pair * (DT / 2) + p) * 2 + 0) * 64 + lane];   // dim tile 2p
+          const u32x4 v1 = sv[((pair * (DT / 2) + p) * 2 + 1) * 64 + lane];   // dim tile 2p+1
 #pragma unroll
           for (int rg = 0; rg < kRowGroups; ++rg) {
-            o[rg][2 * p] = mfma_16x16x16(v0, pb[kb][rg], o[rg][2 * p]);
-            o[rg][2 * p + 1] = mfma_16x16x16(v1, pb[kb][rg], o[rg][2 * p + 1]);
+            o[rg][2 * p] = mfma_16x16x32(v0, pb[pair][rg], o[rg][2 * p]);
+            o[rg][2 * p + 1] = mfma_16x16x32(v1, pb[pair][rg], o[rg][2 * p + 1]);
           }
         }
       }
