@@ -31,6 +31,12 @@
  * default stream) and the calls return without synchronising; only
  * window_safe_match runs synchronously on the host.
  *
+ * Inputs. K/V values (in the pools and in a prefill chunk) must be finite for
+ * the semantics above to hold exactly: prefill contracts V for all rows of a
+ * 64-key tile at once, so a NaN/Inf V value of a key that some row masks out
+ * still reaches that row (0 * NaN = NaN). Unwritten ring slots and page tails
+ * are never read into a product.
+ *
  * Errors. Every call returns ha_status. Arguments are validated on the host
  * before any HIP call, so a rejected call never touches the device.
  * ha_last_error() returns a message for the last failure on the calling
