@@ -23,6 +23,7 @@ other workloads (--workload reuse|ragged) for extra JSON lines.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +31,7 @@ import time
 
 import numpy as np
 
+HERE = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 METRIC = "decode attn HBM GB/s (% peak) + prefill TFLOP/s (% MFMA peak), SWA:full 6:1"
@@ -44,11 +46,14 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", choices=["decode", "reuse", "ragged", "chunked"], default="decode")
+    p.add_argument("--workload", choices=["decode", "reuse", "ragged", "chunked", "copy"], default="decode",
+                   help="copy: 2 GiB elementwise copy, the known-size kernel that scales HBM counters")
     p.add_argument("--prefill-passes", type=int, default=3)
     p.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill part")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU sample")
+    p.add_argument("--cpu-prefill-seconds", type=float, default=10.0,
+                   help="target oracle time for the prefill CPU sample")
     p.add_argument("--eager", action="store_true", help="launch calls directly instead of replaying a HIP graph")
     return p.parse_args()
 
@@ -81,6 +86,61 @@ def decode_layer_bytes(shape, kind, kv_len):
 
 
 # ---------------------------------------------------------------------------
+# HBM traffic per dispatch, from the committed rocprofv3 counter summaries
+
+def sources_digest(paths):
+    """sha256 over the given repository files, in order (identifies the kernel
+    build that a counter summary was taken from)."""
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profile_traffic(name):
+    """Calibrated HBM bytes per dispatch recorded in profiles/<name>, or None
+    when the summary is missing or the kernel's sources changed since the
+    counters were taken."""
+    try:
+        with open(os.path.join(HERE, "profiles", name), encoding="utf-8") as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    fields = {}
+    for line in lines:
+        key, sep, val = line.partition(":")
+        if sep and key.strip() in ("traffic_bytes_per_dispatch", "sources", "sources_sha256"):
+            fields[key.strip()] = val.strip()
+    try:
+        if sources_digest(fields["sources"].split()) != fields["sources_sha256"]:
+            return None
+        return int(float(fields["traffic_bytes_per_dispatch"]))
+    except (KeyError, ValueError, OSError):
+        return None
+
+
+DECODE_PROFILE = "decode_kernel_full_decode64x8192_pmc.txt"
+PREFILL_PROFILE = "prefill_kernel_full_chunked4x32768_pmc.txt"
+
+
+def run_copy(torch, args, device):
+    """Known-size plain copy (dst = -src over 2 GiB of bf16) used to scale
+    the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.bfloat16, device=device).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    reps = 3
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    return {"workload": "calibration copy: dst = -src, 2 GiB bf16 each way", "bytes_read": 2 * n,
+            "bytes_written": 2 * n, "ms": dt * 1e3, "gbs": 4 * n / dt / 1e9}
+
 
 def timed_events(torch, n):
     return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
@@ -203,7 +263,7 @@ def prefill_pass_flops(shape, kinds, batch, total, chunk):
     return flops
 
 
-def run_chunked(torch, ha, grp, synth, args, device):
+def run_chunked(torch, ha, grp, synth, args, device, cpu_seconds=0.0):
     struct = synth.chunked_structure()
     shape = ha.HeadShape(struct.shape.num_q_heads, struct.shape.num_kv_heads, struct.shape.head_dim,
                          struct.shape.window)
@@ -277,39 +337,99 @@ def run_chunked(torch, ha, grp, synth, args, device):
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": flops["full"] / (full_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            "traffic": None,
+            "traffic": profile_traffic(PREFILL_PROFILE),
+            "kernel": "hybrid_attn_prefill, full layer (stage_chunk_kernel + prefill_kernel<128,full>), "
+                      f"mean over the {nchunks} chunk calls",
+            "flops_per_launch": flops["full"] / nchunks,
         },
     }
+    if cpu_seconds > 0:
+        log("[bench] cpu baseline (oracle), prefill rows")
+        res["cpu_baseline"] = cpu_baseline_prefill(torch, shape, group, qs, ks, vs, chunk, cpu_seconds)
     del qs, ks, vs, outs, lses, group
     torch.cuda.empty_cache()
     return res
+
+
+def blas_thread_count():
+    try:
+        import threadpoolctl
+        return max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def cpu_baseline_prefill(torch, shape, group, qs, ks, vs, chunk, target_s):
+    """Time the fp64 oracle on seeded sample rows of the chunked prefill
+    (sequence 0; full and SWA layer alternately; all query heads) until about
+    target_s seconds of CPU work; report algorithmic TFLOP/s."""
+    sys.path.insert(0, HERE)
+    from oracle.attention import attend
+
+    w, d, hq = shape.window, shape.head_dim, shape.num_q_heads
+    nchunks = qs[0].shape[0]
+    total = nchunks * chunk
+    rng = np.random.default_rng(7)
+    layers = {kind: group.kinds.index(kind) for kind in ("full", "swa")}
+    logical = {}
+    for kind, li in layers.items():
+        k = ks[li][:, :chunk].reshape(total, *ks[li].shape[2:]).float().cpu().numpy()
+        v = vs[li][:, :chunk].reshape(total, *vs[li].shape[2:]).float().cpu().numpy()
+        logical[kind] = (k, v)
+    done_flops, done_s, rows = 0, 0.0, {"full": 0, "swa": 0}
+    step = 0
+    while done_s < target_s:
+        kind = ("full", "swa")[step % 2]
+        step += 1
+        li = layers[kind]
+        pos = np.sort(rng.integers(0, total, size=4))
+        q = np.stack([qs[li][p // chunk, p % chunk].float().cpu().numpy() for p in pos])
+        k, v = logical[kind]
+        t0 = time.perf_counter()
+        if kind == "full":
+            attend(q, k, v, pos, kind, w)
+        else:
+            for i, p in enumerate(pos):         # the window's keys only, positions shifted
+                lo = max(0, int(p) - w + 1)
+                attend(q[i:i + 1], k[lo:p + 1], v[lo:p + 1], [int(p) - lo], kind, w)
+        done_s += time.perf_counter() - t0
+        rows[kind] += len(pos)
+        done_flops += int(visible_keys(pos, kind, w).sum()) * hq * 4 * d
+    return {
+        "value": done_flops / done_s / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(blas_thread_count()),
+        "kind": "oracle",
+        "sample": f"{rows['full']} full-layer and {rows['swa']} SWA-layer query rows of sequence 0 "
+                  f"(seeded positions in [0, {total})), all {hq} query heads, {done_s:.1f} s of fp64 NumPy",
+    }
 
 
 def cpu_baseline(torch, shape, group, data, target_s):
     """Time the fp64 oracle on whole sequences of the decode step (all 7
     layers each) until about target_s seconds of CPU work, and express it in
     the metric's unit (algorithmic bytes per second)."""
-    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, HERE)
     from oracle.attention import attend
 
-    try:
-        import threadpoolctl
-        blas_threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        blas_threads = 1
+    blas_threads = blas_thread_count()
     w = shape.window
     hist = data["hist"]
     b_total = len(hist)
     done_bytes, done_s, seqs = 0, 0.0, 0
-    for b in range(b_total):
-        # host copies of this sequence's logical K/V (generator tensors, not pools)
-        per_layer = []
-        for li, layer in enumerate(group.layers):
-            k_hist, v_hist, start, cu = data["logical"][li]
-            k = torch.cat([k_hist[cu[b]:cu[b + 1]], data["k"][li][b:b + 1]]).float().cpu().numpy()
-            v = torch.cat([v_hist[cu[b]:cu[b + 1]], data["v"][li][b:b + 1]]).float().cpu().numpy()
-            q = data["q"][li][b:b + 1].float().cpu().numpy()
-            per_layer.append((layer.kind, k, v, q, int(hist[b] - start[b])))
+    host = {}
+    for b in (i % b_total for i in range(100 * b_total)):   # passes over the step until target_s
+        if b not in host:
+            # host copies of this sequence's logical K/V (generator tensors, not pools)
+            per_layer = []
+            for li, layer in enumerate(group.layers):
+                k_hist, v_hist, start, cu = data["logical"][li]
+                k = torch.cat([k_hist[cu[b]:cu[b + 1]], data["k"][li][b:b + 1]]).float().cpu().numpy()
+                v = torch.cat([v_hist[cu[b]:cu[b + 1]], data["v"][li][b:b + 1]]).float().cpu().numpy()
+                q = data["q"][li][b:b + 1].float().cpu().numpy()
+                per_layer.append((layer.kind, k, v, q, int(hist[b] - start[b])))
+            host[b] = per_layer
+        per_layer = host[b]
         t0 = time.perf_counter()
         for kind, k, v, q, t in per_layer:
             attend(q, k, v, [t], kind, w)
@@ -324,8 +444,8 @@ def cpu_baseline(torch, shape, group, data, target_s):
         "unit": "GB/s",
         "cores": int(blas_threads),
         "kind": "oracle",
-        "sample": f"{seqs} of {b_total} sequences of the decode step, all 7 layers "
-                  f"({done_s:.1f} s of fp64 NumPy, one row per sequence and layer)",
+        "sample": f"{seqs} sequence rows of the decode step ({seqs / b_total:.2f} passes over its {b_total} "
+                  f"sequences), all 7 layers, all query heads ({done_s:.1f} s of fp64 NumPy)",
     }
 
 
@@ -350,6 +470,9 @@ def main():
     if args.workload == "chunked":
         res = run_chunked(torch, ha, grp, synth, args, device)
         print(json.dumps(res))
+        return 0
+    if args.workload == "copy":
+        print(json.dumps(run_copy(torch, args, device)))
         return 0
 
     struct = {"decode": synth.decode_structure, "reuse": None, "ragged": synth.ragged_structure}[args.workload]
@@ -394,14 +517,15 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(info["full_decode_gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel": "hybrid_attn_decode, full layer (decode_kernel<128,full> + split-K reduce)",
+            "traffic": profile_traffic(DECODE_PROFILE) if args.workload == "decode" else None,
+            "kernel": "hybrid_attn_decode, full layer (decode_kernel<128,full> + decode_reduce_kernel<128>)",
             "bytes_per_launch": full_bytes,
         },
     }
     if args.workload == "decode" and not args.no_prefill:
         log("[bench] chunked prefill")
-        line["prefill"] = run_chunked(torch, ha, grp, synth, args, device)
+        line["prefill"] = run_chunked(torch, ha, grp, synth, args, device,
+                                      0.0 if args.no_cpu_baseline else args.cpu_prefill_seconds)
         log(f"[bench] prefill {line['prefill']['tflops']:.1f} TFLOP/s, full layer "
             f"{line['prefill']['full_layer_tflops']:.1f} TFLOP/s")
     if args.workload == "decode" and not args.no_cpu_baseline:

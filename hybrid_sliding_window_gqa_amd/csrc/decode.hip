@@ -278,36 +278,40 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
 }
 
 // a8: lse = log2 sum_s 2^lse_s; o = sum_s 2^(lse_s - lse) o_s (log2 domain),
-// written back in natural-log units. One workgroup per (kv head, sequence):
-// thread e handles output element e of the G*D outputs of the group.
+// written back in natural-log units. One thread per output element (row,
+// channel); the splits are folded with a running max so every split's lse
+// and o load is issued up front (one memory round trip for typical counts).
+// A split that saw no key (lse_s = -inf) contributes nothing.
 template <int D>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
-  const int g = blockIdx.x;
   const int b = blockIdx.y;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;  // element of the sequence's Hq*D outputs
+  if (e >= a.geo.hq * D) return;
   const int len = a.kv_len[b];
   if (len <= 0) return;
   const int nblk = min((len + kBlock - 1) / kBlock, a.table_stride);
   const int nsplit = min((nblk + a.split_blocks - 1) / a.split_blocks, a.splits);
   if (nsplit <= 1) return;
-  const int G = a.geo.group;
-  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
-    const int h = e / D;
-    const int dd = e - h * D;
-    const int64_t row = static_cast<int64_t>(b) * a.geo.hq + g * G + h;
-    const float* pl = a.part_lse + row * a.splits;
-    const float* po = a.part_o + row * a.splits * D + dd;
-    float mx = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, pl[s]);
-    const float mu = (mx == -INFINITY) ? 0.0f : mx;
-    float l = 0.0f, acc = 0.0f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float w = fast_exp2(pl[s] - mu);
-      l += w;
-      acc += w * po[static_cast<int64_t>(s) * D];
-    }
-    a.out[row * D + dd] = acc / l;
-    if (dd == 0) a.lse[row] = (mu + fast_log2(l)) * kLn2;
+  const int h = e / D;
+  const int dd = e - h * D;
+  const int64_t row = static_cast<int64_t>(b) * a.geo.hq + h;
+  const float* pl = a.part_lse + row * a.splits;
+  const float* po = a.part_o + row * a.splits * D + dd;
+  float m = -INFINITY, l = 0.0f, acc = 0.0f;
+#pragma unroll 4
+  for (int s = 0; s < nsplit; ++s) {
+    const float ls = pl[s];
+    const float os = po[static_cast<int64_t>(s) * D];
+    const float mn = fmaxf(m, ls);
+    const float mu = (mn == -INFINITY) ? 0.0f : mn;
+    const float f = fast_exp2(m - mu);
+    const float w = fast_exp2(ls - mu);
+    l = l * f + w;
+    acc = acc * f + (w > 0.0f ? w * os : 0.0f);
+    m = mn;
   }
+  a.out[row * D + dd] = acc / l;
+  if (dd == 0) a.lse[row] = ((m == -INFINITY ? 0.0f : m) + fast_log2(l)) * kLn2;
 }
 
 // Split policy. Every split of the longest sequence is equally long, and the
@@ -361,7 +365,8 @@ static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (a.full && a.splits > 1) {
-    hipLaunchKernelGGL(decode_reduce_kernel<D>, dim3(a.geo.hkv, a.batch), dim3(256), 0, stream, a);
+    const unsigned per_seq = static_cast<unsigned>((a.geo.hq * D + 255) / 256);
+    hipLaunchKernelGGL(decode_reduce_kernel<D>, dim3(per_seq, a.batch), dim3(256), 0, stream, a);
     err = hipGetLastError();
   }
   return err;

@@ -128,3 +128,21 @@ def test_decode_is_deterministic():
     o2, l2 = ha.hybrid_attn_decode(shape, view, i32(lens), q, max(lens))
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_workspace_reused_across_calls():
+    """One caller-provided workspace serves consecutive split-K calls whose
+    split counts differ per sequence and per call (stale partials of an
+    earlier call are never merged into a later one)."""
+    shape = ha.HeadShape(64, 8, 128)
+    lens = [5, 200, 3000, 4097]
+    seq, q, pool, view = build(shape, ha.HA_FULL, lens, seed=6)
+    need = ha.hybrid_attn_workspace_size(shape, ha.HA_FULL, True, len(lens), max(lens), 7)
+    ws = torch.full((need,), 0x7f, dtype=torch.uint8, device="cuda")   # poison: huge floats
+    calls = [(lens, 7), ([4, 199, 1000, 4097], 7), ([5, 17, 3000, 2500], 3), (lens, 7)]
+    for call_lens, splits in calls:
+        out, lse = ha.hybrid_attn_decode(shape, view, i32(call_lens), q, max(lens), num_splits=splits,
+                                         workspace=ws)
+        torch.cuda.synchronize()
+        ref_o, ref_l = oracle_decode(shape, ha.HA_FULL, seq, q, call_lens)
+        assert_close(host(out), host(lse), ref_o, ref_l, f"lens={call_lens} splits={splits}")
