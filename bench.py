@@ -138,8 +138,17 @@ def run_copy(torch, args, device):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / reps
+    # read-only stream of the same buffer (a max-reduction), for the achievable read rate
+    torch.amax(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        torch.amax(src)
+    torch.cuda.synchronize()
+    dr = (time.perf_counter() - t0) / reps
     return {"workload": "calibration copy: dst = -src, 2 GiB bf16 each way", "bytes_read": 2 * n,
-            "bytes_written": 2 * n, "ms": dt * 1e3, "gbs": 4 * n / dt / 1e9}
+            "bytes_written": 2 * n, "ms": dt * 1e3, "copy_gbs": 4 * n / dt / 1e9,
+            "read_only_gbs": 2 * n / dr / 1e9}
 
 
 def timed_events(torch, n):
