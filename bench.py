@@ -5,7 +5,8 @@ Default run (prints ONE JSON line on stdout):
   step     one decode step of a 6:1 layer group (6 SWA layers on W=128 ring
            pools + 1 full layer on a 16-token paged pool) for 64 sequences with
            8192 cached tokens each, Hq/Hkv/D = 64/8/128, bf16 K/V ~ N(0,1):
-           per layer, append the new token then attend.
+           per layer, one call appends the new token and attends
+           (--separate-append: an append call, then the decode call).
   value    decode HBM GB/s = algorithmic bytes per step / step time, where
            algorithmic bytes = K/V rows the queries see + Q read + O (fp32)
            and LSE written.
@@ -55,6 +56,8 @@ def parse():
     p.add_argument("--cpu-prefill-seconds", type=float, default=10.0,
                    help="target oracle time for the prefill CPU sample")
     p.add_argument("--eager", action="store_true", help="launch calls directly instead of replaying a HIP graph")
+    p.add_argument("--separate-append", action="store_true",
+                   help="decode step as append call + decode call per layer instead of one fused call")
     return p.parse_args()
 
 
@@ -155,7 +158,7 @@ def timed_events(torch, n):
     return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
 
 
-def build_decode(torch, ha, grp, synth, struct, device, workload):
+def build_decode(torch, ha, grp, synth, struct, device, workload, fuse=True):
     """Pools filled with each sequence's history; per-layer new-token tensors."""
     shape = ha.HeadShape(struct.shape.num_q_heads, struct.shape.num_kv_heads, struct.shape.head_dim,
                          struct.shape.window)
@@ -188,18 +191,23 @@ def build_decode(torch, ha, grp, synth, struct, device, workload):
         lse_l.append(torch.empty(b, hq, dtype=torch.float32, device=device))
     pos = torch.as_tensor(hist.astype(np.int32), device=device)
     kv_len = torch.as_tensor((hist + 1).astype(np.int32), device=device)
-    plan = grp.plan_decode(group, q_l, k_l, v_l, pos, kv_len, int(hist.max()) + 1, out_l, lse_l)
+    plan = grp.plan_decode(group, q_l, k_l, v_l, pos, kv_len, int(hist.max()) + 1, out_l, lse_l,
+                           fuse_append=fuse)
     torch.cuda.synchronize()
     return shape, group, plan, dict(q=q_l, k=k_l, v=v_l, out=out_l, lse=lse_l, logical=logical,
                                     hist=hist)
 
 
 def run_decode(torch, ha, grp, synth, struct, args, device):
-    shape, group, plan, data = build_decode(torch, ha, grp, synth, struct, device, struct.workload)
+    shape, group, plan, data = build_decode(torch, ha, grp, synth, struct, device, struct.workload,
+                                            fuse=not args.separate_append)
     kv_len = data["hist"] + 1
-    per_layer_bytes = [decode_layer_bytes(shape, layer.kind, kv_len) for layer in group.layers]
+    # per layer: the attention's bytes plus the new token's K/V read and written
+    # by the append (fused into the decode call, or a call of its own)
+    layer_append = struct.batch * kv_bytes_per_token(shape) * 2
+    per_layer_bytes = [decode_layer_bytes(shape, layer.kind, kv_len) + layer_append for layer in group.layers]
     step_bytes = sum(per_layer_bytes)
-    append_bytes = len(group.layers) * struct.batch * kv_bytes_per_token(shape) * 2
+    append_bytes = len(group.layers) * layer_append
 
     stream = torch.cuda.current_stream()
     graph = None
@@ -245,8 +253,9 @@ def run_decode(torch, ha, grp, synth, struct, args, device):
     swa_ms = float(np.mean(call_ms[swa_idx]))
     full_layer = [i for i, layer in enumerate(group.layers) if layer.kind == "full"][0]
     swa_layer = [i for i, layer in enumerate(group.layers) if layer.kind == "swa"][0]
-    full_bytes = per_layer_bytes[full_layer]
-    swa_bytes = per_layer_bytes[swa_layer]
+    call_extra = 0 if app_idx else layer_append     # the decode call appends only when fused
+    full_bytes = per_layer_bytes[full_layer] - layer_append + call_extra
+    swa_bytes = per_layer_bytes[swa_layer] - layer_append + call_extra
     info = {
         "step_bytes": step_bytes,
         "append_bytes": append_bytes,
@@ -254,7 +263,8 @@ def run_decode(torch, ha, grp, synth, struct, args, device):
         "full_decode_gbs": full_bytes / full_ms / 1e6,
         "swa_decode_ms": swa_ms,
         "swa_decode_gbs": swa_bytes / swa_ms / 1e6,
-        "append_ms_avg": float(np.mean(call_ms[app_idx])),
+        "append_ms_avg": float(np.mean(call_ms[app_idx])) if app_idx else None,
+        "fused_append": not app_idx,
         "calls_ms": by_label,
         "graph": graph is not None,
         "splits_full": ha.hybrid_attn_decode_splits(shape, ha.HA_FULL, struct.batch, int(kv_len.max())),

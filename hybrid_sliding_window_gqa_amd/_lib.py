@@ -25,7 +25,7 @@ HA_F32 = 1
 HA_SWA = 0
 HA_FULL = 1
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 # Every symbol include/hybrid_attn.h declares.
 EXPORTS = (
@@ -91,7 +91,7 @@ def load() -> ctypes.CDLL:
     lib.full_pool_append.argtypes = append_args
     lib.window_safe_match.argtypes = [p, i64, p, i64, p, i32, ctypes.POINTER(i64)]
     lib.hybrid_attn_prefill.argtypes = [shp, view, p, p, i32, i32, i32, p, p, p, i32, p, p, p, sz, p]
-    lib.hybrid_attn_decode.argtypes = [shp, view, p, i32, i32, p, i32, p, p, i32, p, sz, p]
+    lib.hybrid_attn_decode.argtypes = [shp, view, p, i32, i32, p, p, p, i32, p, p, i32, p, sz, p]
     lib.hybrid_attn_workspace_size.argtypes = [shp, i32, i32, i32, i32, i32]
     lib.hybrid_attn_workspace_size.restype = sz
     lib.hybrid_attn_decode_splits.argtypes = [shp, i32, i32, i32, i32]

@@ -257,8 +257,13 @@ def hybrid_attn_prefill(shape: HeadShape, kv: KvView, hist_len: torch.Tensor, cu
 
 def hybrid_attn_decode(shape: HeadShape, kv: KvView, kv_len: torch.Tensor, q: torch.Tensor, max_kv_len: int,
                        out: torch.Tensor | None = None, lse: torch.Tensor | None = None, num_splits: int = 0,
-                       workspace: torch.Tensor | None = None, stream=None):
-    """Decode one query per sequence (its own K/V already appended) over the pool.
+                       workspace: torch.Tensor | None = None, stream=None, k_new: torch.Tensor | None = None,
+                       v_new: torch.Tensor | None = None):
+    """Decode one query per sequence at position kv_len - 1 over the pool.
+
+    Without k_new/v_new the query's own K/V must already be in the pool. With
+    them ([B, Hkv, D], same dtype as q) the call also appends that token, in
+    the same launch.
 
     Returns (out float32 [B, Hq, D], lse float32 [B, Hq])."""
     dev = kv.k.device
@@ -266,7 +271,14 @@ def hybrid_attn_decode(shape: HeadShape, kv: KvView, kv_len: torch.Tensor, q: to
     hq, d = shape.num_q_heads, shape.head_dim
     _check(kv_len, "kv_len", (b,), torch.int32, dev)
     _check(q, "q", (b, hq, d), None, dev)
-    dt = _in_dtype(q)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("pass both k_new and v_new (fused append) or neither")
+    if k_new is not None:
+        _check(k_new, "k_new", (b, shape.num_kv_heads, d), None, dev)
+        _check(v_new, "v_new", (b, shape.num_kv_heads, d), None, dev)
+        dt = _in_dtype(q, k_new, v_new)
+    else:
+        dt = _in_dtype(q)
     if out is None:
         out = torch.empty(b, hq, d, dtype=torch.float32, device=dev)
     if lse is None:
@@ -279,7 +291,9 @@ def hybrid_attn_decode(shape: HeadShape, kv: KvView, kv_len: torch.Tensor, q: to
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     c_shape, c_view = shape.c(), kv.c()
+    kp = k_new.data_ptr() if k_new is not None else None
+    vp = v_new.data_ptr() if v_new is not None else None
     check(load().hybrid_attn_decode(ctypes.byref(c_shape), ctypes.byref(c_view), kv_len.data_ptr(), b,
-                                    int(max_kv_len), q.data_ptr(), dt, out.data_ptr(), lse.data_ptr(),
+                                    int(max_kv_len), q.data_ptr(), kp, vp, dt, out.data_ptr(), lse.data_ptr(),
                                     int(num_splits), ws_ptr, ws_bytes, _stream_ptr(stream)))
     return out, lse

@@ -216,8 +216,9 @@ ha_status hybrid_attn_prefill(const ha_shape* shape, const ha_kv_view* kv, const
 }
 
 ha_status hybrid_attn_decode(const ha_shape* shape, const ha_kv_view* kv, const int32_t* kv_len, int32_t batch,
-                             int32_t max_kv_len, const void* q, int32_t in_dtype, float* out, float* lse,
-                             int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+                             int32_t max_kv_len, const void* q, const void* k_new, const void* v_new,
+                             int32_t in_dtype, float* out, float* lse, int32_t num_splits, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   ha::Geometry geo;
   ha_status st = check_shape(shape, &geo);
   if (st != HA_OK) return st;
@@ -228,6 +229,8 @@ ha_status hybrid_attn_decode(const ha_shape* shape, const ha_kv_view* kv, const 
   if (batch == 0) return ok();
   if (batch > 65535) return fail(HA_ERR_RANGE, "decode batch %d exceeds 65535", batch);
   if (!kv_len || !q || !out || !lse) return fail(HA_ERR_NULL, "kv_len, q, out or lse is NULL");
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(HA_ERR_NULL, "k_new and v_new must both be given (fused append) or both be NULL");
   const bool full = kv->kind == HA_FULL;
   const size_t need = decode_workspace(geo, full, batch, max_kv_len, num_splits);
   if (need > 0 && (!workspace || workspace_bytes < need))
@@ -244,6 +247,10 @@ ha_status hybrid_attn_decode(const ha_shape* shape, const ha_kv_view* kv, const 
   a.batch = batch;
   a.q = q;
   a.q_f32 = in_dtype == HA_F32;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_pool_w = static_cast<uint16_t*>(kv->k);
+  a.v_pool_w = static_cast<uint16_t*>(kv->v);
   a.out = out;
   a.lse = lse;
   a.split_blocks = ha::decode_split_blocks(full, geo.window, max_kv_len, batch, geo.hkv, num_splits);

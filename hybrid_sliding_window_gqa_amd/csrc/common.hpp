@@ -64,8 +64,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b));
 }
 
+// Two floats -> two round-to-nearest-even bfloat16 in one word (lo in bits
+// 0..15): a single two-operand v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  const f32x2v f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
 }
 
 // 16 bytes holding 8 bfloat16 values loaded from `src` (bf16 or f32 storage).
@@ -102,16 +107,41 @@ __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t by
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Cross-lane max / sum over the four lane groups (lanes c, c+16, c+32, c+48).
+// gfx950 lane swaps, one VALU instruction each:
+//   permlane32_swap: lanes 32..63 of a <-> lanes 0..31 of b;
+//   permlane16_swap: the odd 16-lane rows of a <-> the even rows of b.
+// Called with a == b, they leave a = the low half (rows 0, 2) duplicated
+// and b = the high half (rows 1, 3) duplicated, so op(a, b) combines lanes
+// l and l^32 (resp. l^16) in every lane. Written as inline asm on two
+// registers: the compiler's builtin folds the two results into one when
+// both operands are the same value, which is wrong for this instruction.
+// The leading s_nop covers the VALU-write -> permlane-read hazard.
+__device__ __forceinline__ void permlane32_swap(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void permlane16_swap(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
+// Max / sum over the four lane groups (lanes c, c+16, c+32, c+48), the same
+// value in all of them.
 __device__ __forceinline__ float group4_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  float a = v, b = v;
+  permlane32_swap(a, b);
+  v = fmaxf(a, b);
+  a = v;
+  b = v;
+  permlane16_swap(a, b);
+  return fmaxf(a, b);
 }
 __device__ __forceinline__ float group4_sum(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  float a = v, b = v;
+  permlane32_swap(a, b);
+  v = a + b;
+  a = v;
+  b = v;
+  permlane16_swap(a, b);
+  return a + b;
 }
 
 }  // namespace ha

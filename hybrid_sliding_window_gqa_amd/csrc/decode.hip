@@ -23,9 +23,17 @@
 //     per lane = two dim tiles, again 1 KiB contiguous per instruction) and
 //     accumulates O^T += V^T P^T, where P^T is the softmax tile in exactly the
 //     accumulator layout.
-// Page ids are scalar loads issued two blocks ahead of their use. The four
-// waves merge through LDS; a workgroup writes either the final row (one
-// split) or a partial (o, lse) for the reduce kernel.
+// Page ids are scalar loads issued two blocks ahead of their use. The waves
+// merge through LDS; a workgroup writes either the final row (one split) or a
+// partial (o, lse) for the reduce kernel.
+//
+// Fused append. When the caller passes the new token's K/V (k_new/v_new), the
+// pool does not hold position t yet: the wave that consumes the block of
+// position t patches the token's K row and V column into its operand
+// registers after the block's load, and after consuming the block writes the
+// token into the pool (ring slot t mod W, or page t/16 at row t mod 16). No
+// other workgroup reads that slot in this launch, so the result equals
+// append-then-decode with one launch instead of two.
 #include <climits>
 #include <cmath>
 
@@ -107,6 +115,29 @@ __device__ __forceinline__ void consume_block(BlockOps<D>& ops, const u32x4* qop
 #pragma unroll
   for (int d = 0; d < DT; ++d) o[d] = mfma_16x16x16(ops.v[d], pb, o[d]);
 }
+
+// Replace 16-bit element r (0..3) of a u32x2 holding four bf16 values.
+__device__ __forceinline__ void set_bf16(u32x2& w, int r, uint32_t bits) {
+  const uint32_t shift = (r & 1) * 16;
+  const uint32_t keep = ~(0xffffu << shift);
+  if (r < 2) w.x = (w.x & keep) | (bits << shift);
+  else w.y = (w.y & keep) | (bits << shift);
+}
+
+template <bool kF32>
+__device__ __forceinline__ uint32_t load_bf16_bits(const void* src, int64_t elem) {
+  if constexpr (kF32) return f32_to_bf16_bits(static_cast<const float*>(src)[elem]);
+  else return static_cast<const uint16_t*>(src)[elem];
+}
+
+// The new token's operand pieces for the wave that owns its block: K chunk
+// (m, q4) of the token row (used by lanes c16 == row) and the V values of
+// channels 32p + c16 and 32p + 16 + c16 (used by lanes q4 == row / 4).
+template <int D>
+struct NewToken {
+  u32x4 k[D / 32];
+  uint32_t v[D / 16];
+};
 
 }  // namespace
 
@@ -195,6 +226,35 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
     }
   }
 
+  // Fused append: block of position t, its row in the block, and whether
+  // this wave consumes that block.
+  const bool fuse = a.k_new != nullptr;
+  const int new_blk = kFull ? (t >> 4) : ((t % W) >> 4);
+  const int new_row = t & (kBlock - 1);
+  const bool new_mine = fuse && new_blk >= first && new_blk < last && (new_blk - first) % kWaves == wave;
+  NewToken<D> nt;
+  if (new_mine) {
+    const int64_t src = (static_cast<int64_t>(b) * hkv + g) * D;
+#pragma unroll
+    for (int m = 0; m < KS; ++m) nt.k[m] = load8_as_bf16<kQF32>(a.k_new, src + 32 * m + 8 * q4);
+#pragma unroll
+    for (int p = 0; p < D / 32; ++p) {
+      nt.v[2 * p] = load_bf16_bits<kQF32>(a.v_new, src + 32 * p + c16);
+      nt.v[2 * p + 1] = load_bf16_bits<kQF32>(a.v_new, src + 32 * p + 16 + c16);
+    }
+  }
+  auto patch_new = [&](BlockOps<D>& ops, int i) {
+    if (!new_mine || i != new_blk) return;
+    if (c16 == new_row) {
+#pragma unroll
+      for (int m = 0; m < KS; ++m) ops.k[m] = nt.k[m];
+    }
+    if (q4 == (new_row >> 2)) {
+#pragma unroll
+      for (int d = 0; d < DT; ++d) set_bf16(ops.v[d], new_row & 3, nt.v[d]);
+    }
+  };
+
   const float sl2 = a.geo.scale * kLog2e;
   float m_run = -INFINITY;  // running max of this head (log2 domain), same in all lane groups
   float l_run = 0.0f;       // partial sum over this lane's keys
@@ -225,19 +285,44 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
   // block is consumed from A after the loop. Loads past `last` read nothing.
   const int nmine = (last > ia) ? (last - ia + kStep - 1) / kStep : 0;
   for (int k = 0; k + 1 < nmine; k += 2) {
+    patch_new(A, ia);
     if (base_a >= 0) consume_block<D>(A, qop, kBlock * ia, t, is_partial(ia), sl2, m_run, l_run, o, q4);
     ia += 2 * kStep;
     base_a = base_of(ia, pg_a2);
     load_block<D>(A, a.k_pool, a.v_pool, base_a, q4, c16);
     if constexpr (kFull) pg_a2 = page_of(ia + 2 * kStep);
+    patch_new(B, ib);
     if (base_b >= 0) consume_block<D>(B, qop, kBlock * ib, t, is_partial(ib), sl2, m_run, l_run, o, q4);
     ib += 2 * kStep;
     base_b = base_of(ib, pg_b2);
     load_block<D>(B, a.k_pool, a.v_pool, base_b, q4, c16);
     if constexpr (kFull) pg_b2 = page_of(ib + 2 * kStep);
   }
-  if ((nmine & 1) && base_a >= 0)
-    consume_block<D>(A, qop, kBlock * ia, t, is_partial(ia), sl2, m_run, l_run, o, q4);
+  if (nmine & 1) {
+    patch_new(A, ia);
+    if (base_a >= 0) consume_block<D>(A, qop, kBlock * ia, t, is_partial(ia), sl2, m_run, l_run, o, q4);
+  }
+
+  // Fused append: the owner wave writes the token into the pool, after its
+  // block has been read and consumed.
+  if (new_mine) {
+    const int64_t nb = base_of(new_blk, kFull ? page_row[new_blk] : 0);
+    if (nb >= 0) {
+      if (c16 == new_row) {
+#pragma unroll
+        for (int m = 0; m < KS; ++m)
+          *reinterpret_cast<u32x4*>(a.k_pool_w + nb + 8 * (64 * m + lane)) = nt.k[m];
+      }
+      if (q4 == (new_row >> 2)) {
+        uint16_t* vb = a.v_pool_w + nb;
+#pragma unroll
+        for (int p = 0; p < D / 32; ++p) {
+          vb[v_elem(new_row, 32 * p + c16)] = static_cast<uint16_t>(nt.v[2 * p]);
+          vb[v_elem(new_row, 32 * p + 16 + c16)] = static_cast<uint16_t>(nt.v[2 * p + 1]);
+        }
+      }
+    }
+  }
 
   // Merge the four waves.
   l_run = group4_sum(l_run);

@@ -48,6 +48,10 @@ struct DecodeArgs {
   int32_t split_blocks;   // 16-token blocks per split
   float* part_o;          // [batch][hq][splits][d]
   float* part_lse;        // [batch][hq][splits]  (log2 domain)
+  const void* k_new;      // [batch][hkv][d] new token's K (NULL: already in the pool)
+  const void* v_new;      // [batch][hkv][d]
+  uint16_t* k_pool_w;     // writable pool views for the fused append
+  uint16_t* v_pool_w;
 };
 
 struct PrefillArgs {

@@ -132,10 +132,11 @@ def _append_call(lib, shape, layer, pos0, cu_new, k_new, v_new):
 
 
 def plan_decode(group: HybridGroup, q, k_new, v_new, pos, kv_len, max_kv_len: int, out, lse,
-                num_splits: int = 0) -> Plan:
+                num_splits: int = 0, fuse_append: bool = True) -> Plan:
     """Decode step over every layer: q/out/lse/k_new/v_new are per-layer lists of
     [B, Hq, D] / [B, Hkv, D] tensors; pos [B] is the new token's position and
-    kv_len [B] = pos + 1."""
+    kv_len [B] = pos + 1. With fuse_append each layer is one call that appends
+    the new token and attends; otherwise an append call precedes each decode."""
     lib = _lib.load()
     shape = group.shape
     b, hq, hkv, d = group.batch, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
@@ -150,16 +151,20 @@ def plan_decode(group: HybridGroup, q, k_new, v_new, pos, kv_len, max_kv_len: in
         _check(v_new[li], "v_new", (b, hkv, d), None, dev)
         _check(out[li], "out", (b, hq, d), torch.float32, dev)
         _check(lse[li], "lse", (b, hq), torch.float32, dev)
-        calls.append(_append_call(lib, shape, layer, pos, cu_one, k_new[li], v_new[li]))
-        labels.append(f"append[{li}:{layer.kind}]")
+        if not fuse_append:
+            calls.append(_append_call(lib, shape, layer, pos, cu_one, k_new[li], v_new[li]))
+            labels.append(f"append[{li}:{layer.kind}]")
         kind = _lib.HA_SWA if layer.kind == SWA else _lib.HA_FULL
         need = hybrid_attn_workspace_size(shape, kind, True, b, max_kv_len, num_splits)
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         c_shape, c_view = shape.c(), layer.view.c()
+        kp = k_new[li].data_ptr() if fuse_append else None
+        vp = v_new[li].data_ptr() if fuse_append else None
         args = (ctypes.byref(c_shape), ctypes.byref(c_view), kv_len.data_ptr(), b, int(max_kv_len),
-                q[li].data_ptr(), _in_dtype(q[li]), out[li].data_ptr(), lse[li].data_ptr(), int(num_splits),
-                ws.data_ptr() if need else None, need)
-        calls.append(_Call(lib.hybrid_attn_decode, args, (c_shape, c_view, ws, kv_len, cu_one)))
+                q[li].data_ptr(), kp, vp, _in_dtype(q[li], k_new[li], v_new[li]), out[li].data_ptr(),
+                lse[li].data_ptr(), int(num_splits), ws.data_ptr() if need else None, need)
+        calls.append(_Call(lib.hybrid_attn_decode, args,
+                           (c_shape, c_view, ws, kv_len, cu_one, k_new[li], v_new[li])))
         labels.append(f"decode[{li}:{layer.kind}]")
     return Plan(calls, labels)
 

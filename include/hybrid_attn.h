@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define HA_ABI_VERSION 1
+#define HA_ABI_VERSION 2
 
 typedef enum ha_status {
   HA_OK = 0,
@@ -178,19 +178,26 @@ ha_status hybrid_attn_prefill(const ha_shape* shape, const ha_kv_view* kv, const
 
 /* ---- a6/a7/a8: decode attention with split-K ([YLY] 为什么选择 Hybrid SWA
  *          架构 and Decode加速与多模态优化: decode cost follows KV bytes read) --
- * One query per sequence at position t = kv_len[b] - 1, whose own K/V must
- * already be appended. Keys are read from the pool only. Full layers split
- * the key range over workgroups (split-K) and merge the partial results with
- * lse = ln sum_s exp(lse_s), o = sum_s exp(lse_s - lse) o_s.
+ * One query per sequence at position t = kv_len[b] - 1; it sees its own
+ * token. Full layers split the key range over workgroups (split-K) and merge
+ * the partial results with lse = ln sum_s exp(lse_s), o = sum_s exp(lse_s -
+ * lse) o_s.
  *   kv_len int32 [batch] device (0 = empty row: out = 0, lse = -inf)
  *   max_kv_len >= every kv_len[b] (host; sizes the split grid)
  *   q [batch][Hq][D] in_dtype; out float32 [batch][Hq][D]; lse float32 [batch][Hq]
+ *   k_new, v_new: the new token's K/V, [batch][Hkv][D] in_dtype, or both NULL.
+ *     Given: the pool holds positions < t and the call also appends position
+ *     t (ring slot t mod W, or page t/16 row t mod 16) -- the same pool and
+ *     outputs as swa_ring_append / full_pool_append followed by this call
+ *     with NULL, in one launch. NULL: position t must already be in the pool
+ *     and the pool is only read.
  *   num_splits: maximum key splits per sequence, 0 = automatic
  *   workspace: hybrid_attn_workspace_size(..., decode = 1) bytes. */
 ha_status hybrid_attn_decode(const ha_shape* shape, const ha_kv_view* kv, const int32_t* kv_len,
-                             int32_t batch, int32_t max_kv_len, const void* q, int32_t in_dtype,
-                             float* out, float* lse, int32_t num_splits, void* workspace,
-                             size_t workspace_bytes, void* stream);
+                             int32_t batch, int32_t max_kv_len, const void* q, const void* k_new,
+                             const void* v_new, int32_t in_dtype, float* out, float* lse,
+                             int32_t num_splits, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* Workspace bytes needed by hybrid_attn_decode (decode = 1: max_kv_len and
  * num_splits as passed to the call) or hybrid_attn_prefill (decode = 0: pass

@@ -53,10 +53,11 @@ def view(kind=_lib.HA_FULL, k=FAKE, v=FAKE, table=FAKE, stride=4, blocks=8):
     return HaKvView(kind, k, v, blocks, table, stride)
 
 
-def decode_call(lib, shape, kv, batch=2, max_len=100, q=FAKE, dtype=0, splits=0, ws=None, ws_bytes=0):
+def decode_call(lib, shape, kv, batch=2, max_len=100, q=FAKE, dtype=0, splits=0, ws=None, ws_bytes=0,
+                k_new=None, v_new=None):
     return lib.hybrid_attn_decode(ctypes.byref(shape) if shape is not None else None,
-                                  ctypes.byref(kv) if kv is not None else None, FAKE, batch, max_len, q, dtype,
-                                  FAKE, FAKE, splits, ws, ws_bytes, None)
+                                  ctypes.byref(kv) if kv is not None else None, FAKE, batch, max_len, q, k_new,
+                                  v_new, dtype, FAKE, FAKE, splits, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize(
@@ -90,6 +91,9 @@ def test_null_and_range_errors(lib):
     assert decode_call(lib, s, view(), dtype=7) == _lib.HA_ERR_UNSUPPORTED
     assert decode_call(lib, s, view(kind=3)) == _lib.HA_ERR_UNSUPPORTED
     assert decode_call(lib, s, view(), batch=70000) == _lib.HA_ERR_RANGE
+    # the fused append needs both new-token tensors or neither
+    assert decode_call(lib, s, view(), k_new=FAKE) == _lib.HA_ERR_NULL
+    assert decode_call(lib, s, view(), v_new=FAKE) == _lib.HA_ERR_NULL
 
 
 def test_decode_workspace_checked(lib):

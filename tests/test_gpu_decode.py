@@ -23,7 +23,9 @@ pytestmark = pytest.mark.gpu
 LENS = [1, 2, 15, 16, 17, 127, 128, 129, 130, 300, 1000, 2049]
 
 
-def build(shape, kind, lens, seed, table_perm_seed=0, ring_order=None):
+def build(shape, kind, lens, seed, table_perm_seed=0, ring_order=None, appended=None):
+    """Pools holding each sequence's positions [0, appended[b]) (default: all
+    lens[b]), page tables sized for lens[b] tokens."""
     gen = make_generator(seed)
     hkv, d = shape.num_kv_heads, shape.head_dim
     seq = [(randn_bf16(gen, max(n, 1), hkv, d), randn_bf16(gen, max(n, 1), hkv, d)) for n in lens]
@@ -45,7 +47,7 @@ def build(shape, kind, lens, seed, table_perm_seed=0, ring_order=None):
             off += c
         pool = ha.FullPagePool(shape, num_pages, "cuda", fill=float("nan"))
         view = pool.view(i32(table))
-    append_history(shape, view, seq, [0] * len(lens), lens)
+    append_history(shape, view, seq, [0] * len(lens), lens if appended is None else appended)
     return seq, q, pool, view
 
 
@@ -146,3 +148,52 @@ def test_workspace_reused_across_calls():
         torch.cuda.synchronize()
         ref_o, ref_l = oracle_decode(shape, ha.HA_FULL, seq, q, call_lens)
         assert_close(host(out), host(lse), ref_o, ref_l, f"lens={call_lens} splits={splits}")
+
+
+def pool_bits(pool):
+    return pool.k.view(torch.int16).clone(), pool.v.view(torch.int16).clone()
+
+
+@pytest.mark.parametrize("kind", [ha.HA_SWA, ha.HA_FULL])
+@pytest.mark.parametrize("hq,hkv,d,window,splits", [(64, 8, 128, 128, 0), (4, 1, 64, 32, 0), (64, 8, 128, 128, 7),
+                                                      (32, 2, 64, 64, 3)])
+def test_fused_append_equals_append_then_decode(kind, hq, hkv, d, window, splits):
+    """Passing the new token's K/V appends it in the same launch: outputs and
+    the pool afterwards are bit-identical to append-then-decode."""
+    shape = ha.HeadShape(hq, hkv, d, window=window)
+    seed = 40 + hq + d
+    seq, q, pool_a, view_a = build(shape, kind, LENS, seed=seed)
+    _, _, pool_b, view_b = build(shape, kind, LENS, seed=seed, appended=[n - 1 for n in LENS])
+    k_new = torch.stack([seq[b][0][n - 1] for b, n in enumerate(LENS)]).contiguous()
+    v_new = torch.stack([seq[b][1][n - 1] for b, n in enumerate(LENS)]).contiguous()
+    oa, la = ha.hybrid_attn_decode(shape, view_a, i32(LENS), q, max(LENS), num_splits=splits)
+    ob, lb = ha.hybrid_attn_decode(shape, view_b, i32(LENS), q, max(LENS), num_splits=splits,
+                                   k_new=k_new, v_new=v_new)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_decode(shape, kind, seq, q, LENS)
+    assert_close(host(ob), host(lb), ref_o, ref_l, f"fused kind={kind} shape={shape}")
+    assert torch.equal(oa, ob) and torch.equal(la, lb)
+    ka, va = pool_bits(pool_a)
+    kb, vb = pool_bits(pool_b)
+    assert torch.equal(ka, kb) and torch.equal(va, vb)
+
+
+@pytest.mark.parametrize("kind", [ha.HA_SWA, ha.HA_FULL])
+def test_fused_append_float32_sources_and_repeat(kind):
+    """float32 q/k_new/v_new are rounded like the append calls round them, and
+    repeating the fused call (the token is then already in the pool) is
+    idempotent."""
+    shape = ha.HeadShape(4, 1, 64, softmax_scale=1.0 / 8.0)
+    lens = [1, 16, 17, 129, 300]
+    seq, q, pool_a, view_a = build(shape, kind, lens, seed=12)
+    _, _, pool_b, view_b = build(shape, kind, lens, seed=12, appended=[n - 1 for n in lens])
+    k_new = torch.stack([seq[b][0][n - 1] for b, n in enumerate(lens)]).float().contiguous()
+    v_new = torch.stack([seq[b][1][n - 1] for b, n in enumerate(lens)]).float().contiguous()
+    oa, la = ha.hybrid_attn_decode(shape, view_a, i32(lens), q.float(), max(lens))
+    for _ in range(2):
+        ob, lb = ha.hybrid_attn_decode(shape, view_b, i32(lens), q.float(), max(lens), k_new=k_new, v_new=v_new)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob) and torch.equal(la, lb)
+        ka, va = pool_bits(pool_a)
+        kb, vb = pool_bits(pool_b)
+        assert torch.equal(ka, kb) and torch.equal(va, vb)

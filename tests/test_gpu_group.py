@@ -1,6 +1,7 @@
-"""a9 on the GPU: a 6:1 layer group runs its calls in order (append then attend
-for decode; attend then append for prefill), matches the oracle per layer,
-and replays bit-identically from a captured HIP graph."""
+"""a9 on the GPU: a 6:1 layer group runs its calls in order (append then
+attend for decode, or one fused call per layer; attend then append for
+prefill), matches the oracle per layer, and replays bit-identically from a
+captured HIP graph."""
 
 import numpy as np
 import pytest
@@ -32,7 +33,8 @@ def setup_group(lens, shape, seed):
     return group, seqs
 
 
-def test_decode_step_order_oracle_and_graph_replay():
+@pytest.mark.parametrize("fuse", [True, False])
+def test_decode_step_order_oracle_and_graph_replay(fuse):
     shape = ha.HeadShape(16, 2, 128)
     lens = [5, 127, 128, 700, 1300]
     b = len(lens)
@@ -48,8 +50,12 @@ def test_decode_step_order_oracle_and_graph_replay():
     vn = [torch.stack([s[1][n] for s, n in zip(seqs[li], lens)]).contiguous() for li in range(7)]
     out = [torch.empty(b, 16, 128, device="cuda") for _ in range(7)]
     lse = [torch.empty(b, 16, device="cuda") for _ in range(7)]
-    plan = grp.plan_decode(group, q, kn, vn, i32(lens), i32([n + 1 for n in lens]), max(lens) + 1, out, lse)
-    assert plan.labels[:2] == ["append[0:swa]", "decode[0:swa]"] and plan.labels[-1] == "decode[6:full]"
+    plan = grp.plan_decode(group, q, kn, vn, i32(lens), i32([n + 1 for n in lens]), max(lens) + 1, out, lse,
+                           fuse_append=fuse)
+    if fuse:   # one call per layer appends the token and attends
+        assert plan.labels == [f"decode[{i}:{k}]" for i, k in enumerate(grp.GROUP_KINDS)]
+    else:
+        assert plan.labels[:2] == ["append[0:swa]", "decode[0:swa]"] and plan.labels[-1] == "decode[6:full]"
     plan.run()
     torch.cuda.synchronize()
     eager = [(o.clone(), l.clone()) for o, l in zip(out, lse)]
