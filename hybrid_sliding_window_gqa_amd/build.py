@@ -71,8 +71,24 @@ def build(verbose: bool = False) -> str:
         list(pool.map(run, cmds))
     tmp = LIB_PATH + ".tmp"
     run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    _check_kernel_stubs(tmp)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
+
+
+def _check_kernel_stubs(lib: str) -> None:
+    """Fail when a kernel's host launch stub is referenced but not defined.
+
+    clang's host pass can drop a kernel template instantiation without a
+    diagnostic (for instance when a device-only construct inside it cannot be
+    checked for the host); the library then links but cannot be loaded."""
+    nm = shutil.which("nm")
+    if nm is None:
+        return
+    res = subprocess.run([nm, "-D", "--undefined-only", lib], capture_output=True, text=True)
+    missing = [line.split()[-1] for line in res.stdout.splitlines() if "__device_stub__" in line]
+    if missing:
+        raise RuntimeError("kernel launch stubs missing from the host objects: " + ", ".join(missing))
 
 
 if __name__ == "__main__":

@@ -18,8 +18,10 @@
 //     kv head); a row is a (query position, query head of the GQA group) pair,
 //     so the whole group shares every K/V tile. Each wave owns 32 rows (two
 //     16-row MFMA column groups). Keys stream in 64-key tiles of four blocks;
-//     wave w stages block w of the next tile (global -> registers -> LDS)
-//     while the current tile is consumed, so one barrier per tile suffices.
+//     wave w stages block w of the next tile while the current tile is
+//     consumed -- K straight from global memory into LDS (buffer loads with
+//     the LDS bit), V through registers -- so one barrier per tile suffices.
+//     LDS operand reads are scheduled two steps ahead of their MFMAs.
 //     The LDS tiles are plain copies of the four blocks; since blocks are in
 //     operand order, every operand read is one ds_read_b128 at 16 * lane:
 //     consecutive lanes, consecutive 16 bytes, no bank conflicts.
@@ -295,9 +297,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  u32x4 stk[CPL], stv[CPL];
+  u32x4 stv[CPL];
   int st_pos = -1;
-  auto load_tile = [&](int tile, int pg) {
+  // K goes global -> LDS directly (buffer_load ... lds: lane l's 16 bytes land
+  // at the wave's LDS base + 16 l), V through registers (partial history
+  // blocks get their unwritten tokens zeroed on the way).
+  auto load_tile = [&](int tile, int pg, int buf) {
     int valid;
     const int64_t base = block_of(tile, pg, valid);
     const int64_t b0 = base >= 0 ? base : 0;
@@ -310,7 +315,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int u = 0; u < CPL; ++u) {
       const int e = lane + 64 * u;      // 16-byte chunk of the block
-      stk[u] = buf_load16(rk, 16 * e);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rk, (__attribute__((address_space(3))) void*)(&sm.k[buf][wave * (kBlk / 8) + 64 * u]), 16, 16 * e, 0, 0, 0);
       stv[u] = buf_load16(rv, 16 * e);
     }
     if (tile < n_hist_tiles && valid < kBlock) {
@@ -327,8 +333,6 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const int slot = wave & 1;
 #pragma unroll
     for (int u = 0; u < CPL; ++u) {
-      const int e = lane + 64 * u;   // unit e of the block
-      sm.k[buf][wave * (kBlk / 8) + e] = stk[u];
       // V unit (a = u, lane): half 0 -> dim tile 2u, half 1 -> dim tile 2u + 1
       const int base = ((pair * CPL + u) * 2) * 64 + lane;        // [pair][a][h=0][lane]
       vpair[2 * base + slot] = u32x2{stv[u].x, stv[u].y};
@@ -371,7 +375,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 
   fetch_pages(0);
   if (n_tiles > 0) {
-    load_tile(0, page_for(0));
+    load_tile(0, page_for(0), 0);
     store_tile(0);
   }
   // Everything loaded so far (Q, first tile) is complete before the loop, so
@@ -383,7 +387,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const int buf = tile & 1;
     const bool has_next = tile + 1 < n_tiles;
     if (((tile + 1) & 63) == 0 && tile + 1 < n_hist_tiles) fetch_pages(tile + 1);
-    if (has_next) load_tile(tile + 1, page_for(tile + 1));
+    if (has_next) load_tile(tile + 1, page_for(tile + 1), buf ^ 1);
 
     int kmin, kmax;
     bool exact;
@@ -397,17 +401,35 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       const u32x4* sk = sm.k[buf];
       const u32x4* sv = sm.v[buf];
       f32x4 s[kTileBlocks][kRowGroups];
+      u32x4 kcur[KS], knxt[KS];
+#pragma unroll
+      for (int m = 0; m < KS; ++m) kcur[m] = sk[64 * m + lane];
 #pragma unroll
       for (int kb = 0; kb < kTileBlocks; ++kb) {
+        if (kb + 1 < kTileBlocks) {
+#pragma unroll
+          for (int m = 0; m < KS; ++m) knxt[m] = sk[(kb + 1) * (kBlk / 8) + 64 * m + lane];
+        }
 #pragma unroll
         for (int rg = 0; rg < kRowGroups; ++rg) s[kb][rg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < KS; ++m) {
-          const u32x4 kop = sk[kb * (kBlk / 8) + 64 * m + lane];
 #pragma unroll
-          for (int rg = 0; rg < kRowGroups; ++rg) s[kb][rg] = mfma_16x16x32(kop, qop[rg][m], s[kb][rg]);
+          for (int rg = 0; rg < kRowGroups; ++rg) s[kb][rg] = mfma_16x16x32(kcur[m], qop[rg][m], s[kb][rg]);
+        }
+        if (kb + 1 < kTileBlocks) {
+#pragma unroll
+          for (int m = 0; m < KS; ++m) kcur[m] = knxt[m];
         }
       }
+      // Keep two blocks of K operands in flight: 8 LDS reads, then 8 MFMAs
+      // alternating with the next block's 4 reads.
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
 
       if (need_mask) {
 #pragma unroll
@@ -451,16 +473,22 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         }
       }
       u32x4 pb[kTileBlocks / 2][kRowGroups];   // P^T for block pairs: B operands of P.V
+      float m_use[kRowGroups], lsum[kRowGroups];
 #pragma unroll
       for (int rg = 0; rg < kRowGroups; ++rg) {
-        const float m_use = (m_run[rg] == -INFINITY) ? 0.0f : m_run[rg];
-        float lsum = 0.0f;
+        m_use[rg] = (m_run[rg] == -INFINITY) ? 0.0f : m_run[rg];
+        lsum[rg] = 0.0f;
+      }
+      // Block pair 0 first: its P.V products can start while pair 1's
+      // probabilities are still being computed.
 #pragma unroll
-        for (int kb = 0; kb < kTileBlocks; ++kb) {
+      for (int kb = 0; kb < kTileBlocks; ++kb) {
+#pragma unroll
+        for (int rg = 0; rg < kRowGroups; ++rg) {
           float p[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s[kb][rg][r] * sl2 - m_use);
-          lsum += (p[0] + p[1]) + (p[2] + p[3]);
+          for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s[kb][rg][r] * sl2 - m_use[rg]);
+          lsum[rg] += (p[0] + p[1]) + (p[2] + p[3]);
           const uint32_t lo = pack_bf16x2(p[0], p[1]), hi = pack_bf16x2(p[2], p[3]);
           if (kb & 1) {
             pb[kb / 2][rg].z = lo;
@@ -470,16 +498,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
             pb[kb / 2][rg].y = hi;
           }
         }
-        l_run[rg] += lsum;
       }
+#pragma unroll
+      for (int rg = 0; rg < kRowGroups; ++rg) l_run[rg] += lsum[rg];
 
       // P.V on v_mfma_f32_16x16x32_bf16, two 16-key blocks per product: the
       // reduction slots 8q..8q+3 of a lane are keys 4q..4q+3 of block kb,
       // slots 8q+4..8q+7 the same keys of block kb+1, in both operands.
 #pragma unroll
-      for (int p = 0; p < DT / 2; ++p) {
+      for (int pair = 0; pair < kTileBlocks / 2; ++pair) {
 #pragma unroll
-        for (int pair = 0; pair < kTileBlocks / 2; ++pair) {
+        for (int p = 0; p < DT / 2; ++p) {
           const u32x4 v0 = sv[((pair * (DT / 2) + p) * 2 + 0) * 64 + lane];   // dim tile 2p
           const u32x4 v1 = sv[((pair * (DT / 2) + p) * 2 + 1) * 64 + lane];   // dim tile 2p+1
 #pragma unroll
@@ -489,9 +518,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
           }
         }
       }
+      // V operand reads run two (dim tile, block pair) steps ahead of their MFMAs.
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+      for (int i = 0; i < (DT / 2) * (kTileBlocks / 2) - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
     }
 
     if (has_next) store_tile(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's direct K loads have landed
     __syncthreads();
   }
 
