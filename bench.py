@@ -378,6 +378,85 @@ def blas_thread_count():
         return 1
 
 
+def run_reuse(torch, ha, grp, synth, args, device):
+    """Prefix-reuse prefill: per sequence, the window-safe match L of the
+    request against its cached prefix, the reused history restored (pages
+    [0, L); ring positions [L-W, L)), then one pass of the recomputed tail +
+    new suffix (n = P + S - L tokens at [L, L+n)) through the 6:1 group
+    (attend, then append)."""
+    struct = synth.reuse_structure()
+    shape = ha.HeadShape(struct.shape.num_q_heads, struct.shape.num_kv_heads, struct.shape.head_dim,
+                         struct.shape.window)
+    b, w = struct.batch, shape.window
+    hq, hkv, d = shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    prefix, suffix = struct.hist.astype(np.int64), struct.new.astype(np.int64)
+    reuse_len = np.array([ha.window_safe_match(*synth.reuse_tokens(struct, s), w) for s in range(b)], np.int64)
+    n_new = prefix + suffix - reuse_len
+    group = grp.HybridGroup(shape, torch.as_tensor(struct.ring_id, device=device), struct.num_rings,
+                            torch.as_tensor(struct.page_table, device=device), struct.num_pages)
+    log(f"[bench] reuse: restoring history ({int(reuse_len.sum())} cached positions)")
+    for li, layer in enumerate(group.layers):
+        first = np.maximum(reuse_len - w, 0) if layer.kind == "swa" else np.zeros(b, np.int64)
+        counts = reuse_len - first
+        total = int(counts.sum())
+        if total == 0:
+            continue
+        k = synth.normal_bf16((total, hkv, d), "reuse", li, synth.K_VALUES, device)
+        v = synth.normal_bf16((total, hkv, d), "reuse", li, synth.V_VALUES, device)
+        fn = ha.swa_ring_append if layer.kind == "swa" else ha.full_pool_append
+        fn(shape, layer.view, torch.as_tensor(first.astype(np.int32), device=device),
+           torch.as_tensor(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32), device=device), k, v)
+        del k, v
+    t_new = int(n_new.sum())
+    qs, ks, vs, outs, lses = [], [], [], [], []
+    for li in range(len(group.layers)):
+        qs.append(synth.normal_bf16((t_new, hq, d), "reuse", li, synth.Q_VALUES + 3, device))
+        ks.append(synth.normal_bf16((t_new, hkv, d), "reuse", li, synth.K_VALUES + 3, device))
+        vs.append(synth.normal_bf16((t_new, hkv, d), "reuse", li, synth.V_VALUES + 3, device))
+        outs.append(torch.empty(t_new, hq, d, dtype=torch.float32, device=device))
+        lses.append(torch.empty(t_new, hq, dtype=torch.float32, device=device))
+    hist = torch.as_tensor(reuse_len.astype(np.int32), device=device)
+    cu = torch.as_tensor(np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32), device=device)
+    plan = grp.plan_prefill(group, qs, ks, vs, hist, cu, int(n_new.max()), outs, lses)
+    flops = {"swa": 0, "full": 0}
+    for kind in ("swa", "full"):
+        pairs = sum(visible_pairs_range(int(reuse_len[s]), int(n_new[s]), kind, w) for s in range(b))
+        flops[kind] = pairs * hq * 4 * d * list(group.kinds).count(kind)
+    total_flops = flops["swa"] + flops["full"]
+    torch.cuda.synchronize()
+    plan.run()                      # warm (re-running appends rewrites the same rows)
+    torch.cuda.synchronize()
+    passes = max(1, args.prefill_passes)
+    t0 = time.perf_counter()
+    for _ in range(passes):
+        plan.run()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / passes
+    evs = timed_events(torch, len(plan.calls))
+    plan.run_timed(evs, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    call_ms = dict(zip(plan.labels, [a.elapsed_time(e) for a, e in evs]))
+    full_ms = sum(v for lab, v in call_ms.items() if lab.startswith("prefill") and "full" in lab)
+    full_tf = flops["full"] / (full_ms * 1e-3) / 1e12
+    return {
+        "metric": METRIC,
+        "workload": f"prefix-reuse prefill: {b} sequences, cached prefix P~U[4096,65536] with evicted SWA slots, "
+                    f"window-safe reuse L (total {int(reuse_len.sum())}), recomputed tail + suffix U[512,2048] "
+                    f"= {t_new} new tokens, one 6:1 group, Hq/Hkv/D {hq}/{hkv}/{d}, bf16",
+        "pass_ms": dt * 1e3,
+        "tflops": total_flops / dt / 1e12,
+        "pct_mfma_peak": 100.0 * total_flops / dt / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "flops_per_pass": total_flops,
+        "full_layer_ms": full_ms,
+        "full_layer_tflops": full_tf,
+        "roofline": {"bound": "mfma", "achieved": full_tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": full_tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "hybrid_attn_prefill, full layer (stage_chunk_kernel + prefill_kernel<128,full>)"},
+        "mean_recomputed_tail": float((prefix - reuse_len).mean()),
+        "data": "synthetic",
+    }
+
+
 def cpu_baseline_prefill(torch, shape, group, qs, ks, vs, chunk, target_s):
     """Time the fp64 oracle on seeded sample rows of the chunked prefill
     (sequence 0; full and SWA layer alternately; all query heads) until about
@@ -494,11 +573,10 @@ def main():
         print(json.dumps(run_copy(torch, args, device)))
         return 0
 
-    struct = {"decode": synth.decode_structure, "reuse": None, "ragged": synth.ragged_structure}[args.workload]
-    if struct is None:
-        print("reuse workload runs in the tests; bench covers decode / ragged / chunked", file=sys.stderr)
-        return 2
-    struct = struct()
+    if args.workload == "reuse":
+        print(json.dumps(run_reuse(torch, ha, grp, synth, args, device)))
+        return 0
+    struct = {"decode": synth.decode_structure, "ragged": synth.ragged_structure}[args.workload]()
     log(f"[bench] workload={args.workload} building inputs")
     shape, group, data, dt, step_bytes, full_bytes, info = run_decode(torch, ha, grp, synth, struct, args, device)
     value = step_bytes / dt / 1e9

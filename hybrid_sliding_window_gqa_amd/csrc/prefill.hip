@@ -14,13 +14,17 @@
 //     operand order, common.hpp), zero-padded past the chunk's end. Every key
 //     source then looks the same to the attention kernel: a K block and a V
 //     block of 16*D bf16 each.
-//  2. prefill_kernel. Workgroup = 4 wavefronts = 128 rows of one (sequence,
-//     kv head); a row is a (query position, query head of the GQA group) pair,
-//     so the whole group shares every K/V tile. Each wave owns 32 rows (two
-//     16-row MFMA column groups). Keys stream in 64-key tiles of four blocks;
-//     wave w stages block w of the next tile while the current tile is
-//     consumed -- K straight from global memory into LDS (buffer loads with
-//     the LDS bit), V through registers -- so one barrier per tile suffices.
+//  2. prefill_kernel. A workgroup holds the rows of one (sequence, kv head);
+//     a row is a (query position, query head of the GQA group) pair, so the
+//     whole group shares every K/V tile. Each wave owns 32 rows (two 16-row
+//     MFMA column groups). Full layers: 8 waves (256 rows) share each staged
+//     tile, one workgroup per CU -- staging per MFMA is half of what 4 waves
+//     would need. SWA layers, bound by their Q reads and O writes: 4 waves,
+//     two workgroups per CU. Keys stream in 64-key tiles of four blocks; the
+//     waves stage the next tile (each a block or half of one) while the
+//     current one is consumed -- K straight from global memory into LDS
+//     (buffer loads with the LDS bit), V through registers -- so one barrier
+//     per tile suffices.
 //     LDS operand reads are scheduled two steps ahead of their MFMAs.
 //     The LDS tiles are plain copies of the four blocks; since blocks are in
 //     operand order, every operand read is one ds_read_b128 at 16 * lane:
@@ -48,12 +52,16 @@ namespace {
 
 constexpr int kRowsPerWave = 32;
 constexpr int kRowGroups = kRowsPerWave / 16;
-constexpr int kWaves = 4;
-constexpr int kRowsPerWg = kRowsPerWave * kWaves;  // 128
 constexpr int kTileKeys = 64;
-constexpr int kTileBlocks = kTileKeys / kBlock;   // 4 == kWaves: one block per wave
+constexpr int kTileBlocks = kTileKeys / kBlock;   // 4
 constexpr int kXcds = 8;
-static_assert(kTileBlocks == kWaves, "each wave stages one block of a tile");
+// Full layers: 8 waves (256 rows) share each staged tile, one workgroup per
+// CU. SWA layers, bound by their Q reads and O writes: 4 waves (128 rows),
+// two workgroups per CU so one's prologue/epilogue overlaps the other.
+template <bool kFull>
+constexpr int waves_per_wg() { return kFull ? 8 : 4; }
+template <bool kFull>
+constexpr int rows_per_wg() { return kRowsPerWave * waves_per_wg<kFull>(); }
 
 // LDS tiles as 16-byte units (alignment known to the compiler, so stores and
 // loads are single ds_write_b128 / ds_read_b128 instructions).
@@ -150,7 +158,11 @@ __global__ __launch_bounds__(256) void stage_chunk_kernel(PrefillArgs a) {
 
 // ---- 2. attention ----
 template <int D, bool kFull, bool kF32>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void prefill_kernel(PrefillArgs a) {
+  constexpr int kWaves = waves_per_wg<kFull>();
+  constexpr int kRowsPerWg = rows_per_wg<kFull>();
+  constexpr int kWavesPerBlock = kWaves / kTileBlocks;
+  static_assert(kWaves % kTileBlocks == 0, "each block of a tile is staged by whole waves");
   constexpr int KS = D / 32;            // QK^T reduction steps
   constexpr int DT = D / 16;            // output dim tiles
   constexpr int CPL = D / 32;           // 16-byte units per lane of one block
@@ -243,11 +255,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   // Page ids of this wave's history blocks, 64 tiles at a time: lane j holds
   // the page of tile (batch_base + j). One vector load per 64 tiles; the
   // per-tile id is a readlane (scalar), so the tile loop never waits on it.
+  // Wave w stages units [part * kStageUnits, +kStageUnits) of block sb.
+  constexpr int kStageUnits = CPL / kWavesPerBlock;
+  const int sb = wave / kWavesPerBlock;
+  const int part = wave % kWavesPerBlock;
   int pg_vec = -1;
   auto fetch_pages = [&](int batch_base) {
     if constexpr (kFull) {
       const int t = batch_base + lane;
-      const int lb = t * kTileBlocks + wave;
+      const int lb = t * kTileBlocks + sb;
       pg_vec = (t < n_hist_tiles && lb < hist_blocks) ? page_row[lb] : -1;
     }
   };
@@ -259,7 +275,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   // plus the number of leading valid keys of that block.
   auto block_of = [&](int tile, int pg, int& valid) -> int64_t {
     if (tile < n_hist_tiles) {
-      const int lb = tile * kTileBlocks + wave;
+      const int lb = tile * kTileBlocks + sb;
       if (lb >= hist_blocks) { valid = 0; return -1; }
       if constexpr (kFull) {
         valid = min(kBlock, hist - lb * kBlock);
@@ -270,7 +286,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         return ((static_cast<int64_t>(ring) * hkv + g) * W + kBlock * lb) * D;
       }
     } else {
-      const int cb = (first_ctile + tile - n_hist_tiles) * kTileBlocks + wave;  // chunk block
+      const int cb = (first_ctile + tile - n_hist_tiles) * kTileBlocks + sb;  // chunk block
       if (kBlock * cb >= i_end) { valid = 0; return -1; }
       valid = min(kBlock, i_end - kBlock * cb);
       return ((stage_blk0 + cb) * hkv + g) * kBlock * D;  // K part; V part is offset by stage_blocks
@@ -297,7 +313,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  u32x4 stv[CPL];
+  u32x4 stv[kStageUnits];
   int st_pos = -1;
   // K goes global -> LDS directly (buffer_load ... lds: lane l's 16 bytes land
   // at the wave's LDS base + 16 l), V through registers (partial history
@@ -313,32 +329,33 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp, bytes);
 #pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-      const int e = lane + 64 * u;      // 16-byte chunk of the block
+    for (int j = 0; j < kStageUnits; ++j) {
+      const int e = lane + 64 * (part * kStageUnits + j);      // 16-byte chunk of the block
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rk, (__attribute__((address_space(3))) void*)(&sm.k[buf][wave * (kBlk / 8) + 64 * u]), 16, 16 * e, 0, 0, 0);
-      stv[u] = buf_load16(rv, 16 * e);
+          rk, (__attribute__((address_space(3))) void*)(&sm.k[buf][sb * (kBlk / 8) + e - lane]), 16, 16 * e, 0, 0, 0);
+      stv[j] = buf_load16(rv, 16 * e);
     }
     if (tile < n_hist_tiles && valid < kBlock) {
       // unwritten or stale slots of a partial history block: zero their V
 #pragma unroll
-      for (int u = 0; u < CPL; ++u) stv[u] = keep_tokens_v(stv[u], lane >> 4, valid);
+      for (int j = 0; j < kStageUnits; ++j) stv[j] = keep_tokens_v(stv[j], lane >> 4, valid);
     }
-    if (lane < kBlock) st_pos = key_position(tile, wave * kBlock + lane);
+    if (part == 0 && lane < kBlock) st_pos = key_position(tile, sb * kBlock + lane);
   };
 
   auto store_tile = [&](int buf) {
     u32x2* vpair = reinterpret_cast<u32x2*>(sm.v[buf]);
-    const int pair = wave >> 1;
-    const int slot = wave & 1;
+    const int pair = sb >> 1;
+    const int slot = sb & 1;
 #pragma unroll
-    for (int u = 0; u < CPL; ++u) {
+    for (int j = 0; j < kStageUnits; ++j) {
+      const int u = part * kStageUnits + j;
       // V unit (a = u, lane): half 0 -> dim tile 2u, half 1 -> dim tile 2u + 1
       const int base = ((pair * CPL + u) * 2) * 64 + lane;        // [pair][a][h=0][lane]
-      vpair[2 * base + slot] = u32x2{stv[u].x, stv[u].y};
-      vpair[2 * (base + 64) + slot] = u32x2{stv[u].z, stv[u].w};
+      vpair[2 * base + slot] = u32x2{stv[j].x, stv[j].y};
+      vpair[2 * (base + 64) + slot] = u32x2{stv[j].z, stv[j].w};
     }
-    if (lane < kBlock) reinterpret_cast<int32_t*>(sm.pos[buf])[wave * kBlock + lane] = st_pos;
+    if (part == 0 && lane < kBlock) reinterpret_cast<int32_t*>(sm.pos[buf])[sb * kBlock + lane] = st_pos;
   };
 
   // Key-position bounds of a tile (uniform): [kmin, kmax]; exact = every key valid.
@@ -556,20 +573,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 template <int D>
 static void launch_prefill_d(const PrefillArgs& a, dim3 grid, hipStream_t stream) {
   const dim3 sgrid((a.max_new + kBlock - 1) / kBlock, a.batch);
+  const dim3 bfull(64 * waves_per_wg<true>()), bswa(64 * waves_per_wg<false>());
   if (a.in_f32) {
     hipLaunchKernelGGL((stage_chunk_kernel<D, true>), sgrid, dim3(256), 0, stream, a);
-    if (a.full) hipLaunchKernelGGL((prefill_kernel<D, true, true>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((prefill_kernel<D, false, true>), grid, dim3(256), 0, stream, a);
+    if (a.full) hipLaunchKernelGGL((prefill_kernel<D, true, true>), grid, bfull, 0, stream, a);
+    else hipLaunchKernelGGL((prefill_kernel<D, false, true>), grid, bswa, 0, stream, a);
   } else {
     hipLaunchKernelGGL((stage_chunk_kernel<D, false>), sgrid, dim3(256), 0, stream, a);
-    if (a.full) hipLaunchKernelGGL((prefill_kernel<D, true, false>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((prefill_kernel<D, false, false>), grid, dim3(256), 0, stream, a);
+    if (a.full) hipLaunchKernelGGL((prefill_kernel<D, true, false>), grid, bfull, 0, stream, a);
+    else hipLaunchKernelGGL((prefill_kernel<D, false, false>), grid, bswa, 0, stream, a);
   }
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (a.batch == 0 || a.max_new == 0) return hipSuccess;
-  const int qb = kRowsPerWg / a.geo.group;
+  const int qb = (a.full ? rows_per_wg<true>() : rows_per_wg<false>()) / a.geo.group;
   const int64_t qb_max = (a.max_new + qb - 1) / qb;
   const int64_t npairs = static_cast<int64_t>(a.batch) * a.geo.hkv;
   const int64_t ppx = (npairs + kXcds - 1) / kXcds;
