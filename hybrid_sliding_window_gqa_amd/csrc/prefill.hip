@@ -16,11 +16,13 @@
 //     block of 16*D bf16 each.
 //  2. prefill_kernel. A workgroup holds the rows of one (sequence, kv head);
 //     a row is a (query position, query head of the GQA group) pair, so the
-//     whole group shares every K/V tile. Each wave owns 32 rows (two 16-row
-//     MFMA column groups). Full layers: 8 waves (256 rows) share each staged
-//     tile, one workgroup per CU -- staging per MFMA is half of what 4 waves
-//     would need. SWA layers, bound by their Q reads and O writes: 4 waves,
-//     two workgroups per CU. Keys stream in 64-key tiles of four blocks; the
+//     whole group shares every K/V tile. Full layers: 8 waves of 48 rows
+//     (three 16-row MFMA column groups; 384 rows) share each staged tile, one
+//     workgroup per CU -- every wave reads the whole tile from LDS, so more
+//     rows per wave means fewer LDS bytes per MFMA, and staging per MFMA is a
+//     third of what 4 waves of 32 rows would need. SWA layers, bound by their
+//     Q reads and O writes: 4 waves of 32 rows, two workgroups per CU. Keys
+//     stream in 64-key tiles of four blocks; the
 //     waves stage the next tile (each a block or half of one) while the
 //     current one is consumed -- K straight from global memory into LDS
 //     (buffer loads with the LDS bit), V through registers -- so one barrier
@@ -30,10 +32,17 @@
 //     operand order, every operand read is one ds_read_b128 at 16 * lane:
 //     consecutive lanes, consecutive 16 bytes, no bank conflicts.
 //     Per tile and wave: S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (Q^T held in
-//     registers), exp2-domain online softmax per row (16 scores in-lane plus
-//     two cross-lane steps), P^T cast to bf16 in the accumulator layout, then
-//     O^T += V^T P^T, also on v_mfma_f32_16x16x32_bf16 (two key blocks per
-//     product; the older 16x16x16 form runs at half the rate on gfx950).
+//     registers), exp2-domain online softmax per row, P^T cast to bf16 in the
+//     accumulator layout, then O^T += V^T P^T, also on
+//     v_mfma_f32_16x16x32_bf16 (two key blocks per product; the older
+//     16x16x16 form runs at half the rate on gfx950). Full layers keep the
+//     softmax's vector work per score at one FMA, one exp2, one add and half
+//     a conversion: the exp2 reference is not the row max but any value that
+//     keeps every probability <= 2^16 (checked on the lane's partial row
+//     sums after the exp2s); only a tile that fails the check, or a row's
+//     first keys, takes the row max (a cross-lane reduction), rescales O and
+//     l and recomputes. SWA layers (a few tiles per row) take the row max
+//     every tile and raise the reference only past a slack.
 //     Tiles a wave sees completely skip masking; tiles no row of the wave
 //     sees are skipped.
 //
@@ -50,8 +59,6 @@ namespace ha {
 
 namespace {
 
-constexpr int kRowsPerWave = 32;
-constexpr int kRowGroups = kRowsPerWave / 16;
 constexpr int kTileKeys = 64;
 constexpr int kTileBlocks = kTileKeys / kBlock;   // 4
 constexpr int kXcds = 8;
@@ -61,7 +68,9 @@ constexpr int kXcds = 8;
 template <bool kFull>
 constexpr int waves_per_wg() { return kFull ? 8 : 4; }
 template <bool kFull>
-constexpr int rows_per_wg() { return kRowsPerWave * waves_per_wg<kFull>(); }
+constexpr int rows_per_wave() { return kFull ? 48 : 32; }
+template <bool kFull>
+constexpr int rows_per_wg() { return rows_per_wave<kFull>() * waves_per_wg<kFull>(); }
 
 // LDS tiles as 16-byte units (alignment known to the compiler, so stores and
 // loads are single ds_write_b128 / ds_read_b128 instructions).
@@ -78,9 +87,12 @@ struct Smem {
   int4 pos[2][kTileKeys / 4];
 };
 
-// Softmax reference slack (log2 units): the running max used as the exp2
-// reference is only raised when a tile's max exceeds it by more than this,
-// so probabilities stay <= 2^8 and the O/l rescale is rarely needed.
+// Largest partial row sum (one lane's 16 probabilities of a tile) accepted
+// without recomputing the tile against a raised reference (full layers).
+constexpr float kAcceptSum = 65536.0f;
+// Softmax reference slack (log2 units, SWA layers): the running max used as
+// the exp2 reference is only raised when a tile's max exceeds it by more
+// than this, so probabilities stay <= 2^8 and the O/l rescale is rare.
 constexpr float kRescaleSlack = 8.0f;
 
 // V unit of lane group q holds tokens 4q..4q+3 (for two channels): zero the
@@ -160,6 +172,8 @@ __global__ __launch_bounds__(256) void stage_chunk_kernel(PrefillArgs a) {
 template <int D, bool kFull, bool kF32>
 __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void prefill_kernel(PrefillArgs a) {
   constexpr int kWaves = waves_per_wg<kFull>();
+  constexpr int kRowsPerWave = rows_per_wave<kFull>();
+  constexpr int kRowGroups = kRowsPerWave / 16;
   constexpr int kRowsPerWg = rows_per_wg<kFull>();
   constexpr int kWavesPerBlock = kWaves / kTileBlocks;
   static_assert(kWaves % kTileBlocks == 0, "each block of a tile is staged by whole waves");
@@ -340,7 +354,10 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
 #pragma unroll
       for (int j = 0; j < kStageUnits; ++j) stv[j] = keep_tokens_v(stv[j], lane >> 4, valid);
     }
-    if (part == 0 && lane < kBlock) st_pos = key_position(tile, sb * kBlock + lane);
+    // Full-layer key positions are contiguous per tile (computed in the
+    // mask); only the SWA ring's positions are staged.
+    if constexpr (!kFull)
+      if (part == 0 && lane < kBlock) st_pos = key_position(tile, sb * kBlock + lane);
   };
 
   auto store_tile = [&](int buf) {
@@ -355,7 +372,8 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
       vpair[2 * base + slot] = u32x2{stv[j].x, stv[j].y};
       vpair[2 * (base + 64) + slot] = u32x2{stv[j].z, stv[j].w};
     }
-    if (part == 0 && lane < kBlock) reinterpret_cast<int32_t*>(sm.pos[buf])[sb * kBlock + lane] = st_pos;
+    if constexpr (!kFull)
+      if (part == 0 && lane < kBlock) reinterpret_cast<int32_t*>(sm.pos[buf])[sb * kBlock + lane] = st_pos;
   };
 
   // Key-position bounds of a tile (uniform): [kmin, kmax]; exact = every key valid.
@@ -418,103 +436,157 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
       const u32x4* sk = sm.k[buf];
       const u32x4* sv = sm.v[buf];
       f32x4 s[kTileBlocks][kRowGroups];
-      u32x4 kcur[KS], knxt[KS];
+      // S^T = K Q^T for the tile (then masked where needed).
+      auto scores = [&]() __attribute__((always_inline)) {
+        // Compiler-only fence: the recomputation must read K again rather
+        // than keep the first reads' registers alive across the softmax.
+        asm volatile("" ::: "memory");
+        // K operands stream through a short register window: operand j
+        // (block j / KS, reduction step j % KS) feeds one MFMA per row group.
+        constexpr int kKOps = kTileBlocks * KS;
+        constexpr int kAhead = kFull ? 3 : 8;   // K operands in flight
+        u32x4 kr[kKOps];
 #pragma unroll
-      for (int m = 0; m < KS; ++m) kcur[m] = sk[64 * m + lane];
+        for (int j = 0; j < kKOps; ++j) kr[j] = sk[(j / KS) * (kBlk / 8) + 64 * (j % KS) + lane];
 #pragma unroll
-      for (int kb = 0; kb < kTileBlocks; ++kb) {
-        if (kb + 1 < kTileBlocks) {
+        for (int kb = 0; kb < kTileBlocks; ++kb)
 #pragma unroll
-          for (int m = 0; m < KS; ++m) knxt[m] = sk[(kb + 1) * (kBlk / 8) + 64 * m + lane];
+          for (int rg = 0; rg < kRowGroups; ++rg) s[kb][rg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kKOps; ++j) {
+#pragma unroll
+          for (int rg = 0; rg < kRowGroups; ++rg) s[j / KS][rg] = mfma_16x16x32(kr[j], qop[rg][j % KS], s[j / KS][rg]);
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
-        for (int rg = 0; rg < kRowGroups; ++rg) s[kb][rg] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < KS; ++m) {
-#pragma unroll
-          for (int rg = 0; rg < kRowGroups; ++rg) s[kb][rg] = mfma_16x16x32(kcur[m], qop[rg][m], s[kb][rg]);
+        for (int j = 0; j < kKOps - kAhead; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, kRowGroups, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        if (kb + 1 < kTileBlocks) {
-#pragma unroll
-          for (int m = 0; m < KS; ++m) kcur[m] = knxt[m];
-        }
-      }
-      // Keep two blocks of K operands in flight: 8 LDS reads, then 8 MFMAs
-      // alternating with the next block's 4 reads.
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kAhead * kRowGroups, 0);
 
-      if (need_mask) {
+        if (need_mask) {
 #pragma unroll
-        for (int kb = 0; kb < kTileBlocks; ++kb) {
-          const int4 kp = sm.pos[buf][4 * kb + q4];
-          const int kps[4] = {kp.x, kp.y, kp.z, kp.w};
+          for (int kb = 0; kb < kTileBlocks; ++kb) {
+            int kps[4];
+            if constexpr (kFull) {
+              // key kk of the tile sits at position kmin + kk, valid up to kmax
 #pragma unroll
-          for (int rg = 0; rg < kRowGroups; ++rg) {
+              for (int r = 0; r < 4; ++r) {
+                const int kpos = kmin + kBlock * kb + 4 * q4 + r;
+                kps[r] = kpos <= kmax ? kpos : -1;
+              }
+            } else {
+              const int4 kp = sm.pos[buf][4 * kb + q4];
+              kps[0] = kp.x; kps[1] = kp.y; kps[2] = kp.z; kps[3] = kp.w;
+            }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              bool ok = kps[r] >= 0 && kps[r] <= qpos[rg];
-              if constexpr (!kFull) ok = ok && kps[r] > qpos[rg] - W;
-              s[kb][rg][r] = ok ? s[kb][rg][r] : -INFINITY;
+            for (int rg = 0; rg < kRowGroups; ++rg) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                bool ok = kps[r] >= 0 && kps[r] <= qpos[rg];
+                if constexpr (!kFull) ok = ok && kps[r] > qpos[rg] - W;
+                s[kb][rg][r] = ok ? s[kb][rg][r] : -INFINITY;
+              }
             }
           }
         }
-      }
+      };
+      scores();
 
-      // Row max of this tile; raise the exp2 reference (and rescale O, l)
-      // only when some row of the wave outgrows it by more than the slack.
-      float tmax[kRowGroups];
-      bool grow = false;
-#pragma unroll
-      for (int rg = 0; rg < kRowGroups; ++rg) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < kTileBlocks; ++kb)
-          mx = fmaxf(mx, fmaxf(fmaxf(s[kb][rg][0], s[kb][rg][1]), fmaxf(s[kb][rg][2], s[kb][rg][3])));
-        tmax[rg] = group4_max(mx) * sl2;
-        grow = grow || (tmax[rg] > m_run[rg] + kRescaleSlack);
-      }
-      if (__any(grow)) {
+      // Probabilities against the current reference m_run, in bf16 for the
+      // matrix cores and summed in fp32 for l.
+      u32x4 pb[kTileBlocks / 2][kRowGroups];   // P^T for block pairs: B operands of P.V
+      float lsum[kRowGroups];
+      auto probabilities = [&]() __attribute__((always_inline)) {
+        float m_use[kRowGroups];
 #pragma unroll
         for (int rg = 0; rg < kRowGroups; ++rg) {
-          const float m_new = fmaxf(m_run[rg], tmax[rg]);
-          const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run[rg] - m_new);
+          m_use[rg] = (m_run[rg] == -INFINITY) ? 0.0f : m_run[rg];
+          lsum[rg] = 0.0f;
+        }
+#pragma unroll
+        for (int kb = 0; kb < kTileBlocks; ++kb) {
+#pragma unroll
+          for (int rg = 0; rg < kRowGroups; ++rg) {
+            float p[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s[kb][rg][r] * sl2 - m_use[rg]);
+            lsum[rg] += (p[0] + p[1]) + (p[2] + p[3]);
+            const uint32_t lo = pack_bf16x2(p[0], p[1]), hi = pack_bf16x2(p[2], p[3]);
+            if (kb & 1) {
+              pb[kb / 2][rg].z = lo;
+              pb[kb / 2][rg].w = hi;
+            } else {
+              pb[kb / 2][rg].x = lo;
+              pb[kb / 2][rg].y = hi;
+            }
+          }
+        }
+      };
+      // Raise each row's reference to the max of its scores in this tile
+      // (a cross-lane reduction) where that is higher, rescaling O and l.
+      auto raise_to_row_max = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int rg = 0; rg < kRowGroups; ++rg) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int kb = 0; kb < kTileBlocks; ++kb)
+            mx = fmaxf(mx, fmaxf(fmaxf(s[kb][rg][0], s[kb][rg][1]), fmaxf(s[kb][rg][2], s[kb][rg][3])));
+          const float m_new = fmaxf(m_run[rg], group4_max(mx) * sl2);
+          const float alpha = (m_new == -INFINITY || m_run[rg] == -INFINITY) ? 1.0f : fast_exp2(m_run[rg] - m_new);
           l_run[rg] *= alpha;
 #pragma unroll
           for (int d = 0; d < DT; ++d) o[rg][d] *= alpha;
           m_run[rg] = m_new;
         }
-      }
-      u32x4 pb[kTileBlocks / 2][kRowGroups];   // P^T for block pairs: B operands of P.V
-      float m_use[kRowGroups], lsum[kRowGroups];
+      };
+      if constexpr (kFull) {
+        // The reference only has to keep every probability finite and l
+        // away from underflow, not equal the row max. Try the tile against
+        // the current reference: while a lane's partial row sum stays at
+        // most 2^16, so does every probability of the tile, and the tile is
+        // accepted. Otherwise -- and while a row has not seen a key yet, so
+        // that its reference is a real score and l >= 1 -- raise the
+        // reference to the row max, rescale, and recompute the tile.
+        probabilities();
+        bool redo = false;
 #pragma unroll
-      for (int rg = 0; rg < kRowGroups; ++rg) {
-        m_use[rg] = (m_run[rg] == -INFINITY) ? 0.0f : m_run[rg];
-        lsum[rg] = 0.0f;
-      }
-      // Block pair 0 first: its P.V products can start while pair 1's
-      // probabilities are still being computed.
-#pragma unroll
-      for (int kb = 0; kb < kTileBlocks; ++kb) {
+        for (int rg = 0; rg < kRowGroups; ++rg) redo = redo || m_run[rg] == -INFINITY || !(lsum[rg] <= kAcceptSum);
+        if (__any(redo)) {
+          // Rare: the scores are not kept across the first attempt (their
+          // registers are reused for the probabilities); recompute them.
+          scores();
+          raise_to_row_max();
+          probabilities();
+        }
+      } else {
+        // A window's few tiles: the row max every tile. The reference is
+        // raised (O and l rescaled) only when a row's tile max exceeds it by
+        // more than the slack, so probabilities stay at most 2^slack.
+        float tmax[kRowGroups];
+        bool grow = false;
 #pragma unroll
         for (int rg = 0; rg < kRowGroups; ++rg) {
-          float p[4];
+          float mx = -INFINITY;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s[kb][rg][r] * sl2 - m_use[rg]);
-          lsum[rg] += (p[0] + p[1]) + (p[2] + p[3]);
-          const uint32_t lo = pack_bf16x2(p[0], p[1]), hi = pack_bf16x2(p[2], p[3]);
-          if (kb & 1) {
-            pb[kb / 2][rg].z = lo;
-            pb[kb / 2][rg].w = hi;
-          } else {
-            pb[kb / 2][rg].x = lo;
-            pb[kb / 2][rg].y = hi;
+          for (int kb = 0; kb < kTileBlocks; ++kb)
+            mx = fmaxf(mx, fmaxf(fmaxf(s[kb][rg][0], s[kb][rg][1]), fmaxf(s[kb][rg][2], s[kb][rg][3])));
+          tmax[rg] = group4_max(mx) * sl2;
+          grow = grow || (tmax[rg] > m_run[rg] + kRescaleSlack);
+        }
+        if (__any(grow)) {
+#pragma unroll
+          for (int rg = 0; rg < kRowGroups; ++rg) {
+            const float m_new = fmaxf(m_run[rg], tmax[rg]);
+            const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run[rg] - m_new);
+            l_run[rg] *= alpha;
+#pragma unroll
+            for (int d = 0; d < DT; ++d) o[rg][d] *= alpha;
+            m_run[rg] = m_new;
           }
         }
+        probabilities();
       }
 #pragma unroll
       for (int rg = 0; rg < kRowGroups; ++rg) l_run[rg] += lsum[rg];
@@ -535,14 +607,16 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
           }
         }
       }
-      // V operand reads run two (dim tile, block pair) steps ahead of their MFMAs.
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+      // V operand reads run kVAhead (dim tile, block pair) steps ahead of
+      // their MFMAs (one step with three row groups: registers are short).
+      constexpr int kVAhead = kRowGroups > 2 ? 1 : 2;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVAhead, 1);
 #pragma unroll
-      for (int i = 0; i < (DT / 2) * (kTileBlocks / 2) - 2; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+      for (int i = 0; i < (DT / 2) * (kTileBlocks / 2) - kVAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * kRowGroups, 1);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kRowGroups * kVAhead, 1);
     }
 
     if (has_next) store_tile(buf ^ 1);
