@@ -22,14 +22,15 @@
 //     rows per wave means fewer LDS bytes per MFMA, and staging per MFMA is a
 //     third of what 4 waves of 32 rows would need. SWA layers, bound by their
 //     Q reads and O writes: 4 waves of 32 rows, two workgroups per CU. Keys
-//     stream in 64-key tiles of four blocks; the
-//     waves stage the next tile (each a block or half of one) while the
-//     current one is consumed -- K straight from global memory into LDS
-//     (buffer loads with the LDS bit), V through registers -- so one barrier
-//     per tile suffices.
-//     LDS operand reads are scheduled two steps ahead of their MFMAs.
-//     The LDS tiles are plain copies of the four blocks; since blocks are in
-//     operand order, every operand read is one ds_read_b128 at 16 * lane:
+//     are consumed in 64-key tiles of four blocks and staged into LDS in
+//     stage tiles of 128 keys (full: one block per wave, two compute tiles
+//     per barrier) or 64 keys (SWA). The waves stage the next stage tile
+//     while the current one is consumed -- K straight from global memory
+//     into LDS (buffer loads with the LDS bit), V through registers, one
+//     phase per compute tile -- so one barrier per stage tile suffices.
+//     LDS operand reads are scheduled ahead of their MFMAs.
+//     The K tiles are plain copies of the blocks; since blocks are in
+//     operand order, every K operand read is one ds_read_b128 at 16 * lane:
 //     consecutive lanes, consecutive 16 bytes, no bank conflicts.
 //     Per tile and wave: S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (Q^T held in
 //     registers), exp2-domain online softmax per row, P^T cast to bf16 in the
@@ -59,8 +60,13 @@ namespace ha {
 
 namespace {
 
+// Keys are consumed in 64-key tiles of four blocks; they are staged into LDS
+// in stage tiles of kStageKeys: 128 keys for full layers (two compute tiles
+// per barrier), 64 for SWA layers.
 constexpr int kTileKeys = 64;
 constexpr int kTileBlocks = kTileKeys / kBlock;   // 4
+template <bool kFull>
+constexpr int stage_keys() { return kFull ? 128 : 64; }
 constexpr int kXcds = 8;
 // Full layers: 8 waves (256 rows) share each staged tile, one workgroup per
 // CU. SWA layers, bound by their Q reads and O writes: 4 waves (128 rows),
@@ -79,12 +85,12 @@ constexpr int rows_per_wg() { return rows_per_wave<kFull>() * waves_per_wg<kFull
 //      8 bytes of half h (dim tile 2a + h) of V unit (a, lane) from block
 //      2*pair, then the same 8 bytes from block 2*pair + 1 -- exactly the
 //      v_mfma_f32_16x16x32_bf16 A operand of a 32-key product.
-template <int D>
+template <int D, int kBlocks>
 struct Smem {
-  static constexpr int kUnits = kTileBlocks * kBlock * D / 8;   // 16-byte units per tile
+  static constexpr int kUnits = kBlocks * kBlock * D / 8;   // 16-byte units per stage tile
   u32x4 k[2][kUnits];
   u32x4 v[2][kUnits];
-  int4 pos[2][kTileKeys / 4];
+  int4 pos[2][kBlocks * kBlock / 4];
 };
 
 // Largest partial row sum (one lane's 16 probabilities of a tile) accepted
@@ -175,13 +181,16 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
   constexpr int kRowsPerWave = rows_per_wave<kFull>();
   constexpr int kRowGroups = kRowsPerWave / 16;
   constexpr int kRowsPerWg = rows_per_wg<kFull>();
-  constexpr int kWavesPerBlock = kWaves / kTileBlocks;
-  static_assert(kWaves % kTileBlocks == 0, "each block of a tile is staged by whole waves");
+  constexpr int kStageKeys = stage_keys<kFull>();
+  constexpr int kStageBlocks = kStageKeys / kBlock;
+  constexpr int kSubTiles = kStageKeys / kTileKeys;   // compute tiles per stage tile
+  constexpr int kWavesPerBlock = kWaves / kStageBlocks;
+  static_assert(kWaves % kStageBlocks == 0, "each block of a stage tile is staged by whole waves");
   constexpr int KS = D / 32;            // QK^T reduction steps
   constexpr int DT = D / 16;            // output dim tiles
   constexpr int CPL = D / 32;           // 16-byte units per lane of one block
   constexpr int kBlk = kBlock * D;      // bf16 per block
-  __shared__ Smem<D> sm;
+  __shared__ Smem<D, kStageBlocks> sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -226,17 +235,17 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
   int hist_blocks = 0;
   if constexpr (kFull) {
     hist_blocks = min((hist + kBlock - 1) / kBlock, a.table_stride);
-    n_hist_tiles = (hist_blocks + kTileBlocks - 1) / kTileBlocks;
+    n_hist_tiles = (hist_blocks + kStageBlocks - 1) / kStageBlocks;
   } else {
     ring = a.table[b];
     const bool ring_ok = ring >= 0 && ring < a.num_blocks;
     hist_blocks = W / kBlock;
-    if (ring_ok && hist > 0 && t_first - W + 1 < hist) n_hist_tiles = (hist_blocks + kTileBlocks - 1) / kTileBlocks;
+    if (ring_ok && hist > 0 && t_first - W + 1 < hist) n_hist_tiles = (hist_blocks + kStageBlocks - 1) / kStageBlocks;
   }
   int c_lo = 0;
   if constexpr (!kFull) c_lo = max(0, i0 - W + 1);
-  const int first_ctile = c_lo / kTileKeys;
-  const int n_chunk_tiles = (i_end + kTileKeys - 1) / kTileKeys - first_ctile;
+  const int first_ctile = c_lo / kStageKeys;
+  const int n_chunk_tiles = (i_end + kStageKeys - 1) / kStageKeys - first_ctile;
   const int n_tiles = n_hist_tiles + n_chunk_tiles;
 
   // ---- rows of this wave ----
@@ -277,7 +286,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
   auto fetch_pages = [&](int batch_base) {
     if constexpr (kFull) {
       const int t = batch_base + lane;
-      const int lb = t * kTileBlocks + sb;
+      const int lb = t * kStageBlocks + sb;
       pg_vec = (t < n_hist_tiles && lb < hist_blocks) ? page_row[lb] : -1;
     }
   };
@@ -289,7 +298,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
   // plus the number of leading valid keys of that block.
   auto block_of = [&](int tile, int pg, int& valid) -> int64_t {
     if (tile < n_hist_tiles) {
-      const int lb = tile * kTileBlocks + sb;
+      const int lb = tile * kStageBlocks + sb;
       if (lb >= hist_blocks) { valid = 0; return -1; }
       if constexpr (kFull) {
         valid = min(kBlock, hist - lb * kBlock);
@@ -300,7 +309,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
         return ((static_cast<int64_t>(ring) * hkv + g) * W + kBlock * lb) * D;
       }
     } else {
-      const int cb = (first_ctile + tile - n_hist_tiles) * kTileBlocks + sb;  // chunk block
+      const int cb = (first_ctile + tile - n_hist_tiles) * kStageBlocks + sb;  // chunk block
       if (kBlock * cb >= i_end) { valid = 0; return -1; }
       valid = min(kBlock, i_end - kBlock * cb);
       return ((stage_blk0 + cb) * hkv + g) * kBlock * D;  // K part; V part is offset by stage_blocks
@@ -310,10 +319,10 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
   auto key_position = [&](int tile, int kk) -> int {   // kk = key within the tile
     if (tile < n_hist_tiles) {
       if constexpr (kFull) {
-        const int p = tile * kTileKeys + kk;
+        const int p = tile * kStageKeys + kk;
         return p < hist ? p : -1;
       } else {
-        const int s = tile * kTileKeys + kk;              // ring slot
+        const int s = tile * kStageKeys + kk;             // ring slot
         if (s >= W) return -1;
         const int last = hist - 1;
         int d = (last - s) % W;
@@ -322,15 +331,23 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
         return p >= 0 ? p : -1;
       }
     } else {
-      const int ci = (first_ctile + tile - n_hist_tiles) * kTileKeys + kk;
+      const int ci = (first_ctile + tile - n_hist_tiles) * kStageKeys + kk;
       return (ci < i_end) ? hist + ci : -1;
     }
   };
 
-  u32x4 stv[kStageUnits];
+  // V is staged in kSubTiles phases (one per compute tile of the stage
+  // tile), so only kVUnits 16-byte units per lane are held in registers at
+  // a time.
+  constexpr int kVUnits = kStageUnits / kSubTiles;
+  static_assert(kStageUnits % kSubTiles == 0, "V phases split the wave's units evenly");
+  u32x4 stv[kVUnits];
   int st_pos = -1;
+  __amdgpu_buffer_rsrc_t st_rv;   // V source of the block being staged
+  int st_valid = kBlock;          // leading valid tokens of that block
+  bool st_partial = false;        // partial history block: zero its unwritten V
   // K goes global -> LDS directly (buffer_load ... lds: lane l's 16 bytes land
-  // at the wave's LDS base + 16 l), V through registers (partial history
+  // at the wave's LDS base + 16 l); V goes through registers (partial history
   // blocks get their unwritten tokens zeroed on the way).
   auto load_tile = [&](int tile, int pg, int buf) {
     int valid;
@@ -341,46 +358,55 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
     const uint16_t* kp = hist_tile ? a.k_pool + b0 : a.stage + b0;
     const uint16_t* vp = hist_tile ? a.v_pool + b0 : a.stage + a.stage_blocks * hkv * kBlock * D + b0;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp, bytes);
+    st_rv = make_rsrc(vp, bytes);
+    st_valid = valid;
+    st_partial = hist_tile && valid < kBlock;
 #pragma unroll
     for (int j = 0; j < kStageUnits; ++j) {
       const int e = lane + 64 * (part * kStageUnits + j);      // 16-byte chunk of the block
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rk, (__attribute__((address_space(3))) void*)(&sm.k[buf][sb * (kBlk / 8) + e - lane]), 16, 16 * e, 0, 0, 0);
-      stv[j] = buf_load16(rv, 16 * e);
-    }
-    if (tile < n_hist_tiles && valid < kBlock) {
-      // unwritten or stale slots of a partial history block: zero their V
-#pragma unroll
-      for (int j = 0; j < kStageUnits; ++j) stv[j] = keep_tokens_v(stv[j], lane >> 4, valid);
     }
     // Full-layer key positions are contiguous per tile (computed in the
     // mask); only the SWA ring's positions are staged.
     if constexpr (!kFull)
       if (part == 0 && lane < kBlock) st_pos = key_position(tile, sb * kBlock + lane);
   };
-
-  auto store_tile = [&](int buf) {
+  auto load_v = [&](int phase) {
+#pragma unroll
+    for (int j = 0; j < kVUnits; ++j) {
+      const int e = lane + 64 * (part * kStageUnits + phase * kVUnits + j);
+      stv[j] = buf_load16(st_rv, 16 * e);
+    }
+    if (st_partial) {
+#pragma unroll
+      for (int j = 0; j < kVUnits; ++j) stv[j] = keep_tokens_v(stv[j], lane >> 4, st_valid);
+    }
+  };
+  auto store_v = [&](int buf, int phase) {
     u32x2* vpair = reinterpret_cast<u32x2*>(sm.v[buf]);
     const int pair = sb >> 1;
     const int slot = sb & 1;
 #pragma unroll
-    for (int j = 0; j < kStageUnits; ++j) {
-      const int u = part * kStageUnits + j;
+    for (int j = 0; j < kVUnits; ++j) {
+      const int u = part * kStageUnits + phase * kVUnits + j;
       // V unit (a = u, lane): half 0 -> dim tile 2u, half 1 -> dim tile 2u + 1
       const int base = ((pair * CPL + u) * 2) * 64 + lane;        // [pair][a][h=0][lane]
       vpair[2 * base + slot] = u32x2{stv[j].x, stv[j].y};
       vpair[2 * (base + 64) + slot] = u32x2{stv[j].z, stv[j].w};
     }
+  };
+  auto store_pos = [&](int buf) {
     if constexpr (!kFull)
       if (part == 0 && lane < kBlock) reinterpret_cast<int32_t*>(sm.pos[buf])[sb * kBlock + lane] = st_pos;
   };
 
-  // Key-position bounds of a tile (uniform): [kmin, kmax]; exact = every key valid.
-  auto tile_bounds = [&](int tile, int& kmin, int& kmax, bool& exact) {
+  // Key-position bounds of compute tile `sub` of stage tile `tile` (uniform):
+  // [kmin, kmax] (empty when kmax < kmin); exact = every key valid.
+  auto tile_bounds = [&](int tile, int sub, int& kmin, int& kmax, bool& exact) {
     if (tile < n_hist_tiles) {
       if constexpr (kFull) {
-        kmin = tile * kTileKeys;
+        kmin = tile * kStageKeys + kTileKeys * sub;
         kmax = min(kmin + kTileKeys, hist) - 1;
         exact = kmin + kTileKeys <= hist;
       } else {
@@ -389,7 +415,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
         exact = false;
       }
     } else {
-      const int c0 = (first_ctile + tile - n_hist_tiles) * kTileKeys;
+      const int c0 = (first_ctile + tile - n_hist_tiles) * kStageKeys + kTileKeys * sub;
       kmin = hist + c0;
       kmax = hist + min(c0 + kTileKeys, i_end) - 1;
       exact = c0 + kTileKeys <= i_end;
@@ -411,7 +437,12 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
   fetch_pages(0);
   if (n_tiles > 0) {
     load_tile(0, page_for(0), 0);
-    store_tile(0);
+#pragma unroll
+    for (int ph = 0; ph < kSubTiles; ++ph) {
+      load_v(ph);
+      store_v(0, ph);
+    }
+    store_pos(0);
   }
   // Everything loaded so far (Q, first tile) is complete before the loop, so
   // the loop's only outstanding global loads are the next tile's staging.
@@ -422,19 +453,24 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
     const int buf = tile & 1;
     const bool has_next = tile + 1 < n_tiles;
     if (((tile + 1) & 63) == 0 && tile + 1 < n_hist_tiles) fetch_pages(tile + 1);
-    if (has_next) load_tile(tile + 1, page_for(tile + 1), buf ^ 1);
+    if (has_next) {
+      load_tile(tile + 1, page_for(tile + 1), buf ^ 1);
+      load_v(0);
+    }
 
+#pragma unroll
+    for (int sub = 0; sub < kSubTiles; ++sub) {
     int kmin, kmax;
     bool exact;
-    tile_bounds(tile, kmin, kmax, exact);
-    bool visible_any = wave_live && kmin <= qhi;
+    tile_bounds(tile, sub, kmin, kmax, exact);
+    bool visible_any = wave_live && kmin <= qhi && kmin <= kmax;
     if constexpr (!kFull) visible_any = visible_any && kmax >= qlo - W + 1;
     bool need_mask = !(exact && kmax <= qlo);
     if constexpr (!kFull) need_mask = need_mask || kmin < qhi - W + 1;
 
     if (visible_any) {
-      const u32x4* sk = sm.k[buf];
-      const u32x4* sv = sm.v[buf];
+      const u32x4* sk = sm.k[buf] + sub * kTileBlocks * (kBlk / 8);
+      const u32x4* sv = sm.v[buf] + sub * (kTileBlocks / 2) * (DT / 2) * 2 * 64;
       f32x4 s[kTileBlocks][kRowGroups];
       // S^T = K Q^T for the tile (then masked where needed).
       auto scores = [&]() __attribute__((always_inline)) {
@@ -477,7 +513,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
                 kps[r] = kpos <= kmax ? kpos : -1;
               }
             } else {
-              const int4 kp = sm.pos[buf][4 * kb + q4];
+              const int4 kp = sm.pos[buf][(sub * kTileBlocks + kb) * 4 + q4];
               kps[0] = kp.x; kps[1] = kp.y; kps[2] = kp.z; kps[3] = kp.w;
             }
 #pragma unroll
@@ -618,8 +654,18 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 2 * kRowGroups * kVAhead, 1);
     }
+    if (sub + 1 < kSubTiles && has_next) {
+      // next V phase: this one's loads (and the K loads before them) are done
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      store_v(buf ^ 1, sub);
+      load_v(sub + 1);
+    }
+    }   // compute tiles of the stage tile
 
-    if (has_next) store_tile(buf ^ 1);
+    if (has_next) {
+      store_v(buf ^ 1, kSubTiles - 1);
+      store_pos(buf ^ 1);
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's direct K loads have landed
     __syncthreads();
   }
