@@ -8,7 +8,9 @@
 //
 // Workgroup = one (split, kv head, sequence): 4 wavefronts for full layers,
 // 8 for SWA layers (one ring block per wave, so a W = 128 ring is fetched in
-// a single round trip). Wave w takes blocks w, w+NW, w+2NW, ... of the split
+// a single round trip; one operand buffer per wave keeps the SWA kernel at
+// 128 VGPRs, so two workgroups share a CU and a whole decode batch runs as a
+// single round of workgroups). Wave w takes blocks w, w+NW, w+2NW, ... of the split
 // and keeps two of them in flight in ping-pong register buffers (no register
 // copies, so a block's loads are only waited for right before it is
 // consumed). For each 16-token block it
@@ -142,7 +144,7 @@ struct NewToken {
 }  // namespace
 
 template <int D, bool kFull, bool kQF32>
-__global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void decode_kernel(DecodeArgs a) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   constexpr int kPad = 4;
@@ -262,45 +264,61 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < DT; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Blocks of this wave: first + wave + 4k. Buffer A holds even k, B odd k.
-  constexpr int kStep = kWaves;
-  int ia = first + wave;
-  int ib = ia + kStep;
-  int pg_a = 0, pg_b = 0, pg_a2 = 0, pg_b2 = 0;
-  if constexpr (kFull) {
-    pg_a = page_of(ia);
-    pg_b = page_of(ib);
-  }
-  int64_t base_a = base_of(ia, pg_a);
-  int64_t base_b = base_of(ib, pg_b);
-  BlockOps<D> A, B;
-  load_block<D>(A, a.k_pool, a.v_pool, base_a, q4, c16);
-  load_block<D>(B, a.k_pool, a.v_pool, base_b, q4, c16);
-  if constexpr (kFull) {
-    pg_a2 = page_of(ia + 2 * kStep);
-    pg_b2 = page_of(ib + 2 * kStep);
-  }
-  // Pairs (A, B) in a loop with a fixed trip count and no early exit, so the
-  // loads in flight at the loop head are the same on every path; an odd last
-  // block is consumed from A after the loop. Loads past `last` read nothing.
-  const int nmine = (last > ia) ? (last - ia + kStep - 1) / kStep : 0;
-  for (int k = 0; k + 1 < nmine; k += 2) {
-    patch_new(A, ia);
-    if (base_a >= 0) consume_block<D>(A, qop, kBlock * ia, t, is_partial(ia), sl2, m_run, l_run, o, q4);
-    ia += 2 * kStep;
-    base_a = base_of(ia, pg_a2);
+  if constexpr (!kFull) {
+    // SWA: with W <= 16 * waves (W = 128: one ring block per wave) every
+    // wave has at most one block; a larger ring is walked a block at a
+    // time. A single operand buffer keeps the kernel at 128 VGPRs, so two
+    // 8-wave workgroups fit on a CU and the whole grid runs in one round.
+    BlockOps<D> A;
+    if (last - first <= kWaves) {
+      const int i = first + wave;
+      if (i < last) {
+        load_block<D>(A, a.k_pool, a.v_pool, base_of(i, 0), q4, c16);
+        patch_new(A, i);
+        consume_block<D>(A, qop, kBlock * i, t, is_partial(i), sl2, m_run, l_run, o, q4);
+      }
+    } else {
+      for (int i = first + wave; i < last; i += kWaves) {
+        load_block<D>(A, a.k_pool, a.v_pool, base_of(i, 0), q4, c16);
+        patch_new(A, i);
+        consume_block<D>(A, qop, kBlock * i, t, is_partial(i), sl2, m_run, l_run, o, q4);
+      }
+    }
+  } else {
+    // Full: blocks of this wave are first + wave + 4k. Buffer A holds even k,
+    // B odd k.
+    constexpr int kStep = kWaves;
+    int ia = first + wave;
+    int ib = ia + kStep;
+    int pg_a = page_of(ia), pg_b = page_of(ib);
+    int64_t base_a = base_of(ia, pg_a);
+    int64_t base_b = base_of(ib, pg_b);
+    BlockOps<D> A, B;
     load_block<D>(A, a.k_pool, a.v_pool, base_a, q4, c16);
-    if constexpr (kFull) pg_a2 = page_of(ia + 2 * kStep);
-    patch_new(B, ib);
-    if (base_b >= 0) consume_block<D>(B, qop, kBlock * ib, t, is_partial(ib), sl2, m_run, l_run, o, q4);
-    ib += 2 * kStep;
-    base_b = base_of(ib, pg_b2);
     load_block<D>(B, a.k_pool, a.v_pool, base_b, q4, c16);
-    if constexpr (kFull) pg_b2 = page_of(ib + 2 * kStep);
-  }
-  if (nmine & 1) {
-    patch_new(A, ia);
-    if (base_a >= 0) consume_block<D>(A, qop, kBlock * ia, t, is_partial(ia), sl2, m_run, l_run, o, q4);
+    int pg_a2 = page_of(ia + 2 * kStep), pg_b2 = page_of(ib + 2 * kStep);
+    // Pairs (A, B) in a loop with a fixed trip count and no early exit, so the
+    // loads in flight at the loop head are the same on every path; an odd last
+    // block is consumed from A after the loop. Loads past `last` read nothing.
+    const int nmine = (last > ia) ? (last - ia + kStep - 1) / kStep : 0;
+    for (int k = 0; k + 1 < nmine; k += 2) {
+      patch_new(A, ia);
+      if (base_a >= 0) consume_block<D>(A, qop, kBlock * ia, t, is_partial(ia), sl2, m_run, l_run, o, q4);
+      ia += 2 * kStep;
+      base_a = base_of(ia, pg_a2);
+      load_block<D>(A, a.k_pool, a.v_pool, base_a, q4, c16);
+      pg_a2 = page_of(ia + 2 * kStep);
+      patch_new(B, ib);
+      if (base_b >= 0) consume_block<D>(B, qop, kBlock * ib, t, is_partial(ib), sl2, m_run, l_run, o, q4);
+      ib += 2 * kStep;
+      base_b = base_of(ib, pg_b2);
+      load_block<D>(B, a.k_pool, a.v_pool, base_b, q4, c16);
+      pg_b2 = page_of(ib + 2 * kStep);
+    }
+    if (nmine & 1) {
+      patch_new(A, ia);
+      if (base_a >= 0) consume_block<D>(A, qop, kBlock * ia, t, is_partial(ia), sl2, m_run, l_run, o, q4);
+    }
   }
 
   // Fused append: the owner wave writes the token into the pool, after its
@@ -463,3 +481,4 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
 }
 
 }  // namespace ha
+

@@ -67,7 +67,8 @@ def oracle_decode(shape, kind, seq, q, lens):
 
 
 @pytest.mark.parametrize("kind", [ha.HA_SWA, ha.HA_FULL])
-@pytest.mark.parametrize("hq,hkv,d,window", [(4, 1, 64, 128), (64, 8, 128, 128), (16, 16, 128, 32), (32, 2, 64, 64)])
+@pytest.mark.parametrize("hq,hkv,d,window", [(4, 1, 64, 128), (64, 8, 128, 128), (16, 16, 128, 32), (32, 2, 64, 64),
+                                              (16, 2, 128, 256), (8, 8, 64, 512)])
 def test_decode_matches_oracle(kind, hq, hkv, d, window):
     shape = ha.HeadShape(hq, hkv, d, window=window)
     seq, q, pool, view = build(shape, kind, LENS, seed=hq * 7 + d)
@@ -156,7 +157,7 @@ def pool_bits(pool):
 
 @pytest.mark.parametrize("kind", [ha.HA_SWA, ha.HA_FULL])
 @pytest.mark.parametrize("hq,hkv,d,window,splits", [(64, 8, 128, 128, 0), (4, 1, 64, 32, 0), (64, 8, 128, 128, 7),
-                                                      (32, 2, 64, 64, 3)])
+                                                      (32, 2, 64, 64, 3), (16, 2, 128, 256, 0)])
 def test_fused_append_equals_append_then_decode(kind, hq, hkv, d, window, splits):
     """Passing the new token's K/V appends it in the same launch: outputs and
     the pool afterwards are bit-identical to append-then-decode."""
