@@ -19,6 +19,8 @@ from .api import (  # noqa: F401
     hybrid_attn_decode,
     hybrid_attn_decode_splits,
     hybrid_attn_prefill,
+    hybrid_attn_verify,
+    hybrid_attn_verify_workspace_size,
     hybrid_attn_workspace_size,
     swa_ring_append,
     window_safe_match,

@@ -25,7 +25,7 @@ HA_F32 = 1
 HA_SWA = 0
 HA_FULL = 1
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 # Every symbol include/hybrid_attn.h declares.
 EXPORTS = (
@@ -36,6 +36,8 @@ EXPORTS = (
     "hybrid_attn_decode",
     "hybrid_attn_workspace_size",
     "hybrid_attn_decode_splits",
+    "hybrid_attn_verify",
+    "hybrid_attn_verify_workspace_size",
     "ha_status_str",
     "ha_last_error",
     "ha_abi_version",
@@ -96,8 +98,11 @@ def load() -> ctypes.CDLL:
     lib.hybrid_attn_workspace_size.restype = sz
     lib.hybrid_attn_decode_splits.argtypes = [shp, i32, i32, i32, i32]
     lib.hybrid_attn_decode_splits.restype = i32
+    lib.hybrid_attn_verify.argtypes = [shp, view, p, i32, i32, i32, p, p, p, i32, p, p, i32, p, sz, p]
+    lib.hybrid_attn_verify_workspace_size.argtypes = [shp, i32, i32, i32, i32, i32]
+    lib.hybrid_attn_verify_workspace_size.restype = sz
     for fn in ("swa_ring_append", "full_pool_append", "window_safe_match", "hybrid_attn_prefill",
-               "hybrid_attn_decode"):
+               "hybrid_attn_decode", "hybrid_attn_verify"):
         getattr(lib, fn).restype = i32
     lib.ha_status_str.argtypes = [i32]
     lib.ha_status_str.restype = ctypes.c_char_p

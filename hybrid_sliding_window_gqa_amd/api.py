@@ -297,3 +297,49 @@ def hybrid_attn_decode(shape: HeadShape, kv: KvView, kv_len: torch.Tensor, q: to
                                     int(max_kv_len), q.data_ptr(), kp, vp, dt, out.data_ptr(), lse.data_ptr(),
                                     int(num_splits), ws_ptr, ws_bytes, _stream_ptr(stream)))
     return out, lse
+
+
+def hybrid_attn_verify_workspace_size(shape: HeadShape, kind: int, batch: int, max_kv_len: int, nq: int,
+                                      num_splits: int = 0) -> int:
+    c_shape = shape.c()
+    return int(load().hybrid_attn_verify_workspace_size(ctypes.byref(c_shape), kind, batch, max_kv_len, nq,
+                                                        num_splits))
+
+
+def hybrid_attn_verify(shape: HeadShape, kv: KvView, kv_len: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
+                       v_new: torch.Tensor, max_kv_len: int, out: torch.Tensor | None = None,
+                       lse: torch.Tensor | None = None, num_splits: int = 0, workspace: torch.Tensor | None = None,
+                       stream=None):
+    """Verify nq new tokens per sequence (positions kv_len - nq .. kv_len - 1),
+    causal among themselves, over the pool history; then append them.
+
+    q [B, nq, Hq, D]; k_new/v_new [B, nq, Hkv, D] (same dtype as q).
+    Returns (out float32 [B, nq, Hq, D], lse float32 [B, nq, Hq])."""
+    dev = kv.k.device
+    b = kv.batch
+    hq, hkv, d = shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B, nq, Hq, D], got shape {tuple(q.shape)}")
+    nq = int(q.shape[1])
+    _check(kv_len, "kv_len", (b,), torch.int32, dev)
+    _check(q, "q", (b, nq, hq, d), None, dev)
+    _check(k_new, "k_new", (b, nq, hkv, d), None, dev)
+    _check(v_new, "v_new", (b, nq, hkv, d), None, dev)
+    dt = _in_dtype(q, k_new, v_new)
+    if out is None:
+        out = torch.empty(b, nq, hq, d, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(b, nq, hq, dtype=torch.float32, device=dev)
+    _check(out, "out", (b, nq, hq, d), torch.float32, dev)
+    _check(lse, "lse", (b, nq, hq), torch.float32, dev)
+    need = hybrid_attn_verify_workspace_size(shape, kv.kind, b, max_kv_len, nq, num_splits)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    c_shape, c_view = shape.c(), kv.c()
+    check(load().hybrid_attn_verify(ctypes.byref(c_shape), ctypes.byref(c_view), kv_len.data_ptr(), b,
+                                    int(max_kv_len), nq, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), dt,
+                                    out.data_ptr(), lse.data_ptr(), int(num_splits), ws_ptr, ws_bytes,
+                                    _stream_ptr(stream)))
+    return out, lse

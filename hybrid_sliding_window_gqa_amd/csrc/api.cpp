@@ -127,6 +127,21 @@ size_t decode_workspace(const ha::Geometry& geo, bool full, int batch, int max_k
   return static_cast<size_t>(batch) * geo.hq * ns * (geo.d + 1) * sizeof(float);
 }
 
+size_t verify_workspace(const ha::Geometry& geo, bool full, int batch, int max_kv_len, int nq, int num_splits) {
+  if (!full) return 0;
+  const int sb = ha::decode_split_blocks(true, geo.window, max_kv_len, batch, geo.hkv, num_splits);
+  const int ns = ha::decode_num_splits(true, geo.window, max_kv_len, sb);
+  if (ns <= 1) return 0;
+  return static_cast<size_t>(batch) * nq * geo.hq * ns * (geo.d + 1) * sizeof(float);
+}
+
+ha_status check_nq(const ha::Geometry& geo, int nq) {
+  if (nq < 1 || nq > 16) return fail(HA_ERR_RANGE, "nq must be in [1, 16] (got %d)", nq);
+  if (nq * geo.group > 32)
+    return fail(HA_ERR_SHAPE, "nq * (Hq / Hkv) must be <= 32 (got %d * %d)", nq, geo.group);
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -262,6 +277,65 @@ ha_status hybrid_attn_decode(const ha_shape* shape, const ha_kv_view* kv, const 
     a.part_lse = ws + static_cast<size_t>(batch) * geo.hq * a.splits * geo.d;
   }
   return hip_status(ha::launch_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
+ha_status hybrid_attn_verify(const ha_shape* shape, const ha_kv_view* kv, const int32_t* kv_len, int32_t batch,
+                             int32_t max_kv_len, int32_t nq, const void* q, const void* k_new, const void* v_new,
+                             int32_t in_dtype, float* out, float* lse, int32_t num_splits, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  ha::Geometry geo;
+  ha_status st = check_shape(shape, &geo);
+  if (st != HA_OK) return st;
+  if (batch < 0 || max_kv_len < 0 || num_splits < 0)
+    return fail(HA_ERR_RANGE, "batch, max_kv_len and num_splits must be >= 0");
+  if ((st = check_nq(geo, nq)) != HA_OK) return st;
+  if ((st = check_view(kv, batch)) != HA_OK) return st;
+  if ((st = check_dtype(in_dtype)) != HA_OK) return st;
+  if (batch == 0) return ok();
+  if (batch > 65535) return fail(HA_ERR_RANGE, "verify batch %d exceeds 65535", batch);
+  if (!kv_len || !q || !out || !lse) return fail(HA_ERR_NULL, "kv_len, q, out or lse is NULL");
+  if (!k_new || !v_new) return fail(HA_ERR_NULL, "k_new and v_new (the new tokens' K/V) are required");
+  const bool full = kv->kind == HA_FULL;
+  const size_t need = verify_workspace(geo, full, batch, max_kv_len, nq, num_splits);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(HA_ERR_WORKSPACE, "verify needs %zu workspace bytes, got %zu", need, workspace ? workspace_bytes : 0);
+  ha::VerifyArgs a{};
+  a.geo = geo;
+  a.full = full;
+  a.k_pool = static_cast<const uint16_t*>(kv->k);
+  a.v_pool = static_cast<const uint16_t*>(kv->v);
+  a.k_pool_w = static_cast<uint16_t*>(kv->k);
+  a.v_pool_w = static_cast<uint16_t*>(kv->v);
+  a.num_blocks = kv->num_blocks;
+  a.table = kv->table;
+  a.table_stride = kv->table_stride;
+  a.kv_len = kv_len;
+  a.batch = batch;
+  a.nq = nq;
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.in_f32 = in_dtype == HA_F32;
+  a.out = out;
+  a.lse = lse;
+  a.split_blocks = ha::decode_split_blocks(full, geo.window, max_kv_len, batch, geo.hkv, num_splits);
+  a.splits = ha::decode_num_splits(full, geo.window, max_kv_len, a.split_blocks);
+  if (a.splits > 65535) return fail(HA_ERR_RANGE, "too many key splits (%d); pass a smaller num_splits", a.splits);
+  if (need > 0) {
+    float* ws = static_cast<float*>(workspace);
+    a.part_o = ws;
+    a.part_lse = ws + static_cast<size_t>(batch) * nq * geo.hq * a.splits * geo.d;
+  }
+  return hip_status(ha::launch_verify(a, static_cast<hipStream_t>(stream)), "verify launch");
+}
+
+size_t hybrid_attn_verify_workspace_size(const ha_shape* shape, int32_t kind, int32_t batch, int32_t max_kv_len,
+                                         int32_t nq, int32_t num_splits) {
+  ha::Geometry geo;
+  if (check_shape(shape, &geo) != HA_OK) return 0;
+  if ((kind != HA_SWA && kind != HA_FULL) || batch < 0 || max_kv_len < 0 || num_splits < 0) return 0;
+  if (check_nq(geo, nq) != HA_OK) return 0;
+  return verify_workspace(geo, kind == HA_FULL, batch, max_kv_len, nq, num_splits);
 }
 
 size_t hybrid_attn_workspace_size(const ha_shape* shape, int32_t kind, int32_t decode, int32_t batch,

@@ -77,6 +77,33 @@ struct PrefillArgs {
   int64_t stage_blocks;   // blocks the workspace holds
 };
 
+// Multi-token verify decode: nq new tokens per sequence at positions
+// kv_len - nq .. kv_len - 1 (their K/V in k_new / v_new [B][nq][Hkv][D]).
+struct VerifyArgs {
+  Geometry geo;
+  bool full;
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  uint16_t* k_pool_w;     // writable views: the new tokens are appended
+  uint16_t* v_pool_w;
+  int32_t num_blocks;
+  const int32_t* table;
+  int32_t table_stride;
+  const int32_t* kv_len;
+  int32_t batch;
+  int32_t nq;
+  const void* q;          // [B][nq][Hq][D]
+  const void* k_new;      // [B][nq][Hkv][D]
+  const void* v_new;
+  bool in_f32;
+  float* out;             // [B][nq][Hq][D]
+  float* lse;             // [B][nq][Hq]
+  int32_t splits;
+  int32_t split_blocks;
+  float* part_o;          // [B][nq][Hq][splits][D]
+  float* part_lse;        // [B][nq][Hq][splits] (log2 domain)
+};
+
 // Workspace of hybrid_attn_prefill: the chunk's K and V in 16-token blocks
 // (same layout as a pool page), sequence b's blocks starting at
 // ceil(cu_new[b] / 16) + b.
@@ -85,6 +112,7 @@ int64_t prefill_stage_blocks(int num_tokens, int batch);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 
 // Decode split policy shared by the workspace query and the launcher.
 int decode_split_blocks(bool full, int window, int max_kv_len, int batch, int hkv, int requested_splits);

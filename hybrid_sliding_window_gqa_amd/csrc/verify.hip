@@ -1,0 +1,445 @@
+// Multi-token verify decode: nq new tokens per sequence (the positions a
+// multi-token-prediction head proposed) attend causally among themselves and
+// to the sequence's history in one launch, then are appended to the pool.
+// The pages run a three-layer MTP head and verify its 1 + 3 tokens per step
+// (htx.com "Xiaomi MiMo's 99% price cut ..." section 工程六; blog.hotdry.top
+// 2026-06-09 "MTP 与多模态流水线"). Decode stays bound by the KV it reads
+// (youleyou.com "小米MiMo首次公开模型推理系统全链路优化降价99%" section 1), so
+// verifying nq tokens costs about one decode step: the K/V bytes are the same
+// and the matrix cores see nq times the columns.
+//
+// Sequence b's new tokens sit at positions t0 .. t0 + nq - 1, t0 = kv_len[b] -
+// nq. The pool holds positions < t0; the new tokens' K/V come from k_new /
+// v_new. Query token i sees keys [0, t0 + i] (full) or [t0 + i - W + 1,
+// t0 + i] (SWA).
+//
+// Workgroup = one (split, kv head, sequence), 4 waves. The S^T = K Q^T
+// columns are (token, head) pairs of the GQA group, 16 per MFMA column group,
+// NG groups (nq * G <= 16 * NG). Each wave takes history blocks w, w + 4, ...
+// of its split and keeps two in flight (ping-pong operand registers), like
+// decode; split 0's wave 0 also consumes one extra block holding the new
+// tokens, built from k_new / v_new. The new tokens are not patched into the
+// ring slots they will occupy: with nq > 1 an earlier query still needs the
+// key a later token overwrites. Every key that does not exist (pool slots at
+// or past t0, unwritten ring slots, rows past nq in the new block) has its V
+// zeroed and its score masked; per-column masks apply the causal and window
+// bounds. Waves merge through LDS; the workgroup writes final rows (one split)
+// or partials for verify_reduce_kernel. After the merge barrier, split 0
+// writes the new tokens into the pool: nothing in the launch reads those
+// slots as keys (they are at or past t0, or, for the ring, read by this
+// workgroup only, before the barrier).
+#include <cmath>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ha {
+
+namespace {
+
+constexpr int kVerifyWaves = 4;
+
+template <int D>
+struct VBlock {
+  u32x4 k[D / 32];
+  u32x2 v[D / 16];
+};
+
+template <int D>
+__device__ __forceinline__ void vload_block(VBlock<D>& ops, const uint16_t* kp, const uint16_t* vp, int64_t base,
+                                            int lane) {
+  const bool ok = base >= 0;
+  const int64_t b0 = ok ? base : 0;
+  const uint32_t bytes = ok ? kBlock * D * 2 : 0;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + b0, bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + b0, bytes);
+#pragma unroll
+  for (int m = 0; m < D / 32; ++m) ops.k[m] = buf_load16(rk, 16 * (64 * m + lane));
+#pragma unroll
+  for (int p = 0; p < D / 32; ++p) {
+    const u32x4 w = buf_load16(rv, 16 * (64 * p + lane));
+    ops.v[2 * p] = u32x2{w.x, w.y};
+    ops.v[2 * p + 1] = u32x2{w.z, w.w};
+  }
+}
+
+template <bool kF32>
+__device__ __forceinline__ uint32_t bf16_at(const void* src, int64_t elem) {
+  if constexpr (kF32) return f32_to_bf16_bits(static_cast<const float*>(src)[elem]);
+  else return static_cast<const uint16_t*>(src)[elem];
+}
+
+// Per-wave softmax state of one column group: lane (q4, c16) holds column c16.
+template <int D>
+struct ColState {
+  float m_run;     // running max (log2 domain), the same in the column's four lanes
+  float l_run;     // partial sum over this lane's keys
+  f32x4 o[D / 16];
+};
+
+}  // namespace
+
+template <int D, bool kFull, bool kF32, int NG>
+__global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs a) {
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int kPad = 4;
+  constexpr int kCols = 16 * NG;
+  __shared__ float sm_o[kVerifyWaves][kCols][D + kPad];
+  __shared__ float sm_m[kVerifyWaves][kCols];
+  __shared__ float sm_l[kVerifyWaves][kCols];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q4 = lane >> 4;
+  const int c16 = lane & 15;
+  const int split = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int G = a.geo.group;
+  const int hq = a.geo.hq;
+  const int hkv = a.geo.hkv;
+  const int W = a.geo.window;
+  const int nq = a.nq;
+
+  const int len = a.kv_len[b];
+  const int t0 = len - nq;   // position of the first new token
+  if (t0 < 0) {
+    // kv_len below nq: no valid query position; rows are zero, LSE -inf.
+    if (split == 0) {
+      for (int e = threadIdx.x; e < nq * G * D; e += blockDim.x) {
+        const int i = e / (G * D);
+        const int r = e - i * G * D;
+        a.out[((static_cast<int64_t>(b) * nq + i) * hq + g * G) * D + r] = 0.0f;
+      }
+      for (int e = threadIdx.x; e < nq * G; e += blockDim.x)
+        a.lse[(static_cast<int64_t>(b) * nq + e / G) * hq + g * G + e % G] = -INFINITY;
+    }
+    return;
+  }
+
+  // History blocks of this split (pool blocks holding positions < t0).
+  int first, last, nsplit;
+  if constexpr (kFull) {
+    const int nblk = min((t0 + kBlock - 1) / kBlock, a.table_stride);
+    nsplit = max(1, min((nblk + a.split_blocks - 1) / a.split_blocks, a.splits));
+    first = split * a.split_blocks;
+    last = min(nblk, first + a.split_blocks);
+  } else {
+    nsplit = 1;
+    first = 0;
+    last = (t0 >= W) ? W / kBlock : (t0 + kBlock - 1) / kBlock;   // ring blocks with a written slot
+  }
+  if (split >= nsplit) return;
+  int ring = 0;
+  if constexpr (!kFull) {
+    ring = a.table[b];
+    if (ring < 0 || ring >= a.num_blocks) last = first;  // invalid ring id: no history
+  }
+  const int32_t* page_row = a.table + static_cast<int64_t>(b) * a.table_stride;
+  auto page_of = [&](int i) -> int { return (kFull && i < last) ? page_row[i] : -1; };
+  auto base_of = [&](int i, int pg) -> int64_t {
+    if (i >= last) return -1;
+    if constexpr (kFull) {
+      if (pg < 0 || pg >= a.num_blocks) return -1;
+      return (static_cast<int64_t>(pg) * hkv + g) * kBlock * D;
+    } else {
+      return ((static_cast<int64_t>(ring) * hkv + g) * W + kBlock * i) * D;
+    }
+  };
+  // Position of key k (0..15) of history block i, or -1 if that slot holds
+  // no key below t0.
+  auto hist_pos = [&](int i, int k) -> int {
+    if constexpr (kFull) {
+      const int p = kBlock * i + k;
+      return p < t0 ? p : -1;
+    } else {
+      const int s = kBlock * i + k;   // ring slot
+      const int last_p = t0 - 1;
+      int d = (last_p - s) % W;
+      if (d < 0) d += W;
+      const int p = last_p - d;
+      return p >= 0 ? p : -1;
+    }
+  };
+
+  // Columns of group gr: column c = 16 gr + c16 = (token i = c / G, head c % G).
+  u32x4 qop[NG][KS];
+  int tcol[NG];   // query position of this lane's column (INT_MIN: padding column)
+#pragma unroll
+  for (int gr = 0; gr < NG; ++gr) {
+    const int c = 16 * gr + c16;
+    const int i = c / G;
+    const bool ok = i < nq;
+    tcol[gr] = ok ? t0 + i : -0x40000000;
+    const int64_t qoff = ((static_cast<int64_t>(b) * nq + (ok ? i : 0)) * hq + g * G + c % G) * D + 8 * q4;
+#pragma unroll
+    for (int m = 0; m < KS; ++m) {
+      qop[gr][m] = load8_as_bf16<kF32>(a.q, qoff + 32 * m);
+      if (!ok) qop[gr][m] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  const float sl2 = a.geo.scale * kLog2e;
+  ColState<D> st[NG];
+#pragma unroll
+  for (int gr = 0; gr < NG; ++gr) {
+    st[gr].m_run = -INFINITY;
+    st[gr].l_run = 0.0f;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) st[gr].o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // One block: keys at positions kp[r] (key 4 q4 + r; -1: no key), shared
+  // by every column group.
+  auto consume = [&](VBlock<D>& ops, const int (&kp)[4]) {
+    // zero V of keys that do not exist (their pool slots may hold anything)
+    uint32_t keep[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) keep[r] = kp[r] >= 0 ? 0xffffu : 0u;
+    const uint32_t mlo = keep[0] | (keep[1] << 16);
+    const uint32_t mhi = keep[2] | (keep[3] << 16);
+#pragma unroll
+    for (int d = 0; d < DT; ++d) {
+      ops.v[d].x &= mlo;
+      ops.v[d].y &= mhi;
+    }
+#pragma unroll
+    for (int gr = 0; gr < NG; ++gr) {
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < KS; ++m) s = mfma_16x16x32(ops.k[m], qop[gr][m], s);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        bool ok = kp[r] >= 0 && kp[r] <= tcol[gr];
+        if constexpr (!kFull) ok = ok && kp[r] > tcol[gr] - W;
+        s[r] = ok ? s[r] : -INFINITY;
+      }
+      ColState<D>& cs = st[gr];
+      const float tmax = group4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))) * sl2;
+      const float m_new = fmaxf(cs.m_run, tmax);
+      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+      const float alpha = fast_exp2(cs.m_run - m_use);
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s[r] * sl2 - m_use);
+      cs.l_run = cs.l_run * alpha + (p[0] + p[1]) + (p[2] + p[3]);
+      cs.m_run = m_new;
+#pragma unroll
+      for (int d = 0; d < DT; ++d) cs.o[d] *= alpha;
+      const u32x2 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+#pragma unroll
+      for (int d = 0; d < DT; ++d) cs.o[d] = mfma_16x16x16(ops.v[d], pb, cs.o[d]);
+    }
+  };
+  auto hist_keys = [&](int i, int (&kp)[4]) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) kp[r] = hist_pos(i, 4 * q4 + r);
+  };
+
+  // History blocks of this wave: first + wave + 4k, two in flight.
+  {
+    int ia = first + wave;
+    int ib = ia + kVerifyWaves;
+    int pg_a2 = 0, pg_b2 = 0;
+    int64_t base_a = base_of(ia, page_of(ia));
+    int64_t base_b = base_of(ib, page_of(ib));
+    VBlock<D> A, B;
+    vload_block<D>(A, a.k_pool, a.v_pool, base_a, lane);
+    vload_block<D>(B, a.k_pool, a.v_pool, base_b, lane);
+    pg_a2 = page_of(ia + 2 * kVerifyWaves);
+    pg_b2 = page_of(ib + 2 * kVerifyWaves);
+    const int nmine = (last > ia) ? (last - ia + kVerifyWaves - 1) / kVerifyWaves : 0;
+    int kp[4];
+    for (int k = 0; k + 1 < nmine; k += 2) {
+      if (base_a >= 0) {
+        hist_keys(ia, kp);
+        consume(A, kp);
+      }
+      ia += 2 * kVerifyWaves;
+      base_a = base_of(ia, pg_a2);
+      vload_block<D>(A, a.k_pool, a.v_pool, base_a, lane);
+      pg_a2 = page_of(ia + 2 * kVerifyWaves);
+      if (base_b >= 0) {
+        hist_keys(ib, kp);
+        consume(B, kp);
+      }
+      ib += 2 * kVerifyWaves;
+      base_b = base_of(ib, pg_b2);
+      vload_block<D>(B, a.k_pool, a.v_pool, base_b, lane);
+      pg_b2 = page_of(ib + 2 * kVerifyWaves);
+    }
+    if ((nmine & 1) && base_a >= 0) {
+      hist_keys(ia, kp);
+      consume(A, kp);
+    }
+  }
+
+  // The new tokens as one more block (split 0, wave 0): key k = token k < nq.
+  if (split == 0 && wave == 0) {
+    VBlock<D> N;
+    const bool krow = c16 < nq;
+    const int64_t ksrc = ((static_cast<int64_t>(b) * nq + (krow ? c16 : 0)) * hkv + g) * D + 8 * q4;
+#pragma unroll
+    for (int m = 0; m < KS; ++m) {
+      N.k[m] = load8_as_bf16<kF32>(a.k_new, ksrc + 32 * m);
+      if (!krow) N.k[m] = u32x4{0u, 0u, 0u, 0u};
+    }
+    // V^T operand: lane (q4, c16), dim tile d holds tokens 4 q4 .. 4 q4 + 3 of
+    // channel 16 d + c16.
+    uint32_t vb[4][DT];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = 4 * q4 + r;
+      const bool ok = tok < nq;
+      const int64_t vsrc = ((static_cast<int64_t>(b) * nq + (ok ? tok : 0)) * hkv + g) * D + c16;
+#pragma unroll
+      for (int d = 0; d < DT; ++d) vb[r][d] = ok ? bf16_at<kF32>(a.v_new, vsrc + 16 * d) : 0u;
+    }
+#pragma unroll
+    for (int d = 0; d < DT; ++d) N.v[d] = u32x2{vb[0][d] | (vb[1][d] << 16), vb[2][d] | (vb[3][d] << 16)};
+    int kp[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) kp[r] = (4 * q4 + r < nq) ? t0 + 4 * q4 + r : -1;
+    consume(N, kp);
+  }
+
+  // Merge the four waves.
+#pragma unroll
+  for (int gr = 0; gr < NG; ++gr) {
+    const float l = group4_sum(st[gr].l_run);
+#pragma unroll
+    for (int d = 0; d < DT; ++d)
+      *reinterpret_cast<f32x4*>(&sm_o[wave][16 * gr + c16][16 * d + 4 * q4]) = st[gr].o[d];
+    if (q4 == 0) {
+      sm_m[wave][16 * gr + c16] = st[gr].m_run;
+      sm_l[wave][16 * gr + c16] = l;
+    }
+  }
+  __syncthreads();
+
+  const bool final_row = (nsplit == 1);
+  const int ncols = nq * G;
+  for (int e = threadIdx.x; e < ncols * D; e += blockDim.x) {
+    const int c = e / D;
+    const int dd = e - c * D;
+    float mx = sm_m[0][c];
+#pragma unroll
+    for (int w = 1; w < kVerifyWaves; ++w) mx = fmaxf(mx, sm_m[w][c]);
+    const float mu = (mx == -INFINITY) ? 0.0f : mx;
+    float l = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kVerifyWaves; ++w) {
+      const float f = fast_exp2(sm_m[w][c] - mu);
+      l += sm_l[w][c] * f;
+      acc += sm_o[w][c][dd] * f;
+    }
+    const int i = c / G;
+    const int64_t row = (static_cast<int64_t>(b) * nq + i) * hq + g * G + c % G;
+    const float lse2 = mu + fast_log2(l);
+    if (final_row) {
+      a.out[row * D + dd] = acc / l;
+      if (dd == 0) a.lse[row] = lse2 * kLn2;
+    } else {
+      a.part_o[(row * a.splits + split) * D + dd] = acc / l;
+      if (dd == 0) a.part_lse[row * a.splits + split] = lse2;
+    }
+  }
+
+  // Append the new tokens (split 0; every read of this workgroup is done).
+  if (split == 0) {
+    for (int e = threadIdx.x; e < nq * D; e += blockDim.x) {
+      const int j = e / D;
+      const int dd = e - j * D;
+      const int p = t0 + j;
+      int64_t blk;
+      if constexpr (kFull) {
+        const int lb = p / kBlock;
+        const int pg = lb < a.table_stride ? page_row[lb] : -1;
+        if (pg < 0 || pg >= a.num_blocks) continue;
+        blk = (static_cast<int64_t>(pg) * hkv + g) * kBlock * D;
+      } else {
+        if (ring < 0 || ring >= a.num_blocks) continue;
+        const int s = p % W;
+        blk = ((static_cast<int64_t>(ring) * hkv + g) * W + kBlock * (s / kBlock)) * D;
+      }
+      const int row = p % kBlock;
+      const int64_t src = ((static_cast<int64_t>(b) * nq + j) * hkv + g) * D + dd;
+      a.k_pool_w[blk + k_elem(row, dd)] = static_cast<uint16_t>(bf16_at<kF32>(a.k_new, src));
+      a.v_pool_w[blk + v_elem(row, dd)] = static_cast<uint16_t>(bf16_at<kF32>(a.v_new, src));
+    }
+  }
+}
+
+// Split-K merge of verify partials: one thread per output element of a
+// sequence's nq * Hq rows, splits folded with a running max (log2 domain).
+template <int D>
+__global__ __launch_bounds__(256) void verify_reduce_kernel(VerifyArgs a) {
+  const int b = blockIdx.y;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  const int nq = a.nq;
+  if (e >= nq * a.geo.hq * D) return;
+  const int t0 = a.kv_len[b] - nq;
+  if (t0 < 0) return;
+  const int nblk = min((t0 + kBlock - 1) / kBlock, a.table_stride);
+  const int nsplit = max(1, min((nblk + a.split_blocks - 1) / a.split_blocks, a.splits));
+  if (nsplit <= 1) return;
+  const int r = e / D;               // row of the sequence: token * hq + head
+  const int dd = e - r * D;
+  const int64_t row = static_cast<int64_t>(b) * nq * a.geo.hq + r;
+  const float* pl = a.part_lse + row * a.splits;
+  const float* po = a.part_o + row * a.splits * D + dd;
+  float m = -INFINITY, l = 0.0f, acc = 0.0f;
+#pragma unroll 4
+  for (int s = 0; s < nsplit; ++s) {
+    const float ls = pl[s];
+    const float os = po[static_cast<int64_t>(s) * D];
+    const float mn = fmaxf(m, ls);
+    const float mu = (mn == -INFINITY) ? 0.0f : mn;
+    const float f = fast_exp2(m - mu);
+    const float w = fast_exp2(ls - mu);
+    l = l * f + w;
+    acc = acc * f + (w > 0.0f ? w * os : 0.0f);
+    m = mn;
+  }
+  a.out[row * D + dd] = acc / l;
+  if (dd == 0) a.lse[row] = ((m == -INFINITY ? 0.0f : m) + fast_log2(l)) * kLn2;
+}
+
+int verify_column_groups(int nq, int group) { return (nq * group + 15) / 16; }
+
+template <int D, bool kFull, int NG>
+static void launch_verify_k(const VerifyArgs& a, dim3 grid, hipStream_t stream) {
+  const dim3 block(64 * kVerifyWaves);
+  if (a.in_f32) hipLaunchKernelGGL((verify_kernel<D, kFull, true, NG>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((verify_kernel<D, kFull, false, NG>), grid, block, 0, stream, a);
+}
+
+template <int D>
+static hipError_t launch_verify_d(const VerifyArgs& a, hipStream_t stream) {
+  const dim3 grid(a.full ? a.splits : 1, a.geo.hkv, a.batch);
+  const int ng = verify_column_groups(a.nq, a.geo.group);
+  if (a.full) {
+    if (ng == 1) launch_verify_k<D, true, 1>(a, grid, stream);
+    else launch_verify_k<D, true, 2>(a, grid, stream);
+  } else {
+    if (ng == 1) launch_verify_k<D, false, 1>(a, grid, stream);
+    else launch_verify_k<D, false, 2>(a, grid, stream);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (a.full && a.splits > 1) {
+    const dim3 rgrid((a.nq * a.geo.hq * D + 255) / 256, a.batch);
+    hipLaunchKernelGGL((verify_reduce_kernel<D>), rgrid, dim3(256), 0, stream, a);
+    err = hipGetLastError();
+  }
+  return err;
+}
+
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
+  if (a.batch == 0 || a.nq == 0) return hipSuccess;
+  if (a.geo.d == 64) return launch_verify_d<64>(a, stream);
+  return launch_verify_d<128>(a, stream);
+}
+
+}  // namespace ha

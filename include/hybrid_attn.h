@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define HA_ABI_VERSION 2
+#define HA_ABI_VERSION 3
 
 typedef enum ha_status {
   HA_OK = 0,
@@ -209,6 +209,33 @@ size_t hybrid_attn_workspace_size(const ha_shape* shape, int32_t kind, int32_t d
  * resolving num_splits = 0), or 0 on invalid input. */
 int32_t hybrid_attn_decode_splits(const ha_shape* shape, int32_t kind, int32_t batch, int32_t max_kv_len,
                                   int32_t num_splits);
+
+/* ---- multi-token verify decode ([HTX] 工程六 and [HD9] "MTP 与多模态流水线":
+ *          the MTP head's 1 + 3 proposed tokens are verified in one step) --
+ * nq new tokens per sequence at positions t0 .. t0 + nq - 1, t0 = kv_len[b] -
+ * nq; the pool holds positions < t0 and the tokens' K/V are given. Query
+ * token i sees keys [0, t0 + i] (full) or [t0 + i - W + 1, t0 + i] (SWA):
+ * causal among the new tokens. The call also appends the nq tokens (ring
+ * slots p mod W, or page p/16 row p mod 16) after reading: pool and outputs
+ * equal hybrid_attn_prefill over a chunk of nq tokens followed by the append.
+ * Full layers split the history over workgroups like hybrid_attn_decode.
+ *   kv_len int32 [batch] device (kv_len[b] < nq: rows out = 0, lse = -inf,
+ *     nothing appended);  max_kv_len >= every kv_len[b] (host)
+ *   nq: 1 <= nq <= 16 and nq * (Hq / Hkv) <= 32
+ *   q [batch][nq][Hq][D], k_new/v_new [batch][nq][Hkv][D] in_dtype (required)
+ *   out float32 [batch][nq][Hq][D]; lse float32 [batch][nq][Hq] (natural log)
+ *   num_splits: maximum key splits per sequence, 0 = automatic
+ *   workspace: hybrid_attn_verify_workspace_size(...) bytes (0 for SWA or a
+ *   single split); scratch for this call only. */
+ha_status hybrid_attn_verify(const ha_shape* shape, const ha_kv_view* kv, const int32_t* kv_len,
+                             int32_t batch, int32_t max_kv_len, int32_t nq, const void* q,
+                             const void* k_new, const void* v_new, int32_t in_dtype, float* out, float* lse,
+                             int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes hybrid_attn_verify needs for these arguments; 0 when none
+ * is needed or on invalid input. */
+size_t hybrid_attn_verify_workspace_size(const ha_shape* shape, int32_t kind, int32_t batch, int32_t max_kv_len,
+                                         int32_t nq, int32_t num_splits);
 
 const char* ha_status_str(int32_t status);
 const char* ha_last_error(void);

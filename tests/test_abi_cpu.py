@@ -152,3 +152,35 @@ def test_errors_do_not_leak_between_calls(lib):
     assert out.value == 0
     assert lib.ha_last_error() == b""
     assert s.window == 128
+
+
+def verify_call(lib, shape, kv, batch=2, max_len=100, nq=4, q=FAKE, k_new=FAKE, v_new=FAKE, dtype=0, splits=0,
+                ws=None, ws_bytes=0):
+    return lib.hybrid_attn_verify(ctypes.byref(shape) if shape is not None else None,
+                                  ctypes.byref(kv) if kv is not None else None, FAKE, batch, max_len, nq, q, k_new,
+                                  v_new, dtype, FAKE, FAKE, splits, ws, ws_bytes, None)
+
+
+def test_verify_errors_and_workspace(lib):
+    s = good_shape()                       # group 8
+    ring = view(kind=_lib.HA_SWA)
+    assert verify_call(lib, s, ring, nq=0) == _lib.HA_ERR_RANGE
+    assert verify_call(lib, s, ring, nq=17) == _lib.HA_ERR_RANGE
+    assert verify_call(lib, s, ring, nq=5) == _lib.HA_ERR_SHAPE          # 5 * 8 columns > 32
+    assert verify_call(lib, good_shape(num_q_heads=8, num_kv_heads=8), ring, nq=16, k_new=None) == \
+        _lib.HA_ERR_NULL                                                  # group 1: nq 16 allowed
+    assert verify_call(lib, s, ring, k_new=None) == _lib.HA_ERR_NULL
+    assert verify_call(lib, s, ring, v_new=None) == _lib.HA_ERR_NULL
+    assert verify_call(lib, s, ring, q=None) == _lib.HA_ERR_NULL
+    assert verify_call(lib, s, ring, batch=70000) == _lib.HA_ERR_RANGE
+    assert verify_call(lib, s, ring, dtype=7) == _lib.HA_ERR_UNSUPPORTED
+    assert verify_call(lib, None, ring) == _lib.HA_ERR_NULL
+    # full layers: split-K partials need a workspace sized for nq rows per sequence
+    need = lib.hybrid_attn_verify_workspace_size(ctypes.byref(s), _lib.HA_FULL, 64, 8196, 4, 0)
+    splits = lib.hybrid_attn_decode_splits(ctypes.byref(s), _lib.HA_FULL, 64, 8196, 0)
+    assert splits > 1 and need == 64 * 4 * 64 * splits * (128 + 1) * 4
+    assert verify_call(lib, s, view(), batch=64, max_len=8196) == _lib.HA_ERR_WORKSPACE
+    assert verify_call(lib, s, view(), batch=64, max_len=8196, ws=FAKE, ws_bytes=need - 1) == _lib.HA_ERR_WORKSPACE
+    assert lib.hybrid_attn_verify_workspace_size(ctypes.byref(s), _lib.HA_SWA, 64, 8196, 4, 0) == 0
+    assert lib.hybrid_attn_verify_workspace_size(ctypes.byref(s), _lib.HA_FULL, 64, 8196, 5, 0) == 0   # invalid nq
+    assert verify_call(lib, s, ring, batch=0) == _lib.HA_OK
