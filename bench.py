@@ -47,7 +47,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", choices=["decode", "reuse", "ragged", "chunked", "copy"], default="decode",
+    p.add_argument("--workload", choices=["decode", "reuse", "ragged", "chunked", "copy", "verify"], default="decode",
                    help="copy: 2 GiB elementwise copy, the known-size kernel that scales HBM counters")
     p.add_argument("--prefill-passes", type=int, default=3)
     p.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill part")
@@ -270,6 +270,105 @@ def run_decode(torch, ha, grp, synth, struct, args, device):
         "splits_full": ha.hybrid_attn_decode_splits(shape, ha.HA_FULL, struct.batch, int(kv_len.max())),
     }
     return shape, group, data, dt, step_bytes, full_bytes, info
+
+
+def verify_layer_bytes(shape, kind, t0, nq):
+    """Algorithmic bytes of one multi-token verify call: the history keys the
+    queries need (all t0 for full layers; the W-1 before t0 for SWA layers),
+    the new tokens' K/V read and appended, Q read, O (fp32) and LSE written."""
+    t0 = np.asarray(t0, dtype=np.int64)
+    hist = t0 if kind == "full" else np.minimum(t0, shape.window - 1)
+    b = len(t0)
+    tok = kv_bytes_per_token(shape)
+    q = b * nq * shape.num_q_heads * shape.head_dim * 2
+    o = b * nq * shape.num_q_heads * shape.head_dim * 4
+    l = b * nq * shape.num_q_heads * 4
+    return int(hist.sum()) * tok + 2 * b * nq * tok + q + o + l
+
+
+def run_verify(torch, ha, grp, synth, args, device, nq=4):
+    """The decode workload's pools, one step verifying nq tokens per sequence
+    in every layer of the group (graph replay), and the full-layer call alone."""
+    struct = synth.decode_structure()
+    shape, group, _plan, data = build_decode(torch, ha, grp, synth, struct, device, struct.workload)
+    b = struct.batch
+    hist = data["hist"].astype(np.int64)
+    hq, hkv, d = shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    kv_len = torch.as_tensor((hist + nq).astype(np.int32), device=device)
+    max_len = int(hist.max()) + nq
+    calls = []
+    for li, layer in enumerate(group.layers):
+        q = synth.normal_bf16((b, nq, hq, d), struct.workload, li, synth.Q_VALUES + 11, device)
+        k = synth.normal_bf16((b, nq, hkv, d), struct.workload, li, synth.K_VALUES + 11, device)
+        v = synth.normal_bf16((b, nq, hkv, d), struct.workload, li, synth.V_VALUES + 11, device)
+        out = torch.empty(b, nq, hq, d, dtype=torch.float32, device=device)
+        lse = torch.empty(b, nq, hq, dtype=torch.float32, device=device)
+        need = ha.hybrid_attn_verify_workspace_size(shape, layer.view.kind, b, max_len, nq)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+        calls.append((layer, q, k, v, out, lse, ws))
+
+    def call(c, stream=None):
+        layer, q, k, v, out, lse, ws = c
+        ha.hybrid_attn_verify(shape, layer.view, kv_len, q, k, v, max_len, out=out, lse=lse, workspace=ws,
+                              stream=stream)
+
+    stream = torch.cuda.current_stream()
+    for c in calls:
+        call(c)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for c in calls:
+            call(c, side)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    full_i = [i for i, layer in enumerate(group.layers) if layer.kind == "full"][0]
+    ev = timed_events(torch, 1)[0]
+    reps = max(5, min(args.steps, 20))
+    ms = 0.0
+    for _ in range(reps):
+        ev[0].record(stream)
+        call(calls[full_i])
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        ms += ev[0].elapsed_time(ev[1])
+    full_ms = ms / reps
+    step_bytes = sum(verify_layer_bytes(shape, layer.kind, hist, nq) for layer in group.layers)
+    full_bytes = verify_layer_bytes(shape, "full", hist, nq)
+    value = step_bytes / dt / 1e9
+    log(f"[bench] verify step {dt * 1e3:.3f} ms, {value:.1f} GB/s, {b * nq / dt:.0f} tokens verified/s; "
+        f"full call {full_ms * 1e3:.1f} us ({full_bytes / full_ms / 1e6:.0f} GB/s)")
+    return {
+        "metric": "multi-token verify decode attn HBM GB/s (% peak), SWA:full 6:1",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dt * 1e3, 4),
+        "higher_is_better": True,
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": (f"verify: {b} sequences x {int(hist[0])} cached tokens + {nq} new tokens each "
+                                f"(causal among them), one 6:1 group, Hq/Hkv/D {hq}/{hkv}/{d}"),
+                   "global_batch": b, "tokens_per_sequence": nq, "parallelism": "none (1 GPU)"},
+        "pct_peak_hbm": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "tokens_verified_per_s": round(b * nq / dt, 1),
+        "roofline": {"bound": "hbm", "achieved": round(full_bytes / full_ms / 1e6, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(full_bytes / full_ms / 1e6 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "hybrid_attn_verify, full layer (verify_kernel<128,full,bf16,2> + reduce)",
+                     "bytes_per_launch": full_bytes},
+    }
 
 
 def prefill_pass_flops(shape, kinds, batch, total, chunk):
@@ -575,6 +674,9 @@ def main():
 
     if args.workload == "reuse":
         print(json.dumps(run_reuse(torch, ha, grp, synth, args, device)))
+        return 0
+    if args.workload == "verify":
+        print(json.dumps(run_verify(torch, ha, grp, synth, args, device)))
         return 0
     struct = {"decode": synth.decode_structure, "ragged": synth.ragged_structure}[args.workload]()
     log(f"[bench] workload={args.workload} building inputs")
