@@ -52,6 +52,7 @@ def parse():
     p.add_argument("--prefill-passes", type=int, default=3)
     p.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill part")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-verify", action="store_true", help="skip the multi-token verify part")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU sample")
     p.add_argument("--cpu-prefill-seconds", type=float, default=10.0,
                    help="target oracle time for the prefill CPU sample")
@@ -727,6 +728,12 @@ def main():
                                       0.0 if args.no_cpu_baseline else args.cpu_prefill_seconds)
         log(f"[bench] prefill {line['prefill']['tflops']:.1f} TFLOP/s, full layer "
             f"{line['prefill']['full_layer_tflops']:.1f} TFLOP/s")
+    if args.workload == "decode" and not args.no_verify:
+        log("[bench] multi-token verify")
+        v = run_verify(torch, ha, grp, synth, args, device)
+        line["verify"] = {k: v[k] for k in ("value", "unit", "ms_per_step", "pct_peak_hbm", "tokens_verified_per_s")}
+        line["verify"]["workload"] = v["config"]["workload"]
+        line["verify"]["full_call_gbs"] = v["roofline"]["achieved"]
     if args.workload == "decode" and not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(torch, shape, group, data, args.cpu_seconds)
