@@ -237,6 +237,34 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
     for (int r = 0; r < 4; ++r) kp[r] = hist_pos(i, 4 * q4 + r);
   };
 
+  // The new tokens as one more block (split 0, wave 0): key k = token k < nq.
+  // Its loads go out first and it is consumed first, so its gathers overlap
+  // the history loads rather than following them.
+  const bool has_new = split == 0 && wave == 0;
+  VBlock<D> N;
+  if (has_new) {
+    const bool krow = c16 < nq;
+    const int64_t ksrc = ((static_cast<int64_t>(b) * nq + (krow ? c16 : 0)) * hkv + g) * D + 8 * q4;
+#pragma unroll
+    for (int m = 0; m < KS; ++m) {
+      N.k[m] = load8_as_bf16<kF32>(a.k_new, ksrc + 32 * m);
+      if (!krow) N.k[m] = u32x4{0u, 0u, 0u, 0u};
+    }
+    // V^T operand: lane (q4, c16), dim tile d holds tokens 4 q4 .. 4 q4 + 3 of
+    // channel 16 d + c16.
+    uint32_t vb[4][DT];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = 4 * q4 + r;
+      const bool ok = tok < nq;
+      const int64_t vsrc = ((static_cast<int64_t>(b) * nq + (ok ? tok : 0)) * hkv + g) * D + c16;
+#pragma unroll
+      for (int d = 0; d < DT; ++d) vb[r][d] = ok ? bf16_at<kF32>(a.v_new, vsrc + 16 * d) : 0u;
+    }
+#pragma unroll
+    for (int d = 0; d < DT; ++d) N.v[d] = u32x2{vb[0][d] | (vb[1][d] << 16), vb[2][d] | (vb[3][d] << 16)};
+  }
+
   // History blocks of this wave: first + wave + 4k, two in flight.
   {
     int ia = first + wave;
@@ -249,6 +277,12 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
     vload_block<D>(B, a.k_pool, a.v_pool, base_b, lane);
     pg_a2 = page_of(ia + 2 * kVerifyWaves);
     pg_b2 = page_of(ib + 2 * kVerifyWaves);
+    if (has_new) {
+      int kpn[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) kpn[r] = (4 * q4 + r < nq) ? t0 + 4 * q4 + r : -1;
+      consume(N, kpn);
+    }
     const int nmine = (last > ia) ? (last - ia + kVerifyWaves - 1) / kVerifyWaves : 0;
     int kp[4];
     for (int k = 0; k + 1 < nmine; k += 2) {
@@ -273,35 +307,6 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
       hist_keys(ia, kp);
       consume(A, kp);
     }
-  }
-
-  // The new tokens as one more block (split 0, wave 0): key k = token k < nq.
-  if (split == 0 && wave == 0) {
-    VBlock<D> N;
-    const bool krow = c16 < nq;
-    const int64_t ksrc = ((static_cast<int64_t>(b) * nq + (krow ? c16 : 0)) * hkv + g) * D + 8 * q4;
-#pragma unroll
-    for (int m = 0; m < KS; ++m) {
-      N.k[m] = load8_as_bf16<kF32>(a.k_new, ksrc + 32 * m);
-      if (!krow) N.k[m] = u32x4{0u, 0u, 0u, 0u};
-    }
-    // V^T operand: lane (q4, c16), dim tile d holds tokens 4 q4 .. 4 q4 + 3 of
-    // channel 16 d + c16.
-    uint32_t vb[4][DT];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tok = 4 * q4 + r;
-      const bool ok = tok < nq;
-      const int64_t vsrc = ((static_cast<int64_t>(b) * nq + (ok ? tok : 0)) * hkv + g) * D + c16;
-#pragma unroll
-      for (int d = 0; d < DT; ++d) vb[r][d] = ok ? bf16_at<kF32>(a.v_new, vsrc + 16 * d) : 0u;
-    }
-#pragma unroll
-    for (int d = 0; d < DT; ++d) N.v[d] = u32x2{vb[0][d] | (vb[1][d] << 16), vb[2][d] | (vb[3][d] << 16)};
-    int kp[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) kp[r] = (4 * q4 + r < nq) ? t0 + 4 * q4 + r : -1;
-    consume(N, kp);
   }
 
   // Merge the four waves.
