@@ -13,6 +13,8 @@ fp64 oracle on sampled rows (bf16 inputs, fp32 accumulation: max |O| error
            token match restores evicted (NaN) slots and produces NaN rows.
   ragged   24 sequences up to 1M cached tokens, one decode step with split-K;
            SWA rows for all, full-layer rows for a sample of sequences.
+  verify   the decode workload's shapes with 4 new tokens per sequence per
+           layer through hybrid_attn_verify; all rows.
 """
 
 import numpy as np
@@ -305,3 +307,33 @@ def test_ragged_long_decode_split_k():
             check_rows(shape, layer.kind, host(q[s:s + 1]), ks, vs_, [int(hist[s] - lo[s])],
                        host(out[li][s:s + 1]), host(lse[li][s:s + 1]), f"ragged layer {li} seq {s} len {hist[s]}")
             del ks, vs_
+
+
+def test_verify_workload_all_rows():
+    """The decode workload's shapes with 4 new tokens per sequence per layer,
+    verified by hybrid_attn_verify in the bench's launch configuration
+    (automatic split-K for the full layer); every row against the oracle."""
+    struct = synth.decode_structure()
+    shape = head_shape(struct)
+    b, hist, nq = struct.batch, int(struct.hist[0]), 4
+    hq, hkv, d, w = shape.num_q_heads, shape.num_kv_heads, shape.head_dim, shape.window
+    group = make_group(struct, shape)
+    results = []
+    for li, layer in enumerate(group.layers):
+        lo = hist - (w - 1) if layer.kind == "swa" else 0          # the history the first new token can see
+        n_hist = hist - lo
+        k = synth.normal_bf16((b, n_hist + nq, hkv, d), "decode", li, synth.K_VALUES + 11, DEV)
+        v = synth.normal_bf16((b, n_hist + nq, hkv, d), "decode", li, synth.V_VALUES + 11, DEV)
+        q = synth.normal_bf16((b, nq, hq, d), "decode", li, synth.Q_VALUES + 11, DEV)
+        append_rows(shape, layer, [lo] * b, k[:, :n_hist].reshape(-1, hkv, d), v[:, :n_hist].reshape(-1, hkv, d),
+                    [n_hist] * b)
+        out, lse = ha.hybrid_attn_verify(shape, layer.view, i32([hist + nq] * b), q, k[:, n_hist:].contiguous(),
+                                         v[:, n_hist:].contiguous(), hist + nq)
+        results.append((k, v, q, lo, out, lse))
+    torch.cuda.synchronize()
+    for li, layer in enumerate(group.layers):
+        k, v, q, lo, out, lse = results[li]
+        for s in range(b):
+            # positions shifted by lo: the SWA window is translation-invariant
+            check_rows(shape, layer.kind, host(q[s]), host(k[s]), host(v[s]), np.arange(nq) + (hist - lo),
+                       host(out[s]), host(lse[s]), f"verify layer {li} seq {s}")
