@@ -111,6 +111,14 @@ __device__ __forceinline__ u32x4 keep_tokens_v(u32x4 v, int q, int nv) {
   return u32x4{v.x & m0, v.y & m1, v.z & m0, v.w & m1};
 }
 
+// Zero token `tok` (0..15) of a V unit of lane group q (tokens 4q..4q+3).
+__device__ __forceinline__ u32x4 drop_token_v(u32x4 v, int q, int tok) {
+  if ((tok >> 2) != q) return v;
+  const uint32_t m = (tok & 1) ? 0x0000ffffu : 0xffff0000u;
+  if (tok & 2) return u32x4{v.x, v.y & m, v.z, v.w & m};
+  return u32x4{v.x & m, v.y, v.z & m, v.w};
+}
+
 }  // namespace
 
 int64_t prefill_stage_blocks(int num_tokens, int batch) {
@@ -346,6 +354,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
   __amdgpu_buffer_rsrc_t st_rv;   // V source of the block being staged
   int st_valid = kBlock;          // leading valid tokens of that block
   bool st_partial = false;        // partial history block: zero its unwritten V
+  int st_drop = -1;               // ring slot of position hist - W in this block (zeroed), or -1
   // K goes global -> LDS directly (buffer_load ... lds: lane l's 16 bytes land
   // at the wave's LDS base + 16 l); V goes through registers (partial history
   // blocks get their unwritten tokens zeroed on the way).
@@ -361,6 +370,13 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
     st_rv = make_rsrc(vp, bytes);
     st_valid = valid;
     st_partial = hist_tile && valid < kBlock;
+    // SWA: the slot of position hist - W is outside every query's window and
+    // need not hold it (the ring only has to keep [hist - W + 1, hist)); its
+    // V is zeroed so that whatever it holds cannot reach O through P = 0.
+    st_drop = -1;
+    if constexpr (!kFull) {
+      if (hist_tile && hist >= W && (hist % W) / kBlock == tile * kStageBlocks + sb) st_drop = (hist % W) % kBlock;
+    }
 #pragma unroll
     for (int j = 0; j < kStageUnits; ++j) {
       const int e = lane + 64 * (part * kStageUnits + j);      // 16-byte chunk of the block
@@ -381,6 +397,12 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
     if (st_partial) {
 #pragma unroll
       for (int j = 0; j < kVUnits; ++j) stv[j] = keep_tokens_v(stv[j], lane >> 4, st_valid);
+    }
+    if constexpr (!kFull) {
+      if (st_drop >= 0) {
+#pragma unroll
+        for (int j = 0; j < kVUnits; ++j) stv[j] = drop_token_v(stv[j], lane >> 4, st_drop);
+      }
     }
   };
   auto store_v = [&](int buf, int phase) {

@@ -148,7 +148,10 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
     }
   };
   // Position of key k (0..15) of history block i, or -1 if that slot holds
-  // no key below t0.
+  // no key a query can see. Ring slots hold positions [t0 - W, t0) at most;
+  // t0 - W is outside every query's window and its slot need not hold it
+  // (the caller only has to keep [t0 - W + 1, t0)), so it counts as no key
+  // and its V is zeroed like any other missing key's.
   auto hist_pos = [&](int i, int k) -> int {
     if constexpr (kFull) {
       const int p = kBlock * i + k;
@@ -159,7 +162,7 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
       int d = (last_p - s) % W;
       if (d < 0) d += W;
       const int p = last_p - d;
-      return p >= 0 ? p : -1;
+      return (p >= 0 && p > t0 - W) ? p : -1;
     }
   };
 
@@ -323,32 +326,42 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
   }
   __syncthreads();
 
+  // Per column: the merged max, the four waves' weights 2^(m_w - mu) / l and
+  // the LSE, once; then the rows as float4 weighted sums of the waves' O.
   const bool final_row = (nsplit == 1);
   const int ncols = nq * G;
-  for (int e = threadIdx.x; e < ncols * D; e += blockDim.x) {
-    const int c = e / D;
-    const int dd = e - c * D;
+  __shared__ float sm_f[kVerifyWaves][kCols];
+  if (threadIdx.x < ncols) {
+    const int c = threadIdx.x;
     float mx = sm_m[0][c];
 #pragma unroll
     for (int w = 1; w < kVerifyWaves; ++w) mx = fmaxf(mx, sm_m[w][c]);
     const float mu = (mx == -INFINITY) ? 0.0f : mx;
-    float l = 0.0f, acc = 0.0f;
+    float f[kVerifyWaves], l = 0.0f;
 #pragma unroll
     for (int w = 0; w < kVerifyWaves; ++w) {
-      const float f = fast_exp2(sm_m[w][c] - mu);
-      l += sm_l[w][c] * f;
-      acc += sm_o[w][c][dd] * f;
+      f[w] = fast_exp2(sm_m[w][c] - mu);
+      l += sm_l[w][c] * f[w];
     }
-    const int i = c / G;
-    const int64_t row = (static_cast<int64_t>(b) * nq + i) * hq + g * G + c % G;
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int w = 0; w < kVerifyWaves; ++w) sm_f[w][c] = f[w] * inv;
+    const int64_t row = (static_cast<int64_t>(b) * nq + c / G) * hq + g * G + c % G;
     const float lse2 = mu + fast_log2(l);
-    if (final_row) {
-      a.out[row * D + dd] = acc / l;
-      if (dd == 0) a.lse[row] = lse2 * kLn2;
-    } else {
-      a.part_o[(row * a.splits + split) * D + dd] = acc / l;
-      if (dd == 0) a.part_lse[row * a.splits + split] = lse2;
-    }
+    if (final_row) a.lse[row] = lse2 * kLn2;
+    else a.part_lse[row * a.splits + split] = lse2;
+  }
+  __syncthreads();
+  constexpr int kD4 = D / 4;
+  for (int e = threadIdx.x; e < ncols * kD4; e += blockDim.x) {
+    const int c = e / kD4;
+    const int d4 = e - c * kD4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kVerifyWaves; ++w) acc += *reinterpret_cast<const f32x4*>(&sm_o[w][c][4 * d4]) * sm_f[w][c];
+    const int64_t row = (static_cast<int64_t>(b) * nq + c / G) * hq + g * G + c % G;
+    float* dst = final_row ? a.out + row * D : a.part_o + (row * a.splits + split) * D;
+    *reinterpret_cast<f32x4*>(dst + 4 * d4) = acc;
   }
 
   // Append the new tokens (split 0; every read of this workgroup is done).

@@ -209,3 +209,26 @@ def test_late_score_jumps_and_wide_dynamic_range(kind):
     for b in range(len(totals)):
         seqs.q[b] = (seqs.q[b].float() * 6.0).to(torch.bfloat16)
     check(*run_chunks(shape, kind, seqs, [[0, 128, t] for t in totals]))
+
+
+def test_swa_ring_holding_only_the_needed_window():
+    """The ring only has to hold positions [hist - W + 1, hist): the slot of
+    hist - W may hold anything (here NaN) and must not reach the output."""
+    shape = ha.HeadShape(64, 8, 128)
+    hist, n = [300, 128, 1000], [40, 77, 5]
+    totals = [h + c for h, c in zip(hist, n)]
+    seqs = Seqs(shape, totals, seed=61)
+    pool = ha.SwaRingPool(shape, len(totals), "cuda", fill=float("nan"))
+    view = pool.view(i32(list(range(len(totals)))))
+    w = shape.window
+    append_history(shape, view, list(zip(seqs.k, seqs.v)), [h - (w - 1) for h in hist], hist)
+    cu = cu_from_counts(n)
+    cat = lambda xs: torch.cat([x[h:t] for x, h, t in zip(xs, hist, totals)]).contiguous()
+    out, lse = ha.hybrid_attn_prefill(shape, view, i32(hist), i32(cu), cat(seqs.q), cat(seqs.k), cat(seqs.v),
+                                      max_new=max(n))
+    torch.cuda.synchronize()
+    o, l = host(out), host(lse)
+    for b, (h, t) in enumerate(zip(hist, totals)):
+        rows = np.arange(h, t)
+        ref_o, ref_l = oracle_rows(host(seqs.q[b])[rows], host(seqs.k[b]), host(seqs.v[b]), rows, "swa", w)
+        assert_close(o[cu[b]:cu[b + 1]], l[cu[b]:cu[b + 1]], ref_o, ref_l, f"seq {b}")

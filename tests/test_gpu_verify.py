@@ -147,3 +147,25 @@ def test_verify_one_token_equals_fused_decode(kind):
     assert np.abs(lse[:, 0] - host(d_lse)).max() <= 1e-3
     assert torch.equal(a.pool.k.view(torch.int16), b.pool.k.view(torch.int16))
     assert torch.equal(a.pool.v.view(torch.int16), b.pool.v.view(torch.int16))
+
+
+def test_swa_verify_with_ring_holding_only_the_needed_window():
+    """The ring only has to hold [t0 - W + 1, t0): the slot of t0 - W holds
+    NaN here and must not reach the output."""
+    shape = ha.HeadShape(64, 8, 128)
+    lens, nq, w = [304, 132, 1004], 4, 128
+    gen = make_generator(71)
+    k = [randn_bf16(gen, n, 8, 128) for n in lens]
+    v = [randn_bf16(gen, n, 8, 128) for n in lens]
+    q = [randn_bf16(gen, n, 64, 128) for n in lens]
+    pool = ha.SwaRingPool(shape, len(lens), "cuda", fill=float("nan"))
+    view = pool.view(i32(list(range(len(lens)))))
+    t0 = [n - nq for n in lens]
+    append_history(shape, view, list(zip(k, v)), [t - (w - 1) for t in t0], t0)
+    rows = lambda xs: torch.stack([x[t:t + nq] for x, t in zip(xs, t0)]).contiguous()
+    out, lse = ha.hybrid_attn_verify(shape, view, i32(lens), rows(q), rows(k), rows(v), max(lens))
+    torch.cuda.synchronize()
+    for b, n in enumerate(lens):
+        pos = np.arange(n - nq, n)
+        ref_o, ref_l = oracle_rows(host(q[b][n - nq:n]), host(k[b]), host(v[b]), pos, "swa", w)
+        assert_close(host(out[b]), host(lse[b]), ref_o, ref_l, f"seq {b}")
