@@ -24,6 +24,7 @@ other workloads (--workload reuse|ragged) for extra JSON lines.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -47,7 +48,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", choices=["decode", "reuse", "ragged", "chunked", "copy", "verify"], default="decode",
+    p.add_argument("--restore-groups", type=int, default=4,
+                   help="groups in the stack the restore workload pipelines (its pools are per group)")
+    p.add_argument("--workload", choices=["decode", "reuse", "ragged", "chunked", "copy", "verify", "restore"],
+                   default="decode",
                    help="copy: 2 GiB elementwise copy, the known-size kernel that scales HBM counters")
     p.add_argument("--prefill-passes", type=int, default=3)
     p.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill part")
@@ -557,6 +561,130 @@ def run_reuse(torch, ha, grp, synth, args, device):
     }
 
 
+def run_restore(torch, ha, grp, synth, args, device):
+    """The prefix-reuse workload with its reused history held in pinned host
+    memory, over a stack of groups: each layer's rows are copied to the
+    device and scattered into its pool on a copy stream, layer l's restore
+    overlapping earlier layers' prefill. Times the restores alone, the
+    prefill passes alone and the overlapped pipeline, and the best that
+    pipeline can do given per-layer times (copy l must end before compute l
+    starts)."""
+    struct = synth.reuse_structure()
+    shape = ha.HeadShape(struct.shape.num_q_heads, struct.shape.num_kv_heads, struct.shape.head_dim,
+                         struct.shape.window)
+    b, w = struct.batch, shape.window
+    hq, hkv, d = shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    ng = args.restore_groups
+    prefix, suffix = struct.hist.astype(np.int64), struct.new.astype(np.int64)
+    reuse_len = np.array([ha.window_safe_match(*synth.reuse_tokens(struct, s), w) for s in range(b)], np.int64)
+    n_new = prefix + suffix - reuse_len
+    ring_id = torch.as_tensor(struct.ring_id, device=device)
+    table = torch.as_tensor(struct.page_table, device=device)
+    groups = [grp.HybridGroup(shape, ring_id, struct.num_rings, table, struct.num_pages) for _ in range(ng)]
+    nl = len(groups[0].layers)
+    log(f"[bench] restore: {ng} groups, pinning {int(reuse_len.sum())} cached positions per full layer")
+    first, counts, k_rows, v_rows = [], [], [], []
+    for li, layer in enumerate(groups[0].layers):
+        f = np.maximum(reuse_len - w, 0) if layer.kind == "swa" else np.zeros(b, np.int64)
+        c = reuse_len - f
+        first.append(f.tolist())
+        counts.append(c.tolist())
+        k_rows.append(synth.normal_bf16((int(c.sum()), hkv, d), "reuse", li, synth.K_VALUES, device))
+        v_rows.append(synth.normal_bf16((int(c.sum()), hkv, d), "reuse", li, synth.V_VALUES, device))
+    # every group restores the same pinned rows (a bandwidth workload): one
+    # pinned copy, one set of staging buffers on the one copy stream
+    host_kv = grp.HostKv(groups[0], first, counts, k_rows, v_rows)
+    del k_rows, v_rows
+    restores = [grp.RestorePlan(groups[0], host_kv)]
+    restores += [grp.RestorePlan(g, host_kv, staging_from=restores[0]) for g in groups[1:]]
+    t_new = int(n_new.sum())
+    qs, ks, vs, outs, lses = [], [], [], [], []
+    for li in range(nl):
+        qs.append(synth.normal_bf16((t_new, hq, d), "reuse", li, synth.Q_VALUES + 3, device))
+        ks.append(synth.normal_bf16((t_new, hkv, d), "reuse", li, synth.K_VALUES + 3, device))
+        vs.append(synth.normal_bf16((t_new, hkv, d), "reuse", li, synth.V_VALUES + 3, device))
+        outs.append(torch.empty(t_new, hq, d, dtype=torch.float32, device=device))
+        lses.append(torch.empty(t_new, hq, dtype=torch.float32, device=device))
+    hist = torch.as_tensor(reuse_len.astype(np.int32), device=device)
+    cu = torch.as_tensor(np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32), device=device)
+    # the groups' passes share their inputs and outputs (in order on one stream)
+    plans = [grp.plan_prefill(g, qs, ks, vs, hist, cu, int(n_new.max()), outs, lses) for g in groups]
+    compute, copy_stream = torch.cuda.current_stream(), torch.cuda.Stream()
+    reps = max(2, args.prefill_passes)
+
+    def timed(fn):
+        fn()                                    # warm
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts))
+
+    def restore_all():
+        for r in restores:
+            r.run(copy_stream)
+
+    def prefill_all():
+        for p in plans:
+            p.run(compute)
+
+    t_restore = timed(restore_all)
+    t_compute = timed(prefill_all)
+    t_overlap = timed(lambda: grp.run_restore_overlapped(restores, plans, compute, copy_stream))
+    # per-layer times of group 0, each stream alone
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nl)]
+    for li in range(nl):
+        ev[li][0].record(copy_stream)
+        restores[0].run_layer(li, copy_stream)
+        ev[li][1].record(copy_stream)
+    torch.cuda.synchronize()
+    r_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    by_layer = grp.layer_calls(plans[0], nl)
+    ptr = ctypes.c_void_p(compute.cuda_stream)
+    for li in range(nl):
+        ev[li][0].record(compute)
+        for call in by_layer[li]:
+            call(ptr)
+        ev[li][1].record(compute)
+    torch.cuda.synchronize()
+    p_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    copy_end = comp_end = 0.0
+    for _ in range(ng):
+        for li in range(nl):
+            copy_end += r_ms[li]
+            comp_end = max(comp_end, copy_end) + p_ms[li]
+    nbytes = host_kv.nbytes() * ng
+    hidden = t_restore + t_compute - t_overlap
+    frac = hidden / min(t_restore, t_compute)
+    log(f"[bench] restore {t_restore * 1e3:.2f} ms ({nbytes / t_restore / 1e9:.1f} GB/s host to device), "
+        f"prefill {t_compute * 1e3:.2f} ms, overlapped {t_overlap * 1e3:.2f} ms (schedule bound "
+        f"{comp_end:.2f} ms); {hidden * 1e3:.2f} ms hidden ({100 * frac:.1f}% of the shorter)")
+    log("[bench] per layer restore ms " + " ".join(f"{x:.2f}" for x in r_ms)
+        + " | prefill ms " + " ".join(f"{x:.2f}" for x in p_ms))
+    return {
+        "metric": "layer-wise KV restore from pinned host memory overlapped with prefill",
+        "workload": f"prefix-reuse prefill ({b} sequences, window-safe reuse L total {int(reuse_len.sum())}, "
+                    f"{t_new} new tokens) over a stack of {ng} 6:1 groups, each layer's reused history "
+                    f"restored from pinned host memory (full layer: all L positions; SWA layers: the last W)",
+        "groups": ng,
+        "restored_bytes": nbytes,
+        "restore_ms": t_restore * 1e3,
+        "h2d_gbs": nbytes / t_restore / 1e9,
+        "prefill_ms": t_compute * 1e3,
+        "serial_ms": (t_restore + t_compute) * 1e3,
+        "overlapped_ms": t_overlap * 1e3,
+        "schedule_bound_ms": comp_end,
+        "hidden_ms": hidden * 1e3,
+        "overlap_fraction_of_shorter": frac,
+        "layer_restore_ms": r_ms,
+        "layer_prefill_ms": p_ms,
+        "data": "synthetic",
+    }
+
+
 def cpu_baseline_prefill(torch, shape, group, qs, ks, vs, chunk, target_s):
     """Time the fp64 oracle on seeded sample rows of the chunked prefill
     (sequence 0; full and SWA layer alternately; all query heads) until about
@@ -678,6 +806,9 @@ def main():
         return 0
     if args.workload == "verify":
         print(json.dumps(run_verify(torch, ha, grp, synth, args, device)))
+        return 0
+    if args.workload == "restore":
+        print(json.dumps(run_restore(torch, ha, grp, synth, args, device)))
         return 0
     struct = {"decode": synth.decode_structure, "ragged": synth.ragged_structure}[args.workload]()
     log(f"[bench] workload={args.workload} building inputs")

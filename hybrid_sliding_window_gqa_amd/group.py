@@ -91,7 +91,7 @@ class _Call:
     def __init__(self, fn, args, keep):
         self.fn = fn
         self.args = args
-        self.keep = keep   # ctypes structs / tensors that must outlive the call
+        self.keep = keep   # ctypes structs and every tensor whose address is in args
 
     def __call__(self, stream_ptr):
         st = self.fn(*self.args, stream_ptr)
@@ -128,7 +128,7 @@ def _append_call(lib, shape, layer, pos0, cu_new, k_new, v_new):
     dt = _in_dtype(k_new, v_new)
     args = (ctypes.byref(c_shape), ctypes.byref(c_view), pos0.data_ptr(), cu_new.data_ptr(),
             layer.view.batch, int(k_new.shape[0]), k_new.data_ptr(), v_new.data_ptr(), dt)
-    return _Call(fn, args, (c_shape, c_view, pos0, cu_new, k_new, v_new))
+    return _Call(fn, args, (c_shape, c_view, layer.view, pos0, cu_new, k_new, v_new))
 
 
 def plan_decode(group: HybridGroup, q, k_new, v_new, pos, kv_len, max_kv_len: int, out, lse,
@@ -164,7 +164,8 @@ def plan_decode(group: HybridGroup, q, k_new, v_new, pos, kv_len, max_kv_len: in
                 q[li].data_ptr(), kp, vp, _in_dtype(q[li], k_new[li], v_new[li]), out[li].data_ptr(),
                 lse[li].data_ptr(), int(num_splits), ws.data_ptr() if need else None, need)
         calls.append(_Call(lib.hybrid_attn_decode, args,
-                           (c_shape, c_view, ws, kv_len, cu_one, k_new[li], v_new[li])))
+                           (c_shape, c_view, layer.view, ws, kv_len, pos, cu_one, q[li], k_new[li], v_new[li],
+                            out[li], lse[li])))
         labels.append(f"decode[{li}:{layer.kind}]")
     return Plan(calls, labels)
 
@@ -196,8 +197,128 @@ def plan_prefill(group: HybridGroup, q, k_new, v_new, hist_len, cu_new, max_new:
                 int(max_new), q[li].data_ptr(), k_new[li].data_ptr(), v_new[li].data_ptr(),
                 _in_dtype(q[li], k_new[li], v_new[li]), out[li].data_ptr(), lse[li].data_ptr(), ws.data_ptr(),
                 ws.numel())
-        calls.append(_Call(lib.hybrid_attn_prefill, args, (c_shape, c_view, ws)))
+        calls.append(_Call(lib.hybrid_attn_prefill, args,
+                           (c_shape, c_view, layer.view, ws, hist_len, cu_new, q[li], k_new[li], v_new[li],
+                            out[li], lse[li])))
         labels.append(f"prefill[{li}:{layer.kind}]")
         calls.append(_append_call(lib, shape, layer, hist_len, cu_new, k_new[li], v_new[li]))
         labels.append(f"append[{li}:{layer.kind}]")
     return Plan(calls, labels)
+
+
+# ---------------------------------------------------------------------------
+# Layer-wise restore of cached prefix KV from pinned host memory, overlapped
+# with attention (blog.hotdry.top 2026-06-09 "三层 KVCache 系统": the reused
+# prefix's KV sits in a host-memory tier and is brought back layer by layer
+# while earlier layers compute; youleyou.com "KVCache系统重构：让缓存真正省下来"
+# for the two pools it is restored into).
+
+class HostKv:
+    """A batch's cached-prefix K/V in pinned host memory, per layer: the
+    token-major rows [n, Hkv, D] (bf16) of the positions the layer restores --
+    every reused position [0, L) for the full layer, the ring's window
+    [max(0, L - W), L) for SWA layers -- with each sequence's first position
+    and row count."""
+
+    def __init__(self, group: HybridGroup, first, counts, k_rows, v_rows):
+        self.first, self.counts, self.k, self.v = [], [], [], []
+        for li in range(len(group.layers)):
+            n = int(sum(int(c) for c in counts[li]))
+            for name, t in (("k_rows", k_rows[li]), ("v_rows", v_rows[li])):
+                if tuple(t.shape) != (n, group.shape.num_kv_heads, group.shape.head_dim) or t.dtype != torch.bfloat16:
+                    raise ValueError(f"layer {li} {name}: expected bf16 [{n}, Hkv, D], got {t.dtype} {tuple(t.shape)}")
+            # new pinned allocations (never registration of existing memory)
+            self.k.append(k_rows[li].cpu().pin_memory())
+            self.v.append(v_rows[li].cpu().pin_memory())
+            self.first.append([int(x) for x in first[li]])
+            self.counts.append([int(x) for x in counts[li]])
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in self.k + self.v)
+
+
+class RestorePlan:
+    """Per layer: a host-to-device copy of the layer's rows into a device
+    staging buffer, then the library's append call scattering them into the
+    layer's pool (ring slots or pages). Restores of one stack run on one copy
+    stream, so groups may share staging buffers (``staging_from``): the copy
+    into a buffer is queued behind the append that last read it."""
+
+    def __init__(self, group: HybridGroup, host: HostKv, staging_from: "RestorePlan | None" = None):
+        lib = _lib.load()
+        dev = group.device
+        self.layers = []
+        for li, layer in enumerate(group.layers):
+            n = host.k[li].shape[0]
+            if n == 0:
+                self.layers.append(None)
+                continue
+            shared = staging_from.layers[li] if staging_from is not None else None
+            if shared is not None and tuple(shared[2].shape) == tuple(host.k[li].shape):
+                k_dev, v_dev = shared[2], shared[3]
+            else:
+                k_dev = torch.empty_like(host.k[li], device=dev)
+                v_dev = torch.empty_like(host.v[li], device=dev)
+            pos0 = torch.as_tensor(host.first[li], dtype=torch.int32, device=dev)
+            cu = torch.as_tensor([0] + list(_cumsum(host.counts[li])), dtype=torch.int32, device=dev)
+            call = _append_call(lib, group.shape, layer, pos0, cu, k_dev, v_dev)
+            self.layers.append((host.k[li], host.v[li], k_dev, v_dev, call))
+
+    def run_layer(self, li: int, stream) -> None:
+        item = self.layers[li]
+        if item is None:
+            return
+        k_host, v_host, k_dev, v_dev, call = item
+        with torch.cuda.stream(stream):
+            k_dev.copy_(k_host, non_blocking=True)
+            v_dev.copy_(v_host, non_blocking=True)
+        call(ctypes.c_void_p(stream.cuda_stream))
+
+    def run(self, stream) -> None:
+        for li in range(len(self.layers)):
+            self.run_layer(li, stream)
+
+
+def _cumsum(xs):
+    s = 0
+    for x in xs:
+        s += x
+        yield s
+
+
+def layer_calls(plan: Plan, num_layers: int):
+    """A group's prefill plan split by layer (labels carry the layer index)."""
+    by_layer = [[] for _ in range(num_layers)]
+    for call, label in zip(plan.calls, plan.labels):
+        by_layer[int(label.split("[", 1)[1].split(":", 1)[0])].append(call)
+    return by_layer
+
+
+def run_restore_overlapped(restores, prefills, compute_stream, copy_stream) -> None:
+    """A stack of groups (layers in forward order, group by group): every
+    layer's restore is queued on the copy stream up front, and each layer's
+    prefill (with its chunk append) waits only for its own restore, so layer
+    l+1's copy runs while layer l computes. The restores start after
+    everything already queued on the compute stream, so a repeated run cannot
+    overwrite a pool an earlier run still reads."""
+    if isinstance(restores, RestorePlan):
+        restores, prefills = [restores], [prefills]
+    if len(restores) != len(prefills):
+        raise ValueError("one restore plan per prefill plan")
+    copy_stream.wait_stream(compute_stream)
+    steps = []
+    for restore, plan in zip(restores, prefills):
+        nl = len(restore.layers)
+        for li, calls in enumerate(layer_calls(plan, nl)):
+            restore.run_layer(li, copy_stream)
+            ev = torch.cuda.Event()
+            ev.record(copy_stream)
+            steps.append((ev, calls))
+    ptr = ctypes.c_void_p(compute_stream.cuda_stream)
+    for ev, calls in steps:
+        compute_stream.wait_event(ev)
+        for call in calls:
+            call(ptr)
+    # the staging buffers and pools are reused by the next run: make later
+    # work on the copy stream wait for this run's compute
+    copy_stream.wait_stream(compute_stream)
