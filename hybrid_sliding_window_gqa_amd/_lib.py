@@ -1,4 +1,4 @@
-"""ctypes declarations of the C ABI in include/hybrid_attn.h.
+"""ctypes declarations of the C ABI in include/hybrid_attn.h and include/prefix_tree.h.
 
 Loading fails loudly when libhybridattn.so has not been built: there is no
 fallback implementation.
@@ -25,9 +25,9 @@ HA_F32 = 1
 HA_SWA = 0
 HA_FULL = 1
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 
-# Every symbol include/hybrid_attn.h declares.
+# Every symbol include/*.h declares.
 EXPORTS = (
     "swa_ring_append",
     "full_pool_append",
@@ -41,6 +41,16 @@ EXPORTS = (
     "ha_status_str",
     "ha_last_error",
     "ha_abi_version",
+    "ha_tree_create",
+    "ha_tree_destroy",
+    "ha_tree_insert",
+    "ha_tree_match",
+    "ha_tree_lock",
+    "ha_tree_ring_advance",
+    "ha_tree_ring_release",
+    "ha_tree_evict_full",
+    "ha_tree_evict_swa",
+    "ha_tree_stats",
 )
 
 
@@ -110,6 +120,23 @@ def load() -> ctypes.CDLL:
     lib.ha_last_error.restype = ctypes.c_char_p
     lib.ha_abi_version.argtypes = []
     lib.ha_abi_version.restype = i32
+    pi64 = ctypes.POINTER(i64)
+    tree_fns = {
+        "ha_tree_create": [i32, i32, ctypes.POINTER(p)],
+        "ha_tree_insert": [p, p, i64, p, i32, i64, i32, p, p],
+        "ha_tree_match": [p, p, i64, pi64, p, p, p],
+        "ha_tree_lock": [p, p, i64, i32],
+        "ha_tree_ring_advance": [p, i32, i64],
+        "ha_tree_ring_release": [p, i32],
+        "ha_tree_evict_full": [p, i64, p, i64, pi64, p, i64, pi64],
+        "ha_tree_evict_swa": [p, i64, p, i64, pi64],
+        "ha_tree_stats": [p, p],
+    }
+    for fn, args in tree_fns.items():
+        getattr(lib, fn).argtypes = args
+        getattr(lib, fn).restype = i32
+    lib.ha_tree_destroy.argtypes = [p]
+    lib.ha_tree_destroy.restype = None
     if lib.ha_abi_version() != ABI_VERSION:
         raise ImportError(f"libhybridattn.so ABI {lib.ha_abi_version()} != binding ABI {ABI_VERSION}")
     _lib = lib

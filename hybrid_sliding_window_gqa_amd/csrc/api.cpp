@@ -11,6 +11,7 @@
 
 #include "../../include/hybrid_attn.h"
 #include "kernels.hpp"
+#include "status.hpp"
 
 namespace {
 
@@ -143,6 +144,25 @@ ha_status check_nq(const ha::Geometry& geo, int nq) {
 }
 
 }  // namespace
+
+namespace ha {
+
+ha_status set_error(ha_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+ha_status clear_error() {
+  g_last_error.clear();
+  return HA_OK;
+}
+
+}  // namespace ha
 
 extern "C" {
 

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define HA_ABI_VERSION 3
+#define HA_ABI_VERSION 4
 
 typedef enum ha_status {
   HA_OK = 0,

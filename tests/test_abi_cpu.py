@@ -19,8 +19,11 @@ def lib():
 
 
 def _declared_functions():
-    with open(os.path.join(ROOT, "include", "hybrid_attn.h")) as f:
-        text = f.read()
+    text = ""
+    for name in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if name.endswith(".h"):
+            with open(os.path.join(ROOT, "include", name)) as f:
+                text += f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
     return sorted(set(names))
