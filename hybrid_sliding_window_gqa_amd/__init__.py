@@ -8,7 +8,7 @@ group driver. Importing the package does not load the library; the first
 call does, and fails loudly if it has not been built.
 """
 
-from ._lib import HA_BF16, HA_F32, HA_FULL, HA_SWA, HybridAttnError  # noqa: F401
+from ._lib import HA_BF16, HA_F32, HA_FULL, HA_KV_BF16, HA_KV_INT8, HA_SWA, HybridAttnError  # noqa: F401
 from .api import (  # noqa: F401
     FullPagePool,
     HeadShape,

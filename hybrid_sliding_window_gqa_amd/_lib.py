@@ -24,8 +24,10 @@ HA_BF16 = 0
 HA_F32 = 1
 HA_SWA = 0
 HA_FULL = 1
+HA_KV_BF16 = 0
+HA_KV_INT8 = 1
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 # Every symbol include/*.h declares.
 EXPORTS = (
@@ -73,6 +75,9 @@ class HaKvView(ctypes.Structure):
         ("num_blocks", ctypes.c_int32),
         ("table", ctypes.c_void_p),
         ("table_stride", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
     ]
 
 

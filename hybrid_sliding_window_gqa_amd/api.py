@@ -16,7 +16,7 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import HA_BF16, HA_F32, HA_FULL, HA_SWA, HaKvView, HaShape, check, load
+from ._lib import HA_BF16, HA_F32, HA_FULL, HA_KV_BF16, HA_KV_INT8, HA_SWA, HaKvView, HaShape, check, load
 
 BLOCK = 16
 
@@ -51,60 +51,95 @@ class KvView:
     num_blocks: int
     table: torch.Tensor          # ring ids [B] or page table [B, stride], int32
     table_stride: int = 0
+    kv_dtype: int = HA_KV_BF16   # HA_KV_INT8: k/v hold int8 codes, scales below
+    k_scale: torch.Tensor | None = None
+    v_scale: torch.Tensor | None = None
 
     def c(self) -> HaKvView:
+        ks = self.k_scale.data_ptr() if self.k_scale is not None else None
+        vs = self.v_scale.data_ptr() if self.v_scale is not None else None
         return HaKvView(self.kind, self.k.data_ptr(), self.v.data_ptr(), self.num_blocks,
-                        self.table.data_ptr(), self.table_stride)
+                        self.table.data_ptr(), self.table_stride, self.kv_dtype, ks, vs)
 
     @property
     def batch(self) -> int:
         return int(self.table.shape[0])
 
 
-class SwaRingPool:
-    """SWA pool of one layer: W slots per (ring, kv head), bfloat16.
+class _PoolStorage:
+    """K/V blocks of one layer in the pool format: bfloat16, or int8 codes
+    with one float32 scale per (block, kv head, token) for K and for V
+    (include/hybrid_attn.h). fill (tests): bf16 values, or int8 scales (the
+    codes then hold 127), so an unwritten slot shows up if it is ever used."""
 
-    K and V are [rings, Hkv, W/16, 16*D]: 16-slot blocks stored in the
-    library's matrix-core operand order (include/hybrid_attn.h)."""
-
-    def __init__(self, shape: HeadShape, num_rings: int, device, fill: float | None = None):
-        w, d, h = shape.window, shape.head_dim, shape.num_kv_heads
-        self.shape = shape
-        self.num_rings = num_rings
-        self.k = torch.empty(num_rings, h, w // BLOCK, BLOCK * d, dtype=torch.bfloat16, device=device)
-        self.v = torch.empty(num_rings, h, w // BLOCK, BLOCK * d, dtype=torch.bfloat16, device=device)
+    def _alloc(self, lead, d, device, kv_dtype: str, fill):
+        if kv_dtype not in ("bf16", "int8"):
+            raise ValueError(f"kv_dtype must be 'bf16' or 'int8', got {kv_dtype!r}")
+        self.kv_dtype = HA_KV_INT8 if kv_dtype == "int8" else HA_KV_BF16
+        dt = torch.int8 if kv_dtype == "int8" else torch.bfloat16
+        self.k = torch.empty(*lead, BLOCK * d, dtype=dt, device=device)
+        self.v = torch.empty(*lead, BLOCK * d, dtype=dt, device=device)
+        self.k_scale = self.v_scale = None
+        if kv_dtype == "int8":
+            self.k_scale = torch.empty(*lead, BLOCK, dtype=torch.float32, device=device)
+            self.v_scale = torch.empty(*lead, BLOCK, dtype=torch.float32, device=device)
         if fill is not None:
-            self.k.fill_(fill)
-            self.v.fill_(fill)
+            if kv_dtype == "int8":
+                self.k.fill_(127)
+                self.v.fill_(127)
+                self.k_scale.fill_(fill)
+                self.v_scale.fill_(fill)
+            else:
+                self.k.fill_(fill)
+                self.v.fill_(fill)
 
-    def view(self, ring_id: torch.Tensor) -> KvView:
-        _check_table(ring_id, 1, self.k.device)
-        return KvView(HA_SWA, self.k, self.v, self.num_rings, ring_id, 0)
+    def _view(self, kind, num_blocks, table, stride) -> KvView:
+        return KvView(kind, self.k, self.v, num_blocks, table, stride, self.kv_dtype, self.k_scale, self.v_scale)
 
     @property
     def nbytes(self) -> int:
-        return self.k.numel() * 2 + self.v.numel() * 2
+        n = self.k.numel() * self.k.element_size() + self.v.numel() * self.v.element_size()
+        if self.k_scale is not None:
+            n += (self.k_scale.numel() + self.v_scale.numel()) * 4
+        return n
 
 
-class FullPagePool:
-    """Full pool of one layer: 16-token pages, bfloat16.
+class SwaRingPool(_PoolStorage):
+    """SWA pool of one layer: W slots per (ring, kv head).
+
+    K and V are [rings, Hkv, W/16, 16*D]: 16-slot blocks stored in the
+    library's matrix-core operand order (include/hybrid_attn.h); int8 pools
+    add k_scale / v_scale [rings, Hkv, W/16, 16]."""
+
+    def __init__(self, shape: HeadShape, num_rings: int, device, fill: float | None = None,
+                 kv_dtype: str = "bf16"):
+        w, d, h = shape.window, shape.head_dim, shape.num_kv_heads
+        self.shape = shape
+        self.num_rings = num_rings
+        self._alloc((num_rings, h, w // BLOCK), d, device, kv_dtype, fill)
+
+    def view(self, ring_id: torch.Tensor) -> KvView:
+        _check_table(ring_id, 1, self.k.device)
+        return self._view(HA_SWA, self.num_rings, ring_id, 0)
+
+
+class FullPagePool(_PoolStorage):
+    """Full pool of one layer: 16-token pages.
 
     K and V are [pages, Hkv, 16*D]: each page is one 16-token block per kv
-    head in the library's matrix-core operand order (include/hybrid_attn.h)."""
+    head in the library's matrix-core operand order (include/hybrid_attn.h);
+    int8 pools add k_scale / v_scale [pages, Hkv, 16]."""
 
-    def __init__(self, shape: HeadShape, num_pages: int, device, fill: float | None = None):
+    def __init__(self, shape: HeadShape, num_pages: int, device, fill: float | None = None,
+                 kv_dtype: str = "bf16"):
         d, h = shape.head_dim, shape.num_kv_heads
         self.shape = shape
         self.num_pages = num_pages
-        self.k = torch.empty(num_pages, h, BLOCK * d, dtype=torch.bfloat16, device=device)
-        self.v = torch.empty(num_pages, h, BLOCK * d, dtype=torch.bfloat16, device=device)
-        if fill is not None:
-            self.k.fill_(fill)
-            self.v.fill_(fill)
+        self._alloc((num_pages, h), d, device, kv_dtype, fill)
 
     def view(self, page_table: torch.Tensor) -> KvView:
         _check_table(page_table, 2, self.k.device)
-        return KvView(HA_FULL, self.k, self.v, self.num_pages, page_table, int(page_table.shape[1]))
+        return self._view(HA_FULL, self.num_pages, page_table, int(page_table.shape[1]))
 
 
 class PageAllocator:

@@ -61,8 +61,12 @@ ha_status check_view(const ha_kv_view* kv, int batch) {
   if (!kv) return fail(HA_ERR_NULL, "kv view is NULL");
   if (kv->kind != HA_SWA && kv->kind != HA_FULL) return fail(HA_ERR_UNSUPPORTED, "unknown layer kind %d", kv->kind);
   if (kv->num_blocks < 0) return fail(HA_ERR_RANGE, "num_blocks is negative");
+  if (kv->kv_dtype != HA_KV_BF16 && kv->kv_dtype != HA_KV_INT8)
+    return fail(HA_ERR_UNSUPPORTED, "unknown pool format %d", kv->kv_dtype);
   if (batch > 0) {
     if (!kv->k || !kv->v) return fail(HA_ERR_NULL, "pool K or V pointer is NULL");
+    if (kv->kv_dtype == HA_KV_INT8 && (!kv->k_scale || !kv->v_scale))
+      return fail(HA_ERR_NULL, "an INT8 pool needs k_scale and v_scale");
     if (!kv->table) return fail(HA_ERR_NULL, "%s is NULL", kv->kind == HA_SWA ? "ring id table" : "page table");
     if (kv->kind == HA_FULL && kv->table_stride <= 0)
       return fail(HA_ERR_RANGE, "page table stride must be positive (got %d)", kv->table_stride);
@@ -111,6 +115,9 @@ ha_status append_common(const ha_shape* shape, const ha_kv_view* view, int32_t w
   a.k_new = k_new;
   a.v_new = v_new;
   a.src_f32 = src_dtype == HA_F32;
+  a.kv8 = view->kv_dtype == HA_KV_INT8;
+  a.k_scale = view->k_scale;
+  a.v_scale = view->v_scale;
   return hip_status(ha::launch_append(a, static_cast<hipStream_t>(stream)), "append launch");
 }
 
@@ -217,6 +224,7 @@ ha_status hybrid_attn_prefill(const ha_shape* shape, const ha_kv_view* kv, const
   if (batch < 0 || num_tokens < 0 || max_new < 0)
     return fail(HA_ERR_RANGE, "batch, num_tokens and max_new must be >= 0");
   if ((st = check_view(kv, batch)) != HA_OK) return st;
+  if (kv->kv_dtype != HA_KV_BF16) return fail(HA_ERR_UNSUPPORTED, "prefill reads bf16 pools only");
   if ((st = check_dtype(in_dtype)) != HA_OK) return st;
   if (batch == 0 || num_tokens == 0 || max_new == 0) return ok();
   if (max_new > num_tokens) return fail(HA_ERR_RANGE, "max_new %d exceeds num_tokens %d", max_new, num_tokens);
@@ -266,6 +274,9 @@ ha_status hybrid_attn_decode(const ha_shape* shape, const ha_kv_view* kv, const 
   if (!kv_len || !q || !out || !lse) return fail(HA_ERR_NULL, "kv_len, q, out or lse is NULL");
   if ((k_new == nullptr) != (v_new == nullptr))
     return fail(HA_ERR_NULL, "k_new and v_new must both be given (fused append) or both be NULL");
+  const bool kv8 = kv->kv_dtype == HA_KV_INT8;
+  if (kv8 && k_new)
+    return fail(HA_ERR_UNSUPPORTED, "decode over an INT8 pool takes no fused append (append the token first)");
   const bool full = kv->kind == HA_FULL;
   const size_t need = decode_workspace(geo, full, batch, max_kv_len, num_splits);
   if (need > 0 && (!workspace || workspace_bytes < need))
@@ -286,6 +297,9 @@ ha_status hybrid_attn_decode(const ha_shape* shape, const ha_kv_view* kv, const 
   a.v_new = v_new;
   a.k_pool_w = static_cast<uint16_t*>(kv->k);
   a.v_pool_w = static_cast<uint16_t*>(kv->v);
+  a.kv8 = kv8;
+  a.k_scale = kv->k_scale;
+  a.v_scale = kv->v_scale;
   a.out = out;
   a.lse = lse;
   a.split_blocks = ha::decode_split_blocks(full, geo.window, max_kv_len, batch, geo.hkv, num_splits);
@@ -310,6 +324,7 @@ ha_status hybrid_attn_verify(const ha_shape* shape, const ha_kv_view* kv, const 
     return fail(HA_ERR_RANGE, "batch, max_kv_len and num_splits must be >= 0");
   if ((st = check_nq(geo, nq)) != HA_OK) return st;
   if ((st = check_view(kv, batch)) != HA_OK) return st;
+  if (kv->kv_dtype != HA_KV_BF16) return fail(HA_ERR_UNSUPPORTED, "verify reads bf16 pools only");
   if ((st = check_dtype(in_dtype)) != HA_OK) return st;
   if (batch == 0) return ok();
   if (batch > 65535) return fail(HA_ERR_RANGE, "verify batch %d exceeds 65535", batch);

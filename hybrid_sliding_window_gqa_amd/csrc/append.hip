@@ -12,7 +12,9 @@
 // (common.hpp): the K channels form one 16-byte unit (one store), the V
 // channels land in 8 different units (8 two-byte stores).
 // Appends are a few KiB per decode step and a few hundred MiB per prefill
-// chunk, far below the attention traffic, so they favour simplicity.
+// chunk, far below the attention traffic, so they favour simplicity. INT8
+// pools (include/hybrid_attn.h) are written by append8_kernel, which
+// quantizes each (token, kv head) row with its own scale.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -77,16 +79,115 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
 }
 
+// INT8 pools: the same thread mapping; the chunks/lanes of one (token, kv
+// head) row are consecutive lanes of a wave, so the row's absmax is a
+// butterfly over them. scale = amax / 127 and code = rint(x / scale), both
+// in IEEE float32 (x = the bf16 value), so the codes are exactly those of
+// the definition; lane 0 of the row writes the two scales.
+template <bool kF32>
+__global__ __launch_bounds__(256) void append8_kernel(AppendArgs a) {
+  const int d = a.geo.d;
+  const int hkv = a.geo.hkv;
+  const int chunks = d >> 3;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(a.num_tokens) * hkv * chunks;
+  if (gid >= total) return;   // whole rows: total and the block size are multiples of chunks
+  const int c = static_cast<int>(gid % chunks);
+  const int64_t rest = gid / chunks;
+  const int g = static_cast<int>(rest % hkv);
+  const int tok = static_cast<int>(rest / hkv);
+
+  int lo = 0, hi = a.batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.cu_new[mid] <= tok) lo = mid; else hi = mid - 1;
+  }
+  const int b = lo;
+  const int i = tok - a.cu_new[b];
+  const int n = a.cu_new[b + 1] - a.cu_new[b];
+  if (i < 0 || i >= n) return;
+  const int64_t p = static_cast<int64_t>(a.pos0[b]) + i;
+  if (p < 0) return;
+
+  int64_t block_base;  // byte offset of the token's 16-token block for head g
+  int in_blk;
+  if (!a.full) {
+    const int w = a.geo.window;
+    if (i < n - w) return;
+    const int r = a.table[b];
+    if (r < 0 || r >= a.num_blocks) return;
+    const int s = static_cast<int>(p % w);
+    block_base = ((static_cast<int64_t>(r) * hkv + g) * w + (s & ~(kBlock - 1))) * d;
+    in_blk = s & (kBlock - 1);
+  } else {
+    const int64_t lp = p >> 4;
+    if (lp >= a.table_stride) return;
+    const int pg = a.table[static_cast<int64_t>(b) * a.table_stride + lp];
+    if (pg < 0 || pg >= a.num_blocks) return;
+    block_base = (static_cast<int64_t>(pg) * hkv + g) * kBlock * d;
+    in_blk = static_cast<int>(p & (kBlock - 1));
+  }
+  // Every early return above is uniform over the lanes of one row, so the
+  // whole row takes part in the butterflies below.
+
+  const int64_t src = (static_cast<int64_t>(tok) * hkv + g) * d + c * 8;
+  const u32x4 kraw = load8_as_bf16<kF32>(a.k_new, src);
+  const u32x4 vraw = load8_as_bf16<kF32>(a.v_new, src);
+  float kx[8], vx[8];
+  const uint32_t kw[4] = {kraw.x, kraw.y, kraw.z, kraw.w};
+  const uint32_t vw[4] = {vraw.x, vraw.y, vraw.z, vraw.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    kx[2 * j] = __uint_as_float(kw[j] << 16);
+    kx[2 * j + 1] = __uint_as_float(kw[j] & 0xffff0000u);
+    vx[2 * j] = __uint_as_float(vw[j] << 16);
+    vx[2 * j + 1] = __uint_as_float(vw[j] & 0xffff0000u);
+  }
+  float ka = 0.0f, va = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    ka = fmaxf(ka, fabsf(kx[j]));
+    va = fmaxf(va, fabsf(vx[j]));
+  }
+  for (int m = chunks >> 1; m >= 1; m >>= 1) {
+    ka = fmaxf(ka, __shfl_xor(ka, m));
+    va = fmaxf(va, __shfl_xor(va, m));
+  }
+  const float ks = ka / 127.0f;
+  const float vs = va / 127.0f;
+  uint32_t kq[2] = {0u, 0u};
+  uint8_t* vblk = reinterpret_cast<uint8_t*>(a.v_pool) + block_base;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int kc = ks > 0.0f ? static_cast<int>(fminf(fmaxf(rintf(kx[j] / ks), -127.0f), 127.0f)) : 0;
+    const int vc = vs > 0.0f ? static_cast<int>(fminf(fmaxf(rintf(vx[j] / vs), -127.0f), 127.0f)) : 0;
+    kq[j >> 2] |= (static_cast<uint32_t>(kc) & 0xffu) << (8 * (j & 3));
+    vblk[v8_elem(in_blk, c * 8 + j)] = static_cast<uint8_t>(vc & 0xff);
+  }
+  *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(a.k_pool) + block_base + k8_elem(in_blk, c * 8)) =
+      u32x2{kq[0], kq[1]};
+  if (c == 0) {
+    const int64_t si = block_base / d + in_blk;
+    a.k_scale[si] = ks;
+    a.v_scale[si] = vs;
+  }
+}
+
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
   const int64_t total = static_cast<int64_t>(a.num_tokens) * a.geo.hkv * (a.geo.d >> 3);
   if (total == 0 || a.batch == 0) return hipSuccess;
   const int threads = 256;
   const int64_t blocks = (total + threads - 1) / threads;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  if (a.src_f32)
-    hipLaunchKernelGGL(append_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(append_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, stream, a);
+  const dim3 grid(static_cast<unsigned>(blocks));
+  if (a.kv8) {
+    if (a.src_f32) hipLaunchKernelGGL(append8_kernel<true>, grid, dim3(threads), 0, stream, a);
+    else hipLaunchKernelGGL(append8_kernel<false>, grid, dim3(threads), 0, stream, a);
+  } else if (a.src_f32) {
+    hipLaunchKernelGGL(append_kernel<true>, grid, dim3(threads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(append_kernel<false>, grid, dim3(threads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

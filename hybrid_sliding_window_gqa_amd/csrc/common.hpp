@@ -41,6 +41,28 @@ __host__ __device__ constexpr int64_t k_elem(int token, int dim) {
 __host__ __device__ constexpr int64_t v_elem(int token, int dim) {
   return (static_cast<int64_t>(dim / 32) * 64 + (token / 4) * 16 + dim % 16) * 8 + ((dim % 32) / 16) * 4 + token % 4;
 }
+// INT8 pools: one byte per value, 16-byte units. A K unit holds a lane's
+// 8-channel chunks of two consecutive 32-channel slices (MFMA A operands m and
+// m+1); a V unit holds a lane's 4 tokens of four 16-channel dim tiles.
+__host__ __device__ constexpr int64_t k8_elem(int token, int dim) {
+  return (static_cast<int64_t>(dim / 64) * 64 + ((dim % 32) / 8) * 16 + token) * 16 + ((dim / 32) % 2) * 8 + dim % 8;
+}
+__host__ __device__ constexpr int64_t v8_elem(int token, int dim) {
+  return (static_cast<int64_t>(dim / 64) * 64 + (token / 4) * 16 + dim % 16) * 16 + ((dim / 16) % 4) * 4 + token % 4;
+}
+
+// Four signed 8-bit codes (one word) -> four bfloat16 values (two words, code
+// 0 in bits 0..15 of the first). |code| <= 127 fits bf16's 8-bit significand,
+// so dropping the low half of the float32 is exact.
+__device__ __forceinline__ u32x2 i8x4_to_bf16x4(uint32_t w) {
+  const float f0 = static_cast<float>(static_cast<int8_t>(w & 0xffu));
+  const float f1 = static_cast<float>(static_cast<int8_t>((w >> 8) & 0xffu));
+  const float f2 = static_cast<float>(static_cast<int8_t>((w >> 16) & 0xffu));
+  const float f3 = static_cast<float>(static_cast<int8_t>(w >> 24));
+  return u32x2{__builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u),
+               __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u)};
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

@@ -25,6 +25,11 @@
 //     per lane = two dim tiles, again 1 KiB contiguous per instruction) and
 //     accumulates O^T += V^T P^T, where P^T is the softmax tile in exactly the
 //     accumulator layout.
+// INT8 pools (include/hybrid_attn.h) take half the bytes per block: the
+// raw codes and the block's scales are what the ping-pong buffers hold, and
+// a block is widened to the same bf16 operands right before it is consumed
+// (codes are exact in bf16), the K scale multiplying the scores and the V
+// scale folded into the probabilities.
 // Page ids are scalar loads issued two blocks ahead of their use. The waves
 // merge through LDS; a workgroup writes either the final row (one split) or a
 // partial (o, lse) for the reduce kernel.
@@ -118,6 +123,123 @@ __device__ __forceinline__ void consume_block(BlockOps<D>& ops, const u32x4* qop
   for (int d = 0; d < DT; ++d) o[d] = mfma_16x16x16(ops.v[d], pb, o[d]);
 }
 
+// INT8 pools: the raw 16-byte units of one block (K: D/64 units holding two
+// 32-channel slices each; V: D/64 units holding four 16-channel tiles each)
+// and the 4 K and 4 V scales of this lane's keys 4*q4 .. 4*q4+3.
+template <int D>
+struct RawBlock8 {
+  u32x4 k[D / 64];
+  u32x4 v[D / 64];
+  f32x4 ks;
+  f32x4 vs;
+};
+
+template <int D>
+__device__ __forceinline__ void load_block8(RawBlock8<D>& raw, const DecodeArgs& a, int64_t base, int q4, int c16) {
+  const bool ok = base >= 0;
+  const int64_t b0 = ok ? base : 0;
+  const uint32_t bytes = ok ? kBlock * D : 0;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const uint8_t*>(a.k_pool) + b0, bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const uint8_t*>(a.v_pool) + b0, bytes);
+  const int lane = 16 * q4 + c16;
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) {
+    raw.k[j] = buf_load16(rk, 16 * (64 * j + lane));
+    raw.v[j] = buf_load16(rv, 16 * (64 * j + lane));
+  }
+  const uint32_t sbytes = ok ? kBlock * 4 : 0;
+  const __amdgpu_buffer_rsrc_t rks = make_rsrc(a.k_scale + b0 / D, sbytes);
+  const __amdgpu_buffer_rsrc_t rvs = make_rsrc(a.v_scale + b0 / D, sbytes);
+  raw.ks = __builtin_bit_cast(f32x4, buf_load16(rks, 16 * q4));
+  raw.vs = __builtin_bit_cast(f32x4, buf_load16(rvs, 16 * q4));
+}
+
+// Codes -> the same bf16 operands the bf16 path loads.
+template <int D>
+__device__ __forceinline__ void widen_block8(const RawBlock8<D>& raw, BlockOps<D>& ops) {
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) {
+    const u32x2 k0 = i8x4_to_bf16x4(raw.k[j].x), k1 = i8x4_to_bf16x4(raw.k[j].y);
+    const u32x2 k2 = i8x4_to_bf16x4(raw.k[j].z), k3 = i8x4_to_bf16x4(raw.k[j].w);
+    ops.k[2 * j] = u32x4{k0.x, k0.y, k1.x, k1.y};
+    ops.k[2 * j + 1] = u32x4{k2.x, k2.y, k3.x, k3.y};
+    ops.v[4 * j] = i8x4_to_bf16x4(raw.v[j].x);
+    ops.v[4 * j + 1] = i8x4_to_bf16x4(raw.v[j].y);
+    ops.v[4 * j + 2] = i8x4_to_bf16x4(raw.v[j].z);
+    ops.v[4 * j + 3] = i8x4_to_bf16x4(raw.v[j].w);
+  }
+}
+
+// consume_block for INT8 pools: score = k_scale * (q . code), and the V scale
+// of each key multiplies its probability before the bf16 cast (P'V = P
+// (scale * code)); l keeps the unscaled probabilities. Masked keys get a zero
+// V scale so an unwritten slot's scale cannot reach O.
+template <int D>
+__device__ __forceinline__ void consume_block8(const RawBlock8<D>& raw, const u32x4* qop, int first_key, int t,
+                                               bool partial, float sl2, float& m_run, float& l_run, f32x4* o,
+                                               int q4) {
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  BlockOps<D> ops;
+  widen_block8<D>(raw, ops);
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < KS; ++m) s = mfma_16x16x32(ops.k[m], qop[m], s);
+  float vs[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    s[r] *= raw.ks[r];
+    vs[r] = raw.vs[r];
+  }
+  if (partial) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool ok = first_key + 4 * q4 + r <= t;
+      s[r] = ok ? s[r] : -INFINITY;
+      vs[r] = ok ? vs[r] : 0.0f;
+    }
+  }
+  const float tmax = group4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))) * sl2;
+  const float m_new = fmaxf(m_run, tmax);
+  const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+  const float alpha = fast_exp2(m_run - m_use);
+  float p[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s[r] * sl2 - m_use);
+  l_run = l_run * alpha + (p[0] + p[1]) + (p[2] + p[3]);
+  m_run = m_new;
+#pragma unroll
+  for (int d = 0; d < DT; ++d) o[d] *= alpha;
+  const u32x2 pb = {pack_bf16x2(p[0] * vs[0], p[1] * vs[1]), pack_bf16x2(p[2] * vs[2], p[3] * vs[3])};
+#pragma unroll
+  for (int d = 0; d < DT; ++d) o[d] = mfma_16x16x16(ops.v[d], pb, o[d]);
+}
+
+// One block's operands in the pool's format.
+template <int D, bool kKv8>
+struct BlockBuf;
+template <int D>
+struct BlockBuf<D, false> {
+  BlockOps<D> ops;
+};
+template <int D>
+struct BlockBuf<D, true> {
+  RawBlock8<D> raw;
+};
+
+template <int D, bool kKv8>
+__device__ __forceinline__ void load_buf(BlockBuf<D, kKv8>& b, const DecodeArgs& a, int64_t base, int q4, int c16) {
+  if constexpr (kKv8) load_block8<D>(b.raw, a, base, q4, c16);
+  else load_block<D>(b.ops, a.k_pool, a.v_pool, base, q4, c16);
+}
+
+template <int D, bool kKv8>
+__device__ __forceinline__ void consume_buf(BlockBuf<D, kKv8>& b, const u32x4* qop, int first_key, int t,
+                                            bool partial, float sl2, float& m_run, float& l_run, f32x4* o, int q4) {
+  if constexpr (kKv8) consume_block8<D>(b.raw, qop, first_key, t, partial, sl2, m_run, l_run, o, q4);
+  else consume_block<D>(b.ops, qop, first_key, t, partial, sl2, m_run, l_run, o, q4);
+}
+
 // Replace 16-bit element r (0..3) of a u32x2 holding four bf16 values.
 __device__ __forceinline__ void set_bf16(u32x2& w, int r, uint32_t bits) {
   const uint32_t shift = (r & 1) * 16;
@@ -143,7 +265,7 @@ struct NewToken {
 
 }  // namespace
 
-template <int D, bool kFull, bool kQF32>
+template <int D, bool kFull, bool kQF32, bool kKv8>
 __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void decode_kernel(DecodeArgs a) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
@@ -230,7 +352,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
 
   // Fused append: block of position t, its row in the block, and whether
   // this wave consumes that block.
-  const bool fuse = a.k_new != nullptr;
+  const bool fuse = !kKv8 && a.k_new != nullptr;
   const int new_blk = kFull ? (t >> 4) : ((t % W) >> 4);
   const int new_row = t & (kBlock - 1);
   const bool new_mine = fuse && new_blk >= first && new_blk < last && (new_blk - first) % kWaves == wave;
@@ -245,7 +367,10 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
       nt.v[2 * p + 1] = load_bf16_bits<kQF32>(a.v_new, src + 32 * p + 16 + c16);
     }
   }
-  auto patch_new = [&](BlockOps<D>& ops, int i) {
+  auto patch_new = [&](BlockBuf<D, kKv8>& buf, int i) {
+    if constexpr (kKv8) return;
+    else {
+    BlockOps<D>& ops = buf.ops;
     if (!new_mine || i != new_blk) return;
     if (c16 == new_row) {
 #pragma unroll
@@ -254,6 +379,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
     if (q4 == (new_row >> 2)) {
 #pragma unroll
       for (int d = 0; d < DT; ++d) set_bf16(ops.v[d], new_row & 3, nt.v[d]);
+    }
     }
   };
 
@@ -269,19 +395,19 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
     // wave has at most one block; a larger ring is walked a block at a
     // time. A single operand buffer keeps the kernel at 128 VGPRs, so two
     // 8-wave workgroups fit on a CU and the whole grid runs in one round.
-    BlockOps<D> A;
+    BlockBuf<D, kKv8> A;
     if (last - first <= kWaves) {
       const int i = first + wave;
       if (i < last) {
-        load_block<D>(A, a.k_pool, a.v_pool, base_of(i, 0), q4, c16);
+        load_buf<D, kKv8>(A, a, base_of(i, 0), q4, c16);
         patch_new(A, i);
-        consume_block<D>(A, qop, kBlock * i, t, is_partial(i), sl2, m_run, l_run, o, q4);
+        consume_buf<D, kKv8>(A, qop, kBlock * i, t, is_partial(i), sl2, m_run, l_run, o, q4);
       }
     } else {
       for (int i = first + wave; i < last; i += kWaves) {
-        load_block<D>(A, a.k_pool, a.v_pool, base_of(i, 0), q4, c16);
+        load_buf<D, kKv8>(A, a, base_of(i, 0), q4, c16);
         patch_new(A, i);
-        consume_block<D>(A, qop, kBlock * i, t, is_partial(i), sl2, m_run, l_run, o, q4);
+        consume_buf<D, kKv8>(A, qop, kBlock * i, t, is_partial(i), sl2, m_run, l_run, o, q4);
       }
     }
   } else {
@@ -293,9 +419,9 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
     int pg_a = page_of(ia), pg_b = page_of(ib);
     int64_t base_a = base_of(ia, pg_a);
     int64_t base_b = base_of(ib, pg_b);
-    BlockOps<D> A, B;
-    load_block<D>(A, a.k_pool, a.v_pool, base_a, q4, c16);
-    load_block<D>(B, a.k_pool, a.v_pool, base_b, q4, c16);
+    BlockBuf<D, kKv8> A, B;
+    load_buf<D, kKv8>(A, a, base_a, q4, c16);
+    load_buf<D, kKv8>(B, a, base_b, q4, c16);
     int pg_a2 = page_of(ia + 2 * kStep), pg_b2 = page_of(ib + 2 * kStep);
     // Pairs (A, B) in a loop with a fixed trip count and no early exit, so the
     // loads in flight at the loop head are the same on every path; an odd last
@@ -303,21 +429,21 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
     const int nmine = (last > ia) ? (last - ia + kStep - 1) / kStep : 0;
     for (int k = 0; k + 1 < nmine; k += 2) {
       patch_new(A, ia);
-      if (base_a >= 0) consume_block<D>(A, qop, kBlock * ia, t, is_partial(ia), sl2, m_run, l_run, o, q4);
+      if (base_a >= 0) consume_buf<D, kKv8>(A, qop, kBlock * ia, t, is_partial(ia), sl2, m_run, l_run, o, q4);
       ia += 2 * kStep;
       base_a = base_of(ia, pg_a2);
-      load_block<D>(A, a.k_pool, a.v_pool, base_a, q4, c16);
+      load_buf<D, kKv8>(A, a, base_a, q4, c16);
       pg_a2 = page_of(ia + 2 * kStep);
       patch_new(B, ib);
-      if (base_b >= 0) consume_block<D>(B, qop, kBlock * ib, t, is_partial(ib), sl2, m_run, l_run, o, q4);
+      if (base_b >= 0) consume_buf<D, kKv8>(B, qop, kBlock * ib, t, is_partial(ib), sl2, m_run, l_run, o, q4);
       ib += 2 * kStep;
       base_b = base_of(ib, pg_b2);
-      load_block<D>(B, a.k_pool, a.v_pool, base_b, q4, c16);
+      load_buf<D, kKv8>(B, a, base_b, q4, c16);
       pg_b2 = page_of(ib + 2 * kStep);
     }
     if (nmine & 1) {
       patch_new(A, ia);
-      if (base_a >= 0) consume_block<D>(A, qop, kBlock * ia, t, is_partial(ia), sl2, m_run, l_run, o, q4);
+      if (base_a >= 0) consume_buf<D, kKv8>(A, qop, kBlock * ia, t, is_partial(ia), sl2, m_run, l_run, o, q4);
     }
   }
 
@@ -458,12 +584,24 @@ static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.full ? a.splits : 1, a.geo.hkv, a.batch);
   if (a.full) {
     const dim3 block(64 * waves_per_wg<true>());
-    if (a.q_f32) hipLaunchKernelGGL((decode_kernel<D, true, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((decode_kernel<D, true, false>), grid, block, 0, stream, a);
+    if (a.kv8) {
+      if (a.q_f32) hipLaunchKernelGGL((decode_kernel<D, true, true, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((decode_kernel<D, true, false, true>), grid, block, 0, stream, a);
+    } else if (a.q_f32) {
+      hipLaunchKernelGGL((decode_kernel<D, true, true, false>), grid, block, 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((decode_kernel<D, true, false, false>), grid, block, 0, stream, a);
+    }
   } else {
     const dim3 block(64 * waves_per_wg<false>());
-    if (a.q_f32) hipLaunchKernelGGL((decode_kernel<D, false, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((decode_kernel<D, false, false>), grid, block, 0, stream, a);
+    if (a.kv8) {
+      if (a.q_f32) hipLaunchKernelGGL((decode_kernel<D, false, true, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((decode_kernel<D, false, false, true>), grid, block, 0, stream, a);
+    } else if (a.q_f32) {
+      hipLaunchKernelGGL((decode_kernel<D, false, true, false>), grid, block, 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((decode_kernel<D, false, false, false>), grid, block, 0, stream, a);
+    }
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

@@ -28,6 +28,9 @@ struct AppendArgs {
   const void* k_new;
   const void* v_new;
   bool src_f32;
+  bool kv8;               // INT8 pools: codes in k_pool/v_pool (bytes), scales below
+  float* k_scale;
+  float* v_scale;
 };
 
 struct DecodeArgs {
@@ -52,6 +55,9 @@ struct DecodeArgs {
   const void* v_new;      // [batch][hkv][d]
   uint16_t* k_pool_w;     // writable pool views for the fused append
   uint16_t* v_pool_w;
+  bool kv8;               // INT8 pools (no fused append): codes + per-token scales
+  const float* k_scale;
+  const float* v_scale;
 };
 
 struct PrefillArgs {

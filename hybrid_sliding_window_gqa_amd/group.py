@@ -54,8 +54,9 @@ class HybridGroup:
     """Pools and index tables of one layer group for a fixed batch."""
 
     def __init__(self, shape: HeadShape, ring_id: torch.Tensor, num_rings: int, page_table: torch.Tensor,
-                 num_pages: int, kinds=GROUP_KINDS, fill: float | None = None):
+                 num_pages: int, kinds=GROUP_KINDS, fill: float | None = None, kv_dtype: str = "bf16"):
         self.shape = shape
+        self.kv_dtype = kv_dtype
         self.kinds = tuple(kinds)
         self.device = ring_id.device
         self.ring_id = ring_id
@@ -63,10 +64,10 @@ class HybridGroup:
         self.layers = []
         for kind in self.kinds:
             if kind == SWA:
-                pool = SwaRingPool(shape, num_rings, self.device, fill)
+                pool = SwaRingPool(shape, num_rings, self.device, fill, kv_dtype)
                 view = pool.view(ring_id)
             elif kind == FULL:
-                pool = FullPagePool(shape, num_pages, self.device, fill)
+                pool = FullPagePool(shape, num_pages, self.device, fill, kv_dtype)
                 view = pool.view(page_table)
             else:
                 raise ValueError(f"unknown layer kind {kind!r}")
@@ -79,7 +80,7 @@ class HybridGroup:
     def pool_bytes(self) -> dict:
         out = {SWA: 0, FULL: 0}
         for layer in self.layers:
-            out[layer.kind] += layer.pool.k.numel() * 2 + layer.pool.v.numel() * 2
+            out[layer.kind] += layer.pool.nbytes
         return out
 
 
@@ -144,6 +145,8 @@ def plan_decode(group: HybridGroup, q, k_new, v_new, pos, kv_len, max_kv_len: in
     _check(pos, "pos", (b,), torch.int32, dev)
     _check(kv_len, "kv_len", (b,), torch.int32, dev)
     cu_one = torch.arange(b + 1, dtype=torch.int32, device=dev)
+    if fuse_append and group.kv_dtype != "bf16":
+        raise ValueError("decode over int8 pools appends the token in a call of its own (fuse_append=False)")
     calls, labels = [], []
     for li, layer in enumerate(group.layers):
         _check(q[li], "q", (b, hq, d), None, dev)

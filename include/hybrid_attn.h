@@ -61,7 +61,22 @@
  *   i.e. K(t, ch) is value ((ch/32)*64 + ((ch%32)/8)*16 + t)*8 + ch%8 and
  *   V(t, ch) is value ((ch/32)*64 + (t/4)*16 + ch%16)*8 + ((ch%32)/16)*4 + t%4.
  *   A wavefront then loads each operand set with fully contiguous 1 KiB reads.
- */
+ *
+ * INT8 pools (kv_dtype = HA_KV_INT8; next to the bf16 format, for decode,
+ * which is bound by the KV bytes it reads -- [HD12] "KV Cache 量化策略的技术
+ * 选型" names low-bit KV storage). Same blocks, one signed byte per value,
+ * 16*D bytes per (block, kv head), plus one float32 scale per (block, kv
+ * head, token) for K and for V:
+ *   code(t, ch) = clamp(rint(x / s), -127, 127), s = max_ch |x| / 127 over
+ *   the token's D channels of that kv head (float32 arithmetic; s = 0 for an
+ *   all-zero row), value = code * s; x is the bf16 value.
+ *   K(t, ch) is byte ((ch/64)*64 + ((ch%32)/8)*16 + t)*16 + ((ch/32)%2)*8 + ch%8,
+ *   V(t, ch) is byte ((ch/64)*64 + (t/4)*16 + ch%16)*16 + ((ch/16)%4)*4 + t%4,
+ *   so a lane's K chunks of two 32-channel slices and its V values of four
+ *   16-channel tiles are each one 16-byte load.
+ *   Scales: k_scale / v_scale float32 [num_blocks][Hkv][16] for pages and
+ *   [rings][Hkv][W/16][16] for rings, i.e. the scale of the value at element
+ *   offset e of the codes is at e / (16*D) * 16 + token. */
 #ifndef HYBRID_ATTN_H
 #define HYBRID_ATTN_H
 
@@ -72,7 +87,7 @@
 extern "C" {
 #endif
 
-#define HA_ABI_VERSION 4
+#define HA_ABI_VERSION 5
 
 typedef enum ha_status {
   HA_OK = 0,
@@ -87,6 +102,9 @@ typedef enum ha_status {
 typedef enum ha_dtype { HA_BF16 = 0, HA_F32 = 1 } ha_dtype;
 
 typedef enum ha_layer_kind { HA_SWA = 0, HA_FULL = 1 } ha_layer_kind;
+
+/* Element format of a pool. */
+typedef enum ha_kv_dtype { HA_KV_BF16 = 0, HA_KV_INT8 = 1 } ha_kv_dtype;
 
 /* Head geometry shared by every call of one layer stack, so the window used by
  * the kernels and by window_safe_match cannot drift apart ([HD12] notes that
@@ -108,7 +126,11 @@ typedef struct ha_shape {
  *            num_blocks = rings in the pool; table_stride ignored.
  *   HA_FULL: table = page table, int32 [batch][table_stride] (device);
  *            num_blocks = pages in the pool. The page table is the
- *            authoritative logical->physical index of the sequence ([YLY]). */
+ *            authoritative logical->physical index of the sequence ([YLY]).
+ * kv_dtype selects bf16 pools (HA_KV_BF16, scales unused) or INT8 pools
+ * (HA_KV_INT8: k_scale / v_scale required, layout above). INT8 pools are
+ * written by the two append calls and read by hybrid_attn_decode without a
+ * fused append; prefill and verify reject them (HA_ERR_UNSUPPORTED). */
 typedef struct ha_kv_view {
   int32_t kind;
   void* k;
@@ -116,6 +138,9 @@ typedef struct ha_kv_view {
   int32_t num_blocks;
   const int32_t* table;
   int32_t table_stride;
+  int32_t kv_dtype;
+  float* k_scale;
+  float* v_scale;
 } ha_kv_view;
 
 /* ---- a1: SWA ring append ([YLY] KVCache系统重构; [HD12] 双池分治) ----------

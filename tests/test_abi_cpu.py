@@ -187,3 +187,24 @@ def test_verify_errors_and_workspace(lib):
     assert lib.hybrid_attn_verify_workspace_size(ctypes.byref(s), _lib.HA_SWA, 64, 8196, 4, 0) == 0
     assert lib.hybrid_attn_verify_workspace_size(ctypes.byref(s), _lib.HA_FULL, 64, 8196, 5, 0) == 0   # invalid nq
     assert verify_call(lib, s, ring, batch=0) == _lib.HA_OK
+
+
+def test_int8_view_errors(lib):
+    s = good_shape()
+    int8 = lambda kind, ks=FAKE, vs=FAKE: HaKvView(kind, FAKE, FAKE, 8, FAKE, 4, _lib.HA_KV_INT8, ks, vs)
+    pages, ring = int8(_lib.HA_FULL), int8(_lib.HA_SWA)
+    # scales are required, and the format must be known
+    for bad, status in ((int8(_lib.HA_FULL, ks=None), _lib.HA_ERR_NULL),
+                        (int8(_lib.HA_FULL, vs=None), _lib.HA_ERR_NULL),
+                        (HaKvView(_lib.HA_FULL, FAKE, FAKE, 8, FAKE, 4, 7, FAKE, FAKE), _lib.HA_ERR_UNSUPPORTED)):
+        assert decode_call(lib, s, bad) == status
+        assert lib.full_pool_append(ctypes.byref(s), ctypes.byref(bad), FAKE, FAKE, 2, 10, FAKE, FAKE, 0,
+                                    None) == status
+    # decode over int8 takes no fused append; prefill and verify read bf16 pools only
+    assert decode_call(lib, s, pages, k_new=FAKE, v_new=FAKE) == _lib.HA_ERR_UNSUPPORTED
+    args = [FAKE, FAKE, 2, 10, 5, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, 1 << 30, None]
+    assert lib.hybrid_attn_prefill(ctypes.byref(s), ctypes.byref(ring), *args) == _lib.HA_ERR_UNSUPPORTED
+    assert lib.hybrid_attn_verify(ctypes.byref(s), ctypes.byref(pages), FAKE, 2, 100, 4, FAKE, FAKE, FAKE, 0,
+                                  FAKE, FAKE, 0, FAKE, 1 << 30, None) == _lib.HA_ERR_UNSUPPORTED
+    # the zero-initialised tail of a view is a bf16 pool
+    assert HaKvView(_lib.HA_FULL, FAKE, FAKE, 8, FAKE, 4).kv_dtype == _lib.HA_KV_BF16
