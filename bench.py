@@ -50,13 +50,15 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--restore-groups", type=int, default=4,
                    help="groups in the stack the restore workload pipelines (its pools are per group)")
-    p.add_argument("--workload", choices=["decode", "reuse", "ragged", "chunked", "copy", "verify", "restore"],
+    p.add_argument("--workload", choices=["decode", "reuse", "ragged", "chunked", "copy", "verify", "restore",
+                                          "decode_int8"],
                    default="decode",
                    help="copy: 2 GiB elementwise copy, the known-size kernel that scales HBM counters")
     p.add_argument("--prefill-passes", type=int, default=3)
     p.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill part")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-verify", action="store_true", help="skip the multi-token verify part")
+    p.add_argument("--no-int8", action="store_true", help="skip the INT8-pool decode part")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU sample")
     p.add_argument("--cpu-prefill-seconds", type=float, default=10.0,
                    help="target oracle time for the prefill CPU sample")
@@ -163,7 +165,7 @@ def timed_events(torch, n):
     return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
 
 
-def build_decode(torch, ha, grp, synth, struct, device, workload, fuse=True):
+def build_decode(torch, ha, grp, synth, struct, device, workload, fuse=True, kv_dtype="bf16"):
     """Pools filled with each sequence's history; per-layer new-token tensors."""
     shape = ha.HeadShape(struct.shape.num_q_heads, struct.shape.num_kv_heads, struct.shape.head_dim,
                          struct.shape.window)
@@ -171,7 +173,7 @@ def build_decode(torch, ha, grp, synth, struct, device, workload, fuse=True):
     hist = struct.hist.astype(np.int64)
     ring_id = torch.as_tensor(struct.ring_id, device=device)
     table = torch.as_tensor(struct.page_table, device=device)
-    group = grp.HybridGroup(shape, ring_id, struct.num_rings, table, struct.num_pages)
+    group = grp.HybridGroup(shape, ring_id, struct.num_rings, table, struct.num_pages, kv_dtype=kv_dtype)
     hkv, hq, d, w = shape.num_kv_heads, shape.num_q_heads, shape.head_dim, shape.window
     logical = []   # per layer: (k_hist, v_hist, first_position) host-side recipe for the oracle
     q_l, k_l, v_l, out_l, lse_l = [], [], [], [], []
@@ -275,6 +277,81 @@ def run_decode(torch, ha, grp, synth, struct, args, device):
         "splits_full": ha.hybrid_attn_decode_splits(shape, ha.HA_FULL, struct.batch, int(kv_len.max())),
     }
     return shape, group, data, dt, step_bytes, full_bytes, info
+
+
+def kv8_bytes_per_token(shape):
+    """INT8 pools: codes of K and V plus one float32 scale each, per kv head."""
+    return shape.num_kv_heads * (shape.head_dim * 2 + 8)
+
+
+def run_decode_int8(torch, ha, grp, synth, args, device):
+    """The decode workload on INT8 pools: per layer an append call (quantizes
+    the new token) and a decode call, graph replay; and the full-layer decode
+    call alone."""
+    struct = synth.decode_structure()
+    shape, group, plan, data = build_decode(torch, ha, grp, synth, struct, device, struct.workload, fuse=False,
+                                            kv_dtype="int8")
+    b = struct.batch
+    kv_len = data["hist"] + 1
+    hq, d = shape.num_q_heads, shape.head_dim
+    qol = b * hq * (d * 2 + d * 4 + 4)                       # Q read, O and LSE written
+    append = b * (shape.num_kv_heads * shape.head_dim * 2 * 2 + kv8_bytes_per_token(shape))
+    per_layer = [int(visible_keys(kv_len - 1, layer.kind, shape.window).sum()) * kv8_bytes_per_token(shape) + qol
+                 for layer in group.layers]
+    step_bytes = sum(per_layer) + append * len(group.layers)
+    stream = torch.cuda.current_stream()
+    plan.run()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        plan.run()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    evs = timed_events(torch, len(plan.calls))
+    sums = np.zeros(len(plan.calls))
+    reps = max(5, min(args.steps, 20))
+    for _ in range(reps):
+        plan.run_timed(evs, stream)
+        torch.cuda.synchronize()
+        sums += np.array([a.elapsed_time(c) for a, c in evs])
+    call_ms = sums / reps
+    lab = plan.labels
+    full_ms = float(np.mean([call_ms[i] for i, x in enumerate(lab) if x.startswith("decode") and "full" in x]))
+    swa_ms = float(np.mean([call_ms[i] for i, x in enumerate(lab) if x.startswith("decode") and "swa" in x]))
+    app_ms = float(np.mean([call_ms[i] for i, x in enumerate(lab) if x.startswith("append")]))
+    full_layer = [i for i, layer in enumerate(group.layers) if layer.kind == "full"][0]
+    full_bytes = per_layer[full_layer]
+    value = step_bytes / dt / 1e9
+    log(f"[bench] int8 decode step {dt * 1e3:.3f} ms, {value:.1f} GB/s, {b / dt:.0f} tokens/s; full call "
+        f"{full_ms * 1e3:.1f} us ({full_bytes / full_ms / 1e6:.0f} GB/s), swa call {swa_ms * 1e3:.1f} us, "
+        f"append {app_ms * 1e3:.1f} us")
+    return {
+        "metric": "decode attn HBM GB/s (% peak) on INT8 KV pools, SWA:full 6:1",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "ms_per_step": round(dt * 1e3, 4),
+        "tokens_per_s": round(b / dt, 1),
+        "pct_peak_hbm": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "step_bytes": step_bytes,
+        "workload": (f"decode: {b} sequences x {int(kv_len[0]) - 1} cached tokens on INT8 pools (per-token "
+                     f"scales), one 6:1 group, per layer an append call then a decode call"),
+        "full_call_us": round(full_ms * 1e3, 2),
+        "full_call_gbs": round(full_bytes / full_ms / 1e6, 2),
+        "full_call_frac": round(full_bytes / full_ms / 1e6 / HBM_PEAK_GBS, 4),
+        "full_call_bytes": full_bytes,
+        "swa_call_us": round(swa_ms * 1e3, 2),
+        "append_call_us": round(app_ms * 1e3, 2),
+        "calls_ms": dict(zip(lab, call_ms.tolist())),
+    }
 
 
 def verify_layer_bytes(shape, kind, t0, nq):
@@ -810,6 +887,9 @@ def main():
     if args.workload == "restore":
         print(json.dumps(run_restore(torch, ha, grp, synth, args, device)))
         return 0
+    if args.workload == "decode_int8":
+        print(json.dumps(run_decode_int8(torch, ha, grp, synth, args, device)))
+        return 0
     struct = {"decode": synth.decode_structure, "ragged": synth.ragged_structure}[args.workload]()
     log(f"[bench] workload={args.workload} building inputs")
     shape, group, data, dt, step_bytes, full_bytes, info = run_decode(torch, ha, grp, synth, struct, args, device)
@@ -865,6 +945,12 @@ def main():
         line["verify"] = {k: v[k] for k in ("value", "unit", "ms_per_step", "pct_peak_hbm", "tokens_verified_per_s")}
         line["verify"]["workload"] = v["config"]["workload"]
         line["verify"]["full_call_gbs"] = v["roofline"]["achieved"]
+    if args.workload == "decode" and not args.no_int8:
+        log("[bench] decode on INT8 pools")
+        q8 = run_decode_int8(torch, ha, grp, synth, args, device)
+        line["int8_kv"] = {k: q8[k] for k in ("value", "unit", "ms_per_step", "tokens_per_s", "pct_peak_hbm",
+                                              "workload", "full_call_us", "full_call_gbs", "full_call_frac",
+                                              "swa_call_us", "append_call_us")}
     if args.workload == "decode" and not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(torch, shape, group, data, args.cpu_seconds)

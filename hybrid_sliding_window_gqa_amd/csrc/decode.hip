@@ -543,28 +543,32 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
   if (dd == 0) a.lse[row] = ((m == -INFINITY ? 0.0f : m) + fast_log2(l)) * kLn2;
 }
 
-// Split policy. Every split of the longest sequence is equally long, and the
-// split count is chosen to minimise (workgroup rounds) x (blocks per
-// workgroup + a fixed cost), where a round is what the chip runs at once
-// (256 CUs x 3 resident decode workgroups on MI355X). Equal workgroups and
-// whole rounds avoid a long tail of partly idle CUs. Workgroups are capped at
-// 256 blocks (2 MiB of K/V) so ragged batches still spread over the chip.
+// Split policy. Every split of the longest sequence is equally long. Decode
+// is bound by HBM, and two resident 4-wave workgroups per CU already keep a
+// CU's share of the bandwidth busy (measured: a third one adds nothing), so
+// a round is 256 CUs x 2 workgroups. The split count minimises
+// (rounds) x (blocks per workgroup + a fixed cost), plus the merge's cost
+// when there is more than one split (the reduce launch and the partial rows,
+// about 8 blocks' worth at full load on MI355X). Equal workgroups and whole rounds avoid
+// a tail of partly idle CUs. When one split per sequence cannot give every
+// CU two workgroups, workgroups are capped at 256 blocks (2 MiB of K/V) so
+// ragged batches still spread over the chip.
 int decode_split_blocks(bool full, int window, int max_kv_len, int batch, int hkv, int requested_splits) {
   if (!full) return window / kBlock;
   const int nblk = (max(max_kv_len, 1) + kBlock - 1) / kBlock;
   if (requested_splits > 0) return max(1, (nblk + requested_splits - 1) / requested_splits);
-  constexpr int64_t kResident = 256 * 3;
-  constexpr int kMaxBlocks = 256, kMinBlocks = 4, kFixedCost = 4;
+  constexpr int64_t kSlots = 256 * 2;
+  constexpr int kMaxBlocks = 256, kMinBlocks = 4, kFixedCost = 4, kMergeCost = 8;
   const int64_t pairs = static_cast<int64_t>(max(batch, 1)) * max(hkv, 1);
-  const int s_lo = max(1, (nblk + kMaxBlocks - 1) / kMaxBlocks);
-  const int s_hi = min(max(1, nblk / kMinBlocks), s_lo + 512);
+  const int s_lo = pairs >= kSlots ? 1 : max(1, (nblk + kMaxBlocks - 1) / kMaxBlocks);
+  const int s_hi = min(max(s_lo, nblk / kMinBlocks), s_lo + 512);
   int best_sb = (nblk + s_lo - 1) / s_lo;
   int64_t best_cost = INT64_MAX;
   for (int s = s_lo; s <= s_hi; ++s) {
     const int sb = (nblk + s - 1) / s;
     const int64_t s_eff = (nblk + sb - 1) / sb;
-    const int64_t rounds = (pairs * s_eff + kResident - 1) / kResident;
-    const int64_t cost = rounds * (sb + kFixedCost);
+    const int64_t rounds = (pairs * s_eff + kSlots - 1) / kSlots;
+    const int64_t cost = rounds * (sb + kFixedCost) + (s_eff > 1 ? kMergeCost : 0);
     if (cost < best_cost) {
       best_cost = cost;
       best_sb = sb;

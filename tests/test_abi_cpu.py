@@ -101,12 +101,16 @@ def test_null_and_range_errors(lib):
 
 def test_decode_workspace_checked(lib):
     s = good_shape()
-    need = lib.hybrid_attn_workspace_size(ctypes.byref(s), _lib.HA_FULL, 1, 64, 8193, 0)
-    splits = lib.hybrid_attn_decode_splits(ctypes.byref(s), _lib.HA_FULL, 64, 8193, 0)
+    # 8 sequences x 8 kv heads cannot fill 256 CUs twice over: the keys are split
+    need = lib.hybrid_attn_workspace_size(ctypes.byref(s), _lib.HA_FULL, 1, 8, 32768, 0)
+    splits = lib.hybrid_attn_decode_splits(ctypes.byref(s), _lib.HA_FULL, 8, 32768, 0)
     assert splits > 1
-    assert need == 64 * 64 * splits * (128 + 1) * 4
-    assert decode_call(lib, s, view(), batch=64, max_len=8193) == _lib.HA_ERR_WORKSPACE
-    assert decode_call(lib, s, view(), batch=64, max_len=8193, ws=FAKE, ws_bytes=need - 1) == _lib.HA_ERR_WORKSPACE
+    assert need == 8 * 64 * splits * (128 + 1) * 4
+    assert decode_call(lib, s, view(), batch=8, max_len=32768) == _lib.HA_ERR_WORKSPACE
+    assert decode_call(lib, s, view(), batch=8, max_len=32768, ws=FAKE, ws_bytes=need - 1) == _lib.HA_ERR_WORKSPACE
+    # 64 x 8 pairs give every CU two workgroups: one split, no merge, no workspace
+    assert lib.hybrid_attn_decode_splits(ctypes.byref(s), _lib.HA_FULL, 64, 8193, 0) == 1
+    assert lib.hybrid_attn_workspace_size(ctypes.byref(s), _lib.HA_FULL, 1, 64, 8193, 0) == 0
     # SWA decode and prefill need none
     assert lib.hybrid_attn_workspace_size(ctypes.byref(s), _lib.HA_SWA, 1, 64, 8193, 0) == 0
     assert lib.hybrid_attn_workspace_size(ctypes.byref(s), _lib.HA_FULL, 0, 64, 8193, 0) == \
@@ -179,11 +183,12 @@ def test_verify_errors_and_workspace(lib):
     assert verify_call(lib, s, ring, dtype=7) == _lib.HA_ERR_UNSUPPORTED
     assert verify_call(lib, None, ring) == _lib.HA_ERR_NULL
     # full layers: split-K partials need a workspace sized for nq rows per sequence
-    need = lib.hybrid_attn_verify_workspace_size(ctypes.byref(s), _lib.HA_FULL, 64, 8196, 4, 0)
-    splits = lib.hybrid_attn_decode_splits(ctypes.byref(s), _lib.HA_FULL, 64, 8196, 0)
-    assert splits > 1 and need == 64 * 4 * 64 * splits * (128 + 1) * 4
-    assert verify_call(lib, s, view(), batch=64, max_len=8196) == _lib.HA_ERR_WORKSPACE
-    assert verify_call(lib, s, view(), batch=64, max_len=8196, ws=FAKE, ws_bytes=need - 1) == _lib.HA_ERR_WORKSPACE
+    need = lib.hybrid_attn_verify_workspace_size(ctypes.byref(s), _lib.HA_FULL, 8, 32772, 4, 0)
+    splits = lib.hybrid_attn_decode_splits(ctypes.byref(s), _lib.HA_FULL, 8, 32772, 0)
+    assert splits > 1 and need == 8 * 4 * 64 * splits * (128 + 1) * 4
+    assert lib.hybrid_attn_verify_workspace_size(ctypes.byref(s), _lib.HA_FULL, 64, 8196, 4, 0) == 0   # one split
+    assert verify_call(lib, s, view(), batch=8, max_len=32772) == _lib.HA_ERR_WORKSPACE
+    assert verify_call(lib, s, view(), batch=8, max_len=32772, ws=FAKE, ws_bytes=need - 1) == _lib.HA_ERR_WORKSPACE
     assert lib.hybrid_attn_verify_workspace_size(ctypes.byref(s), _lib.HA_SWA, 64, 8196, 4, 0) == 0
     assert lib.hybrid_attn_verify_workspace_size(ctypes.byref(s), _lib.HA_FULL, 64, 8196, 5, 0) == 0   # invalid nq
     assert verify_call(lib, s, ring, batch=0) == _lib.HA_OK
