@@ -302,18 +302,21 @@ def run_decode_int8(torch, ha, grp, synth, args, device):
     stream = torch.cuda.current_stream()
     plan.run()
     torch.cuda.synchronize()
-    side = torch.cuda.Stream()
-    side.wait_stream(stream)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=side):
-        plan.run()
-    torch.cuda.synchronize()
+    step = plan.run
+    if not args.eager:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            plan.run()
+        torch.cuda.synchronize()
+        step = graph.replay
     for _ in range(args.warmup):
-        graph.replay()
+        step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        graph.replay()
+        step()
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / args.steps
     evs = timed_events(torch, len(plan.calls))
@@ -929,7 +932,9 @@ def main():
             "unit": "GB/s",
             "frac": round(info["full_decode_gbs"] / HBM_PEAK_GBS, 4),
             "traffic": profile_traffic(DECODE_PROFILE) if args.workload == "decode" else None,
-            "kernel": "hybrid_attn_decode, full layer (decode_kernel<128,full> + decode_reduce_kernel<128>)",
+            "kernel": ("hybrid_attn_decode, full layer (decode_kernel<128,full>"
+                       + (f" + decode_reduce_kernel<128>, {info['splits_full']} splits)" if info["splits_full"] > 1
+                          else ", one split per sequence: no merge)")),
             "bytes_per_launch": full_bytes,
         },
     }
