@@ -16,6 +16,7 @@ from .api import (  # noqa: F401
     PageAllocator,
     SwaRingPool,
     full_pool_append,
+    full_pool_read,
     hybrid_attn_decode,
     hybrid_attn_decode_splits,
     hybrid_attn_prefill,
@@ -23,5 +24,6 @@ from .api import (  # noqa: F401
     hybrid_attn_verify_workspace_size,
     hybrid_attn_workspace_size,
     swa_ring_append,
+    swa_ring_read,
     window_safe_match,
 )

@@ -27,12 +27,14 @@ HA_FULL = 1
 HA_KV_BF16 = 0
 HA_KV_INT8 = 1
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 # Every symbol include/*.h declares.
 EXPORTS = (
     "swa_ring_append",
     "full_pool_append",
+    "swa_ring_read",
+    "full_pool_read",
     "window_safe_match",
     "hybrid_attn_prefill",
     "hybrid_attn_decode",
@@ -106,6 +108,8 @@ def load() -> ctypes.CDLL:
     append_args = [shp, view, p, p, i32, i32, p, p, i32, p]
     lib.swa_ring_append.argtypes = append_args
     lib.full_pool_append.argtypes = append_args
+    lib.swa_ring_read.argtypes = [shp, view, p, p, i32, i32, p, p, p]
+    lib.full_pool_read.argtypes = [shp, view, p, p, i32, i32, p, p, p]
     lib.window_safe_match.argtypes = [p, i64, p, i64, p, i32, ctypes.POINTER(i64)]
     lib.hybrid_attn_prefill.argtypes = [shp, view, p, p, i32, i32, i32, p, p, p, i32, p, p, p, sz, p]
     lib.hybrid_attn_decode.argtypes = [shp, view, p, i32, i32, p, p, p, i32, p, p, i32, p, sz, p]
@@ -116,7 +120,8 @@ def load() -> ctypes.CDLL:
     lib.hybrid_attn_verify.argtypes = [shp, view, p, i32, i32, i32, p, p, p, i32, p, p, i32, p, sz, p]
     lib.hybrid_attn_verify_workspace_size.argtypes = [shp, i32, i32, i32, i32, i32]
     lib.hybrid_attn_verify_workspace_size.restype = sz
-    for fn in ("swa_ring_append", "full_pool_append", "window_safe_match", "hybrid_attn_prefill",
+    for fn in ("swa_ring_append", "full_pool_append", "swa_ring_read", "full_pool_read", "window_safe_match",
+               "hybrid_attn_prefill",
                "hybrid_attn_decode", "hybrid_attn_verify"):
         getattr(lib, fn).restype = i32
     lib.ha_status_str.argtypes = [i32]

@@ -230,6 +230,38 @@ def full_pool_append(shape: HeadShape, pages: KvView, pos0: torch.Tensor, cu_new
     _append(load().full_pool_append, shape, pages, pos0, cu_new, k_new, v_new, stream)
 
 
+def _read(fn, shape: HeadShape, view: KvView, pos0, cu, k_out, v_out, stream):
+    dev = view.k.device
+    b = view.batch
+    _check(pos0, "pos0", (b,), torch.int32, dev)
+    _check(cu, "cu", (b + 1,), torch.int32, dev)
+    if k_out is None or v_out is None:
+        raise ValueError("k_out and v_out are required (their first dim is the row count)")
+    t = int(k_out.shape[0])
+    _check(k_out, "k_out", (t, shape.num_kv_heads, shape.head_dim), torch.bfloat16, dev)
+    _check(v_out, "v_out", (t, shape.num_kv_heads, shape.head_dim), torch.bfloat16, dev)
+    c_shape, c_view = shape.c(), view.c()
+    check(fn(ctypes.byref(c_shape), ctypes.byref(c_view), pos0.data_ptr(), cu.data_ptr(), b, t, k_out.data_ptr(),
+             v_out.data_ptr(), _stream_ptr(stream)))
+    return k_out, v_out
+
+
+def swa_ring_read(shape: HeadShape, ring: KvView, pos0: torch.Tensor, cu: torch.Tensor, k_out: torch.Tensor,
+                  v_out: torch.Tensor, stream=None):
+    """Copy positions pos0[b] + i out of each sequence's ring (slot = position mod W) into token-major rows."""
+    if ring.kind != HA_SWA:
+        raise ValueError("swa_ring_read needs an SWA ring view")
+    return _read(load().swa_ring_read, shape, ring, pos0, cu, k_out, v_out, stream)
+
+
+def full_pool_read(shape: HeadShape, pages: KvView, pos0: torch.Tensor, cu: torch.Tensor, k_out: torch.Tensor,
+                   v_out: torch.Tensor, stream=None):
+    """Copy positions pos0[b] + i out of each sequence's pages into token-major rows."""
+    if pages.kind != HA_FULL:
+        raise ValueError("full_pool_read needs a Full page view")
+    return _read(load().full_pool_read, shape, pages, pos0, cu, k_out, v_out, stream)
+
+
 def window_safe_match(req_tokens, cached_tokens, swa_valid, window: int) -> int:
     """Reusable prefix length under the window-safe rule (host call)."""
     req = np.ascontiguousarray(req_tokens, dtype=np.int32)

@@ -121,6 +121,37 @@ ha_status append_common(const ha_shape* shape, const ha_kv_view* view, int32_t w
   return hip_status(ha::launch_append(a, static_cast<hipStream_t>(stream)), "append launch");
 }
 
+ha_status read_common(const ha_shape* shape, const ha_kv_view* view, int32_t want_kind, const int32_t* pos0,
+                      const int32_t* cu, int32_t batch, int32_t num_tokens, void* k_out, void* v_out,
+                      void* stream) {
+  ha::Geometry geo;
+  ha_status st = check_shape(shape, &geo);
+  if (st != HA_OK) return st;
+  if (batch < 0 || num_tokens < 0) return fail(HA_ERR_RANGE, "batch and num_tokens must be >= 0");
+  st = check_view(view, batch);
+  if (st != HA_OK) return st;
+  if (view->kind != want_kind)
+    return fail(HA_ERR_UNSUPPORTED, "%s needs a %s view", want_kind == HA_SWA ? "swa_ring_read" : "full_pool_read",
+                want_kind == HA_SWA ? "HA_SWA" : "HA_FULL");
+  if (view->kv_dtype != HA_KV_BF16) return fail(HA_ERR_UNSUPPORTED, "reads return bf16 rows of bf16 pools only");
+  if (batch == 0 || num_tokens == 0) return ok();
+  if (!pos0 || !cu) return fail(HA_ERR_NULL, "pos0 or cu is NULL");
+  if (!k_out || !v_out) return fail(HA_ERR_NULL, "k_out or v_out is NULL");
+  ha::AppendArgs a{};
+  a.geo = geo;
+  a.full = want_kind == HA_FULL;
+  a.k_pool = static_cast<uint16_t*>(view->k);
+  a.v_pool = static_cast<uint16_t*>(view->v);
+  a.num_blocks = view->num_blocks;
+  a.table = view->table;
+  a.table_stride = view->table_stride;
+  a.pos0 = pos0;
+  a.cu_new = cu;
+  a.batch = batch;
+  a.num_tokens = num_tokens;
+  return hip_status(ha::launch_read(a, k_out, v_out, static_cast<hipStream_t>(stream)), "read launch");
+}
+
 size_t prefill_workspace(const ha::Geometry& geo, int batch, int num_tokens) {
   if (batch <= 0 || num_tokens <= 0) return 0;
   // K and V of every staged 16-token block, bf16
@@ -183,6 +214,16 @@ ha_status full_pool_append(const ha_shape* shape, const ha_kv_view* pages, const
                            const int32_t* cu_new, int32_t batch, int32_t num_tokens, const void* k_new,
                            const void* v_new, int32_t src_dtype, void* stream) {
   return append_common(shape, pages, HA_FULL, pos0, cu_new, batch, num_tokens, k_new, v_new, src_dtype, stream);
+}
+
+ha_status swa_ring_read(const ha_shape* shape, const ha_kv_view* ring, const int32_t* pos0, const int32_t* cu,
+                        int32_t batch, int32_t num_tokens, void* k_out, void* v_out, void* stream) {
+  return read_common(shape, ring, HA_SWA, pos0, cu, batch, num_tokens, k_out, v_out, stream);
+}
+
+ha_status full_pool_read(const ha_shape* shape, const ha_kv_view* pages, const int32_t* pos0, const int32_t* cu,
+                         int32_t batch, int32_t num_tokens, void* k_out, void* v_out, void* stream) {
+  return read_common(shape, pages, HA_FULL, pos0, cu, batch, num_tokens, k_out, v_out, stream);
 }
 
 ha_status window_safe_match(const int32_t* req_tokens, int64_t req_len, const int32_t* cached_tokens,

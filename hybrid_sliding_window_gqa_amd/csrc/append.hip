@@ -173,6 +173,69 @@ __global__ __launch_bounds__(256) void append8_kernel(AppendArgs a) {
   }
 }
 
+// Inverse of append_kernel: one thread per (token, kv head, 8 channels)
+// gathers the K unit and the 8 V values from the block and writes them as
+// token-major rows. Every position is read (no ring overwrite skipping).
+__global__ __launch_bounds__(256) void read_kernel(AppendArgs a, uint16_t* k_out, uint16_t* v_out) {
+  const int d = a.geo.d;
+  const int hkv = a.geo.hkv;
+  const int chunks = d >> 3;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(a.num_tokens) * hkv * chunks;
+  if (gid >= total) return;
+  const int c = static_cast<int>(gid % chunks);
+  const int64_t rest = gid / chunks;
+  const int g = static_cast<int>(rest % hkv);
+  const int tok = static_cast<int>(rest / hkv);
+  int lo = 0, hi = a.batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.cu_new[mid] <= tok) lo = mid; else hi = mid - 1;
+  }
+  const int b = lo;
+  const int i = tok - a.cu_new[b];
+  if (i < 0 || i >= a.cu_new[b + 1] - a.cu_new[b]) return;
+  const int64_t p = static_cast<int64_t>(a.pos0[b]) + i;
+  if (p < 0) return;
+  int64_t block_base;
+  int in_blk;
+  if (!a.full) {
+    const int w = a.geo.window;
+    const int r = a.table[b];
+    if (r < 0 || r >= a.num_blocks) return;
+    const int s = static_cast<int>(p % w);
+    block_base = ((static_cast<int64_t>(r) * hkv + g) * w + (s & ~(kBlock - 1))) * d;
+    in_blk = s & (kBlock - 1);
+  } else {
+    const int64_t lp = p >> 4;
+    if (lp >= a.table_stride) return;
+    const int pg = a.table[static_cast<int64_t>(b) * a.table_stride + lp];
+    if (pg < 0 || pg >= a.num_blocks) return;
+    block_base = (static_cast<int64_t>(pg) * hkv + g) * kBlock * d;
+    in_blk = static_cast<int>(p & (kBlock - 1));
+  }
+  const int64_t dst = (static_cast<int64_t>(tok) * hkv + g) * d + c * 8;
+  *reinterpret_cast<u32x4*>(k_out + dst) =
+      *reinterpret_cast<const u32x4*>(a.k_pool + block_base + k_elem(in_blk, c * 8));
+  const uint16_t* vblk = a.v_pool + block_base;
+  uint32_t w4[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    w4[j] = static_cast<uint32_t>(vblk[v_elem(in_blk, c * 8 + 2 * j)]) |
+            (static_cast<uint32_t>(vblk[v_elem(in_blk, c * 8 + 2 * j + 1)]) << 16);
+  *reinterpret_cast<u32x4*>(v_out + dst) = u32x4{w4[0], w4[1], w4[2], w4[3]};
+}
+
+hipError_t launch_read(const AppendArgs& a, void* k_out, void* v_out, hipStream_t stream) {
+  const int64_t total = static_cast<int64_t>(a.num_tokens) * a.geo.hkv * (a.geo.d >> 3);
+  if (total == 0 || a.batch == 0) return hipSuccess;
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(read_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a,
+                     static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out));
+  return hipGetLastError();
+}
+
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
   const int64_t total = static_cast<int64_t>(a.num_tokens) * a.geo.hkv * (a.geo.d >> 3);
   if (total == 0 || a.batch == 0) return hipSuccess;

@@ -116,6 +116,8 @@ struct VerifyArgs {
 int64_t prefill_stage_blocks(int num_tokens, int batch);
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+// Pool -> token-major rows (k_new / v_new of the args are the outputs).
+hipError_t launch_read(const AppendArgs& a, void* k_out, void* v_out, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);

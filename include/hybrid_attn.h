@@ -87,7 +87,7 @@
 extern "C" {
 #endif
 
-#define HA_ABI_VERSION 5
+#define HA_ABI_VERSION 6
 
 typedef enum ha_status {
   HA_OK = 0,
@@ -167,6 +167,23 @@ ha_status swa_ring_append(const ha_shape* shape, const ha_kv_view* ring, const i
 ha_status full_pool_append(const ha_shape* shape, const ha_kv_view* pages, const int32_t* pos0,
                            const int32_t* cu_new, int32_t batch, int32_t num_tokens,
                            const void* k_new, const void* v_new, int32_t src_dtype, void* stream);
+
+/* ---- reading positions back out of a pool (the inverse of the appends) ----
+ * Copies position p = pos0[b] + i (i < cu[b+1] - cu[b]) of sequence b from the
+ * pool into row cu[b] + i of k_out / v_out, [num_tokens][Hkv][D] bfloat16
+ * (device, caller-owned). Used to move a reused prefix's window between
+ * requests' rings, to copy a page a new request only partly shares before it
+ * writes to it, and to save a layer's K/V to a host-memory tier ([YLY]
+ * KVCache系统重构: the prefix tree's SWA map and Full index point into
+ * these pools; [HD9] "三层 KVCache 系统": KV moves between HBM and host
+ * memory). A ring returns slot p mod W, whatever position it holds now: the
+ * caller reads only positions the ring still holds. Page ids and ring ids
+ * out of range give rows that are left unwritten. bf16 pools only
+ * (HA_ERR_UNSUPPORTED for INT8). Arguments otherwise as for the appends. */
+ha_status swa_ring_read(const ha_shape* shape, const ha_kv_view* ring, const int32_t* pos0, const int32_t* cu,
+                        int32_t batch, int32_t num_tokens, void* k_out, void* v_out, void* stream);
+ha_status full_pool_read(const ha_shape* shape, const ha_kv_view* pages, const int32_t* pos0, const int32_t* cu,
+                         int32_t batch, int32_t num_tokens, void* k_out, void* v_out, void* stream);
 
 /* ---- a3: window-safe prefix match ([HTX] 工程三; [YLY] KVCache系统重构;
  *          [HD9] Hybrid SWA 节; [HD12] 双池分治) ------------------------------

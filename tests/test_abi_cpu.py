@@ -213,3 +213,18 @@ def test_int8_view_errors(lib):
                                   FAKE, FAKE, 0, FAKE, 1 << 30, None) == _lib.HA_ERR_UNSUPPORTED
     # the zero-initialised tail of a view is a bf16 pool
     assert HaKvView(_lib.HA_FULL, FAKE, FAKE, 8, FAKE, 4).kv_dtype == _lib.HA_KV_BF16
+
+
+def test_read_errors(lib):
+    s = good_shape()
+    ring, pages = view(kind=_lib.HA_SWA), view(kind=_lib.HA_FULL)
+    rd = lambda fn, v, **kw: fn(ctypes.byref(s), ctypes.byref(v), kw.get("pos0", FAKE), FAKE, kw.get("batch", 2),
+                                kw.get("n", 10), kw.get("k", FAKE), FAKE, None)
+    assert rd(lib.swa_ring_read, pages) == _lib.HA_ERR_UNSUPPORTED
+    assert rd(lib.full_pool_read, ring) == _lib.HA_ERR_UNSUPPORTED
+    assert rd(lib.swa_ring_read, ring, pos0=None) == _lib.HA_ERR_NULL
+    assert rd(lib.full_pool_read, pages, k=None) == _lib.HA_ERR_NULL
+    assert rd(lib.full_pool_read, pages, n=-1) == _lib.HA_ERR_RANGE
+    assert rd(lib.swa_ring_read, ring, batch=0, n=0) == 0
+    int8 = HaKvView(_lib.HA_FULL, FAKE, FAKE, 8, FAKE, 4, _lib.HA_KV_INT8, FAKE, FAKE)
+    assert rd(lib.full_pool_read, int8) == _lib.HA_ERR_UNSUPPORTED
