@@ -285,12 +285,12 @@ def kv8_bytes_per_token(shape):
 
 
 def run_decode_int8(torch, ha, grp, synth, args, device):
-    """The decode workload on INT8 pools: per layer an append call (quantizes
-    the new token) and a decode call, graph replay; and the full-layer decode
-    call alone."""
+    """The decode workload on INT8 pools: per layer one call that quantizes
+    and appends the new token and attends (--separate-append: an append call
+    and a decode call), graph replay; and the full-layer decode call alone."""
     struct = synth.decode_structure()
-    shape, group, plan, data = build_decode(torch, ha, grp, synth, struct, device, struct.workload, fuse=False,
-                                            kv_dtype="int8")
+    shape, group, plan, data = build_decode(torch, ha, grp, synth, struct, device, struct.workload,
+                                            fuse=not args.separate_append, kv_dtype="int8")
     b = struct.batch
     kv_len = data["hist"] + 1
     hq, d = shape.num_q_heads, shape.head_dim
@@ -330,9 +330,10 @@ def run_decode_int8(torch, ha, grp, synth, args, device):
     lab = plan.labels
     full_ms = float(np.mean([call_ms[i] for i, x in enumerate(lab) if x.startswith("decode") and "full" in x]))
     swa_ms = float(np.mean([call_ms[i] for i, x in enumerate(lab) if x.startswith("decode") and "swa" in x]))
-    app_ms = float(np.mean([call_ms[i] for i, x in enumerate(lab) if x.startswith("append")]))
+    app = [call_ms[i] for i, x in enumerate(lab) if x.startswith("append")]
+    app_ms = float(np.mean(app)) if app else 0.0
     full_layer = [i for i, layer in enumerate(group.layers) if layer.kind == "full"][0]
-    full_bytes = per_layer[full_layer]
+    full_bytes = per_layer[full_layer] + (0 if app else append)    # a fused call also appends
     value = step_bytes / dt / 1e9
     log(f"[bench] int8 decode step {dt * 1e3:.3f} ms, {value:.1f} GB/s, {b / dt:.0f} tokens/s; full call "
         f"{full_ms * 1e3:.1f} us ({full_bytes / full_ms / 1e6:.0f} GB/s), swa call {swa_ms * 1e3:.1f} us, "
@@ -346,7 +347,8 @@ def run_decode_int8(torch, ha, grp, synth, args, device):
         "pct_peak_hbm": round(100.0 * value / HBM_PEAK_GBS, 2),
         "step_bytes": step_bytes,
         "workload": (f"decode: {b} sequences x {int(kv_len[0]) - 1} cached tokens on INT8 pools (per-token "
-                     f"scales), one 6:1 group, per layer an append call then a decode call"),
+                     f"scales), one 6:1 group, per layer "
+                     + ("an append call then a decode call" if app else "one call (quantize, append, attend)")),
         "full_call_us": round(full_ms * 1e3, 2),
         "full_call_gbs": round(full_bytes / full_ms / 1e6, 2),
         "full_call_frac": round(full_bytes / full_ms / 1e6 / HBM_PEAK_GBS, 4),

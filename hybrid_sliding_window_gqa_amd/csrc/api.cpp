@@ -316,8 +316,6 @@ ha_status hybrid_attn_decode(const ha_shape* shape, const ha_kv_view* kv, const 
   if ((k_new == nullptr) != (v_new == nullptr))
     return fail(HA_ERR_NULL, "k_new and v_new must both be given (fused append) or both be NULL");
   const bool kv8 = kv->kv_dtype == HA_KV_INT8;
-  if (kv8 && k_new)
-    return fail(HA_ERR_UNSUPPORTED, "decode over an INT8 pool takes no fused append (append the token first)");
   const bool full = kv->kind == HA_FULL;
   const size_t need = decode_workspace(geo, full, batch, max_kv_len, num_splits);
   if (need > 0 && (!workspace || workspace_bytes < need))

@@ -29,7 +29,10 @@
 // raw codes and the block's scales are what the ping-pong buffers hold, and
 // a block is widened to the same bf16 operands right before it is consumed
 // (codes are exact in bf16), the K scale multiplying the scores and the V
-// scale folded into the probabilities.
+// scale folded into the probabilities. A fused append quantizes the token in
+// the owning wave with append8_kernel's arithmetic (absmax butterflies over
+// the lanes that hold the K row and the V row) and patches codes and scales
+// into the raw operands.
 // Page ids are scalar loads issued two blocks ahead of their use. The waves
 // merge through LDS; a workgroup writes either the final row (one split) or a
 // partial (o, lse) for the reduce kernel.
@@ -254,6 +257,23 @@ __device__ __forceinline__ uint32_t load_bf16_bits(const void* src, int64_t elem
   else return static_cast<const uint16_t*>(src)[elem];
 }
 
+// INT8 pools: the new token's codes in the raw operand format (K: the units
+// of lanes c16 == row; V: byte dt%4 of word dt/4 holds dim tile dt's code of
+// this lane's channel) and its two scales.
+template <int D>
+struct NewToken8 {
+  u32x4 k[D / 64];
+  uint32_t v[D / 64];
+  float ks;
+  float vs;
+};
+
+// The quantized code of x, exactly as append8_kernel computes it.
+__device__ __forceinline__ uint32_t code8(float x, float scale) {
+  return scale > 0.0f ? static_cast<uint32_t>(static_cast<int>(fminf(fmaxf(rintf(x / scale), -127.0f), 127.0f))) & 0xffu
+                      : 0u;
+}
+
 // The new token's operand pieces for the wave that owns its block: K chunk
 // (m, q4) of the token row (used by lanes c16 == row) and the V values of
 // channels 32p + c16 and 32p + 16 + c16 (used by lanes q4 == row / 4).
@@ -352,12 +372,58 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
 
   // Fused append: block of position t, its row in the block, and whether
   // this wave consumes that block.
-  const bool fuse = !kKv8 && a.k_new != nullptr;
+  const bool fuse = a.k_new != nullptr;
   const int new_blk = kFull ? (t >> 4) : ((t % W) >> 4);
   const int new_row = t & (kBlock - 1);
   const bool new_mine = fuse && new_blk >= first && new_blk < last && (new_blk - first) % kWaves == wave;
   NewToken<D> nt;
-  if (new_mine) {
+  NewToken8<D> n8;
+  if constexpr (kKv8) {
+    // Quantize the token as append8_kernel does: the 4 lanes of a c16
+    // column hold the K row (channels 32m + 8*q4 + j), the 16 lanes of a q4
+    // row hold the V row (channel 16*dt + c16 for dim tile dt).
+    if (new_mine) {
+      const int64_t src = (static_cast<int64_t>(b) * hkv + g) * D;
+      float kx[KS][8];
+      float ka = 0.0f;
+#pragma unroll
+      for (int m = 0; m < KS; ++m) {
+        const u32x4 w = load8_as_bf16<kQF32>(a.k_new, src + 32 * m + 8 * q4);
+        const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          kx[m][2 * j] = __uint_as_float(w4[j] << 16);
+          kx[m][2 * j + 1] = __uint_as_float(w4[j] & 0xffff0000u);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ka = fmaxf(ka, fabsf(kx[m][j]));
+      }
+      ka = fmaxf(ka, __shfl_xor(ka, 16));
+      ka = fmaxf(ka, __shfl_xor(ka, 32));
+      float vx[DT];
+      float va = 0.0f;
+#pragma unroll
+      for (int p = 0; p < D / 32; ++p) {
+        vx[2 * p] = __uint_as_float(load_bf16_bits<kQF32>(a.v_new, src + 32 * p + c16) << 16);
+        vx[2 * p + 1] = __uint_as_float(load_bf16_bits<kQF32>(a.v_new, src + 32 * p + 16 + c16) << 16);
+        va = fmaxf(va, fmaxf(fabsf(vx[2 * p]), fabsf(vx[2 * p + 1])));
+      }
+#pragma unroll
+      for (int mask = 1; mask < 16; mask <<= 1) va = fmaxf(va, __shfl_xor(va, mask));
+      n8.ks = ka / 127.0f;
+      n8.vs = va / 127.0f;
+#pragma unroll
+      for (int j = 0; j < D / 64; ++j) {
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) w[e >> 2] |= code8(kx[2 * j + (e >> 3)][e & 7], n8.ks) << (8 * (e & 3));
+        n8.k[j] = u32x4{w[0], w[1], w[2], w[3]};
+        n8.v[j] = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) n8.v[j] |= code8(vx[4 * j + e], n8.vs) << (8 * e);
+      }
+    }
+  } else if (new_mine) {
     const int64_t src = (static_cast<int64_t>(b) * hkv + g) * D;
 #pragma unroll
     for (int m = 0; m < KS; ++m) nt.k[m] = load8_as_bf16<kQF32>(a.k_new, src + 32 * m + 8 * q4);
@@ -368,10 +434,33 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
     }
   }
   auto patch_new = [&](BlockBuf<D, kKv8>& buf, int i) {
-    if constexpr (kKv8) return;
-    else {
-    BlockOps<D>& ops = buf.ops;
     if (!new_mine || i != new_blk) return;
+    if constexpr (kKv8) {
+      RawBlock8<D>& raw = buf.raw;
+      if (c16 == new_row) {
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j) raw.k[j] = n8.k[j];
+      }
+      if (q4 == (new_row >> 2)) {
+        const uint32_t sh = 8 * (new_row & 3);
+        const uint32_t keep = ~(0xffu << sh);
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j) {
+          raw.v[j].x = (raw.v[j].x & keep) | ((n8.v[j] & 0xffu) << sh);
+          raw.v[j].y = (raw.v[j].y & keep) | (((n8.v[j] >> 8) & 0xffu) << sh);
+          raw.v[j].z = (raw.v[j].z & keep) | (((n8.v[j] >> 16) & 0xffu) << sh);
+          raw.v[j].w = (raw.v[j].w & keep) | ((n8.v[j] >> 24) << sh);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (r == (new_row & 3)) {
+            raw.ks[r] = n8.ks;
+            raw.vs[r] = n8.vs;
+          }
+        }
+      }
+    } else {
+    BlockOps<D>& ops = buf.ops;
     if (c16 == new_row) {
 #pragma unroll
       for (int m = 0; m < KS; ++m) ops.k[m] = nt.k[m];
@@ -449,7 +538,26 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
 
   // Fused append: the owner wave writes the token into the pool, after its
   // block has been read and consumed.
-  if (new_mine) {
+  if (kKv8 && new_mine) {
+    const int64_t nb = base_of(new_blk, kFull ? page_row[new_blk] : 0);
+    if (nb >= 0) {
+      uint8_t* kb = reinterpret_cast<uint8_t*>(a.k_pool_w) + nb;
+      uint8_t* vb = reinterpret_cast<uint8_t*>(a.v_pool_w) + nb;
+      if (c16 == new_row) {
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j) *reinterpret_cast<u32x4*>(kb + 16 * (64 * j + lane)) = n8.k[j];
+      }
+      if (q4 == (new_row >> 2)) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          vb[v8_elem(new_row, 16 * dt + c16)] = static_cast<uint8_t>((n8.v[dt >> 2] >> (8 * (dt & 3))) & 0xffu);
+      }
+      if (lane == 0) {
+        a.k_scale[nb / D + new_row] = n8.ks;
+        a.v_scale[nb / D + new_row] = n8.vs;
+      }
+    }
+  } else if (new_mine) {
     const int64_t nb = base_of(new_blk, kFull ? page_row[new_blk] : 0);
     if (nb >= 0) {
       if (c16 == new_row) {

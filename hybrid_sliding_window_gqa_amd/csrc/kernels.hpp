@@ -55,9 +55,9 @@ struct DecodeArgs {
   const void* v_new;      // [batch][hkv][d]
   uint16_t* k_pool_w;     // writable pool views for the fused append
   uint16_t* v_pool_w;
-  bool kv8;               // INT8 pools (no fused append): codes + per-token scales
-  const float* k_scale;
-  const float* v_scale;
+  bool kv8;               // INT8 pools: codes + per-token scales (written by a fused append)
+  float* k_scale;
+  float* v_scale;
 };
 
 struct PrefillArgs {

@@ -145,8 +145,6 @@ def plan_decode(group: HybridGroup, q, k_new, v_new, pos, kv_len, max_kv_len: in
     _check(pos, "pos", (b,), torch.int32, dev)
     _check(kv_len, "kv_len", (b,), torch.int32, dev)
     cu_one = torch.arange(b + 1, dtype=torch.int32, device=dev)
-    if fuse_append and group.kv_dtype != "bf16":
-        raise ValueError("decode over int8 pools appends the token in a call of its own (fuse_append=False)")
     calls, labels = [], []
     for li, layer in enumerate(group.layers):
         _check(q[li], "q", (b, hq, d), None, dev)

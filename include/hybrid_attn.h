@@ -129,8 +129,9 @@ typedef struct ha_shape {
  *            authoritative logical->physical index of the sequence ([YLY]).
  * kv_dtype selects bf16 pools (HA_KV_BF16, scales unused) or INT8 pools
  * (HA_KV_INT8: k_scale / v_scale required, layout above). INT8 pools are
- * written by the two append calls and read by hybrid_attn_decode without a
- * fused append; prefill and verify reject them (HA_ERR_UNSUPPORTED). */
+ * written by the two append calls (and by hybrid_attn_decode's fused append,
+ * which quantizes the token the same way) and read by hybrid_attn_decode;
+ * prefill, verify and the pool reads reject them (HA_ERR_UNSUPPORTED). */
 typedef struct ha_kv_view {
   int32_t kind;
   void* k;

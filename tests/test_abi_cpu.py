@@ -205,8 +205,7 @@ def test_int8_view_errors(lib):
         assert decode_call(lib, s, bad) == status
         assert lib.full_pool_append(ctypes.byref(s), ctypes.byref(bad), FAKE, FAKE, 2, 10, FAKE, FAKE, 0,
                                     None) == status
-    # decode over int8 takes no fused append; prefill and verify read bf16 pools only
-    assert decode_call(lib, s, pages, k_new=FAKE, v_new=FAKE) == _lib.HA_ERR_UNSUPPORTED
+    # prefill and verify read bf16 pools only
     args = [FAKE, FAKE, 2, 10, 5, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, 1 << 30, None]
     assert lib.hybrid_attn_prefill(ctypes.byref(s), ctypes.byref(ring), *args) == _lib.HA_ERR_UNSUPPORTED
     assert lib.hybrid_attn_verify(ctypes.byref(s), ctypes.byref(pages), FAKE, 2, 100, 4, FAKE, FAKE, FAKE, 0,

@@ -158,9 +158,9 @@ def test_int8_decode_is_close_to_bf16_decode():
 
 
 def test_decode_workload_with_int8_pools_sampled_sequences():
-    """The decode workload's group (64 x 8192, 7 layers) on INT8 pools: the
-    token is appended by its own call, then decoded; sampled sequences of
-    every layer against the oracle."""
+    """The decode workload's group (64 x 8192, 7 layers) on INT8 pools, one
+    fused call per layer (quantize and append the token, attend); sampled
+    sequences of every layer against the oracle."""
     struct = synth.decode_structure()
     shape = ha.HeadShape(struct.shape.num_q_heads, struct.shape.num_kv_heads, struct.shape.head_dim,
                          struct.shape.window)
@@ -183,7 +183,7 @@ def test_decode_workload_with_int8_pools_sampled_sequences():
     lse = [torch.empty(b, hq, device=DEV) for _ in group.layers]
     plan = grp.plan_decode(group, [x[2] for x in data], [x[0][:, -1].contiguous() for x in data],
                            [x[1][:, -1].contiguous() for x in data], i32([hist] * b), i32([hist + 1] * b),
-                           hist + 1, out, lse, fuse_append=False)
+                           hist + 1, out, lse, fuse_append=True)
     plan.run()
     torch.cuda.synchronize()
     for li, layer in enumerate(group.layers):
@@ -191,3 +191,42 @@ def test_decode_workload_with_int8_pools_sampled_sequences():
         for s in (0, 17, b - 1):
             ref_o, ref_l = oracle_decode(host(q[s]), host(k[s]), host(v[s]), hist - lo + 1, layer.kind, w)
             assert_close(host(out[li][s:s + 1]), host(lse[li][s:s + 1]), ref_o, ref_l, f"layer {li} seq {s}")
+
+
+@pytest.mark.parametrize("kind", [ha.HA_SWA, ha.HA_FULL])
+@pytest.mark.parametrize("d,window,qsrc", [(128, 128, None), (64, 32, torch.float32)])
+def test_fused_append_equals_append_then_decode(kind, d, window, qsrc):
+    """Decode with the new token's K/V quantizes and appends it in the same
+    launch: pools and outputs bit-identical to append8 followed by decode."""
+    shape = ha.HeadShape(16, 2, d, window=window)
+    lens = [1, 2, 16, 17, window, window + 1, 300, 2049]
+    gen = make_generator(d + window + kind)
+    k = [randn_bf16(gen, n, 2, d) for n in lens]
+    v = [randn_bf16(gen, n, 2, d) for n in lens]
+    k[3][-1] = 0                                    # an all-zero new row: scale 0
+    q = randn_bf16(gen, len(lens), 16, d)
+    hist = [n - 1 for n in lens]
+    starts = [max(0, h - window) if kind == ha.HA_SWA else 0 for h in hist]
+    runs = []
+    for fused in (True, False):
+        pool, view, _ = make_pools(shape, kind, lens, seed=d)
+        append_history(shape, view, list(zip(k, v)), starts, hist)
+        k_new = torch.stack([x[-1] for x in k]).contiguous()
+        v_new = torch.stack([x[-1] for x in v]).contiguous()
+        if qsrc is not None:
+            k_new, v_new = k_new.to(qsrc), v_new.to(qsrc)
+        qq = q if qsrc is None else q.to(qsrc)
+        if fused:
+            out, lse = ha.hybrid_attn_decode(shape, view, i32(lens), qq, max(lens), k_new=k_new, v_new=v_new)
+        else:
+            fn = ha.swa_ring_append if kind == ha.HA_SWA else ha.full_pool_append
+            fn(shape, view, i32(hist), i32(np.arange(len(lens) + 1)), k_new, v_new)
+            out, lse = ha.hybrid_attn_decode(shape, view, i32(lens), qq, max(lens))
+        torch.cuda.synchronize()
+        runs.append((pool, host(out), host(lse)))
+    (pa, oa, la), (pb, ob, lb) = runs
+    assert torch.equal(pa.k, pb.k) and torch.equal(pa.v, pb.v)
+    assert torch.equal(pa.k_scale.view(torch.int32), pb.k_scale.view(torch.int32))
+    assert torch.equal(pa.v_scale.view(torch.int32), pb.v_scale.view(torch.int32))
+    np.testing.assert_array_equal(oa, ob)
+    np.testing.assert_array_equal(la, lb)
