@@ -74,10 +74,10 @@ __device__ __forceinline__ void load_block(BlockOps<D>& ops, const uint16_t* kp,
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + b0, bytes);
   const int lane = 16 * q4 + c16;
 #pragma unroll
-  for (int m = 0; m < D / 32; ++m) ops.k[m] = buf_load16(rk, 16 * (64 * m + lane));
+  for (int m = 0; m < D / 32; ++m) ops.k[m] = buf_load16_stream(rk, 16 * (64 * m + lane));
 #pragma unroll
   for (int p = 0; p < D / 32; ++p) {
-    const u32x4 w = buf_load16(rv, 16 * (64 * p + lane));
+    const u32x4 w = buf_load16_stream(rv, 16 * (64 * p + lane));
     ops.v[2 * p] = u32x2{w.x, w.y};
     ops.v[2 * p + 1] = u32x2{w.z, w.w};
   }
@@ -147,14 +147,14 @@ __device__ __forceinline__ void load_block8(RawBlock8<D>& raw, const DecodeArgs&
   const int lane = 16 * q4 + c16;
 #pragma unroll
   for (int j = 0; j < D / 64; ++j) {
-    raw.k[j] = buf_load16(rk, 16 * (64 * j + lane));
-    raw.v[j] = buf_load16(rv, 16 * (64 * j + lane));
+    raw.k[j] = buf_load16_stream(rk, 16 * (64 * j + lane));
+    raw.v[j] = buf_load16_stream(rv, 16 * (64 * j + lane));
   }
   const uint32_t sbytes = ok ? kBlock * 4 : 0;
   const __amdgpu_buffer_rsrc_t rks = make_rsrc(a.k_scale + b0 / D, sbytes);
   const __amdgpu_buffer_rsrc_t rvs = make_rsrc(a.v_scale + b0 / D, sbytes);
-  raw.ks = __builtin_bit_cast(f32x4, buf_load16(rks, 16 * q4));
-  raw.vs = __builtin_bit_cast(f32x4, buf_load16(rvs, 16 * q4));
+  raw.ks = __builtin_bit_cast(f32x4, buf_load16_stream(rks, 16 * q4));
+  raw.vs = __builtin_bit_cast(f32x4, buf_load16_stream(rvs, 16 * q4));
 }
 
 // Codes -> the same bf16 operands the bf16 path loads.

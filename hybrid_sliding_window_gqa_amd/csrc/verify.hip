@@ -54,10 +54,10 @@ __device__ __forceinline__ void vload_block(VBlock<D>& ops, const uint16_t* kp, 
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + b0, bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + b0, bytes);
 #pragma unroll
-  for (int m = 0; m < D / 32; ++m) ops.k[m] = buf_load16(rk, 16 * (64 * m + lane));
+  for (int m = 0; m < D / 32; ++m) ops.k[m] = buf_load16_stream(rk, 16 * (64 * m + lane));
 #pragma unroll
   for (int p = 0; p < D / 32; ++p) {
-    const u32x4 w = buf_load16(rv, 16 * (64 * p + lane));
+    const u32x4 w = buf_load16_stream(rv, 16 * (64 * p + lane));
     ops.v[2 * p] = u32x2{w.x, w.y};
     ops.v[2 * p + 1] = u32x2{w.z, w.w};
   }
