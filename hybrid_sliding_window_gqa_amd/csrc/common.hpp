@@ -135,6 +135,21 @@ __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t by
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
 }
 
+// Query rows [row0, row0 + nrows) of a bf16 [rows][D] array as matrix-core
+// B operands: lane (q4, c16) gets row row0 + c16, channels 32m + 8 q4 .. +7.
+// Lanes with c16 >= nrows read past the buffer's end and get zeros from the
+// range check, so no select on the loaded value has to wait for the load
+// before the loads that follow it are issued.
+template <int D>
+__device__ __forceinline__ void load_q_rows(u32x4 (&qop)[D / 32], const void* q, int64_t row0, int nrows,
+                                            int q4, int c16) {
+  const __amdgpu_buffer_rsrc_t r =
+      make_rsrc(static_cast<const uint16_t*>(q) + row0 * D, static_cast<uint32_t>(nrows) * D * 2);
+  const uint32_t off = c16 < nrows ? 2u * static_cast<uint32_t>(c16 * D + 8 * q4) : 0x40000000u;
+#pragma unroll
+  for (int m = 0; m < D / 32; ++m) qop[m] = buf_load16(r, off + 64 * m);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -308,6 +308,14 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
   const int W = a.geo.window;
 
   const int len = a.kv_len[b];
+  // The SWA ring id is read beside the length, so the two scalar loads share
+  // one memory round trip before the first K/V load can be addressed.
+  const int ring_id = kFull ? 0 : a.table[b];
+  // Compiler-only: keeps the ring-id load, and the argument loads of the
+  // pointers the first Q and K/V loads need, above the branch below, where
+  // the compiler would otherwise sink them (and their waits) past the length
+  // check, one dependent round trip each.
+  if constexpr (!kFull) asm volatile("" ::"s"(ring_id), "s"(a.q), "s"(a.k_pool), "s"(a.v_pool));
   if (len <= 0) {
     if (split == 0) {
       for (int e = threadIdx.x; e < G * D; e += blockDim.x)
@@ -335,9 +343,8 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
   }
   if (split >= nsplit) return;
 
-  int ring = 0;
+  const int ring = ring_id;
   if constexpr (!kFull) {
-    ring = a.table[b];
     if (ring < 0 || ring >= a.num_blocks) last = first;  // invalid ring id: no keys
   }
   const int32_t* page_row = a.table + static_cast<int64_t>(b) * a.table_stride;
@@ -360,7 +367,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
 
   // Q^T as the B operand: column c16 = query head g*G + c16 (zero past the group).
   u32x4 qop[KS];
-  {
+  if constexpr (kQF32) {
     const bool head_ok = c16 < G;
     const int64_t qoff = (static_cast<int64_t>(b) * hq + g * G + (head_ok ? c16 : 0)) * D + 8 * q4;
 #pragma unroll
@@ -368,6 +375,8 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
       qop[m] = load8_as_bf16<kQF32>(a.q, qoff + 32 * m);
       if (!head_ok) qop[m] = u32x4{0u, 0u, 0u, 0u};
     }
+  } else {
+    load_q_rows<D>(qop, a.q, static_cast<int64_t>(b) * hq + g * G, G, q4, c16);
   }
 
   // Fused append: block of position t, its row in the block, and whether
@@ -479,6 +488,49 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
 #pragma unroll
   for (int i = 0; i < DT; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Fused append: the owner wave writes the token into the pool, after its
+  // block has been read and consumed. (Issued right after the patch instead,
+  // the stores made the SWA call about 1 us slower.)
+  auto store_new = [&]() {
+    if (kKv8 && new_mine) {
+      const int64_t nb = base_of(new_blk, kFull ? page_row[new_blk] : 0);
+      if (nb >= 0) {
+        uint8_t* kb = reinterpret_cast<uint8_t*>(a.k_pool_w) + nb;
+        uint8_t* vb = reinterpret_cast<uint8_t*>(a.v_pool_w) + nb;
+        if (c16 == new_row) {
+#pragma unroll
+          for (int j = 0; j < D / 64; ++j) *reinterpret_cast<u32x4*>(kb + 16 * (64 * j + lane)) = n8.k[j];
+        }
+        if (q4 == (new_row >> 2)) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            vb[v8_elem(new_row, 16 * dt + c16)] = static_cast<uint8_t>((n8.v[dt >> 2] >> (8 * (dt & 3))) & 0xffu);
+        }
+        if (lane == 0) {
+          a.k_scale[nb / D + new_row] = n8.ks;
+          a.v_scale[nb / D + new_row] = n8.vs;
+        }
+      }
+    } else if (new_mine) {
+      const int64_t nb = base_of(new_blk, kFull ? page_row[new_blk] : 0);
+      if (nb >= 0) {
+        if (c16 == new_row) {
+#pragma unroll
+          for (int m = 0; m < KS; ++m)
+            *reinterpret_cast<u32x4*>(a.k_pool_w + nb + 8 * (64 * m + lane)) = nt.k[m];
+        }
+        if (q4 == (new_row >> 2)) {
+          uint16_t* vb = a.v_pool_w + nb;
+#pragma unroll
+          for (int p = 0; p < D / 32; ++p) {
+            vb[v_elem(new_row, 32 * p + c16)] = static_cast<uint16_t>(nt.v[2 * p]);
+            vb[v_elem(new_row, 32 * p + 16 + c16)] = static_cast<uint16_t>(nt.v[2 * p + 1]);
+          }
+        }
+      }
+    }
+  };
+
   if constexpr (!kFull) {
     // SWA: with W <= 16 * waves (W = 128: one ring block per wave) every
     // wave has at most one block; a larger ring is walked a block at a
@@ -536,45 +588,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
     }
   }
 
-  // Fused append: the owner wave writes the token into the pool, after its
-  // block has been read and consumed.
-  if (kKv8 && new_mine) {
-    const int64_t nb = base_of(new_blk, kFull ? page_row[new_blk] : 0);
-    if (nb >= 0) {
-      uint8_t* kb = reinterpret_cast<uint8_t*>(a.k_pool_w) + nb;
-      uint8_t* vb = reinterpret_cast<uint8_t*>(a.v_pool_w) + nb;
-      if (c16 == new_row) {
-#pragma unroll
-        for (int j = 0; j < D / 64; ++j) *reinterpret_cast<u32x4*>(kb + 16 * (64 * j + lane)) = n8.k[j];
-      }
-      if (q4 == (new_row >> 2)) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          vb[v8_elem(new_row, 16 * dt + c16)] = static_cast<uint8_t>((n8.v[dt >> 2] >> (8 * (dt & 3))) & 0xffu);
-      }
-      if (lane == 0) {
-        a.k_scale[nb / D + new_row] = n8.ks;
-        a.v_scale[nb / D + new_row] = n8.vs;
-      }
-    }
-  } else if (new_mine) {
-    const int64_t nb = base_of(new_blk, kFull ? page_row[new_blk] : 0);
-    if (nb >= 0) {
-      if (c16 == new_row) {
-#pragma unroll
-        for (int m = 0; m < KS; ++m)
-          *reinterpret_cast<u32x4*>(a.k_pool_w + nb + 8 * (64 * m + lane)) = nt.k[m];
-      }
-      if (q4 == (new_row >> 2)) {
-        uint16_t* vb = a.v_pool_w + nb;
-#pragma unroll
-        for (int p = 0; p < D / 32; ++p) {
-          vb[v_elem(new_row, 32 * p + c16)] = static_cast<uint16_t>(nt.v[2 * p]);
-          vb[v_elem(new_row, 32 * p + 16 + c16)] = static_cast<uint16_t>(nt.v[2 * p + 1]);
-        }
-      }
-    }
-  }
+  store_new();
 
   // Merge the four waves.
   l_run = group4_sum(l_run);

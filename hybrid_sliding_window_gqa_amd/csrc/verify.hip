@@ -103,6 +103,11 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
   const int nq = a.nq;
 
   const int len = a.kv_len[b];
+  // The SWA ring id is read beside the length (one memory round trip), and
+  // the pointers the first loads need are fetched in the same batch; the
+  // compiler-only statement keeps them above the branch below.
+  const int ring_id = kFull ? 0 : a.table[b];
+  if constexpr (!kFull) asm volatile("" ::"s"(ring_id), "s"(a.q), "s"(a.k_pool), "s"(a.v_pool));
   const int t0 = len - nq;   // position of the first new token
   if (t0 < 0) {
     // kv_len below nq: no valid query position; rows are zero, LSE -inf.
@@ -131,9 +136,8 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
     last = (t0 >= W) ? W / kBlock : (t0 + kBlock - 1) / kBlock;   // ring blocks with a written slot
   }
   if (split >= nsplit) return;
-  int ring = 0;
+  const int ring = ring_id;
   if constexpr (!kFull) {
-    ring = a.table[b];
     if (ring < 0 || ring >= a.num_blocks) last = first;  // invalid ring id: no history
   }
   const int32_t* page_row = a.table + static_cast<int64_t>(b) * a.table_stride;
@@ -175,11 +179,22 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
     const int i = c / G;
     const bool ok = i < nq;
     tcol[gr] = ok ? t0 + i : -0x40000000;
-    const int64_t qoff = ((static_cast<int64_t>(b) * nq + (ok ? i : 0)) * hq + g * G + c % G) * D + 8 * q4;
+    if constexpr (kF32) {
+      const int64_t qoff = ((static_cast<int64_t>(b) * nq + (ok ? i : 0)) * hq + g * G + c % G) * D + 8 * q4;
 #pragma unroll
-    for (int m = 0; m < KS; ++m) {
-      qop[gr][m] = load8_as_bf16<kF32>(a.q, qoff + 32 * m);
-      if (!ok) qop[gr][m] = u32x4{0u, 0u, 0u, 0u};
+      for (int m = 0; m < KS; ++m) {
+        qop[gr][m] = load8_as_bf16<kF32>(a.q, qoff + 32 * m);
+        if (!ok) qop[gr][m] = u32x4{0u, 0u, 0u, 0u};
+      }
+    } else {
+      // One buffer over the sequence's nq query rows; padding columns read
+      // past its end and get zeros from the range check (no select that
+      // would wait for the load).
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const uint16_t*>(a.q) + static_cast<int64_t>(b) * nq * hq * D,
+                                                  static_cast<uint32_t>(nq * hq * D * 2));
+      const uint32_t off = ok ? 2u * static_cast<uint32_t>((i * hq + g * G + c % G) * D + 8 * q4) : 0x40000000u;
+#pragma unroll
+      for (int m = 0; m < KS; ++m) qop[gr][m] = buf_load16(rq, off + 64 * m);
     }
   }
 
@@ -245,27 +260,48 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
   // the history loads rather than following them.
   const bool has_new = split == 0 && wave == 0;
   VBlock<D> N;
+  // V^T operand of the new block: lane (q4, c16), dim tile d holds tokens
+  // 4 q4 .. 4 q4 + 3 of channel 16 d + c16. Packed only right before the
+  // block is consumed, so that no wait on these loads precedes the history
+  // loads.
+  uint32_t vb[4][DT];
   if (has_new) {
-    const bool krow = c16 < nq;
-    const int64_t ksrc = ((static_cast<int64_t>(b) * nq + (krow ? c16 : 0)) * hkv + g) * D + 8 * q4;
+    if constexpr (kF32) {
+      const bool krow = c16 < nq;
+      const int64_t ksrc = ((static_cast<int64_t>(b) * nq + (krow ? c16 : 0)) * hkv + g) * D + 8 * q4;
 #pragma unroll
-    for (int m = 0; m < KS; ++m) {
-      N.k[m] = load8_as_bf16<kF32>(a.k_new, ksrc + 32 * m);
-      if (!krow) N.k[m] = u32x4{0u, 0u, 0u, 0u};
+      for (int m = 0; m < KS; ++m) {
+        N.k[m] = load8_as_bf16<kF32>(a.k_new, ksrc + 32 * m);
+        if (!krow) N.k[m] = u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = 4 * q4 + r;
+        const bool ok = tok < nq;
+        const int64_t vsrc = ((static_cast<int64_t>(b) * nq + (ok ? tok : 0)) * hkv + g) * D + c16;
+#pragma unroll
+        for (int d = 0; d < DT; ++d) vb[r][d] = ok ? bf16_at<kF32>(a.v_new, vsrc + 16 * d) : 0u;
+      }
+    } else {
+      // Buffers over the sequence's nq new rows: lanes of tokens >= nq read
+      // past the end and get zeros from the range check, so the loads need
+      // no branch or select and all of them are in flight at once.
+      const int64_t row0 = static_cast<int64_t>(b) * nq * hkv * D;
+      const uint32_t bytes = static_cast<uint32_t>(nq * hkv * D * 2);
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const uint16_t*>(a.k_new) + row0, bytes);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const uint16_t*>(a.v_new) + row0, bytes);
+      const uint32_t koff = c16 < nq ? 2u * static_cast<uint32_t>((c16 * hkv + g) * D + 8 * q4) : 0x40000000u;
+#pragma unroll
+      for (int m = 0; m < KS; ++m) N.k[m] = buf_load16(rk, koff + 64 * m);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = 4 * q4 + r;
+        const uint32_t voff = tok < nq ? 2u * static_cast<uint32_t>((tok * hkv + g) * D + c16) : 0x40000000u;
+#pragma unroll
+        for (int d = 0; d < DT; ++d)
+          vb[r][d] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rv, voff + 32 * d, 0, 0));
+      }
     }
-    // V^T operand: lane (q4, c16), dim tile d holds tokens 4 q4 .. 4 q4 + 3 of
-    // channel 16 d + c16.
-    uint32_t vb[4][DT];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tok = 4 * q4 + r;
-      const bool ok = tok < nq;
-      const int64_t vsrc = ((static_cast<int64_t>(b) * nq + (ok ? tok : 0)) * hkv + g) * D + c16;
-#pragma unroll
-      for (int d = 0; d < DT; ++d) vb[r][d] = ok ? bf16_at<kF32>(a.v_new, vsrc + 16 * d) : 0u;
-    }
-#pragma unroll
-    for (int d = 0; d < DT; ++d) N.v[d] = u32x2{vb[0][d] | (vb[1][d] << 16), vb[2][d] | (vb[3][d] << 16)};
   }
 
   // History blocks of this wave: first + wave + 4k, two in flight.
@@ -281,6 +317,8 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
     pg_a2 = page_of(ia + 2 * kVerifyWaves);
     pg_b2 = page_of(ib + 2 * kVerifyWaves);
     if (has_new) {
+#pragma unroll
+      for (int d = 0; d < DT; ++d) N.v[d] = u32x2{vb[0][d] | (vb[1][d] << 16), vb[2][d] | (vb[3][d] << 16)};
       int kpn[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) kpn[r] = (4 * q4 + r < nq) ? t0 + 4 * q4 + r : -1;
