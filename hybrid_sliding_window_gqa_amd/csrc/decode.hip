@@ -673,14 +673,16 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
 // when there is more than one split (the reduce launch and the partial rows,
 // about 8 blocks' worth at full load on MI355X). Equal workgroups and whole rounds avoid
 // a tail of partly idle CUs. When one split per sequence cannot give every
-// CU two workgroups, workgroups are capped at 256 blocks (2 MiB of K/V) so
-// ragged batches still spread over the chip.
+// CU two workgroups, workgroups are capped at 208 blocks (1.6 MiB of K/V) so
+// ragged batches still spread over the chip. (Ragged decode workload, 24
+// sequences of 1K to 1M tokens, full-layer call on one MI355X: 224 splits
+// of up to 256 blocks 2651 us; 255 to 320 splits 2547 to 2575 us.)
 int decode_split_blocks(bool full, int window, int max_kv_len, int batch, int hkv, int requested_splits) {
   if (!full) return window / kBlock;
   const int nblk = (max(max_kv_len, 1) + kBlock - 1) / kBlock;
   if (requested_splits > 0) return max(1, (nblk + requested_splits - 1) / requested_splits);
   constexpr int64_t kSlots = 256 * 2;
-  constexpr int kMaxBlocks = 256, kMinBlocks = 4, kFixedCost = 4, kMergeCost = 8;
+  constexpr int kMaxBlocks = 208, kMinBlocks = 4, kFixedCost = 4, kMergeCost = 8;
   const int64_t pairs = static_cast<int64_t>(max(batch, 1)) * max(hkv, 1);
   const int s_lo = pairs >= kSlots ? 1 : max(1, (nblk + kMaxBlocks - 1) / kMaxBlocks);
   const int s_hi = min(max(s_lo, nblk / kMinBlocks), s_lo + 512);
