@@ -198,6 +198,29 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
     }
   }
 
+  // The new tokens' K/V elements this thread appends after the merge
+  // (element e = threadIdx.x + 256 j of the nq x D rows), loaded up front so
+  // that their latency overlaps the attention instead of following the
+  // merge. Elements past nq x D read past the buffer's end and get zeros.
+  constexpr int kAppendRegs = 4;
+  uint32_t app_k[kAppendRegs], app_v[kAppendRegs];
+  const bool app_pre = !kF32 && split == 0 && nq * D <= kAppendRegs * 64 * kVerifyWaves;
+  if constexpr (!kF32) {
+    if (app_pre) {
+      const int64_t row0 = static_cast<int64_t>(b) * nq * hkv * D;
+      const uint32_t bytes = static_cast<uint32_t>(nq * hkv * D * 2);
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const uint16_t*>(a.k_new) + row0, bytes);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const uint16_t*>(a.v_new) + row0, bytes);
+#pragma unroll
+      for (int j = 0; j < kAppendRegs; ++j) {
+        const int e = threadIdx.x + 64 * kVerifyWaves * j;
+        const uint32_t off = e < nq * D ? 2u * static_cast<uint32_t>(((e / D) * hkv + g) * D + e % D) : 0x40000000u;
+        app_k[j] = __builtin_amdgcn_raw_buffer_load_b16(rk, off, 0, 0);
+        app_v[j] = __builtin_amdgcn_raw_buffer_load_b16(rv, off, 0, 0);
+      }
+    }
+  }
+
   const float sl2 = a.geo.scale * kLog2e;
   ColState<D> st[NG];
 #pragma unroll
@@ -264,7 +287,7 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
   // 4 q4 .. 4 q4 + 3 of channel 16 d + c16. Packed only right before the
   // block is consumed, so that no wait on these loads precedes the history
   // loads.
-  uint32_t vb[4][DT];
+  uint16_t vb[4][DT];
   if (has_new) {
     if constexpr (kF32) {
       const bool krow = c16 < nq;
@@ -280,7 +303,7 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
         const bool ok = tok < nq;
         const int64_t vsrc = ((static_cast<int64_t>(b) * nq + (ok ? tok : 0)) * hkv + g) * D + c16;
 #pragma unroll
-        for (int d = 0; d < DT; ++d) vb[r][d] = ok ? bf16_at<kF32>(a.v_new, vsrc + 16 * d) : 0u;
+        for (int d = 0; d < DT; ++d) vb[r][d] = ok ? static_cast<uint16_t>(bf16_at<kF32>(a.v_new, vsrc + 16 * d)) : 0;
       }
     } else {
       // Buffers over the sequence's nq new rows: lanes of tokens >= nq read
@@ -299,7 +322,7 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
         const uint32_t voff = tok < nq ? 2u * static_cast<uint32_t>((tok * hkv + g) * D + c16) : 0x40000000u;
 #pragma unroll
         for (int d = 0; d < DT; ++d)
-          vb[r][d] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rv, voff + 32 * d, 0, 0));
+          vb[r][d] = __builtin_amdgcn_raw_buffer_load_b16(rv, voff + 32 * d, 0, 0);
       }
     }
   }
@@ -317,8 +340,22 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
     pg_a2 = page_of(ia + 2 * kVerifyWaves);
     pg_b2 = page_of(ib + 2 * kVerifyWaves);
     if (has_new) {
+      // Compiler-only: the values pass through these statements after the
+      // history loads above are issued, so the packing (and its wait for the
+      // new-token loads) cannot be hoisted in front of them.
 #pragma unroll
-      for (int d = 0; d < DT; ++d) N.v[d] = u32x2{vb[0][d] | (vb[1][d] << 16), vb[2][d] | (vb[3][d] << 16)};
+      for (int r = 0; r < 4; ++r) {
+        static_assert(DT == 4 || DT == 8, "pinned as 8 or 4 registers per token");
+        if constexpr (DT == 8)
+          asm volatile("" : "+v"(vb[r][0]), "+v"(vb[r][1]), "+v"(vb[r][2]), "+v"(vb[r][3]), "+v"(vb[r][4]),
+                       "+v"(vb[r][5]), "+v"(vb[r][6]), "+v"(vb[r][7])::"memory");
+        else
+          asm volatile("" : "+v"(vb[r][0]), "+v"(vb[r][1]), "+v"(vb[r][2]), "+v"(vb[r][3])::"memory");
+      }
+#pragma unroll
+      for (int d = 0; d < DT; ++d)
+        N.v[d] = u32x2{static_cast<uint32_t>(vb[0][d]) | (static_cast<uint32_t>(vb[1][d]) << 16),
+                       static_cast<uint32_t>(vb[2][d]) | (static_cast<uint32_t>(vb[3][d]) << 16)};
       int kpn[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) kpn[r] = (4 * q4 + r < nq) ? t0 + 4 * q4 + r : -1;
@@ -403,26 +440,35 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
   }
 
   // Append the new tokens (split 0; every read of this workgroup is done).
-  if (split == 0) {
+  auto append_elem = [&](int e, uint32_t kv, uint32_t vv) {
+    const int j = e / D;
+    const int dd = e - j * D;
+    const int p = t0 + j;
+    int64_t blk;
+    if constexpr (kFull) {
+      const int lb = p / kBlock;
+      const int pg = lb < a.table_stride ? page_row[lb] : -1;
+      if (pg < 0 || pg >= a.num_blocks) return;
+      blk = (static_cast<int64_t>(pg) * hkv + g) * kBlock * D;
+    } else {
+      if (ring < 0 || ring >= a.num_blocks) return;
+      const int s = p % W;
+      blk = ((static_cast<int64_t>(ring) * hkv + g) * W + kBlock * (s / kBlock)) * D;
+    }
+    const int row = p % kBlock;
+    a.k_pool_w[blk + k_elem(row, dd)] = static_cast<uint16_t>(kv);
+    a.v_pool_w[blk + v_elem(row, dd)] = static_cast<uint16_t>(vv);
+  };
+  if (app_pre) {
+#pragma unroll
+    for (int j = 0; j < kAppendRegs; ++j) {
+      const int e = threadIdx.x + 64 * kVerifyWaves * j;
+      if (e < nq * D) append_elem(e, app_k[j], app_v[j]);
+    }
+  } else if (split == 0) {
     for (int e = threadIdx.x; e < nq * D; e += blockDim.x) {
-      const int j = e / D;
-      const int dd = e - j * D;
-      const int p = t0 + j;
-      int64_t blk;
-      if constexpr (kFull) {
-        const int lb = p / kBlock;
-        const int pg = lb < a.table_stride ? page_row[lb] : -1;
-        if (pg < 0 || pg >= a.num_blocks) continue;
-        blk = (static_cast<int64_t>(pg) * hkv + g) * kBlock * D;
-      } else {
-        if (ring < 0 || ring >= a.num_blocks) continue;
-        const int s = p % W;
-        blk = ((static_cast<int64_t>(ring) * hkv + g) * W + kBlock * (s / kBlock)) * D;
-      }
-      const int row = p % kBlock;
-      const int64_t src = ((static_cast<int64_t>(b) * nq + j) * hkv + g) * D + dd;
-      a.k_pool_w[blk + k_elem(row, dd)] = static_cast<uint16_t>(bf16_at<kF32>(a.k_new, src));
-      a.v_pool_w[blk + v_elem(row, dd)] = static_cast<uint16_t>(bf16_at<kF32>(a.v_new, src));
+      const int64_t src = ((static_cast<int64_t>(b) * nq + e / D) * hkv + g) * D + e % D;
+      append_elem(e, bf16_at<kF32>(a.k_new, src), bf16_at<kF32>(a.v_new, src));
     }
   }
 }
