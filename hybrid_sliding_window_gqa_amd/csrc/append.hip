@@ -79,6 +79,85 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
 }
 
+// Full pools, prefill-sized appends: one workgroup per (16-token page block
+// of a sequence's appended range, all kv heads). Each K row chunk is one
+// 16-byte store; V goes through LDS so that a 16-byte V unit (4 tokens x 2
+// channels) whose four slots are all appended in this call is written with
+// one store, where append_kernel needs eight 2-byte stores. Units with a slot
+// outside the appended range (at its first and last block) keep that slot
+// and get 2-byte stores for the others. The slots written, and their values,
+// are exactly append_kernel's.
+template <bool kF32>
+__global__ __launch_bounds__(256) void append_pages_kernel(AppendArgs a) {
+  __shared__ uint16_t tile[kBlock][128 + 2];   // one head's V rows (D <= 128)
+  const int d = a.geo.d;
+  const int hkv = a.geo.hkv;
+  const int cpr = d >> 3;                       // 16-byte chunks per row
+  const int b = blockIdx.y;
+  const int tok_b = a.cu_new[b];
+  const int n = min(a.cu_new[b + 1], a.num_tokens) - tok_b;   // rows past num_tokens are never read
+  const int64_t p0 = a.pos0[b];
+  const int64_t start = p0 > 0 ? p0 : 0;       // positions below 0 are dropped
+  const int64_t end = p0 + n;
+  if (tok_b < 0 || start >= end) return;
+  const int64_t jb = (start >> 4) + blockIdx.x; // page index in the table row
+  const int64_t lo = max(start, jb * kBlock), hi = min(end, jb * kBlock + kBlock);
+  if (lo >= hi || jb >= a.table_stride) return;
+  const int pg = a.table[static_cast<int64_t>(b) * a.table_stride + jb];
+  if (pg < 0 || pg >= a.num_blocks) return;
+  const int first = static_cast<int>(lo - jb * kBlock);   // slots [first, last) are appended
+  const int last = static_cast<int>(hi - jb * kBlock);
+  const int64_t tok_slot0 = tok_b + (jb * kBlock - p0);   // token index of slot 0
+  const int tid = threadIdx.x;
+  for (int g = 0; g < hkv; ++g) {
+    const int64_t blk = (static_cast<int64_t>(pg) * hkv + g) * kBlock * d;
+    for (int e = tid; e < kBlock * cpr; e += blockDim.x) {
+      const int key = e / cpr;
+      const int col = e - key * cpr;
+      if (key < first || key >= last) continue;
+      const int64_t src = ((tok_slot0 + key) * hkv + g) * d + col * 8;
+      *reinterpret_cast<u32x4*>(a.k_pool + blk + k_elem(key, col * 8)) = load8_as_bf16<kF32>(a.k_new, src);
+      const u32x4 vv = load8_as_bf16<kF32>(a.v_new, src);
+      const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        tile[key][col * 8 + 2 * j] = static_cast<uint16_t>(w4[j] & 0xffffu);
+        tile[key][col * 8 + 2 * j + 1] = static_cast<uint16_t>(w4[j] >> 16);
+      }
+    }
+    __syncthreads();
+    // V unit e = (p, q, c): tokens 4q..4q+3 of channels 32p + c and 32p + 16 + c
+    for (int e = tid; e < 2 * d; e += blockDim.x) {
+      const int p = e / 64;
+      const int q = (e / 16) & 3;
+      const int c = e & 15;
+      if (4 * q + 3 < first || 4 * q >= last) continue;
+      if (4 * q >= first && 4 * q + 3 < last) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int ch = 32 * p + 16 * h + c;
+          w4[2 * h] = static_cast<uint32_t>(tile[4 * q][ch]) | (static_cast<uint32_t>(tile[4 * q + 1][ch]) << 16);
+          w4[2 * h + 1] = static_cast<uint32_t>(tile[4 * q + 2][ch]) | (static_cast<uint32_t>(tile[4 * q + 3][ch]) << 16);
+        }
+        *reinterpret_cast<u32x4*>(a.v_pool + blk + 8 * e) = u32x4{w4[0], w4[1], w4[2], w4[3]};
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = 4 * q + r;
+          if (key < first || key >= last) continue;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int ch = 32 * p + 16 * h + c;
+            a.v_pool[blk + v_elem(key, ch)] = tile[key][ch];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // INT8 pools: the same thread mapping; the chunks/lanes of one (token, kv
 // head) row are consecutive lanes of a wave, so the row's absmax is a
 // butterfly over them. scale = amax / 127 and code = rint(x / scale), both
@@ -243,7 +322,18 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
   const int64_t blocks = (total + threads - 1) / threads;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks));
-  if (a.kv8) {
+  // Full pools with at least 16 new tokens per sequence on average: one
+  // workgroup per page block (grid.x bounds the blocks any one sequence's
+  // range can touch; workgroups past a sequence's range exit at once).
+  const bool by_pages = a.full && !a.kv8 && a.geo.d <= 128 &&
+                        static_cast<int64_t>(a.num_tokens) >= static_cast<int64_t>(kBlock) * a.batch;
+  if (by_pages) {
+    const int64_t gx = (static_cast<int64_t>(a.num_tokens) + kBlock - 1) / kBlock + 1;
+    if (gx > 0x7fffffff || a.batch > 65535) return hipErrorInvalidValue;
+    const dim3 pgrid(static_cast<unsigned>(gx), a.batch);
+    if (a.src_f32) hipLaunchKernelGGL(append_pages_kernel<true>, pgrid, dim3(threads), 0, stream, a);
+    else hipLaunchKernelGGL(append_pages_kernel<false>, pgrid, dim3(threads), 0, stream, a);
+  } else if (a.kv8) {
     if (a.src_f32) hipLaunchKernelGGL(append8_kernel<true>, grid, dim3(threads), 0, stream, a);
     else hipLaunchKernelGGL(append8_kernel<false>, grid, dim3(threads), 0, stream, a);
   } else if (a.src_f32) {
