@@ -6,7 +6,8 @@ import pytest
 import torch
 
 import hybrid_sliding_window_gqa_amd as ha
-from gpu_util import append_history, check_pages, check_ring, host, i32, make_generator, page_blocks, randn_bf16
+from gpu_util import DEV, append_history, check_pages, check_ring, host, i32, make_generator, page_blocks, randn_bf16
+from oracle.indexing import page_location
 
 pytestmark = pytest.mark.gpu
 
@@ -100,3 +101,61 @@ def test_out_of_range_ids_are_dropped():
     np.testing.assert_array_equal(kb[1], k[48:64, 0])
     assert torch.isnan(pool.k[0].float()).all() and torch.isnan(pool.k[3].float()).all()
     assert torch.isnan(ring.k.float()).all()
+
+
+@pytest.mark.parametrize("src", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("hkv,d", [(2, 64), (8, 128)])
+def test_page_block_append_matches_row_append(src, hkv, d):
+    """A full-pool call that brings at least 16 tokens per sequence on average
+    is written page block by page block; the same call with the batch padded
+    by empty sequences takes the per-row path. Both must write the same
+    slots with the same bits (untouched slots keep their NaN), and those
+    slots must be where the oracle's page model puts each position.
+    Starts are unaligned, page-aligned and negative (positions below 0 are
+    dropped); float32 sources are rounded to bfloat16 on the way."""
+    shape = ha.HeadShape(hkv * 4, hkv, d)
+    gen = make_generator(404 + d + hkv)
+    rng = np.random.default_rng(9)
+    starts = [0, 5, 16, 37, -3]
+    counts = [40, 11, 64, 100, 30]
+    ends = [s + c for s, c in zip(starts, counts)]
+    pages_per = [-(-max(e, 0) // 16) for e in ends]
+    num_pages = sum(pages_per) + 5
+    perm = rng.permutation(num_pages)
+    stride = max(pages_per) + 1
+    table = np.full((len(starts), stride), -1, np.int32)
+    off = 0
+    for b, c in enumerate(pages_per):
+        table[b, :c] = perm[off:off + c]
+        off += c
+    total = sum(counts)
+    k_new = torch.randn(total, hkv, d, generator=gen, device=DEV)
+    v_new = torch.randn(total, hkv, d, generator=gen, device=DEV)
+    if src == torch.bfloat16:
+        k_new, v_new = k_new.to(torch.bfloat16), v_new.to(torch.bfloat16)
+    expect_k, expect_v = host(k_new.to(torch.bfloat16)), host(v_new.to(torch.bfloat16))
+    cu = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    pad = 4 * len(starts)                      # average falls below 16 tokens per sequence
+    pools = []
+    for extra in (0, pad):
+        pool = ha.FullPagePool(shape, num_pages, device=DEV, fill=float("nan"))
+        tab = np.concatenate([table, np.full((extra, stride), -1, np.int32)])
+        pos0 = np.concatenate([starts, np.zeros(extra, np.int32)])
+        cu_b = np.concatenate([cu, np.full(extra, total, np.int32)])
+        ha.full_pool_append(shape, pool.view(i32(tab)), i32(pos0), i32(cu_b), k_new.contiguous(), v_new.contiguous())
+        pools.append(pool)
+    torch.cuda.synchronize()
+    a, b_ = pools
+    assert torch.equal(a.k.view(torch.int16), b_.k.view(torch.int16))
+    assert torch.equal(a.v.view(torch.int16), b_.v.view(torch.int16))
+    written = np.zeros((num_pages, 16), bool)
+    for g in range(hkv):
+        kb, vb = page_blocks(a, g)
+        for b in range(len(starts)):
+            pos = np.arange(max(starts[b], 0), ends[b])
+            pages, offs = page_location(table[b], pos, 16)
+            rows = cu[b] + (pos - starts[b])
+            np.testing.assert_array_equal(kb[pages, offs], expect_k[rows, g])
+            np.testing.assert_array_equal(vb[pages, offs], expect_v[rows, g])
+            written[pages, offs] = True
+        assert np.isnan(kb[~written]).all() and np.isnan(vb[~written]).all()
