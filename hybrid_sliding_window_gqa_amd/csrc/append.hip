@@ -116,8 +116,8 @@ __global__ __launch_bounds__(256) void append_pages_kernel(AppendArgs a) {
       const int col = e - key * cpr;
       if (key < first || key >= last) continue;
       const int64_t src = ((tok_slot0 + key) * hkv + g) * d + col * 8;
-      *reinterpret_cast<u32x4*>(a.k_pool + blk + k_elem(key, col * 8)) = load8_as_bf16<kF32>(a.k_new, src);
-      const u32x4 vv = load8_as_bf16<kF32>(a.v_new, src);
+      *reinterpret_cast<u32x4*>(a.k_pool + blk + k_elem(key, col * 8)) = load8_as_bf16_stream<kF32>(a.k_new, src);
+      const u32x4 vv = load8_as_bf16_stream<kF32>(a.v_new, src);
       const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {

@@ -152,8 +152,8 @@ __global__ __launch_bounds__(256) void stage_chunk_kernel(PrefillArgs a) {
       u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
       if (ci < n) {
         const int64_t off = (static_cast<int64_t>(tok0 + ci) * hkv + g) * D + col * 8;
-        kv = load8_as_bf16<kF32>(a.k_new, off);
-        vv = load8_as_bf16<kF32>(a.v_new, off);
+        kv = load8_as_bf16_stream<kF32>(a.k_new, off);
+        vv = load8_as_bf16_stream<kF32>(a.v_new, off);
       }
       *reinterpret_cast<u32x4*>(ws_k + g * blk_elems + k_elem(key, col * 8)) = kv;
       const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
