@@ -15,6 +15,11 @@ Default run (prints ONE JSON line on stdout):
            4*D flops per visible (query head, key) pair.
   roofline achieved/peak of the dominant kernel (the full-layer decode
            call), timed with HIP events on the launch stream.
+  verify, int8_kv, ragged, reuse
+           the decode pools with 4 new tokens per sequence; the decode step
+           on INT8 pools; ragged long-context decode (24 sequences, 1K to 1M
+           cached tokens, split-K); prefix-reuse prefill (32 sequences,
+           window-safe reuse) -- each skippable with --no-<name>.
   cpu_baseline  the fp64 oracle on a bounded sample of the decode step.
 
 Inputs are synthetic and resident in HBM before timing starts. Options select
@@ -59,6 +64,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-verify", action="store_true", help="skip the multi-token verify part")
     p.add_argument("--no-int8", action="store_true", help="skip the INT8-pool decode part")
+    p.add_argument("--no-ragged", action="store_true", help="skip the ragged long-context decode part")
+    p.add_argument("--no-reuse", action="store_true", help="skip the prefix-reuse prefill part")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU sample")
     p.add_argument("--cpu-prefill-seconds", type=float, default=10.0,
                    help="target oracle time for the prefill CPU sample")
@@ -958,6 +965,27 @@ def main():
         line["int8_kv"] = {k: q8[k] for k in ("value", "unit", "ms_per_step", "tokens_per_s", "pct_peak_hbm",
                                               "workload", "full_call_us", "full_call_gbs", "full_call_frac",
                                               "swa_call_us", "append_call_us")}
+    if args.workload == "decode" and not args.no_ragged:
+        log("[bench] ragged long-context decode")
+        torch.cuda.empty_cache()        # its 17.7 GB of pools come from fresh allocations
+        rstruct = synth.ragged_structure()
+        _, rgroup, rdata, rdt, rbytes, _, rinfo = run_decode(torch, ha, grp, synth, rstruct, args, device)
+        line["ragged"] = {
+            "value": round(rbytes / rdt / 1e9, 2), "unit": "GB/s", "ms_per_step": round(rdt * 1e3, 4),
+            "pct_peak_hbm": round(100.0 * rbytes / rdt / 1e9 / HBM_PEAK_GBS, 2),
+            "workload": (f"ragged decode: {rstruct.batch} sequences, cached lengths 12xU[1K,64K] 8xU[64K,256K] "
+                         f"4xU[256K,1M] (total {int(rstruct.hist.sum())}), one 6:1 group, split-K over full pages"),
+            "full_call_gbs": round(rinfo["full_decode_gbs"], 2), "splits_full": rinfo["splits_full"],
+        }
+        del rgroup, rdata
+        torch.cuda.empty_cache()
+    if args.workload == "decode" and not args.no_reuse:
+        log("[bench] prefix-reuse prefill")
+        ru = run_reuse(torch, ha, grp, synth, args, device)
+        line["reuse"] = {k: ru[k] for k in ("workload", "pass_ms", "tflops", "pct_mfma_peak", "full_layer_tflops",
+                                            "mean_recomputed_tail")}
+        line["reuse"]["full_layer_frac"] = ru["roofline"]["frac"]
+        torch.cuda.empty_cache()
     if args.workload == "decode" and not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(torch, shape, group, data, args.cpu_seconds)
