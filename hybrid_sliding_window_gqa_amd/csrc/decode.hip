@@ -126,6 +126,9 @@ __device__ __forceinline__ void consume_block(BlockOps<D>& ops, const u32x4* qop
   for (int d = 0; d < DT; ++d) o[d] = mfma_16x16x16(ops.v[d], pb, o[d]);
 }
 
+// Slack of the INT8 path's exp2 reference (log2 units); see consume_block8.
+constexpr float kDecodeSlack = 8.0f;
+
 // INT8 pools: the raw 16-byte units of one block (K: D/64 units holding two
 // 32-channel slices each; V: D/64 units holding four 16-channel tiles each)
 // and the 4 K and 4 V scales of this lane's keys 4*q4 .. 4*q4+3.
@@ -202,17 +205,24 @@ __device__ __forceinline__ void consume_block8(const RawBlock8<D>& raw, const u3
       vs[r] = ok ? vs[r] : 0.0f;
     }
   }
+  // The exp2 reference m_run is raised only when a column's block max exceeds
+  // it by more than kDecodeSlack (log2 units), so probabilities stay at most
+  // 2^kDecodeSlack and O and l are rescaled only on those blocks, not on
+  // every block: the widening already makes this path the vector-heavier one.
   const float tmax = group4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))) * sl2;
-  const float m_new = fmaxf(m_run, tmax);
-  const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-  const float alpha = fast_exp2(m_run - m_use);
+  if (__any(tmax > m_run + kDecodeSlack)) {
+    const float m_new = (tmax > m_run + kDecodeSlack) ? tmax : m_run;
+    const float alpha = (m_new == m_run) ? 1.0f : (m_run == -INFINITY ? 0.0f : fast_exp2(m_run - m_new));
+    l_run *= alpha;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) o[d] *= alpha;
+    m_run = m_new;
+  }
+  const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
   float p[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s[r] * sl2 - m_use);
-  l_run = l_run * alpha + (p[0] + p[1]) + (p[2] + p[3]);
-  m_run = m_new;
-#pragma unroll
-  for (int d = 0; d < DT; ++d) o[d] *= alpha;
+  l_run += (p[0] + p[1]) + (p[2] + p[3]);
   const u32x2 pb = {pack_bf16x2(p[0] * vs[0], p[1] * vs[1]), pack_bf16x2(p[2] * vs[2], p[3] * vs[3])};
 #pragma unroll
   for (int d = 0; d < DT; ++d) o[d] = mfma_16x16x16(ops.v[d], pb, o[d]);
