@@ -38,6 +38,8 @@ namespace ha {
 namespace {
 
 constexpr int kVerifyWaves = 4;
+// Slack of the exp2 reference (log2 units); see the consume step.
+constexpr float kVerifySlack = 8.0f;
 
 template <int D>
 struct VBlock {
@@ -234,16 +236,19 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
   // One block: keys at positions kp[r] (key 4 q4 + r; -1: no key), shared
   // by every column group.
   auto consume = [&](VBlock<D>& ops, const int (&kp)[4]) {
-    // zero V of keys that do not exist (their pool slots may hold anything)
-    uint32_t keep[4];
+    // zero V of keys that do not exist (their pool slots may hold anything);
+    // blocks whose keys all exist (every full history block) skip it
+    if (!__all(kp[0] >= 0 && kp[1] >= 0 && kp[2] >= 0 && kp[3] >= 0)) {
+      uint32_t keep[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) keep[r] = kp[r] >= 0 ? 0xffffu : 0u;
-    const uint32_t mlo = keep[0] | (keep[1] << 16);
-    const uint32_t mhi = keep[2] | (keep[3] << 16);
+      for (int r = 0; r < 4; ++r) keep[r] = kp[r] >= 0 ? 0xffffu : 0u;
+      const uint32_t mlo = keep[0] | (keep[1] << 16);
+      const uint32_t mhi = keep[2] | (keep[3] << 16);
 #pragma unroll
-    for (int d = 0; d < DT; ++d) {
-      ops.v[d].x &= mlo;
-      ops.v[d].y &= mhi;
+      for (int d = 0; d < DT; ++d) {
+        ops.v[d].x &= mlo;
+        ops.v[d].y &= mhi;
+      }
     }
 #pragma unroll
     for (int gr = 0; gr < NG; ++gr) {
@@ -257,17 +262,24 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
         s[r] = ok ? s[r] : -INFINITY;
       }
       ColState<D>& cs = st[gr];
+      // The exp2 reference is raised only when a column's block max passes it
+      // by more than kVerifySlack (log2 units): probabilities stay at most
+      // 2^kVerifySlack, and O and l are rescaled on those blocks only.
       const float tmax = group4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))) * sl2;
-      const float m_new = fmaxf(cs.m_run, tmax);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = fast_exp2(cs.m_run - m_use);
+      if (__any(tmax > cs.m_run + kVerifySlack)) {
+        const float m_new = (tmax > cs.m_run + kVerifySlack) ? tmax : cs.m_run;
+        const float alpha =
+            (m_new == cs.m_run) ? 1.0f : (cs.m_run == -INFINITY ? 0.0f : fast_exp2(cs.m_run - m_new));
+        cs.l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < DT; ++d) cs.o[d] *= alpha;
+        cs.m_run = m_new;
+      }
+      const float m_use = (cs.m_run == -INFINITY) ? 0.0f : cs.m_run;
       float p[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s[r] * sl2 - m_use);
-      cs.l_run = cs.l_run * alpha + (p[0] + p[1]) + (p[2] + p[3]);
-      cs.m_run = m_new;
-#pragma unroll
-      for (int d = 0; d < DT; ++d) cs.o[d] *= alpha;
+      cs.l_run += (p[0] + p[1]) + (p[2] + p[3]);
       const u32x2 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
 #pragma unroll
       for (int d = 0; d < DT; ++d) cs.o[d] = mfma_16x16x16(ops.v[d], pb, cs.o[d]);
