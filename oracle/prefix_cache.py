@@ -17,19 +17,27 @@ the set of such tuples, and every question is answered by looking tuples up:
     page_of[prefix]  -> Full page id recorded for that position's page index
     src[prefix]      -> id of the ring holding that position's SWA KV
     rings[id]        -> owned flag, last use, the prefixes it holds
-Rules (the same ones include/prefix_tree.h states):
-  - insert: positions not cached yet take the caller's page for their page
-    index; cached positions keep theirs. The ring first drops positions
-    below ring_len - W, then claims positions [ring_len - W, ring_len) below
-    n: a position without a source takes it; a position whose source is live
-    takes it only when this ring is handed over; otherwise it keeps its source.
-  - match: m = longest cached prefix; validity and ring per position < m;
-    page of index i = page_of of position min(m, (i + 1) * ps) - 1.
-  - advance / release: a live ring drops positions below new_len - W / all.
-  - SWA eviction: handed-over rings in order of (last use, id).
-  - clock: one tick per insert and per match; an insert marks its ring used,
+The pages fix what the cache must answer (a match whose SWA map feeds the
+window-safe rule; Full and SWA parts evicted independently; SWA eviction tied
+to the request's lifecycle, so a ring never names more than W positions) but
+not who owns which KV or in which order rings leave. The rules below are the
+plainest readings that fit, each pinned by hand-worked cases in
+tests/golden/prefix_cache_cases.json (reading ids as given there):
+  - R19, SWA sources: a request's ring holds its last W positions. A position
+    has one source: a position without one takes the inserting ring; a
+    position held by a live ring moves to a ring that is handed over (the
+    live one will move on, the handed-over one stays); otherwise the first
+    source stays. A ring that already held positions keeps only its window
+    at ring_len.
+  - R20, pages: paths are token-granular; a cached position keeps its page,
+    a new position takes the caller's page for its page index. The match
+    reports, for page index i, the page of position min(m, (i + 1) * ps) - 1.
+  - R21, lifecycle: a live ring drops positions below new_len - W when its
+    request advances and all of them on release; handed-over rings leave only
+    by SWA eviction, least recently used first, ties by lower ring id. The
+    clock ticks once per insert and per match; an insert marks its ring used,
     a match marks every ring it reports.
-Full eviction (whole least-recently-used leaves) depends on where the tree's
+Full eviction (whole least-recently-used leaves) depends on where a tree's
 nodes are split and is not modelled: tests check its invariants and re-sync
 this model from the tree's answers with forget().
 """
@@ -62,6 +70,8 @@ class PrefixCacheModel:
     def insert(self, tokens, pages, ring_id=-1, ring_len=0, transfer=False):
         tokens = [int(t) for t in tokens]
         n = len(tokens)
+        if ring_id >= 0 and ring_id in self.rings and self.rings[ring_id]["owned"]:
+            raise ValueError("ring belongs to the tree")   # refused: nothing changes
         self.clock += 1
         for q in range(n):
             key = tuple(tokens[: q + 1])
@@ -69,8 +79,6 @@ class PrefixCacheModel:
                 self.page_of[key] = int(pages[q // self.ps])
         ring_kept = False
         if ring_id >= 0:
-            if ring_id in self.rings and self.rings[ring_id]["owned"]:
-                raise ValueError("ring belongs to the tree")
             ring = self.rings.setdefault(ring_id, {"owned": False, "use": 0, "held": set()})
             ring["owned"] = bool(transfer)
             ring["use"] = self.clock
