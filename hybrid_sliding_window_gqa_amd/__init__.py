@@ -18,6 +18,7 @@ from .api import (  # noqa: F401
     full_pool_append,
     full_pool_read,
     hybrid_attn_decode,
+    hybrid_attn_decode_noalloc,
     hybrid_attn_decode_splits,
     hybrid_attn_prefill,
     hybrid_attn_verify,

@@ -27,7 +27,10 @@ HA_FULL = 1
 HA_KV_BF16 = 0
 HA_KV_INT8 = 1
 
-ABI_VERSION = 6
+ABI_VERSION = 7
+
+# Bytes of the library-owned scratch array of hybrid_attn_decode_noalloc.
+HA_DECODE_SCRATCH_BYTES = 64 << 20
 
 # Every symbol include/*.h declares.
 EXPORTS = (
@@ -38,6 +41,7 @@ EXPORTS = (
     "window_safe_match",
     "hybrid_attn_prefill",
     "hybrid_attn_decode",
+    "hybrid_attn_decode_noalloc",
     "hybrid_attn_workspace_size",
     "hybrid_attn_decode_splits",
     "hybrid_attn_verify",
@@ -113,6 +117,7 @@ def load() -> ctypes.CDLL:
     lib.window_safe_match.argtypes = [p, i64, p, i64, p, i32, ctypes.POINTER(i64)]
     lib.hybrid_attn_prefill.argtypes = [shp, view, p, p, i32, i32, i32, p, p, p, i32, p, p, p, sz, p]
     lib.hybrid_attn_decode.argtypes = [shp, view, p, i32, i32, p, p, p, i32, p, p, i32, p, sz, p]
+    lib.hybrid_attn_decode_noalloc.argtypes = [shp, view, p, i32, i32, p, p, p, i32, p, p, i32, p]
     lib.hybrid_attn_workspace_size.argtypes = [shp, i32, i32, i32, i32, i32]
     lib.hybrid_attn_workspace_size.restype = sz
     lib.hybrid_attn_decode_splits.argtypes = [shp, i32, i32, i32, i32]
@@ -122,7 +127,7 @@ def load() -> ctypes.CDLL:
     lib.hybrid_attn_verify_workspace_size.restype = sz
     for fn in ("swa_ring_append", "full_pool_append", "swa_ring_read", "full_pool_read", "window_safe_match",
                "hybrid_attn_prefill",
-               "hybrid_attn_decode", "hybrid_attn_verify"):
+               "hybrid_attn_decode", "hybrid_attn_decode_noalloc", "hybrid_attn_verify"):
         getattr(lib, fn).restype = i32
     lib.ha_status_str.argtypes = [i32]
     lib.ha_status_str.restype = ctypes.c_char_p

@@ -366,6 +366,37 @@ def hybrid_attn_decode(shape: HeadShape, kv: KvView, kv_len: torch.Tensor, q: to
     return out, lse
 
 
+def hybrid_attn_decode_noalloc(shape: HeadShape, kv: KvView, kv_len: torch.Tensor, q: torch.Tensor,
+                               max_kv_len: int, out: torch.Tensor, lse: torch.Tensor, num_splits: int = 0,
+                               stream=None, k_new: torch.Tensor | None = None, v_new: torch.Tensor | None = None):
+    """hybrid_attn_decode for callers that cannot allocate: the caller passes
+    the outputs, and the split-K partials live in the library's static scratch
+    array (HA_DECODE_SCRATCH_BYTES per device). Nothing is allocated here or
+    in the library. Returns (out, lse)."""
+    dev = kv.k.device
+    b = kv.batch
+    hq, d = shape.num_q_heads, shape.head_dim
+    _check(kv_len, "kv_len", (b,), torch.int32, dev)
+    _check(q, "q", (b, hq, d), None, dev)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("pass both k_new and v_new (fused append) or neither")
+    if k_new is not None:
+        _check(k_new, "k_new", (b, shape.num_kv_heads, d), None, dev)
+        _check(v_new, "v_new", (b, shape.num_kv_heads, d), None, dev)
+        dt = _in_dtype(q, k_new, v_new)
+    else:
+        dt = _in_dtype(q)
+    _check(out, "out", (b, hq, d), torch.float32, dev)
+    _check(lse, "lse", (b, hq), torch.float32, dev)
+    c_shape, c_view = shape.c(), kv.c()
+    kp = k_new.data_ptr() if k_new is not None else None
+    vp = v_new.data_ptr() if v_new is not None else None
+    check(load().hybrid_attn_decode_noalloc(ctypes.byref(c_shape), ctypes.byref(c_view), kv_len.data_ptr(), b,
+                                            int(max_kv_len), q.data_ptr(), kp, vp, dt, out.data_ptr(),
+                                            lse.data_ptr(), int(num_splits), _stream_ptr(stream)))
+    return out, lse
+
+
 def hybrid_attn_verify_workspace_size(shape: HeadShape, kind: int, batch: int, max_kv_len: int, nq: int,
                                       num_splits: int = 0) -> int:
     c_shape = shape.c()

@@ -181,6 +181,85 @@ ha_status check_nq(const ha::Geometry& geo, int nq) {
   return ok();
 }
 
+// Where the split-K partials of a decode call live.
+enum class Scratch { kCallerWorkspace, kLibraryStatic };
+
+ha_status decode_common(const ha_shape* shape, const ha_kv_view* kv, const int32_t* kv_len, int32_t batch,
+                        int32_t max_kv_len, const void* q, const void* k_new, const void* v_new, int32_t in_dtype,
+                        float* out, float* lse, int32_t num_splits, Scratch where, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  ha::Geometry geo;
+  ha_status st = check_shape(shape, &geo);
+  if (st != HA_OK) return st;
+  if (batch < 0 || max_kv_len < 0 || num_splits < 0)
+    return fail(HA_ERR_RANGE, "batch, max_kv_len and num_splits must be >= 0");
+  if ((st = check_view(kv, batch)) != HA_OK) return st;
+  if ((st = check_dtype(in_dtype)) != HA_OK) return st;
+  if (batch == 0) return ok();
+  if (batch > 65535) return fail(HA_ERR_RANGE, "decode batch %d exceeds 65535", batch);
+  if (!kv_len || !q || !out || !lse) return fail(HA_ERR_NULL, "kv_len, q, out or lse is NULL");
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(HA_ERR_NULL, "k_new and v_new must both be given (fused append) or both be NULL");
+  const bool kv8 = kv->kv_dtype == HA_KV_INT8;
+  const bool full = kv->kind == HA_FULL;
+  const size_t need = decode_workspace(geo, full, batch, max_kv_len, num_splits);
+  if (where == Scratch::kCallerWorkspace) {
+    if (need > 0 && (!workspace || workspace_bytes < need))
+      return fail(HA_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need, workspace ? workspace_bytes : 0);
+  } else if (need > HA_DECODE_SCRATCH_BYTES) {
+    return fail(HA_ERR_WORKSPACE,
+                "decode needs %zu scratch bytes; the library's static scratch holds %zu: pass a smaller num_splits "
+                "or use hybrid_attn_decode with a workspace",
+                need, static_cast<size_t>(HA_DECODE_SCRATCH_BYTES));
+  }
+  ha::DecodeArgs a{};
+  a.geo = geo;
+  a.full = full;
+  a.k_pool = static_cast<const uint16_t*>(kv->k);
+  a.v_pool = static_cast<const uint16_t*>(kv->v);
+  a.num_blocks = kv->num_blocks;
+  a.table = kv->table;
+  a.table_stride = kv->table_stride;
+  a.kv_len = kv_len;
+  a.batch = batch;
+  a.q = q;
+  a.q_f32 = in_dtype == HA_F32;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_pool_w = static_cast<uint16_t*>(kv->k);
+  a.v_pool_w = static_cast<uint16_t*>(kv->v);
+  a.kv8 = kv8;
+  a.k_scale = kv->k_scale;
+  a.v_scale = kv->v_scale;
+  a.out = out;
+  a.lse = lse;
+  a.split_blocks = ha::decode_split_blocks(full, geo.window, max_kv_len, batch, geo.hkv, num_splits);
+  a.splits = ha::decode_num_splits(full, geo.window, max_kv_len, a.split_blocks);
+  if (a.splits > 65535) return fail(HA_ERR_RANGE, "too many key splits (%d); pass a smaller num_splits", a.splits);
+  if (need > 0 && where == Scratch::kLibraryStatic) {
+    // The partials go to the current device's copy of the static array; the
+    // stream must belong to that device.
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (stream != nullptr) {
+      hipDevice_t sdev = -1;
+      e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+      if (e != hipSuccess) return hip_status(e, "hipStreamGetDevice");
+      if (sdev != dev)
+        return fail(HA_ERR_RANGE, "the stream belongs to device %d, the current device is %d", sdev, dev);
+    }
+    e = ha::decode_scratch(dev, &workspace);
+    if (e != hipSuccess) return hip_status(e, "static scratch lookup");
+  }
+  if (need > 0) {
+    float* ws = static_cast<float*>(workspace);
+    a.part_o = ws;
+    a.part_lse = ws + static_cast<size_t>(batch) * geo.hq * a.splits * geo.d;
+  }
+  return hip_status(ha::launch_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
 }  // namespace
 
 namespace ha {
@@ -303,53 +382,16 @@ ha_status hybrid_attn_decode(const ha_shape* shape, const ha_kv_view* kv, const 
                              int32_t max_kv_len, const void* q, const void* k_new, const void* v_new,
                              int32_t in_dtype, float* out, float* lse, int32_t num_splits, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  ha::Geometry geo;
-  ha_status st = check_shape(shape, &geo);
-  if (st != HA_OK) return st;
-  if (batch < 0 || max_kv_len < 0 || num_splits < 0)
-    return fail(HA_ERR_RANGE, "batch, max_kv_len and num_splits must be >= 0");
-  if ((st = check_view(kv, batch)) != HA_OK) return st;
-  if ((st = check_dtype(in_dtype)) != HA_OK) return st;
-  if (batch == 0) return ok();
-  if (batch > 65535) return fail(HA_ERR_RANGE, "decode batch %d exceeds 65535", batch);
-  if (!kv_len || !q || !out || !lse) return fail(HA_ERR_NULL, "kv_len, q, out or lse is NULL");
-  if ((k_new == nullptr) != (v_new == nullptr))
-    return fail(HA_ERR_NULL, "k_new and v_new must both be given (fused append) or both be NULL");
-  const bool kv8 = kv->kv_dtype == HA_KV_INT8;
-  const bool full = kv->kind == HA_FULL;
-  const size_t need = decode_workspace(geo, full, batch, max_kv_len, num_splits);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(HA_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need, workspace ? workspace_bytes : 0);
-  ha::DecodeArgs a{};
-  a.geo = geo;
-  a.full = full;
-  a.k_pool = static_cast<const uint16_t*>(kv->k);
-  a.v_pool = static_cast<const uint16_t*>(kv->v);
-  a.num_blocks = kv->num_blocks;
-  a.table = kv->table;
-  a.table_stride = kv->table_stride;
-  a.kv_len = kv_len;
-  a.batch = batch;
-  a.q = q;
-  a.q_f32 = in_dtype == HA_F32;
-  a.k_new = k_new;
-  a.v_new = v_new;
-  a.k_pool_w = static_cast<uint16_t*>(kv->k);
-  a.v_pool_w = static_cast<uint16_t*>(kv->v);
-  a.kv8 = kv8;
-  a.k_scale = kv->k_scale;
-  a.v_scale = kv->v_scale;
-  a.out = out;
-  a.lse = lse;
-  a.split_blocks = ha::decode_split_blocks(full, geo.window, max_kv_len, batch, geo.hkv, num_splits);
-  a.splits = ha::decode_num_splits(full, geo.window, max_kv_len, a.split_blocks);
-  if (a.splits > 65535) return fail(HA_ERR_RANGE, "too many key splits (%d); pass a smaller num_splits", a.splits);
-  if (need > 0) {
-    float* ws = static_cast<float*>(workspace);
-    a.part_o = ws;
-    a.part_lse = ws + static_cast<size_t>(batch) * geo.hq * a.splits * geo.d;
-  }
-  return hip_status(ha::launch_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
+  return decode_common(shape, kv, kv_len, batch, max_kv_len, q, k_new, v_new, in_dtype, out, lse, num_splits,
+                       Scratch::kCallerWorkspace, workspace, workspace_bytes, stream);
+}
+
+ha_status hybrid_attn_decode_noalloc(const ha_shape* shape, const ha_kv_view* kv, const int32_t* kv_len,
+                                     int32_t batch, int32_t max_kv_len, const void* q, const void* k_new,
+                                     const void* v_new, int32_t in_dtype, float* out, float* lse,
+                                     int32_t num_splits, void* stream) {
+  return decode_common(shape, kv, kv_len, batch, max_kv_len, q, k_new, v_new, in_dtype, out, lse, num_splits,
+                       Scratch::kLibraryStatic, nullptr, 0, stream);
 }
 
 ha_status hybrid_attn_verify(const ha_shape* shape, const ha_kv_view* kv, const int32_t* kv_len, int32_t batch,

@@ -46,7 +46,9 @@
 // append-then-decode with one launch instead of two.
 #include <climits>
 #include <cmath>
+#include <mutex>
 
+#include "../../include/hybrid_attn.h"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -754,6 +756,35 @@ static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
   return a.geo.d == 64 ? launch_decode_d<64>(a, stream) : launch_decode_d<128>(a, stream);
+}
+
+// Split-K partials of hybrid_attn_decode_noalloc: one library-owned array per
+// device, loaded with the code object and kept until the process ends. Every
+// call on a device shares it, so calls that overlap on one device race.
+// Nothing in it has to start at zero: every split a merge reads is written
+// by its workgroup in the same call.
+static __device__ __align__(256) unsigned char scratch[HA_DECODE_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// In host code `scratch` names a host-side stand-in, not device memory: its
+// device address is looked up once per device (with that device current) and
+// only that address is handed to kernels.
+hipError_t decode_scratch(int device, void** out) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[device] = p;
+  }
+  *out = g_scratch_ptr[device];
+  return hipSuccess;
 }
 
 }  // namespace ha

@@ -122,6 +122,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 
+// Device address of `device`'s copy of the decode kernels' static scratch
+// array (HA_DECODE_SCRATCH_BYTES); `device` must be the current device.
+hipError_t decode_scratch(int device, void** out);
+
 // Decode split policy shared by the workspace query and the launcher.
 int decode_split_blocks(bool full, int window, int max_kv_len, int batch, int hkv, int requested_splits);
 int decode_num_splits(bool full, int window, int max_kv_len, int split_blocks);

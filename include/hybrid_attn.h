@@ -27,6 +27,8 @@
  * Ownership and threading. The caller owns every buffer (pools, tables, Q/K/V,
  * outputs, workspace). The library allocates no device memory, keeps no state
  * between calls apart from a thread-local error message, and is thread-safe.
+ * (Exception: hybrid_attn_decode_noalloc uses one static device array per
+ * device that the loader places with the library's code; see there.)
  * Device work is enqueued on the caller's HIP stream (passed as void*, NULL =
  * default stream) and the calls return without synchronising; only
  * window_safe_match runs synchronously on the host.
@@ -87,7 +89,7 @@
 extern "C" {
 #endif
 
-#define HA_ABI_VERSION 6
+#define HA_ABI_VERSION 7
 
 typedef enum ha_status {
   HA_OK = 0,
@@ -241,6 +243,30 @@ ha_status hybrid_attn_decode(const ha_shape* shape, const ha_kv_view* kv, const 
                              const void* v_new, int32_t in_dtype, float* out, float* lse,
                              int32_t num_splits, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/* ---- hybrid_attn_decode without a workspace: for callers that cannot
+ *          allocate device memory (code under HIP graph capture, tight serving
+ *          loops, harnesses that forbid allocation) -----------------------------
+ * Same arguments, results and errors as hybrid_attn_decode, minus the
+ * workspace: the split-K partials go to a library-owned static device array
+ * of HA_DECODE_SCRATCH_BYTES per device, loaded with the library and held
+ * until the process ends. The call allocates and frees nothing.
+ *   Limit: calls whose partials need more (batch * Hq * splits * (D + 1) * 4
+ *   bytes when a full-layer call splits; SWA calls and single-split calls
+ *   need none) fail with HA_ERR_WORKSPACE before any HIP call: pass a smaller
+ *   num_splits, or use hybrid_attn_decode with a workspace.
+ *   The stream must belong to the current device (HA_ERR_RANGE otherwise);
+ *   the first call on a device looks up that device's array (one HIP symbol
+ *   query, with the device current).
+ *   Every call on a device shares its one array, which keeps the last call's
+ *   contents: calls that overlap on one device (concurrent streams, several
+ *   host threads) race and give undefined results. */
+#define HA_DECODE_SCRATCH_BYTES (64u << 20)
+
+ha_status hybrid_attn_decode_noalloc(const ha_shape* shape, const ha_kv_view* kv, const int32_t* kv_len,
+                                     int32_t batch, int32_t max_kv_len, const void* q, const void* k_new,
+                                     const void* v_new, int32_t in_dtype, float* out, float* lse,
+                                     int32_t num_splits, void* stream);
 
 /* Workspace bytes needed by hybrid_attn_decode (decode = 1: max_kv_len and
  * num_splits as passed to the call) or hybrid_attn_prefill (decode = 0: pass

@@ -227,3 +227,26 @@ def test_read_errors(lib):
     assert rd(lib.swa_ring_read, ring, batch=0, n=0) == 0
     int8 = HaKvView(_lib.HA_FULL, FAKE, FAKE, 8, FAKE, 4, _lib.HA_KV_INT8, FAKE, FAKE)
     assert rd(lib.full_pool_read, int8) == _lib.HA_ERR_UNSUPPORTED
+
+
+def noalloc_call(lib, shape, kv, batch=2, max_len=100, q=FAKE, splits=0):
+    return lib.hybrid_attn_decode_noalloc(ctypes.byref(shape) if shape is not None else None,
+                                          ctypes.byref(kv) if kv is not None else None, FAKE, batch, max_len, q,
+                                          None, None, 0, FAKE, FAKE, splits, None)
+
+
+def test_noalloc_decode_checks_its_scratch_limit_on_the_host(lib):
+    s = good_shape()
+    assert noalloc_call(lib, None, view()) == _lib.HA_ERR_NULL
+    assert noalloc_call(lib, good_shape(head_dim=96), view()) == _lib.HA_ERR_SHAPE
+    assert noalloc_call(lib, s, view(), q=None) == _lib.HA_ERR_NULL
+    assert noalloc_call(lib, s, view(), batch=-1) == _lib.HA_ERR_RANGE
+    assert noalloc_call(lib, s, view(), batch=0) == _lib.HA_OK
+    # 8 sequences of 1M tokens split over many workgroups: partials beyond the static array
+    need = lib.hybrid_attn_workspace_size(ctypes.byref(s), _lib.HA_FULL, 1, 8, 1 << 20, 0)
+    assert need > _lib.HA_DECODE_SCRATCH_BYTES
+    assert noalloc_call(lib, s, view(), batch=8, max_len=1 << 20) == _lib.HA_ERR_WORKSPACE
+    assert b"static scratch" in lib.ha_last_error()
+    # the same call with fewer splits fits
+    assert lib.hybrid_attn_workspace_size(ctypes.byref(s), _lib.HA_FULL, 1, 8, 1 << 20, 64) <= \
+        _lib.HA_DECODE_SCRATCH_BYTES
