@@ -188,11 +188,14 @@ def test_late_score_jumps_and_wide_dynamic_range(kind):
             seqs.k[b][pos] = (seqs.k[b][pos].float() * 40.0).to(torch.bfloat16)
 
     def check(outs, lses):
-        # Near one-hot rows put the whole output on a few keys, so the bf16
-        # rounding of P (relative 2^-9 per probability, in the numerator's
-        # weights and nowhere else) bounds the output error by about
-        # 2^-8 * max|V| rather than by the N(0,1)-workload bound; LSE sums
-        # the unrounded probabilities in fp32 and keeps its 1e-3 bound.
+        # Near one-hot rows put the whole output on one key. The prefill
+        # kernels round P to bf16 against a lazily raised exp2 reference, so
+        # the dominant weight carries a relative rounding error of up to 2^-8
+        # that nothing else averages out: the output error is bounded by
+        # 2^-8 * max|V| (+1e-3 for the rest of the row), not by the 1e-2 of
+        # the N(0,1) workloads. Measured here: up to 1.4e-2 with max|V| of
+        # about 5 (bound 2.0e-2). LSE sums the unrounded probabilities in fp32
+        # and keeps its 1e-3 bound.
         for b, total in enumerate(totals):
             sel = np.arange(total)
             v = host(seqs.v[b])
@@ -200,6 +203,8 @@ def test_late_score_jumps_and_wide_dynamic_range(kind):
             tol_o = 2.0 ** -8 * float(np.abs(v).max()) + 1e-3
             err_o = float(np.abs(outs[b] - ref_o).max())
             err_l = float(np.abs(lses[b] - ref_l).max())
+            print(f"[score-jump error] prefill kind={kname} seq={b}: max|O - oracle| {err_o:.3e} "
+                  f"(max|V| {float(np.abs(v).max()):.2f}), max|LSE - oracle| {err_l:.3e}", flush=True)
             assert np.isfinite(outs[b]).all() and np.isfinite(lses[b]).all()
             assert err_o <= tol_o, f"max |O - oracle| = {err_o:.3e} > {tol_o:.3e} kind={kname} seq={b}"
             assert err_l <= 1e-3, f"max |LSE - oracle| = {err_l:.3e} kind={kname} seq={b}"

@@ -5,16 +5,19 @@ raise it (rescaling O and l) only when a block's scores pass it by a margin;
 the INT8 decode path and verify raise it lazily. Keys scaled up at early,
 middle and late positions force those raises deep into a row (also across
 split-K boundaries), and scaled-up queries widen every row's score range.
-Near one-hot rows put the whole output on a few keys, so the bf16 rounding of
-the probabilities bounds the output error by about 2^-8 * max|V| (the
-prefill spike test's bound); LSE keeps its 1e-3 bound."""
+The bf16 decode kernel references each block's own maximum, so a row's
+dominant key gets probability exactly 1 and its rounding costs nothing; the
+lazily raised references of INT8 decode and verify leave the dominant weight
+rounded (relative 2^-8), which these rows keep well inside the same bounds
+as every other parity test: max |O - oracle| <= 1e-2, max |LSE - oracle| <=
+1e-3. Each case prints the error it reaches."""
 
 import numpy as np
 import pytest
 import torch
 
 import hybrid_sliding_window_gqa_amd as ha
-from gpu_util import DEV, append_history, host, i32, make_generator, oracle_rows, randn_bf16
+from gpu_util import DEV, LSE_TOL, OUT_TOL, append_history, host, i32, make_generator, oracle_rows, randn_bf16
 from oracle.quant import dequantize_rows, quantize_rows
 from oracle.attention import attend
 
@@ -46,12 +49,14 @@ def pools(shape, kind, lens, kv_dtype="bf16", seed=3):
 
 
 def check_rows(out, lse, ref_o, ref_l, v_max, what):
-    tol_o = 2.0 ** -8 * v_max + 1e-3
+    tol_o = OUT_TOL
     assert np.isfinite(out).all() and np.isfinite(lse).all(), what
     err_o = float(np.abs(out - ref_o).max())
     err_l = float(np.abs(lse - ref_l).max())
+    print(f"[score-jump error] {what}: max|O - oracle| {err_o:.3e} (max|V| {v_max:.2f}), "
+          f"max|LSE - oracle| {err_l:.3e}", flush=True)
     assert err_o <= tol_o, f"max |O - oracle| = {err_o:.3e} > {tol_o:.3e} {what}"
-    assert err_l <= 1e-3, f"max |LSE - oracle| = {err_l:.3e} {what}"
+    assert err_l <= LSE_TOL, f"max |LSE - oracle| = {err_l:.3e} {what}"
 
 
 def dequantized(x_seq):
