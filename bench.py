@@ -70,6 +70,14 @@ def parse():
     p.add_argument("--cpu-prefill-seconds", type=float, default=10.0,
                    help="target oracle time for the prefill CPU sample")
     p.add_argument("--eager", action="store_true", help="launch calls directly instead of replaying a HIP graph")
+    p.add_argument("--cold-bytes", type=float, default=768e6,
+                   help="rotate decode steps over ring copies so that a ring is read again only after this "
+                        "many bytes of other rings (0: one copy)")
+    p.add_argument("--no-ceilings", action="store_true", help="skip the copy / read-pattern / MFMA ceilings")
+    p.add_argument("--no-restore", action="store_true", help="skip the layer-wise restore part")
+    p.add_argument("--no-quant-error", action="store_true", help="skip the INT8 quantization-error sample")
+    p.add_argument("--cpu-ragged-seconds", type=float, default=8.0)
+    p.add_argument("--cpu-reuse-seconds", type=float, default=8.0)
     p.add_argument("--separate-append", action="store_true",
                    help="decode step as append call + decode call per layer instead of one fused call")
     return p.parse_args()
@@ -139,6 +147,9 @@ def profile_traffic(name):
 
 DECODE_PROFILE = "decode_kernel_full_decode64x8192_pmc.txt"
 PREFILL_PROFILE = "prefill_kernel_full_chunked4x32768_pmc.txt"
+VERIFY_PROFILE = "verify_kernel_full_verify64x8192_pmc.txt"
+RAGGED_PROFILE = "decode_kernel_full_ragged24_pmc.txt"
+REUSE_PROFILE = "prefill_kernel_full_reuse32_pmc.txt"
 
 
 def run_copy(torch, args, device):
@@ -155,6 +166,14 @@ def run_copy(torch, args, device):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / reps
+    # write-only stream of the same size (a fill)
+    dst.fill_(0.5)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.fill_(0.5)
+    torch.cuda.synchronize()
+    dw = (time.perf_counter() - t0) / reps
     # read-only stream of the same buffer (a max-reduction), for the achievable read rate
     torch.amax(src)
     torch.cuda.synchronize()
@@ -165,26 +184,39 @@ def run_copy(torch, args, device):
     dr = (time.perf_counter() - t0) / reps
     return {"workload": "calibration copy: dst = -src, 2 GiB bf16 each way", "bytes_read": 2 * n,
             "bytes_written": 2 * n, "ms": dt * 1e3, "copy_gbs": 4 * n / dt / 1e9,
-            "read_only_gbs": 2 * n / dr / 1e9}
+            "read_only_gbs": 2 * n / dr / 1e9, "write_only_gbs": 2 * n / dw / 1e9}
 
 
 def timed_events(torch, n):
     return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
 
 
-def build_decode(torch, ha, grp, synth, struct, device, workload, fuse=True, kv_dtype="bf16"):
-    """Pools filled with each sequence's history; per-layer new-token tensors."""
+def build_decode(torch, ha, grp, synth, struct, device, workload, fuse=True, kv_dtype="bf16", share=None):
+    """Pools filled with each sequence's history; per-layer new-token tensors.
+
+    share: an earlier build of the same structure. The new copy then uses
+    that build's full-layer pool and its Q/K/V/O tensors and owns only its
+    SWA rings (filled with the same values), so a step can rotate over ring
+    copies whose total exceeds the last-level cache while the full layer
+    keeps reading one 16-token-paged pool."""
     shape = ha.HeadShape(struct.shape.num_q_heads, struct.shape.num_kv_heads, struct.shape.head_dim,
                          struct.shape.window)
     b = struct.batch
     hist = struct.hist.astype(np.int64)
     ring_id = torch.as_tensor(struct.ring_id, device=device)
     table = torch.as_tensor(struct.page_table, device=device)
-    group = grp.HybridGroup(shape, ring_id, struct.num_rings, table, struct.num_pages, kv_dtype=kv_dtype)
+    pools = {}
+    if share is not None:
+        sgroup = share[1]
+        pools = {li: layer.pool for li, layer in enumerate(sgroup.layers) if layer.kind == "full"}
+    group = grp.HybridGroup(shape, ring_id, struct.num_rings, table, struct.num_pages, kv_dtype=kv_dtype,
+                            pools=pools)
     hkv, hq, d, w = shape.num_kv_heads, shape.num_q_heads, shape.head_dim, shape.window
     logical = []   # per layer: (k_hist, v_hist, first_position) host-side recipe for the oracle
     q_l, k_l, v_l, out_l, lse_l = [], [], [], [], []
     for li, layer in enumerate(group.layers):
+        if share is not None and li in pools:
+            continue
         if layer.kind == "swa":
             start = np.maximum(hist - (w - 1), 0)
         else:
@@ -197,24 +229,153 @@ def build_decode(torch, ha, grp, synth, struct, device, workload, fuse=True, kv_
         pos0 = torch.as_tensor(start.astype(np.int32), device=device)
         fn = ha.swa_ring_append if layer.kind == "swa" else ha.full_pool_append
         fn(shape, layer.view, pos0, cu, k_hist, v_hist)
-        logical.append((k_hist, v_hist, start, cu.cpu().numpy()))
-        q_l.append(synth.normal_bf16((b, hq, d), workload, li, synth.Q_VALUES, device))
-        k_l.append(synth.normal_bf16((b, hkv, d), workload, li, synth.K_VALUES + 3, device))
-        v_l.append(synth.normal_bf16((b, hkv, d), workload, li, synth.V_VALUES + 3, device))
-        out_l.append(torch.empty(b, hq, d, dtype=torch.float32, device=device))
-        lse_l.append(torch.empty(b, hq, dtype=torch.float32, device=device))
+        if share is None:
+            logical.append((k_hist, v_hist, start, cu.cpu().numpy()))
+            q_l.append(synth.normal_bf16((b, hq, d), workload, li, synth.Q_VALUES, device))
+            k_l.append(synth.normal_bf16((b, hkv, d), workload, li, synth.K_VALUES + 3, device))
+            v_l.append(synth.normal_bf16((b, hkv, d), workload, li, synth.V_VALUES + 3, device))
+            out_l.append(torch.empty(b, hq, d, dtype=torch.float32, device=device))
+            lse_l.append(torch.empty(b, hq, dtype=torch.float32, device=device))
+        del k_hist, v_hist
+    if share is not None:
+        data = share[3]
+        q_l, k_l, v_l, out_l, lse_l = data["q"], data["k"], data["v"], data["out"], data["lse"]
+    else:
+        data = dict(q=q_l, k=k_l, v=v_l, out=out_l, lse=lse_l, logical=logical, hist=hist)
+    # SWA pool size is O(W) per sequence and layer, independent of the history length
+    swa_layers = sum(1 for layer in group.layers if layer.kind == "swa")
+    tok = kv8_bytes_per_token(shape) if kv_dtype == "int8" else kv_bytes_per_token(shape)
+    assert group.pool_bytes()["swa"] == swa_layers * struct.num_rings * w * tok, "SWA pool is not O(W)"
     pos = torch.as_tensor(hist.astype(np.int32), device=device)
     kv_len = torch.as_tensor((hist + 1).astype(np.int32), device=device)
     plan = grp.plan_decode(group, q_l, k_l, v_l, pos, kv_len, int(hist.max()) + 1, out_l, lse_l,
                            fuse_append=fuse)
     torch.cuda.synchronize()
-    return shape, group, plan, dict(q=q_l, k=k_l, v=v_l, out=out_l, lse=lse_l, logical=logical,
-                                    hist=hist)
+    return shape, group, plan, data
+
+
+_CAPTURE_STREAM = None
+
+
+def capture_stream(torch):
+    """The one side stream every graph capture of this run uses. A process
+    gets few hardware queues (4 by default) and streams share them round-robin
+    in creation order, so a stream per capture would leave later streams (the
+    restore's copy stream) on the same queue as the compute stream, where
+    they serialize instead of overlapping."""
+    global _CAPTURE_STREAM
+    if _CAPTURE_STREAM is None:
+        _CAPTURE_STREAM = torch.cuda.Stream()
+    return _CAPTURE_STREAM
+
+
+def rotation_copies(args, ring_bytes):
+    """Ring copies so that a ring is read again only after at least
+    args.cold_bytes of other rings (0: one copy, warm replay only)."""
+    if args.cold_bytes <= 0 or ring_bytes <= 0:
+        return 1
+    return max(2, 1 + -(-int(args.cold_bytes) // int(ring_bytes)))
+
+
+def time_steps(torch, plans, args, labels_of_interest=None):
+    """Times one step (a plan per pool copy) four ways, all with inputs
+    resident in HBM:
+      cold   graph replays rotating over the copies, so every ring is read
+             after more than the last-level cache of other rings (the
+             headline; K steps bracketed by synchronize, wall clock);
+      steps  the same rotation with HIP events around each replay (median,
+             p10, p90 of the per-step times);
+      warm   graph replays of copy 0 only (its rings stay cache-resident);
+      eager  the rotation launched call by call, no graph.
+    And the per-call durations (HIP events on the launch stream, eager
+    launches rotating over the copies)."""
+    stream = torch.cuda.current_stream()
+    graphs = []
+    if not args.eager:
+        side = capture_stream(torch)
+        for pl in plans:
+            pl.run()                                # eager warm call before capture
+            torch.cuda.synchronize()
+            side.wait_stream(stream)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                pl.run()
+            graphs.append(g)
+        torch.cuda.synchronize()
+    n = len(plans)
+
+    def step(i):
+        if graphs:
+            graphs[i % n].replay()
+        else:
+            plans[i % n].run()
+
+    def wall(fn, k):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(k):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / k
+
+    cold = wall(step, args.steps)
+    warm = wall(lambda i: graphs[0].replay() if graphs else plans[0].run(), args.steps)
+    eager = wall(lambda i: plans[i % n].run(), args.steps)
+    evs = timed_events(torch, args.steps)
+    for i in range(args.warmup):
+        step(i)
+    for i, (e0, e1) in enumerate(evs):
+        e0.record(stream)
+        step(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    ncalls = len(plans[0].calls)
+    cevs = timed_events(torch, ncalls)
+    sums = np.zeros(ncalls)
+    reps = max(5, min(args.steps, 20))
+    for r in range(reps):
+        plans[r % n].run_timed(cevs, stream)
+        torch.cuda.synchronize()
+        sums += np.array([a.elapsed_time(c) for a, c in cevs])
+    return {
+        "cold_s": cold, "warm_s": warm, "eager_s": eager,
+        "step_ms_p10": float(np.percentile(per_step, 10)), "step_ms_p50": float(np.median(per_step)),
+        "step_ms_p90": float(np.percentile(per_step, 90)), "copies": n,
+        "call_ms": sums / reps, "labels": list(plans[0].labels),
+    }
+
+
+def build_copies(torch, ha, grp, synth, struct, args, device, fuse=True, kv_dtype="bf16"):
+    """Copy 0 of the decode pools, then ring copies sharing its full pool."""
+    first = build_decode(torch, ha, grp, synth, struct, device, struct.workload, fuse=fuse, kv_dtype=kv_dtype)
+    ring_bytes = first[1].pool_bytes()["swa"]
+    copies = [first]
+    for _ in range(rotation_copies(args, ring_bytes) - 1):
+        copies.append(build_decode(torch, ha, grp, synth, struct, device, struct.workload, fuse=fuse,
+                                   kv_dtype=kv_dtype, share=first))
+    return copies, ring_bytes
+
+
+def timing_fields(t, step_bytes):
+    """JSON fields of time_steps() for a step of step_bytes algorithmic bytes."""
+    return {
+        "cold_ms_per_step": round(t["cold_s"] * 1e3, 4),
+        "step_ms_p10": round(t["step_ms_p10"], 4), "step_ms_p50": round(t["step_ms_p50"], 4),
+        "step_ms_p90": round(t["step_ms_p90"], 4),
+        "warm_ms_per_step": round(t["warm_s"] * 1e3, 4),
+        "warm_gbs": round(step_bytes / t["warm_s"] / 1e9, 2),
+        "eager_ms_per_step": round(t["eager_s"] * 1e3, 4),
+        "eager_gbs": round(step_bytes / t["eager_s"] / 1e9, 2),
+        "ring_copies_rotated": t["copies"],
+    }
 
 
 def run_decode(torch, ha, grp, synth, struct, args, device):
-    shape, group, plan, data = build_decode(torch, ha, grp, synth, struct, device, struct.workload,
-                                            fuse=not args.separate_append)
+    copies, ring_bytes = build_copies(torch, ha, grp, synth, struct, args, device, fuse=not args.separate_append)
+    shape, group, plan, data = copies[0]
     kv_len = data["hist"] + 1
     # per layer: the attention's bytes plus the new token's K/V read and written
     # by the append (fused into the decode call, or a call of its own)
@@ -222,47 +383,13 @@ def run_decode(torch, ha, grp, synth, struct, args, device):
     per_layer_bytes = [decode_layer_bytes(shape, layer.kind, kv_len) + layer_append for layer in group.layers]
     step_bytes = sum(per_layer_bytes)
     append_bytes = len(group.layers) * layer_append
-
-    stream = torch.cuda.current_stream()
-    graph = None
-    if not args.eager:
-        plan.run()                              # eager warm call before capture
-        torch.cuda.synchronize()
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=side):
-            plan.run()
-        torch.cuda.synchronize()
-
-    def step():
-        if graph is not None:
-            graph.replay()
-        else:
-            plan.run()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / args.steps
-
-    # Per-call durations with HIP events on the launch stream (eager launches).
-    evs = timed_events(torch, len(plan.calls))
-    sums = np.zeros(len(plan.calls))
-    reps = max(5, min(args.steps, 20))
-    for _ in range(reps):
-        plan.run_timed(evs, stream)
-        torch.cuda.synchronize()
-        sums += np.array([a.elapsed_time(b) for a, b in evs])
-    call_ms = sums / reps
-    by_label = dict(zip(plan.labels, call_ms.tolist()))
-    full_idx = [i for i, lab in enumerate(plan.labels) if lab.startswith("decode") and "full" in lab]
-    swa_idx = [i for i, lab in enumerate(plan.labels) if lab.startswith("decode") and "swa" in lab]
-    app_idx = [i for i, lab in enumerate(plan.labels) if lab.startswith("append")]
+    t = time_steps(torch, [c[2] for c in copies], args)
+    call_ms = t["call_ms"]
+    labels = t["labels"]
+    by_label = dict(zip(labels, call_ms.tolist()))
+    full_idx = [i for i, lab in enumerate(labels) if lab.startswith("decode") and "full" in lab]
+    swa_idx = [i for i, lab in enumerate(labels) if lab.startswith("decode") and "swa" in lab]
+    app_idx = [i for i, lab in enumerate(labels) if lab.startswith("append")]
     full_ms = float(np.mean(call_ms[full_idx]))
     swa_ms = float(np.mean(call_ms[swa_idx]))
     full_layer = [i for i, layer in enumerate(group.layers) if layer.kind == "full"][0]
@@ -270,9 +397,12 @@ def run_decode(torch, ha, grp, synth, struct, args, device):
     call_extra = 0 if app_idx else layer_append     # the decode call appends only when fused
     full_bytes = per_layer_bytes[full_layer] - layer_append + call_extra
     swa_bytes = per_layer_bytes[swa_layer] - layer_append + call_extra
+    pool = group.pool_bytes()
+    full_used = int(kv_len.sum()) * kv_bytes_per_token(shape)
     info = {
         "step_bytes": step_bytes,
         "append_bytes": append_bytes,
+        **timing_fields(t, step_bytes),
         "full_decode_ms": full_ms,
         "full_decode_gbs": full_bytes / full_ms / 1e6,
         "swa_decode_ms": swa_ms,
@@ -280,10 +410,14 @@ def run_decode(torch, ha, grp, synth, struct, args, device):
         "append_ms_avg": float(np.mean(call_ms[app_idx])) if app_idx else None,
         "fused_append": not app_idx,
         "calls_ms": by_label,
-        "graph": graph is not None,
+        "graph": not args.eager,
         "splits_full": ha.hybrid_attn_decode_splits(shape, ha.HA_FULL, struct.batch, int(kv_len.max())),
+        "swa_pool_bytes": pool["swa"],
+        "swa_pool_bytes_per_ring_layer": pool["swa"] // (struct.num_rings * 6),
+        "kv_bytes_vs_all_full": round((pool["swa"] // struct.num_rings * struct.batch + full_used)
+                                      / (len(group.layers) * full_used), 4),
     }
-    return shape, group, data, dt, step_bytes, full_bytes, info
+    return shape, group, data, t["cold_s"], step_bytes, full_bytes, info, copies
 
 
 def kv8_bytes_per_token(shape):
@@ -294,10 +428,11 @@ def kv8_bytes_per_token(shape):
 def run_decode_int8(torch, ha, grp, synth, args, device):
     """The decode workload on INT8 pools: per layer one call that quantizes
     and appends the new token and attends (--separate-append: an append call
-    and a decode call), graph replay; and the full-layer decode call alone."""
+    and a decode call), timed like the bf16 step; and the full-layer call."""
     struct = synth.decode_structure()
-    shape, group, plan, data = build_decode(torch, ha, grp, synth, struct, device, struct.workload,
-                                            fuse=not args.separate_append, kv_dtype="int8")
+    copies, _ = build_copies(torch, ha, grp, synth, struct, args, device, fuse=not args.separate_append,
+                             kv_dtype="int8")
+    shape, group, plan, data = copies[0]
     b = struct.batch
     kv_len = data["hist"] + 1
     hq, d = shape.num_q_heads, shape.head_dim
@@ -306,35 +441,10 @@ def run_decode_int8(torch, ha, grp, synth, args, device):
     per_layer = [int(visible_keys(kv_len - 1, layer.kind, shape.window).sum()) * kv8_bytes_per_token(shape) + qol
                  for layer in group.layers]
     step_bytes = sum(per_layer) + append * len(group.layers)
-    stream = torch.cuda.current_stream()
-    plan.run()
-    torch.cuda.synchronize()
-    step = plan.run
-    if not args.eager:
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=side):
-            plan.run()
-        torch.cuda.synchronize()
-        step = graph.replay
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / args.steps
-    evs = timed_events(torch, len(plan.calls))
-    sums = np.zeros(len(plan.calls))
-    reps = max(5, min(args.steps, 20))
-    for _ in range(reps):
-        plan.run_timed(evs, stream)
-        torch.cuda.synchronize()
-        sums += np.array([a.elapsed_time(c) for a, c in evs])
-    call_ms = sums / reps
-    lab = plan.labels
+    t = time_steps(torch, [c[2] for c in copies], args)
+    dt = t["cold_s"]
+    call_ms = t["call_ms"]
+    lab = t["labels"]
     full_ms = float(np.mean([call_ms[i] for i, x in enumerate(lab) if x.startswith("decode") and "full" in x]))
     swa_ms = float(np.mean([call_ms[i] for i, x in enumerate(lab) if x.startswith("decode") and "swa" in x]))
     app = [call_ms[i] for i, x in enumerate(lab) if x.startswith("append")]
@@ -353,6 +463,7 @@ def run_decode_int8(torch, ha, grp, synth, args, device):
         "tokens_per_s": round(b / dt, 1),
         "pct_peak_hbm": round(100.0 * value / HBM_PEAK_GBS, 2),
         "step_bytes": step_bytes,
+        **timing_fields(t, step_bytes),
         "workload": (f"decode: {b} sequences x {int(kv_len[0]) - 1} cached tokens on INT8 pools (per-token "
                      f"scales), one 6:1 group, per layer "
                      + ("an append call then a decode call" if app else "one call (quantize, append, attend)")),
@@ -363,7 +474,35 @@ def run_decode_int8(torch, ha, grp, synth, args, device):
         "swa_call_us": round(swa_ms * 1e3, 2),
         "append_call_us": round(app_ms * 1e3, 2),
         "calls_ms": dict(zip(lab, call_ms.tolist())),
+        "copies": copies,
     }
+
+
+def int8_quant_error(torch, synth, q8, args):
+    """max |O_int8 - O_oracle| and |LSE_int8 - LSE_oracle| on sampled
+    sequences of the INT8 decode step, where the oracle attends over the
+    unquantized bf16 K/V: the end-to-end error the 8-bit format adds."""
+    sys.path.insert(0, HERE)
+    from oracle.attention import attend
+
+    shape, group, _plan, data = q8["copies"][0]
+    hist = data["hist"]
+    rows = [0, len(hist) // 3, 2 * len(hist) // 3, len(hist) - 1]
+    err_o = err_l = 0.0
+    for li, layer in enumerate(group.layers):
+        if li not in (0, len(group.layers) - 1):
+            continue
+        k_hist, v_hist, start, cu = data["logical"][li]
+        for b in rows:
+            k = torch.cat([k_hist[cu[b]:cu[b + 1]], data["k"][li][b:b + 1]]).float().cpu().numpy()
+            v = torch.cat([v_hist[cu[b]:cu[b + 1]], data["v"][li][b:b + 1]]).float().cpu().numpy()
+            q = data["q"][li][b:b + 1].float().cpu().numpy()
+            o_ref, l_ref = attend(q, k, v, [int(hist[b] - start[b])], layer.kind, shape.window)
+            err_o = max(err_o, float(np.abs(data["out"][li][b].cpu().numpy() - o_ref[0]).max()))
+            err_l = max(err_l, float(np.abs(data["lse"][li][b].cpu().numpy() - l_ref[0]).max()))
+    return {"max_abs_o": err_o, "max_abs_lse": err_l,
+            "sample": f"sequences {rows} of the INT8 decode step, SWA layer 0 and the full layer, all query "
+                      f"heads, against the fp64 oracle over the unquantized bf16 K/V ({int(hist[0]) + 1} keys)"}
 
 
 def verify_layer_bytes(shape, kind, t0, nq):
@@ -382,60 +521,28 @@ def verify_layer_bytes(shape, kind, t0, nq):
 
 def run_verify(torch, ha, grp, synth, args, device, nq=4):
     """The decode workload's pools, one step verifying nq tokens per sequence
-    in every layer of the group (graph replay), and the full-layer call alone."""
+    in every layer of the group, timed like the decode step (cold rotation
+    over ring copies, warm, eager); and the full-layer call alone."""
     struct = synth.decode_structure()
-    shape, group, _plan, data = build_decode(torch, ha, grp, synth, struct, device, struct.workload)
+    copies, _ = build_copies(torch, ha, grp, synth, struct, args, device)
+    shape, group, _plan, data = copies[0]
     b = struct.batch
     hist = data["hist"].astype(np.int64)
     hq, hkv, d = shape.num_q_heads, shape.num_kv_heads, shape.head_dim
     kv_len = torch.as_tensor((hist + nq).astype(np.int32), device=device)
     max_len = int(hist.max()) + nq
-    calls = []
-    for li, layer in enumerate(group.layers):
-        q = synth.normal_bf16((b, nq, hq, d), struct.workload, li, synth.Q_VALUES + 11, device)
-        k = synth.normal_bf16((b, nq, hkv, d), struct.workload, li, synth.K_VALUES + 11, device)
-        v = synth.normal_bf16((b, nq, hkv, d), struct.workload, li, synth.V_VALUES + 11, device)
-        out = torch.empty(b, nq, hq, d, dtype=torch.float32, device=device)
-        lse = torch.empty(b, nq, hq, dtype=torch.float32, device=device)
-        need = ha.hybrid_attn_verify_workspace_size(shape, layer.view.kind, b, max_len, nq)
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
-        calls.append((layer, q, k, v, out, lse, ws))
-
-    def call(c, stream=None):
-        layer, q, k, v, out, lse, ws = c
-        ha.hybrid_attn_verify(shape, layer.view, kv_len, q, k, v, max_len, out=out, lse=lse, workspace=ws,
-                              stream=stream)
-
-    stream = torch.cuda.current_stream()
-    for c in calls:
-        call(c)
-    torch.cuda.synchronize()
-    side = torch.cuda.Stream()
-    side.wait_stream(stream)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=side):
-        for c in calls:
-            call(c, side)
-    torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        graph.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        graph.replay()
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / args.steps
+    q_l, k_l, v_l, out_l, lse_l = [], [], [], [], []
+    for li in range(len(group.layers)):
+        q_l.append(synth.normal_bf16((b, nq, hq, d), struct.workload, li, synth.Q_VALUES + 11, device))
+        k_l.append(synth.normal_bf16((b, nq, hkv, d), struct.workload, li, synth.K_VALUES + 11, device))
+        v_l.append(synth.normal_bf16((b, nq, hkv, d), struct.workload, li, synth.V_VALUES + 11, device))
+        out_l.append(torch.empty(b, nq, hq, d, dtype=torch.float32, device=device))
+        lse_l.append(torch.empty(b, nq, hq, dtype=torch.float32, device=device))
+    plans = [grp.plan_verify(c[1], q_l, k_l, v_l, kv_len, max_len, out_l, lse_l) for c in copies]
+    t = time_steps(torch, plans, args)
+    dt = t["cold_s"]
     full_i = [i for i, layer in enumerate(group.layers) if layer.kind == "full"][0]
-    ev = timed_events(torch, 1)[0]
-    reps = max(5, min(args.steps, 20))
-    ms = 0.0
-    for _ in range(reps):
-        ev[0].record(stream)
-        call(calls[full_i])
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        ms += ev[0].elapsed_time(ev[1])
-    full_ms = ms / reps
+    full_ms = float(t["call_ms"][full_i])
     step_bytes = sum(verify_layer_bytes(shape, layer.kind, hist, nq) for layer in group.layers)
     full_bytes = verify_layer_bytes(shape, "full", hist, nq)
     value = step_bytes / dt / 1e9
@@ -458,8 +565,10 @@ def run_verify(torch, ha, grp, synth, args, device, nq=4):
                    "global_batch": b, "tokens_per_sequence": nq, "parallelism": "none (1 GPU)"},
         "pct_peak_hbm": round(100.0 * value / HBM_PEAK_GBS, 2),
         "tokens_verified_per_s": round(b * nq / dt, 1),
+        **timing_fields(t, step_bytes),
         "roofline": {"bound": "hbm", "achieved": round(full_bytes / full_ms / 1e6, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(full_bytes / full_ms / 1e6 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(full_bytes / full_ms / 1e6 / HBM_PEAK_GBS, 4),
+                     "traffic": profile_traffic(VERIFY_PROFILE),
                      "kernel": "hybrid_attn_verify, full layer (verify_kernel<128,full,bf16,2> + reduce)",
                      "bytes_per_launch": full_bytes},
     }
@@ -558,6 +667,8 @@ def run_chunked(torch, ha, grp, synth, args, device, cpu_seconds=0.0):
     if cpu_seconds > 0:
         log("[bench] cpu baseline (oracle), prefill rows")
         res["cpu_baseline"] = cpu_baseline_prefill(torch, shape, group, qs, ks, vs, chunk, cpu_seconds)
+        res["cpu_baseline"]["extrapolated_pass_s"] = total_flops / (res["cpu_baseline"]["value"] * 1e12)
+        res["cpu_baseline"]["extrapolated"] = True
     del qs, ks, vs, outs, lses, group
     torch.cuda.empty_cache()
     return res
@@ -571,7 +682,7 @@ def blas_thread_count():
         return 1
 
 
-def run_reuse(torch, ha, grp, synth, args, device):
+def run_reuse(torch, ha, grp, synth, args, device, cpu_seconds=0.0):
     """Prefix-reuse prefill: per sequence, the window-safe match L of the
     request against its cached prefix, the reused history restored (pages
     [0, L); ring positions [L-W, L)), then one pass of the recomputed tail +
@@ -588,6 +699,9 @@ def run_reuse(torch, ha, grp, synth, args, device):
     group = grp.HybridGroup(shape, torch.as_tensor(struct.ring_id, device=device), struct.num_rings,
                             torch.as_tensor(struct.page_table, device=device), struct.num_pages)
     log(f"[bench] reuse: restoring history ({int(reuse_len.sum())} cached positions)")
+    # sequence 0's logical K/V of one SWA and the full layer, kept for the oracle baseline
+    oracle_layers = {"swa": list(group.kinds).index("swa"), "full": list(group.kinds).index("full")}
+    seq0_hist = {}
     for li, layer in enumerate(group.layers):
         first = np.maximum(reuse_len - w, 0) if layer.kind == "swa" else np.zeros(b, np.int64)
         counts = reuse_len - first
@@ -599,6 +713,9 @@ def run_reuse(torch, ha, grp, synth, args, device):
         fn = ha.swa_ring_append if layer.kind == "swa" else ha.full_pool_append
         fn(shape, layer.view, torch.as_tensor(first.astype(np.int32), device=device),
            torch.as_tensor(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32), device=device), k, v)
+        if cpu_seconds > 0 and oracle_layers.get(layer.kind) == li:
+            c0 = int(counts[0])
+            seq0_hist[layer.kind] = (k[:c0].float().cpu().numpy(), v[:c0].float().cpu().numpy(), int(first[0]))
         del k, v
     t_new = int(n_new.sum())
     qs, ks, vs, outs, lses = [], [], [], [], []
@@ -631,6 +748,17 @@ def run_reuse(torch, ha, grp, synth, args, device):
     call_ms = dict(zip(plan.labels, [a.elapsed_time(e) for a, e in evs]))
     full_ms = sum(v for lab, v in call_ms.items() if lab.startswith("prefill") and "full" in lab)
     full_tf = flops["full"] / (full_ms * 1e-3) / 1e12
+    cpu = None
+    if cpu_seconds > 0 and len(seq0_hist) == 2:
+        log("[bench] cpu baseline (oracle), prefix-reuse rows")
+        n0 = int(n_new[0])
+        seq0 = {"L": int(reuse_len[0]), "n": n0}
+        for kind, li in oracle_layers.items():
+            kh, vh, first0 = seq0_hist[kind]
+            seq0[kind] = (qs[li][:n0].float().cpu().numpy(),
+                          np.concatenate([kh, ks[li][:n0].float().cpu().numpy()]),
+                          np.concatenate([vh, vs[li][:n0].float().cpu().numpy()]), first0)
+        cpu = cpu_baseline_reuse(torch, shape, list(group.kinds), seq0, cpu_seconds, total_flops)
     return {
         "metric": METRIC,
         "workload": f"prefix-reuse prefill: {b} sequences, cached prefix P~U[4096,65536] with evicted SWA slots, "
@@ -643,10 +771,12 @@ def run_reuse(torch, ha, grp, synth, args, device):
         "full_layer_ms": full_ms,
         "full_layer_tflops": full_tf,
         "roofline": {"bound": "mfma", "achieved": full_tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": full_tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
-                     "kernel": "hybrid_attn_prefill, full layer (stage_chunk_kernel + prefill_kernel<128,full>)"},
+                     "frac": full_tf / MFMA_BF16_PEAK_TFLOPS, "traffic": profile_traffic(REUSE_PROFILE),
+                     "kernel": "hybrid_attn_prefill, full layer (stage_chunk_kernel + prefill_kernel<128,full>)",
+                     "flops_per_launch": flops["full"]},
         "mean_recomputed_tail": float((prefix - reuse_len).mean()),
         "data": "synthetic",
+        **({"cpu_baseline": cpu} if cpu else {}),
     }
 
 
@@ -768,9 +898,97 @@ def run_restore(torch, ha, grp, synth, args, device):
         "schedule_bound_ms": comp_end,
         "hidden_ms": hidden * 1e3,
         "overlap_fraction_of_shorter": frac,
+        "overlap_fraction_of_allowed": hidden / ((t_restore + t_compute) - comp_end * 1e-3),
         "layer_restore_ms": r_ms,
         "layer_prefill_ms": p_ms,
         "data": "synthetic",
+    }
+
+
+def run_ceilings(torch, shape, group, data, device):
+    """Achievable ceilings measured in the same run, next to the published
+    peaks: a plain 2 GiB copy and a read-only reduction (torch), decode's
+    own read pattern over the decode workload's full pool with and without
+    the non-temporal bit (include/ha_probe.h), and the matrix cores alone."""
+    from hybrid_sliding_window_gqa_amd import _lib
+
+    lib = _lib.load()
+    res = run_copy(torch, None, device)
+    out = {"copy_gbs": round(res["copy_gbs"], 1), "write_only_gbs": round(res["write_only_gbs"], 1)}
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    full = [layer for layer in group.layers if layer.kind == "full"][0]
+    kv_len_np = (data["hist"] + 1).astype(np.int32)
+    kv_len = torch.as_tensor(kv_len_np, device=device)
+    b = len(kv_len_np)
+    sink = torch.empty(b * shape.num_kv_heads * 256, dtype=torch.int32, device=device)
+    nbytes = int(np.sum(-(-kv_len_np // 16))) * shape.num_kv_heads * 16 * shape.head_dim * 2 * 2
+    c_shape, c_view = shape.c(), full.view.c()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(launch, reps=10):
+        for _ in range(3):
+            launch()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    for nt, key in ((1, "decode_pattern_read_nt_gbs"), (0, "decode_pattern_read_gbs")):
+        dt = timed(lambda: _lib.check(lib.ha_probe_paged_read(ctypes.byref(c_shape), ctypes.byref(c_view),
+                                                               kv_len.data_ptr(), b, sink.data_ptr(), nt, sptr)))
+        out[key] = round(nbytes / dt / 1e9, 1)
+    iters = 8192
+    fsink = torch.empty(1024 * 256, dtype=torch.float32, device=device)
+    best = (0.0, 0)
+    for wgs in (256, 512, 1024):             # 1, 2 and 4 waves per SIMD
+        dt = timed(lambda: _lib.check(lib.ha_probe_mfma_bf16(wgs, iters, fsink.data_ptr(), sptr)), reps=5)
+        best = max(best, (wgs * 4 * iters * 8 * 16384 / dt / 1e12, wgs))
+    out["mfma_bf16_tflops"] = round(best[0], 1)
+    out["what"] = ("copy: dst = -src over 2 GiB; write_only: a fill of 2 GiB; decode_pattern_read: every K/V block of the decode "
+                   f"workload's full pool ({nbytes} B) read as the full-layer decode kernel walks it, no "
+                   "arithmetic (nt: non-temporal loads, as decode issues them); mfma: v_mfma_f32_16x16x32_bf16 "
+                   f"with register operands, best of 1, 2 and 4 waves per SIMD ({best[1] // 256} per SIMD)")
+    del sink, fsink
+    return out
+
+
+def cpu_baseline_reuse(torch, shape, kinds, seq0, target_s, total_flops):
+    """The fp64 oracle on seeded rows of sequence 0 of the prefix-reuse pass
+    (its reused history plus its new tokens; full and SWA layer alternately,
+    all query heads) for about target_s seconds; TFLOP/s of algorithmic
+    flops and the whole pass's time extrapolated from that rate."""
+    sys.path.insert(0, HERE)
+    from oracle.attention import attend
+
+    w, d, hq = shape.window, shape.head_dim, shape.num_q_heads
+    reuse_len, n_new = seq0["L"], seq0["n"]
+    rng = np.random.default_rng(11)
+    done_flops, done_s, rows = 0, 0.0, {"full": 0, "swa": 0}
+    step = 0
+    while done_s < target_s:
+        kind = ("full", "swa")[step % 2]
+        step += 1
+        q, k, v, first = seq0[kind]            # q [n, Hq, D]; k/v rows from position `first`
+        pos = np.sort(rng.choice(n_new, size=min(4, n_new), replace=False)) + reuse_len
+        t0 = time.perf_counter()
+        attend(q[pos - reuse_len], k, v, pos - first, kind, w)
+        done_s += time.perf_counter() - t0
+        rows[kind] += len(pos)
+        done_flops += int(visible_keys(pos, kind, w).sum()) * hq * 4 * d
+    rate = done_flops / done_s
+    return {
+        "value": rate / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(blas_thread_count()),
+        "kind": "oracle",
+        "sample": f"{rows['full']} full-layer and {rows['swa']} SWA-layer query rows of sequence 0 (reused "
+                  f"{reuse_len}, new {n_new}; seeded), all {hq} query heads, {done_s:.1f} s of fp64 NumPy",
+        "extrapolated_pass_s": total_flops / rate,
+        "extrapolated": True,
     }
 
 
@@ -904,11 +1122,14 @@ def main():
         return 0
     struct = {"decode": synth.decode_structure, "ragged": synth.ragged_structure}[args.workload]()
     log(f"[bench] workload={args.workload} building inputs")
-    shape, group, data, dt, step_bytes, full_bytes, info = run_decode(torch, ha, grp, synth, struct, args, device)
+    shape, group, data, dt, step_bytes, full_bytes, info, copies = run_decode(torch, ha, grp, synth, struct, args,
+                                                                               device)
     value = step_bytes / dt / 1e9
-    log(f"[bench] step {dt * 1e3:.3f} ms, {value:.1f} GB/s; full decode {info['full_decode_ms'] * 1e3:.1f} us "
-        f"({info['full_decode_gbs']:.0f} GB/s), swa decode {info['swa_decode_ms'] * 1e3:.1f} us "
-        f"({info['swa_decode_gbs']:.0f} GB/s)")
+    log(f"[bench] step {dt * 1e3:.3f} ms cold ({value:.1f} GB/s; p10/p50/p90 {info['step_ms_p10']:.3f}/"
+        f"{info['step_ms_p50']:.3f}/{info['step_ms_p90']:.3f} ms over {info['ring_copies_rotated']} ring copies), "
+        f"warm {info['warm_ms_per_step']:.3f} ms, eager {info['eager_ms_per_step']:.3f} ms; full decode "
+        f"{info['full_decode_ms'] * 1e3:.1f} us ({info['full_decode_gbs']:.0f} GB/s), swa decode "
+        f"{info['swa_decode_ms'] * 1e3:.1f} us ({info['swa_decode_gbs']:.0f} GB/s)")
     if args.workload == "decode":
         wl = (f"decode: {struct.batch} sequences x {int(struct.hist[0])} cached tokens, one 6:1 group "
               f"(6 SWA layers W={shape.window} ring + 1 full layer, 16-token pages, seeded page permutation), "
@@ -932,6 +1153,9 @@ def main():
         "config": {"workload": wl, "global_batch": struct.batch, "seq_len": int(struct.hist.max()) + 1,
                    "parallelism": "none (1 GPU)"},
         "pct_peak_hbm": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "timing": ("value and ms_per_step: graph replays rotating over ring copies (cold caches: each ring "
+                   "is read again only after more than the last-level cache of other rings); warm: replays "
+                   "of one copy; eager: the rotation launched call by call"),
         "decode_detail": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in info.items()
                           if k != "calls_ms"},
         "roofline": {
@@ -940,13 +1164,18 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(info["full_decode_gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": profile_traffic(DECODE_PROFILE) if args.workload == "decode" else None,
+            "traffic": profile_traffic(DECODE_PROFILE if args.workload == "decode" else RAGGED_PROFILE),
             "kernel": ("hybrid_attn_decode, full layer (decode_kernel<128,full>"
                        + (f" + decode_reduce_kernel<128>, {info['splits_full']} splits)" if info["splits_full"] > 1
                           else ", one split per sequence: no merge)")),
             "bytes_per_launch": full_bytes,
         },
     }
+    if args.workload == "decode" and not args.no_ceilings:
+        log("[bench] ceilings")
+        line["ceilings"] = run_ceilings(torch, shape, group, data, device)
+        log(f"[bench] ceilings {line['ceilings']}")
+    del copies
     if args.workload == "decode" and not args.no_prefill:
         log("[bench] chunked prefill")
         line["prefill"] = run_chunked(torch, ha, grp, synth, args, device,
@@ -956,39 +1185,82 @@ def main():
     if args.workload == "decode" and not args.no_verify:
         log("[bench] multi-token verify")
         v = run_verify(torch, ha, grp, synth, args, device)
-        line["verify"] = {k: v[k] for k in ("value", "unit", "ms_per_step", "pct_peak_hbm", "tokens_verified_per_s")}
+        line["verify"] = {k: v[k] for k in ("value", "unit", "ms_per_step", "pct_peak_hbm", "tokens_verified_per_s",
+                                            "step_ms_p50", "warm_ms_per_step", "eager_ms_per_step")}
         line["verify"]["workload"] = v["config"]["workload"]
         line["verify"]["full_call_gbs"] = v["roofline"]["achieved"]
+        line["verify"]["roofline"] = v["roofline"]
+        torch.cuda.empty_cache()
     if args.workload == "decode" and not args.no_int8:
         log("[bench] decode on INT8 pools")
         q8 = run_decode_int8(torch, ha, grp, synth, args, device)
         line["int8_kv"] = {k: q8[k] for k in ("value", "unit", "ms_per_step", "tokens_per_s", "pct_peak_hbm",
                                               "workload", "full_call_us", "full_call_gbs", "full_call_frac",
-                                              "swa_call_us", "append_call_us")}
+                                              "swa_call_us", "append_call_us", "step_ms_p50", "warm_ms_per_step",
+                                              "eager_ms_per_step")}
+        if not args.no_quant_error:
+            line["int8_kv"]["quant_error"] = int8_quant_error(torch, synth, q8, args)
+        del q8
+        torch.cuda.empty_cache()
     if args.workload == "decode" and not args.no_ragged:
         log("[bench] ragged long-context decode")
         torch.cuda.empty_cache()        # its 17.7 GB of pools come from fresh allocations
         rstruct = synth.ragged_structure()
-        _, rgroup, rdata, rdt, rbytes, _, rinfo = run_decode(torch, ha, grp, synth, rstruct, args, device)
+        _, rgroup, rdata, rdt, rbytes, rfull, rinfo, rcopies = run_decode(torch, ha, grp, synth, rstruct, args,
+                                                                          device)
         line["ragged"] = {
             "value": round(rbytes / rdt / 1e9, 2), "unit": "GB/s", "ms_per_step": round(rdt * 1e3, 4),
             "pct_peak_hbm": round(100.0 * rbytes / rdt / 1e9 / HBM_PEAK_GBS, 2),
             "workload": (f"ragged decode: {rstruct.batch} sequences, cached lengths 12xU[1K,64K] 8xU[64K,256K] "
                          f"4xU[256K,1M] (total {int(rstruct.hist.sum())}), one 6:1 group, split-K over full pages"),
             "full_call_gbs": round(rinfo["full_decode_gbs"], 2), "splits_full": rinfo["splits_full"],
+            **{k: rinfo[k] for k in ("step_ms_p50", "warm_ms_per_step", "eager_ms_per_step", "ring_copies_rotated")},
+            "roofline": {"bound": "hbm", "achieved": round(rinfo["full_decode_gbs"], 2), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(rinfo["full_decode_gbs"] / HBM_PEAK_GBS, 4),
+                         "traffic": profile_traffic(RAGGED_PROFILE),
+                         "kernel": f"hybrid_attn_decode, full layer (decode_kernel<128,full> + decode_reduce_kernel"
+                                   f"<128>, {rinfo['splits_full']} splits)",
+                         "bytes_per_launch": rfull},
         }
-        del rgroup, rdata
+        if not args.no_cpu_baseline:
+            log("[bench] cpu baseline (oracle), ragged decode")
+            cb = cpu_baseline(torch, shape, rgroup, rdata, args.cpu_ragged_seconds)
+            cb["extrapolated_step_s"] = rbytes / (cb["value"] * 1e9)
+            cb["extrapolated"] = True
+            line["ragged"]["cpu_baseline"] = cb
+        del rgroup, rdata, rcopies
         torch.cuda.empty_cache()
     if args.workload == "decode" and not args.no_reuse:
         log("[bench] prefix-reuse prefill")
-        ru = run_reuse(torch, ha, grp, synth, args, device)
+        ru = run_reuse(torch, ha, grp, synth, args, device,
+                       0.0 if args.no_cpu_baseline else args.cpu_reuse_seconds)
         line["reuse"] = {k: ru[k] for k in ("workload", "pass_ms", "tflops", "pct_mfma_peak", "full_layer_tflops",
-                                            "mean_recomputed_tail")}
+                                            "mean_recomputed_tail", "roofline")}
         line["reuse"]["full_layer_frac"] = ru["roofline"]["frac"]
+        if "cpu_baseline" in ru:
+            line["reuse"]["cpu_baseline"] = ru["cpu_baseline"]
         torch.cuda.empty_cache()
+    if args.workload == "decode" and not args.no_restore:
+        log("[bench] layer-wise restore")
+        rs = run_restore(torch, ha, grp, synth, args, device)
+        line["restore"] = {k: rs[k] for k in ("workload", "groups", "restored_bytes", "restore_ms", "h2d_gbs",
+                                              "prefill_ms", "serial_ms", "overlapped_ms", "schedule_bound_ms",
+                                              "hidden_ms", "overlap_fraction_of_shorter",
+                                              "overlap_fraction_of_allowed")}
+        torch.cuda.empty_cache()
+    if args.workload == "decode":
+        line["targets"] = {
+            "decode_step_pct_hbm": line["pct_peak_hbm"], "decode_target_pct_hbm": 70.0,
+            "decode_met": line["pct_peak_hbm"] >= 70.0,
+        }
+        if "prefill" in line:
+            pf = 100.0 * line["prefill"]["roofline"]["frac"]
+            line["targets"].update({"prefill_full_layer_pct_mfma": round(pf, 2),
+                                    "prefill_target_pct_mfma": 50.0, "prefill_met": pf >= 50.0})
     if args.workload == "decode" and not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(torch, shape, group, data, args.cpu_seconds)
+        line["cpu_baseline"]["extrapolated_step_s"] = step_bytes / (line["cpu_baseline"]["value"] * 1e9)
     print(json.dumps(line), flush=True)
     return 0
 

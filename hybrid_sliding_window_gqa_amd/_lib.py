@@ -1,4 +1,4 @@
-"""ctypes declarations of the C ABI in include/hybrid_attn.h and include/prefix_tree.h.
+"""ctypes declarations of the C ABI in include/hybrid_attn.h, include/prefix_tree.h and include/ha_probe.h.
 
 Loading fails loudly when libhybridattn.so has not been built: there is no
 fallback implementation.
@@ -59,6 +59,8 @@ EXPORTS = (
     "ha_tree_evict_full",
     "ha_tree_evict_swa",
     "ha_tree_stats",
+    "ha_probe_paged_read",
+    "ha_probe_mfma_bf16",
 )
 
 
@@ -150,6 +152,10 @@ def load() -> ctypes.CDLL:
     for fn, args in tree_fns.items():
         getattr(lib, fn).argtypes = args
         getattr(lib, fn).restype = i32
+    lib.ha_probe_paged_read.argtypes = [shp, view, p, i32, p, i32, p]
+    lib.ha_probe_paged_read.restype = i32
+    lib.ha_probe_mfma_bf16.argtypes = [i32, i32, p, p]
+    lib.ha_probe_mfma_bf16.restype = i32
     lib.ha_tree_destroy.argtypes = [p]
     lib.ha_tree_destroy.restype = None
     if lib.ha_abi_version() != ABI_VERSION:

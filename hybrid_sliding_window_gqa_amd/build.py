@@ -21,7 +21,7 @@ ROOT = os.path.dirname(HERE)
 LIB_NAME = "libhybridattn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.cpp", "append.hip", "decode.hip", "prefill.hip", "verify.hip", "prefix_tree.cpp"]
+SOURCES = ["api.cpp", "append.hip", "decode.hip", "prefill.hip", "verify.hip", "prefix_tree.cpp", "probe.hip"]
 ARCH = "gfx950"
 
 

@@ -14,8 +14,11 @@ enough to keep the GPU fed, and capturable in a HIP graph because each call
 takes the current stream at run time.
 
 Step order:
-  decode   per layer: append the new token (ring or pages), then attend
-           (decode reads the query's own K/V from the pool);
+  decode   per layer: one call that attends and appends the new token (the
+           wave that consumes the token's block patches it into its operands
+           and writes it to the pool afterwards); with fuse_append=False an
+           append call (ring or pages) precedes a decode call that reads the
+           query's own K/V from the pool;
   prefill  per layer: attend over pool history + the chunk, then append the
            chunk (SWA chunks longer than one token would overwrite ring
            slots their first queries still need).
@@ -54,7 +57,11 @@ class HybridGroup:
     """Pools and index tables of one layer group for a fixed batch."""
 
     def __init__(self, shape: HeadShape, ring_id: torch.Tensor, num_rings: int, page_table: torch.Tensor,
-                 num_pages: int, kinds=GROUP_KINDS, fill: float | None = None, kv_dtype: str = "bf16"):
+                 num_pages: int, kinds=GROUP_KINDS, fill: float | None = None, kv_dtype: str = "bf16",
+                 pools: dict | None = None):
+        """pools (optional): layer index -> an existing pool of the right kind
+        to use for that layer instead of a new allocation (copies of a group
+        that share one layer's pool)."""
         self.shape = shape
         self.kv_dtype = kv_dtype
         self.kinds = tuple(kinds)
@@ -62,12 +69,17 @@ class HybridGroup:
         self.ring_id = ring_id
         self.page_table = page_table
         self.layers = []
-        for kind in self.kinds:
+        pools = pools or {}
+        for li, kind in enumerate(self.kinds):
             if kind == SWA:
-                pool = SwaRingPool(shape, num_rings, self.device, fill, kv_dtype)
+                pool = pools[li] if li in pools else SwaRingPool(shape, num_rings, self.device, fill, kv_dtype)
+                if not isinstance(pool, SwaRingPool):
+                    raise ValueError(f"layer {li} needs an SWA ring pool")
                 view = pool.view(ring_id)
             elif kind == FULL:
-                pool = FullPagePool(shape, num_pages, self.device, fill, kv_dtype)
+                pool = pools[li] if li in pools else FullPagePool(shape, num_pages, self.device, fill, kv_dtype)
+                if not isinstance(pool, FullPagePool):
+                    raise ValueError(f"layer {li} needs a Full page pool")
                 view = pool.view(page_table)
             else:
                 raise ValueError(f"unknown layer kind {kind!r}")
@@ -168,6 +180,40 @@ def plan_decode(group: HybridGroup, q, k_new, v_new, pos, kv_len, max_kv_len: in
                            (c_shape, c_view, layer.view, ws, kv_len, pos, cu_one, q[li], k_new[li], v_new[li],
                             out[li], lse[li])))
         labels.append(f"decode[{li}:{layer.kind}]")
+    return Plan(calls, labels)
+
+
+def plan_verify(group: HybridGroup, q, k_new, v_new, kv_len, max_kv_len: int, out, lse,
+                num_splits: int = 0) -> Plan:
+    """Multi-token verify step over every layer: per-layer lists of
+    q [B, nq, Hq, D], k_new/v_new [B, nq, Hkv, D], out [B, nq, Hq, D],
+    lse [B, nq, Hq]; kv_len [B] includes the nq new tokens. Each layer is
+    one call that attends and then appends the nq tokens."""
+    lib = _lib.load()
+    shape = group.shape
+    b, hq, hkv, d = group.batch, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    dev = group.device
+    _check(kv_len, "kv_len", (b,), torch.int32, dev)
+    calls, labels = [], []
+    for li, layer in enumerate(group.layers):
+        nq = int(q[li].shape[1])
+        _check(q[li], "q", (b, nq, hq, d), None, dev)
+        _check(k_new[li], "k_new", (b, nq, hkv, d), None, dev)
+        _check(v_new[li], "v_new", (b, nq, hkv, d), None, dev)
+        _check(out[li], "out", (b, nq, hq, d), torch.float32, dev)
+        _check(lse[li], "lse", (b, nq, hq), torch.float32, dev)
+        kind = _lib.HA_SWA if layer.kind == SWA else _lib.HA_FULL
+        c_shape, c_view = shape.c(), layer.view.c()
+        need = int(lib.hybrid_attn_verify_workspace_size(ctypes.byref(c_shape), kind, b, int(max_kv_len), nq,
+                                                         int(num_splits)))
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        args = (ctypes.byref(c_shape), ctypes.byref(c_view), kv_len.data_ptr(), b, int(max_kv_len), nq,
+                q[li].data_ptr(), k_new[li].data_ptr(), v_new[li].data_ptr(),
+                _in_dtype(q[li], k_new[li], v_new[li]), out[li].data_ptr(), lse[li].data_ptr(), int(num_splits),
+                ws.data_ptr() if need else None, need)
+        calls.append(_Call(lib.hybrid_attn_verify, args,
+                           (c_shape, c_view, layer.view, ws, kv_len, q[li], k_new[li], v_new[li], out[li], lse[li])))
+        labels.append(f"verify[{li}:{layer.kind}]")
     return Plan(calls, labels)
 
 

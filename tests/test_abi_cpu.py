@@ -250,3 +250,21 @@ def test_noalloc_decode_checks_its_scratch_limit_on_the_host(lib):
     # the same call with fewer splits fits
     assert lib.hybrid_attn_workspace_size(ctypes.byref(s), _lib.HA_FULL, 1, 8, 1 << 20, 64) <= \
         _lib.HA_DECODE_SCRATCH_BYTES
+
+
+def test_probe_argument_errors(lib):
+    s = good_shape()
+    pages = view(kind=_lib.HA_FULL)
+    ring = view(kind=_lib.HA_SWA)
+    assert lib.ha_probe_paged_read(None, ctypes.byref(pages), FAKE, 2, FAKE, 1, None) == _lib.HA_ERR_NULL
+    assert lib.ha_probe_paged_read(ctypes.byref(good_shape(head_dim=96)), ctypes.byref(pages), FAKE, 2, FAKE, 1,
+                                   None) == _lib.HA_ERR_SHAPE
+    assert lib.ha_probe_paged_read(ctypes.byref(s), ctypes.byref(ring), FAKE, 2, FAKE, 1, None) == \
+        _lib.HA_ERR_UNSUPPORTED
+    assert lib.ha_probe_paged_read(ctypes.byref(s), ctypes.byref(pages), None, 2, FAKE, 1, None) == _lib.HA_ERR_NULL
+    assert lib.ha_probe_paged_read(ctypes.byref(s), ctypes.byref(pages), FAKE, -1, FAKE, 1, None) == \
+        _lib.HA_ERR_RANGE
+    assert lib.ha_probe_paged_read(ctypes.byref(s), ctypes.byref(pages), FAKE, 0, FAKE, 1, None) == _lib.HA_OK
+    assert lib.ha_probe_mfma_bf16(0, 10, FAKE, None) == _lib.HA_ERR_RANGE
+    assert lib.ha_probe_mfma_bf16(4, 0, FAKE, None) == _lib.HA_ERR_RANGE
+    assert lib.ha_probe_mfma_bf16(4, 10, None, None) == _lib.HA_ERR_NULL

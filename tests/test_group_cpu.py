@@ -62,3 +62,38 @@ def test_decode_plan_holds_its_tensors():
         del plan
         gc.collect()
         assert all(r() is None for r in refs), fuse
+
+
+def test_group_copies_share_a_pool_and_the_swa_pool_is_o_of_w():
+    shape, group = small_group()
+    full_i = group.kinds.index("full")
+    ring = torch.arange(2, dtype=torch.int32)
+    table = torch.arange(8, dtype=torch.int32).reshape(2, 4)
+    copy = grp.HybridGroup(shape, ring, 2, table, 8, pools={full_i: group.layers[full_i].pool})
+    assert copy.layers[full_i].pool is group.layers[full_i].pool
+    assert all(copy.layers[i].pool is not group.layers[i].pool for i in range(len(group.layers)) if i != full_i)
+    # 6 SWA layers x 2 rings x W slots x Hkv * D * 2 (K, V) * 2 bytes, whatever the history length
+    assert group.pool_bytes()["swa"] == 6 * 2 * shape.window * shape.num_kv_heads * shape.head_dim * 4
+    try:
+        grp.HybridGroup(shape, ring, 2, table, 8, pools={0: group.layers[full_i].pool})
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("a Full pool was accepted for an SWA layer")
+
+
+def test_verify_plan_holds_its_tensors():
+    shape, group = small_group()
+    nl, nq = len(group.layers), 3
+    q = [torch.zeros(2, nq, 8, 64, dtype=torch.bfloat16) for _ in range(nl)]
+    k = [torch.zeros(2, nq, 2, 64, dtype=torch.bfloat16) for _ in range(nl)]
+    v = [torch.zeros(2, nq, 2, 64, dtype=torch.bfloat16) for _ in range(nl)]
+    out = [torch.empty(2, nq, 8, 64) for _ in range(nl)]
+    lse = [torch.empty(2, nq, 8) for _ in range(nl)]
+    kv_len = torch.tensor([10, 40], dtype=torch.int32)
+    refs = [weakref.ref(t) for t in q + k + v + out + lse]
+    plan = grp.plan_verify(group, q, k, v, kv_len, 40, out, lse)
+    del q, k, v, out, lse
+    gc.collect()
+    assert all(r() is not None for r in refs)
+    assert len(plan.calls) == nl and plan.labels[-1] == f"verify[{nl - 1}:full]"
