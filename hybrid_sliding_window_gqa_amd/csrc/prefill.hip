@@ -77,6 +77,12 @@ template <bool kFull>
 constexpr int rows_per_wave() { return kFull ? 48 : 32; }
 template <bool kFull>
 constexpr int rows_per_wg() { return rows_per_wave<kFull>() * waves_per_wg<kFull>(); }
+// SWA layers write O through LDS with full-row non-temporal stores (see the
+// kernel's epilogue): 2% faster SWA layers on the chunked workload; full
+// layers, whose epilogue is a small part of a workgroup's time, measured the
+// same either way and keep the direct stores.
+template <bool kFull>
+constexpr bool lds_epilogue() { return !kFull; }
 
 // LDS tiles as 16-byte units (alignment known to the compiler, so stores and
 // loads are single ds_write_b128 / ds_read_b128 instructions).
@@ -693,6 +699,48 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
   }
 
   // ---- epilogue: normalise and write rows ----
+  if constexpr (lds_epilogue<kFull>()) {
+    // Each 16-row group goes through the wave's own LDS slab (the K/V tiles
+    // are no longer read: every wave passed the last tile's barrier), so
+    // that a store instruction writes two whole rows (2 x D floats,
+    // contiguous: consecutive heads of one position) instead of 16 rows x
+    // 64 bytes. O is written once and never read here: non-temporal stores.
+    constexpr int kPitch = D + 4;                                  // floats per LDS row
+    static_assert(kWaves * 16 * kPitch * 4 <= sizeof(sm), "O slabs fit in the tile buffers");
+    float* slab = reinterpret_cast<float*>(&sm) + wave * 16 * kPitch;
+    constexpr int kLanesPerRow = D / 4;                           // 16-byte pieces per row
+    constexpr int kRowsPerStore = 64 / kLanesPerRow;              // rows one instruction covers
+#pragma unroll
+    for (int rg = 0; rg < kRowGroups; ++rg) {
+      const float l = group4_sum(l_run[rg]);
+      const float inv = 1.0f / l;
+#pragma unroll
+      for (int d = 0; d < DT; ++d)
+        *reinterpret_cast<f32x4*>(&slab[c16 * kPitch + 16 * d + 4 * q4]) = o[rg][d] * inv;
+      {
+        const int rho = row0 + 16 * rg + c16;
+        const int ci = i0 + rho / G;
+        if (q4 == 0 && ci < i_end) {
+          const float mu = (m_run[rg] == -INFINITY) ? 0.0f : m_run[rg];
+          a.lse[static_cast<int64_t>(tok0 + ci) * hq + g * G + rho % G] = (mu + fast_log2(l)) * kLn2;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);                          // lgkmcnt(0): the slab is written
+#pragma unroll
+      for (int j = 0; j < 16 / kRowsPerStore; ++j) {
+        const int r = j * kRowsPerStore + lane / kLanesPerRow;     // row of the slab
+        const int col = 4 * (lane % kLanesPerRow);
+        const f32x4 val = *reinterpret_cast<const f32x4*>(&slab[r * kPitch + col]);
+        const int rho = row0 + 16 * rg + r;
+        const int ci = i0 + rho / G;
+        if (ci < i_end) {
+          const int64_t row = static_cast<int64_t>(tok0 + ci) * hq + g * G + rho % G;
+          __builtin_nontemporal_store(val, reinterpret_cast<f32x4*>(&a.out[row * D + col]));
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);                          // reads done before the slab is rewritten
+    }
+  } else {
 #pragma unroll
   for (int rg = 0; rg < kRowGroups; ++rg) {
     const float l = group4_sum(l_run[rg]);
@@ -709,6 +757,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
       const float mu = (m_run[rg] == -INFINITY) ? 0.0f : m_run[rg];
       a.lse[row] = (mu + fast_log2(l)) * kLn2;
     }
+  }
   }
 }
 
