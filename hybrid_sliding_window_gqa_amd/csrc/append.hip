@@ -225,12 +225,12 @@ __global__ __launch_bounds__(256) void append8_kernel(AppendArgs a) {
   float ka = 0.0f, va = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    ka = fmaxf(ka, fabsf(kx[j]));
-    va = fmaxf(va, fabsf(vx[j]));
+    ka = max_prop(ka, fabsf(kx[j]));
+    va = max_prop(va, fabsf(vx[j]));
   }
   for (int m = chunks >> 1; m >= 1; m >>= 1) {
-    ka = fmaxf(ka, __shfl_xor(ka, m));
-    va = fmaxf(va, __shfl_xor(va, m));
+    ka = max_prop(ka, __shfl_xor(ka, m));
+    va = max_prop(va, __shfl_xor(va, m));
   }
   const float ks = ka / 127.0f;
   const float vs = va / 127.0f;

@@ -159,6 +159,13 @@ __device__ __forceinline__ void load_q_rows(u32x4 (&qop)[D / 32], const void* q,
   for (int m = 0; m < D / 32; ++m) qop[m] = buf_load16(r, off + 64 * m);
 }
 
+// Float maximum that propagates NaN (the IEEE 754-2019 maximum): gfx950 has
+// it natively (v_maximum3_f32, three operands), and unlike fmaxf it needs no
+// NaN-quieting copy of each operand when NaNs are honoured. A NaN score, e.g.
+// from a stray read of poisoned memory, reaches the row's maximum and so its
+// output.
+__device__ __forceinline__ float max_prop(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -183,11 +190,11 @@ __device__ __forceinline__ void permlane16_swap(float& a, float& b) {
 __device__ __forceinline__ float group4_max(float v) {
   float a = v, b = v;
   permlane32_swap(a, b);
-  v = fmaxf(a, b);
+  v = max_prop(a, b);
   a = v;
   b = v;
   permlane16_swap(a, b);
-  return fmaxf(a, b);
+  return max_prop(a, b);
 }
 __device__ __forceinline__ float group4_sum(float v) {
   float a = v, b = v;

@@ -112,8 +112,8 @@ __device__ __forceinline__ void consume_block(BlockOps<D>& ops, const u32x4* qop
       ops.v[d].y &= mhi;
     }
   }
-  const float tmax = group4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))) * sl2;
-  const float m_new = fmaxf(m_run, tmax);
+  const float tmax = group4_max(max_prop(max_prop(s[0], s[1]), max_prop(s[2], s[3]))) * sl2;
+  const float m_new = max_prop(m_run, tmax);
   const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
   const float alpha = fast_exp2(m_run - m_use);
   float p[4];
@@ -211,7 +211,7 @@ __device__ __forceinline__ void consume_block8(const RawBlock8<D>& raw, const u3
   // it by more than kDecodeSlack (log2 units), so probabilities stay at most
   // 2^kDecodeSlack and O and l are rescaled only on those blocks, not on
   // every block: the widening already makes this path the vector-heavier one.
-  const float tmax = group4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))) * sl2;
+  const float tmax = group4_max(max_prop(max_prop(s[0], s[1]), max_prop(s[2], s[3]))) * sl2;
   if (__any(tmax > m_run + kDecodeSlack)) {
     const float m_new = (tmax > m_run + kDecodeSlack) ? tmax : m_run;
     const float alpha = (m_new == m_run) ? 1.0f : (m_run == -INFINITY ? 0.0f : fast_exp2(m_run - m_new));
@@ -417,20 +417,20 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
           kx[m][2 * j + 1] = __uint_as_float(w4[j] & 0xffff0000u);
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ka = fmaxf(ka, fabsf(kx[m][j]));
+        for (int j = 0; j < 8; ++j) ka = max_prop(ka, fabsf(kx[m][j]));
       }
-      ka = fmaxf(ka, __shfl_xor(ka, 16));
-      ka = fmaxf(ka, __shfl_xor(ka, 32));
+      ka = max_prop(ka, __shfl_xor(ka, 16));
+      ka = max_prop(ka, __shfl_xor(ka, 32));
       float vx[DT];
       float va = 0.0f;
 #pragma unroll
       for (int p = 0; p < D / 32; ++p) {
         vx[2 * p] = __uint_as_float(load_bf16_bits<kQF32>(a.v_new, src + 32 * p + c16) << 16);
         vx[2 * p + 1] = __uint_as_float(load_bf16_bits<kQF32>(a.v_new, src + 32 * p + 16 + c16) << 16);
-        va = fmaxf(va, fmaxf(fabsf(vx[2 * p]), fabsf(vx[2 * p + 1])));
+        va = max_prop(va, max_prop(fabsf(vx[2 * p]), fabsf(vx[2 * p + 1])));
       }
 #pragma unroll
-      for (int mask = 1; mask < 16; mask <<= 1) va = fmaxf(va, __shfl_xor(va, mask));
+      for (int mask = 1; mask < 16; mask <<= 1) va = max_prop(va, __shfl_xor(va, mask));
       n8.ks = ka / 127.0f;
       n8.vs = va / 127.0f;
 #pragma unroll
@@ -619,7 +619,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
     const int dd = e - h * D;
     float mx = sm_m[0][h];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, sm_m[w][h]);
+    for (int w = 1; w < kWaves; ++w) mx = max_prop(mx, sm_m[w][h]);
     const float mu = (mx == -INFINITY) ? 0.0f : mx;
     float l = 0.0f, acc = 0.0f;
 #pragma unroll
@@ -631,7 +631,8 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
     const int64_t row = static_cast<int64_t>(b) * hq + g * G + h;
     const float lse2 = mu + fast_log2(l);
     if (final_row) {
-      a.out[row * D + dd] = acc / l;
+      // l = 0: no valid key (an invalid ring id, or no valid page): O = 0, LSE = -inf
+      a.out[row * D + dd] = l > 0.0f ? acc / l : 0.0f;
       if (dd == 0) a.lse[row] = lse2 * kLn2;
     } else {
       a.part_o[(row * a.splits + split) * D + dd] = acc / l;
@@ -665,7 +666,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
   for (int s = 0; s < nsplit; ++s) {
     const float ls = pl[s];
     const float os = po[static_cast<int64_t>(s) * D];
-    const float mn = fmaxf(m, ls);
+    const float mn = max_prop(m, ls);
     const float mu = (mn == -INFINITY) ? 0.0f : mn;
     const float f = fast_exp2(m - mu);
     const float w = fast_exp2(ls - mu);
@@ -673,7 +674,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
     acc = acc * f + (w > 0.0f ? w * os : 0.0f);
     m = mn;
   }
-  a.out[row * D + dd] = acc / l;
+  a.out[row * D + dd] = l > 0.0f ? acc / l : 0.0f;
   if (dd == 0) a.lse[row] = ((m == -INFINITY ? 0.0f : m) + fast_log2(l)) * kLn2;
 }
 

@@ -309,14 +309,17 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
     else return -1;
   };
   // Element offset of this wave's block of tile `tile` (-1: nothing to load),
-  // plus the number of leading valid keys of that block.
-  auto block_of = [&](int tile, int pg, int& valid) -> int64_t {
+  // plus the number of leading valid keys of that block. `no_page`: a full
+  // history block whose page id is out of range; like decode and verify,
+  // prefill then treats its 16 positions as missing keys (masked).
+  auto block_of = [&](int tile, int pg, int& valid, bool& no_page) -> int64_t {
+    no_page = false;
     if (tile < n_hist_tiles) {
       const int lb = tile * kStageBlocks + sb;
       if (lb >= hist_blocks) { valid = 0; return -1; }
       if constexpr (kFull) {
         valid = min(kBlock, hist - lb * kBlock);
-        if (pg < 0 || pg >= a.num_blocks) { valid = 0; return -1; }
+        if (pg < 0 || pg >= a.num_blocks) { valid = 0; no_page = true; return -1; }
         return (static_cast<int64_t>(pg) * hkv + g) * kBlock * D;
       } else {
         valid = hist >= W ? kBlock : min(kBlock, max(0, hist - lb * kBlock));  // unwritten slots
@@ -361,12 +364,13 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
   int st_valid = kBlock;          // leading valid tokens of that block
   bool st_partial = false;        // partial history block: zero its unwritten V
   int st_drop = -1;               // ring slot of position hist - W in this block (zeroed), or -1
+  bool st_no_page = false;        // full history block without a valid page (its keys are masked)
   // K goes global -> LDS directly (buffer_load ... lds: lane l's 16 bytes land
   // at the wave's LDS base + 16 l); V goes through registers (partial history
   // blocks get their unwritten tokens zeroed on the way).
   auto load_tile = [&](int tile, int pg, int buf) {
     int valid;
-    const int64_t base = block_of(tile, pg, valid);
+    const int64_t base = block_of(tile, pg, valid, st_no_page);
     const int64_t b0 = base >= 0 ? base : 0;
     const uint32_t bytes = base >= 0 ? kBlock * D * 2 : 0;   // 0: loads return zeros, no traffic
     const bool hist_tile = tile < n_hist_tiles;
@@ -425,8 +429,12 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
     }
   };
   auto store_pos = [&](int buf) {
-    if constexpr (!kFull)
+    if constexpr (!kFull) {
       if (part == 0 && lane < kBlock) reinterpret_cast<int32_t*>(sm.pos[buf])[sb * kBlock + lane] = st_pos;
+    } else {
+      // one flag per block of the stage tile: 1 = no valid page
+      if (part == 0 && lane == 0) reinterpret_cast<int32_t*>(sm.pos[buf])[sb] = st_no_page ? 1 : 0;
+    }
   };
 
   // Key-position bounds of compute tile `sub` of stage tile `tile` (uniform):
@@ -495,6 +503,16 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
     if constexpr (!kFull) visible_any = visible_any && kmax >= qlo - W + 1;
     bool need_mask = !(exact && kmax <= qlo);
     if constexpr (!kFull) need_mask = need_mask || kmin < qhi - W + 1;
+    // Full history tiles: bit kb set = block kb of this compute tile has no valid page.
+    int no_page_bits = 0;
+    if constexpr (kFull) {
+      if (tile < n_hist_tiles) {
+        const int4 f = reinterpret_cast<const int4*>(sm.pos[buf])[sub];
+        no_page_bits = __builtin_amdgcn_readfirstlane((f.x & 1) | ((f.y & 1) << 1) | ((f.z & 1) << 2) |
+                                                      ((f.w & 1) << 3));
+        need_mask = need_mask || no_page_bits != 0;
+      }
+    }
 
     if (visible_any) {
       const u32x4* sk = sm.k[buf] + sub * kTileBlocks * (kBlk / 8);
@@ -538,7 +556,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 const int kpos = kmin + kBlock * kb + 4 * q4 + r;
-                kps[r] = kpos <= kmax ? kpos : -1;
+                kps[r] = (kpos <= kmax && !((no_page_bits >> kb) & 1)) ? kpos : -1;
               }
             } else {
               const int4 kp = sm.pos[buf][(sub * kTileBlocks + kb) * 4 + q4];
@@ -596,8 +614,8 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
           float mx = -INFINITY;
 #pragma unroll
           for (int kb = 0; kb < kTileBlocks; ++kb)
-            mx = fmaxf(mx, fmaxf(fmaxf(s[kb][rg][0], s[kb][rg][1]), fmaxf(s[kb][rg][2], s[kb][rg][3])));
-          const float m_new = fmaxf(m_run[rg], group4_max(mx) * sl2);
+            mx = max_prop(mx, max_prop(max_prop(s[kb][rg][0], s[kb][rg][1]), max_prop(s[kb][rg][2], s[kb][rg][3])));
+          const float m_new = max_prop(m_run[rg], group4_max(mx) * sl2);
           const float alpha = (m_new == -INFINITY || m_run[rg] == -INFINITY) ? 1.0f : fast_exp2(m_run[rg] - m_new);
           l_run[rg] *= alpha;
 #pragma unroll
@@ -635,14 +653,14 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
           float mx = -INFINITY;
 #pragma unroll
           for (int kb = 0; kb < kTileBlocks; ++kb)
-            mx = fmaxf(mx, fmaxf(fmaxf(s[kb][rg][0], s[kb][rg][1]), fmaxf(s[kb][rg][2], s[kb][rg][3])));
+            mx = max_prop(mx, max_prop(max_prop(s[kb][rg][0], s[kb][rg][1]), max_prop(s[kb][rg][2], s[kb][rg][3])));
           tmax[rg] = group4_max(mx) * sl2;
           grow = grow || (tmax[rg] > m_run[rg] + kRescaleSlack);
         }
         if (__any(grow)) {
 #pragma unroll
           for (int rg = 0; rg < kRowGroups; ++rg) {
-            const float m_new = fmaxf(m_run[rg], tmax[rg]);
+            const float m_new = max_prop(m_run[rg], tmax[rg]);
             const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run[rg] - m_new);
             l_run[rg] *= alpha;
 #pragma unroll

@@ -265,7 +265,7 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
       // The exp2 reference is raised only when a column's block max passes it
       // by more than kVerifySlack (log2 units): probabilities stay at most
       // 2^kVerifySlack, and O and l are rescaled on those blocks only.
-      const float tmax = group4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))) * sl2;
+      const float tmax = group4_max(max_prop(max_prop(s[0], s[1]), max_prop(s[2], s[3]))) * sl2;
       if (__any(tmax > cs.m_run + kVerifySlack)) {
         const float m_new = (tmax > cs.m_run + kVerifySlack) ? tmax : cs.m_run;
         const float alpha =
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
     const int c = threadIdx.x;
     float mx = sm_m[0][c];
 #pragma unroll
-    for (int w = 1; w < kVerifyWaves; ++w) mx = fmaxf(mx, sm_m[w][c]);
+    for (int w = 1; w < kVerifyWaves; ++w) mx = max_prop(mx, sm_m[w][c]);
     const float mu = (mx == -INFINITY) ? 0.0f : mx;
     float f[kVerifyWaves], l = 0.0f;
 #pragma unroll
@@ -508,7 +508,7 @@ __global__ __launch_bounds__(256) void verify_reduce_kernel(VerifyArgs a) {
   for (int s = 0; s < nsplit; ++s) {
     const float ls = pl[s];
     const float os = po[static_cast<int64_t>(s) * D];
-    const float mn = fmaxf(m, ls);
+    const float mn = max_prop(m, ls);
     const float mu = (mn == -INFINITY) ? 0.0f : mn;
     const float f = fast_exp2(m - mu);
     const float w = fast_exp2(ls - mu);

@@ -42,10 +42,14 @@
  * Errors. Every call returns ha_status. Arguments are validated on the host
  * before any HIP call, so a rejected call never touches the device.
  * ha_last_error() returns a message for the last failure on the calling
- * thread. Out-of-range ring or page ids found inside a kernel are not
- * reported: their keys are skipped (reads) or their writes dropped, and the
- * results for that sequence are undefined, but no memory outside the pools
- * is touched.
+ * thread. Ring or page ids out of range (negative, or >= the view's
+ * num_blocks) are not reported, and no memory outside the pools is touched:
+ *   - a history block whose page-table entry is out of range holds no keys:
+ *     decode, verify and prefill alike attend over the remaining positions,
+ *     and the appends drop their writes to it;
+ *   - a sequence whose ring id is out of range has no history keys (prefill
+ *     and verify still see their new tokens; decode then has no key at all
+ *     and returns O = 0, LSE = -inf, as for an empty row).
  *
  * Pool layouts (bfloat16, per layer). Both pools are made of blocks of 16
  * tokens x D channels (D = head_dim) of one kv head, 16*D values each:
