@@ -230,3 +230,34 @@ def test_fused_append_equals_append_then_decode(kind, d, window, qsrc):
     assert torch.equal(pa.v_scale.view(torch.int32), pb.v_scale.view(torch.int32))
     np.testing.assert_array_equal(oa, ob)
     np.testing.assert_array_equal(la, lb)
+
+
+def test_int8_quantization_error_at_long_context():
+    """The INT8 format's own error on the output at long context: decode of
+    the full layer over INT8 pools against the oracle over the unquantized
+    bf16 K/V, for the shortest, a middle and the longest sequence of the
+    ragged long-context workload (1K to 1M cached tokens). Long sequences
+    need the check most (blog.hotdry.top 2026-06-12, section "生产环境监控
+    要点": sampled before/after-quantization checks, especially on long
+    sequences). V's quantization alone moves O by at most half a step,
+    max|V| / 254, per key; the bound allows one whole step."""
+    shape = ha.HeadShape(64, 8, 128)
+    hist = np.sort(synth.ragged_structure().hist.astype(np.int64))
+    lens = [int(hist[0]) + 1, int(hist[len(hist) // 2]) + 1, int(hist[-1]) + 1]
+    gen = make_generator(77)
+    k = [randn_bf16(gen, n, 8, 128) for n in lens]
+    v = [randn_bf16(gen, n, 8, 128) for n in lens]
+    q = randn_bf16(gen, len(lens), 64, 128)
+    pool, view, _ = make_pools(shape, ha.HA_FULL, lens, seed=5)
+    append_history(shape, view, list(zip(k, v)), [0] * len(lens), lens)
+    out, lse = ha.hybrid_attn_decode(shape, view, i32(lens), q, max(lens))
+    torch.cuda.synchronize()
+    for s, n in enumerate(lens):
+        v_host = host(v[s])
+        ref_o, ref_l = attend(host(q[s:s + 1]), host(k[s]), v_host, np.array([n - 1]), "full", shape.window)
+        err_o = float(np.abs(host(out[s:s + 1]) - ref_o).max())
+        err_l = float(np.abs(host(lse[s:s + 1]) - ref_l).max())
+        v_max = float(np.abs(v_host).max())
+        print(f"[int8 quantization error] {n} keys: max|O - oracle(bf16 K/V)| {err_o:.3e}, "
+              f"max|LSE - oracle| {err_l:.3e} (max|V| {v_max:.2f})", flush=True)
+        assert err_o <= v_max / 127 and err_l <= 1e-2, (n, err_o, err_l)
