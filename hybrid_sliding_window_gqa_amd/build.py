@@ -21,7 +21,8 @@ ROOT = os.path.dirname(HERE)
 LIB_NAME = "libhybridattn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.cpp", "append.hip", "decode.hip", "prefill.hip", "verify.hip", "prefix_tree.cpp", "probe.hip"]
+SOURCES = ["api.cpp", "split_policy.cpp", "append.hip", "decode.hip", "prefill.hip", "verify.hip", "prefix_tree.cpp",
+           "probe.hip"]
 ARCH = "gfx950"
 
 
@@ -71,6 +72,30 @@ def build(verbose: bool = False) -> str:
     _check_kernel_stubs(tmp)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
+
+
+HOST_SANITIZED_SOURCES = ["api.cpp", "split_policy.cpp", "prefix_tree.cpp", "sanitize_stubs.cpp"]
+HOST_SANITIZED_DIR = os.path.join(BUILD_DIR, "host_sanitized")
+
+
+def build_host_sanitized() -> str:
+    """Host-only copy of the library for AddressSanitizer and
+    UndefinedBehaviorSanitizer: the host sources built by the host compiler
+    (no HIP code), the kernel launchers stubbed (sanitize_stubs.cpp). Returns
+    the library path. The GPU library is not touched."""
+    gxx = shutil.which("g++")
+    if gxx is None:
+        raise RuntimeError("g++ not found")
+    os.makedirs(HOST_SANITIZED_DIR, exist_ok=True)
+    out = os.path.join(HOST_SANITIZED_DIR, LIB_NAME)
+    sanitize = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-Wall", "-Wno-unused-function",
+           "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include", "-I", os.path.join(ROOT, "include"), *sanitize,
+           *[os.path.join(CSRC, s) for s in HOST_SANITIZED_SOURCES], "-o", out]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"host sanitizer build failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    return out
 
 
 def _check_kernel_stubs(lib: str) -> None:

@@ -678,48 +678,6 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
   if (dd == 0) a.lse[row] = ((m == -INFINITY ? 0.0f : m) + fast_log2(l)) * kLn2;
 }
 
-// Split policy. Every split of the longest sequence is equally long. Decode
-// is bound by HBM, and two resident 4-wave workgroups per CU already keep a
-// CU's share of the bandwidth busy (measured: a third one adds nothing), so
-// a round is 256 CUs x 2 workgroups. The split count minimises
-// (rounds) x (blocks per workgroup + a fixed cost), plus the merge's cost
-// when there is more than one split (the reduce launch and the partial rows,
-// about 8 blocks' worth at full load on MI355X). Equal workgroups and whole rounds avoid
-// a tail of partly idle CUs. When one split per sequence cannot give every
-// CU two workgroups, workgroups are capped at 208 blocks (1.6 MiB of K/V) so
-// ragged batches still spread over the chip. (Ragged decode workload, 24
-// sequences of 1K to 1M tokens, full-layer call on one MI355X: 224 splits
-// of up to 256 blocks 2651 us; 255 to 320 splits 2547 to 2575 us.)
-int decode_split_blocks(bool full, int window, int max_kv_len, int batch, int hkv, int requested_splits) {
-  if (!full) return window / kBlock;
-  const int nblk = (max(max_kv_len, 1) + kBlock - 1) / kBlock;
-  if (requested_splits > 0) return max(1, (nblk + requested_splits - 1) / requested_splits);
-  constexpr int64_t kSlots = 256 * 2;
-  constexpr int kMaxBlocks = 208, kMinBlocks = 4, kFixedCost = 4, kMergeCost = 8;
-  const int64_t pairs = static_cast<int64_t>(max(batch, 1)) * max(hkv, 1);
-  const int s_lo = pairs >= kSlots ? 1 : max(1, (nblk + kMaxBlocks - 1) / kMaxBlocks);
-  const int s_hi = min(max(s_lo, nblk / kMinBlocks), s_lo + 512);
-  int best_sb = (nblk + s_lo - 1) / s_lo;
-  int64_t best_cost = INT64_MAX;
-  for (int s = s_lo; s <= s_hi; ++s) {
-    const int sb = (nblk + s - 1) / s;
-    const int64_t s_eff = (nblk + sb - 1) / sb;
-    const int64_t rounds = (pairs * s_eff + kSlots - 1) / kSlots;
-    const int64_t cost = rounds * (sb + kFixedCost) + (s_eff > 1 ? kMergeCost : 0);
-    if (cost < best_cost) {
-      best_cost = cost;
-      best_sb = sb;
-    }
-  }
-  return best_sb;
-}
-
-int decode_num_splits(bool full, int window, int max_kv_len, int split_blocks) {
-  if (!full) return 1;
-  const int nblk = (max(max_kv_len, 1) + kBlock - 1) / kBlock;
-  return (nblk + split_blocks - 1) / split_blocks;
-}
-
 template <int D>
 static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.full ? a.splits : 1, a.geo.hkv, a.batch);

@@ -127,10 +127,6 @@ __device__ __forceinline__ u32x4 drop_token_v(u32x4 v, int q, int tok) {
 
 }  // namespace
 
-int64_t prefill_stage_blocks(int num_tokens, int batch) {
-  return (static_cast<int64_t>(num_tokens) + kBlock - 1) / kBlock + batch;
-}
-
 // ---- 1. stage the chunk's K/V as 16-token blocks ----
 // Grid (ceil(max_new/16), batch); one workgroup per (sequence, block), all kv heads.
 template <int D, bool kF32>

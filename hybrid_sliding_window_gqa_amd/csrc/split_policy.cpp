@@ -1,0 +1,67 @@
+// Host-side sizing policies shared by the workspace queries (api.cpp) and the
+// kernel launchers: how decode splits a sequence's keys over workgroups, and
+// how many 16-token blocks prefill's chunk staging needs. Plain host code, so
+// the host-only sanitizer build of the library links it unchanged.
+#include <climits>
+
+#include "kernels.hpp"
+
+namespace ha {
+
+namespace {
+constexpr int kBlockTokens = 16;   // tokens per page / ring block
+template <typename T>
+T max_of(T a, T b) { return a > b ? a : b; }
+template <typename T>
+T min_of(T a, T b) { return a < b ? a : b; }
+}  // namespace
+
+// Workspace of hybrid_attn_prefill: sequence b's staged blocks start at
+// ceil(cu_new[b] / 16) + b, so every sequence's first block is its own.
+int64_t prefill_stage_blocks(int num_tokens, int batch) {
+  return (static_cast<int64_t>(num_tokens) + kBlockTokens - 1) / kBlockTokens + batch;
+}
+
+// Split policy. Every split of the longest sequence is equally long. Decode
+// is bound by HBM, and two resident 4-wave workgroups per CU already keep a
+// CU's share of the bandwidth busy (measured: a third one adds nothing), so
+// a round is 256 CUs x 2 workgroups. The split count minimises
+// (rounds) x (blocks per workgroup + a fixed cost), plus the merge's cost
+// when there is more than one split (the reduce launch and the partial rows,
+// about 8 blocks' worth at full load on MI355X). Equal workgroups and whole rounds avoid
+// a tail of partly idle CUs. When one split per sequence cannot give every
+// CU two workgroups, workgroups are capped at 208 blocks (1.6 MiB of K/V) so
+// ragged batches still spread over the chip. (Ragged decode workload, 24
+// sequences of 1K to 1M tokens, full-layer call on one MI355X: 224 splits
+// of up to 256 blocks 2651 us; 255 to 320 splits 2547 to 2575 us.)
+int decode_split_blocks(bool full, int window, int max_kv_len, int batch, int hkv, int requested_splits) {
+  if (!full) return window / kBlockTokens;
+  const int nblk = (max_of(max_kv_len, 1) + kBlockTokens - 1) / kBlockTokens;
+  if (requested_splits > 0) return max_of(1, (nblk + requested_splits - 1) / requested_splits);
+  constexpr int64_t kSlots = 256 * 2;
+  constexpr int kMaxBlocks = 208, kMinBlocks = 4, kFixedCost = 4, kMergeCost = 8;
+  const int64_t pairs = static_cast<int64_t>(max_of(batch, 1)) * max_of(hkv, 1);
+  const int s_lo = pairs >= kSlots ? 1 : max_of(1, (nblk + kMaxBlocks - 1) / kMaxBlocks);
+  const int s_hi = min_of(max_of(s_lo, nblk / kMinBlocks), s_lo + 512);
+  int best_sb = (nblk + s_lo - 1) / s_lo;
+  int64_t best_cost = INT64_MAX;
+  for (int s = s_lo; s <= s_hi; ++s) {
+    const int sb = (nblk + s - 1) / s;
+    const int64_t s_eff = (nblk + sb - 1) / sb;
+    const int64_t rounds = (pairs * s_eff + kSlots - 1) / kSlots;
+    const int64_t cost = rounds * (sb + kFixedCost) + (s_eff > 1 ? kMergeCost : 0);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best_sb = sb;
+    }
+  }
+  return best_sb;
+}
+
+int decode_num_splits(bool full, int window, int max_kv_len, int split_blocks) {
+  if (!full) return 1;
+  const int nblk = (max_of(max_kv_len, 1) + kBlockTokens - 1) / kBlockTokens;
+  return (nblk + split_blocks - 1) / split_blocks;
+}
+
+}  // namespace ha
