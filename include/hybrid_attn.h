@@ -98,7 +98,11 @@ extern "C" {
 typedef enum ha_status {
   HA_OK = 0,
   HA_ERR_NULL = 1,        /* a required pointer is NULL                        */
-  HA_ERR_SHAPE = 2,       /* unsupported head counts, head_dim, window, page   */
+  HA_ERR_SHAPE = 2,       /* unsupported geometry: Hq % Hkv != 0, group not in
+                             {1,2,4,8,16}, head_dim not 64 or 128, window not a
+                             positive multiple of 16 (the ring is made of
+                             16-slot blocks), page_size != 16, or a
+                             non-finite softmax_scale                         */
   HA_ERR_RANGE = 3,       /* negative or inconsistent sizes                    */
   HA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required        */
   HA_ERR_UNSUPPORTED = 5, /* dtype or layer kind not supported                 */

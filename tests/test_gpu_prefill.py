@@ -237,3 +237,19 @@ def test_swa_ring_holding_only_the_needed_window():
         rows = np.arange(h, t)
         ref_o, ref_l = oracle_rows(host(seqs.q[b])[rows], host(seqs.k[b]), host(seqs.v[b]), rows, "swa", w)
         assert_close(o[cu[b]:cu[b + 1]], l[cu[b]:cu[b + 1]], ref_o, ref_l, f"seq {b}")
+
+
+@pytest.mark.parametrize("boundaries", [
+    [[0, 2100], [0, 129], [0, 700]],                       # one-shot, ragged ends
+    [[0, 300, 2400], [0, 5, 1000], [0, 1601, 1745]],       # chunks after a history that is not page-aligned
+])
+def test_swa_long_chunks_match_oracle(boundaries):
+    """SWA prefill at the workloads' geometry (Hq/Hkv/D 64/8/128, W = 128,
+    bf16) over chunks of up to 2100 tokens: every row against the oracle,
+    with ragged ends, partial last blocks and histories that end inside a
+    page."""
+    shape = ha.HeadShape(64, 8, 128)
+    totals = [bd[-1] for bd in boundaries]
+    seqs = Seqs(shape, totals, seed=123)
+    outs, lses = run_chunks(shape, ha.HA_SWA, seqs, boundaries)
+    check_against_oracle(shape, ha.HA_SWA, seqs, outs, lses)
