@@ -522,7 +522,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
         // K operands stream through a short register window: operand j
         // (block j / KS, reduction step j % KS) feeds one MFMA per row group.
         constexpr int kKOps = kTileBlocks * KS;
-        constexpr int kAhead = kFull ? 3 : 8;   // K operands in flight
+        constexpr int kAhead = kFull ? 5 : 8;   // K operands in flight
         u32x4 kr[kKOps];
 #pragma unroll
         for (int j = 0; j < kKOps; ++j) kr[j] = sk[(j / KS) * (kBlk / 8) + 64 * (j % KS) + lane];
@@ -685,9 +685,10 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
           }
         }
       }
-      // V operand reads run kVAhead (dim tile, block pair) steps ahead of
-      // their MFMAs (one step with three row groups: registers are short).
-      constexpr int kVAhead = kRowGroups > 2 ? 1 : 2;
+      // V operand reads run two (dim tile, block pair) steps ahead of their
+      // MFMAs: on one MI355X, 3.9% faster full layers than one step ahead,
+      // with K operands five reads ahead instead of three.
+      constexpr int kVAhead = 2;
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVAhead, 1);
 #pragma unroll
       for (int i = 0; i < (DT / 2) * (kTileBlocks / 2) - kVAhead; ++i) {
