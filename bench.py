@@ -150,6 +150,8 @@ PREFILL_PROFILE = "prefill_kernel_full_chunked4x32768_pmc.txt"
 VERIFY_PROFILE = "verify_kernel_full_verify64x8192_pmc.txt"
 RAGGED_PROFILE = "decode_kernel_full_ragged24_pmc.txt"
 REUSE_PROFILE = "prefill_kernel_full_reuse32_pmc.txt"
+SWA_DECODE_PROFILE = "decode_kernel_swa_decode64x8192_pmc.txt"
+SWA_PREFILL_PROFILE = "prefill_kernel_swa_chunked4x32768_pmc.txt"
 
 
 def run_copy(torch, args, device):
@@ -407,6 +409,7 @@ def run_decode(torch, ha, grp, synth, struct, args, device):
         "full_decode_gbs": full_bytes / full_ms / 1e6,
         "swa_decode_ms": swa_ms,
         "swa_decode_gbs": swa_bytes / swa_ms / 1e6,
+        "swa_decode_bytes": swa_bytes,
         "append_ms_avg": float(np.mean(call_ms[app_idx])) if app_idx else None,
         "fused_append": not app_idx,
         "calls_ms": by_label,
@@ -479,14 +482,15 @@ def run_decode_int8(torch, ha, grp, synth, args, device):
 
 
 def int8_quant_error(torch, synth, q8, args):
-    """max |O_int8 - O_oracle| and |LSE_int8 - LSE_oracle| on sampled
-    sequences of the INT8 decode step, where the oracle attends over the
-    unquantized bf16 K/V: the end-to-end error the 8-bit format adds."""
-    sys.path.insert(0, HERE)
-    from oracle.attention import attend
-
+    """max |O_int8 - O_ref| and |LSE_int8 - LSE_ref| on sampled sequences of
+    the INT8 decode step. O_ref is plain float32 attention (torch products
+    and softmax on the GPU) over the unquantized bf16 K/V the pools were
+    quantized from: the output change that the 8-bit format causes."""
     shape, group, _plan, data = q8["copies"][0]
     hist = data["hist"]
+    hq, hkv, d = shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    g = hq // hkv
+    scale = shape.softmax_scale if shape.softmax_scale > 0 else 1.0 / float(np.sqrt(d))
     rows = [0, len(hist) // 3, 2 * len(hist) // 3, len(hist) - 1]
     err_o = err_l = 0.0
     for li, layer in enumerate(group.layers):
@@ -494,15 +498,19 @@ def int8_quant_error(torch, synth, q8, args):
             continue
         k_hist, v_hist, start, cu = data["logical"][li]
         for b in rows:
-            k = torch.cat([k_hist[cu[b]:cu[b + 1]], data["k"][li][b:b + 1]]).float().cpu().numpy()
-            v = torch.cat([v_hist[cu[b]:cu[b + 1]], data["v"][li][b:b + 1]]).float().cpu().numpy()
-            q = data["q"][li][b:b + 1].float().cpu().numpy()
-            o_ref, l_ref = attend(q, k, v, [int(hist[b] - start[b])], layer.kind, shape.window)
-            err_o = max(err_o, float(np.abs(data["out"][li][b].cpu().numpy() - o_ref[0]).max()))
-            err_l = max(err_l, float(np.abs(data["lse"][li][b].cpu().numpy() - l_ref[0]).max()))
+            k = torch.cat([k_hist[cu[b]:cu[b + 1]], data["k"][li][b:b + 1]]).float()
+            v = torch.cat([v_hist[cu[b]:cu[b + 1]], data["v"][li][b:b + 1]]).float()
+            if layer.kind == "swa":                  # keys at positions > t - W
+                k, v = k[-shape.window:], v[-shape.window:]
+            q = data["q"][li][b].float().reshape(hkv, g, d)
+            s = torch.bmm(q, k.permute(1, 2, 0).contiguous()) * scale          # [hkv, g, n]
+            lse = torch.logsumexp(s, dim=-1)
+            o = torch.bmm(torch.softmax(s, dim=-1), v.permute(1, 0, 2).contiguous())
+            err_o = max(err_o, float((data["out"][li][b] - o.reshape(hq, d)).abs().max()))
+            err_l = max(err_l, float((data["lse"][li][b] - lse.reshape(hq)).abs().max()))
     return {"max_abs_o": err_o, "max_abs_lse": err_l,
             "sample": f"sequences {rows} of the INT8 decode step, SWA layer 0 and the full layer, all query "
-                      f"heads, against the fp64 oracle over the unquantized bf16 K/V ({int(hist[0]) + 1} keys)"}
+                      f"heads, against float32 attention over the unquantized bf16 K/V ({int(hist[0]) + 1} keys)"}
 
 
 def verify_layer_bytes(shape, kind, t0, nq):
@@ -652,6 +660,8 @@ def run_chunked(torch, ha, grp, synth, args, device, cpu_seconds=0.0):
         "full_layer_tflops": flops["full"] / (full_ms * 1e-3) / 1e12,
         "swa_layers_ms": swa_ms,
         "swa_layer_gbs": swa_bytes_per_layer * n_swa / (swa_ms * 1e-3) / 1e9,
+        "swa_call_bytes": swa_bytes_per_layer // nchunks,
+        "swa_call_traffic": profile_traffic(SWA_PREFILL_PROFILE),
         "roofline": {
             "bound": "mfma",
             "achieved": flops["full"] / (full_ms * 1e-3) / 1e12,
@@ -774,6 +784,8 @@ def run_reuse(torch, ha, grp, synth, args, device, cpu_seconds=0.0):
                      "frac": full_tf / MFMA_BF16_PEAK_TFLOPS, "traffic": profile_traffic(REUSE_PROFILE),
                      "kernel": "hybrid_attn_prefill, full layer (stage_chunk_kernel + prefill_kernel<128,full>)",
                      "flops_per_launch": flops["full"]},
+        "full_call_compulsory_bytes": int(t_new * hq * d * (2 + 4) + t_new * hq * 4
+                                          + (t_new + int(reuse_len.sum())) * kv_bytes_per_token(shape)),
         "mean_recomputed_tail": float((prefix - reuse_len).mean()),
         "data": "synthetic",
         **({"cpu_baseline": cpu} if cpu else {}),
@@ -1118,7 +1130,11 @@ def main():
         print(json.dumps(run_restore(torch, ha, grp, synth, args, device)))
         return 0
     if args.workload == "decode_int8":
-        print(json.dumps(run_decode_int8(torch, ha, grp, synth, args, device)))
+        q8 = run_decode_int8(torch, ha, grp, synth, args, device)
+        if not args.no_quant_error:
+            q8["quant_error"] = int8_quant_error(torch, synth, q8, args)
+        del q8["copies"]                # the pools, kept for the quantization-error sample
+        print(json.dumps(q8))
         return 0
     struct = {"decode": synth.decode_structure, "ragged": synth.ragged_structure}[args.workload]()
     log(f"[bench] workload={args.workload} building inputs")
@@ -1171,6 +1187,8 @@ def main():
             "bytes_per_launch": full_bytes,
         },
     }
+    if args.workload == "decode":
+        line["decode_detail"]["swa_decode_traffic"] = profile_traffic(SWA_DECODE_PROFILE)
     if args.workload == "decode" and not args.no_ceilings:
         log("[bench] ceilings")
         line["ceilings"] = run_ceilings(torch, shape, group, data, device)
@@ -1235,7 +1253,7 @@ def main():
         ru = run_reuse(torch, ha, grp, synth, args, device,
                        0.0 if args.no_cpu_baseline else args.cpu_reuse_seconds)
         line["reuse"] = {k: ru[k] for k in ("workload", "pass_ms", "tflops", "pct_mfma_peak", "full_layer_tflops",
-                                            "mean_recomputed_tail", "roofline")}
+                                            "mean_recomputed_tail", "full_call_compulsory_bytes", "roofline")}
         line["reuse"]["full_layer_frac"] = ru["roofline"]["frac"]
         if "cpu_baseline" in ru:
             line["reuse"]["cpu_baseline"] = ru["cpu_baseline"]
