@@ -52,6 +52,7 @@
 // dispatched back to back (heaviest, i.e. latest, first), so the workgroups
 // resident on an XCD stream one pair's K/V in near lockstep through its L2.
 #include <cmath>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -106,6 +107,9 @@ constexpr float kAcceptSum = 65536.0f;
 // the exp2 reference is only raised when a tile's max exceeds it by more
 // than this, so probabilities stay <= 2^8 and the O/l rescale is rare.
 constexpr float kRescaleSlack = 8.0f;
+// Position staged for an SWA ring slot that holds no key: far enough below
+// every query position that the window test's unsigned distance exceeds W.
+constexpr int kNoKey = -(1 << 30);
 
 // V unit of lane group q holds tokens 4q..4q+3 (for two channels): zero the
 // tokens at index >= nv.
@@ -252,10 +256,13 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
     hist_blocks = W / kBlock;
     if (ring_ok && hist > 0 && t_first - W + 1 < hist) n_hist_tiles = (hist_blocks + kStageBlocks - 1) / kStageBlocks;
   }
-  int c_lo = 0;
-  if constexpr (!kFull) c_lo = max(0, i0 - W + 1);
-  const int first_ctile = c_lo / kStageKeys;
-  const int n_chunk_tiles = (i_end + kStageKeys - 1) / kStageKeys - first_ctile;
+  // Chunk tiles start at chunk index c_first: 0 for full layers; for SWA
+  // layers the block holding the first key any row of the workgroup sees,
+  // so a 16-position query block's window (143 keys) takes 9 blocks -- two
+  // full tiles and a 1-block tile -- instead of three 64-aligned tiles.
+  int c_first = 0;
+  if constexpr (!kFull) c_first = kBlock * (max(0, i0 - W + 1) / kBlock);
+  const int n_chunk_tiles = (i_end - c_first + kStageKeys - 1) / kStageKeys;
   const int n_tiles = n_hist_tiles + n_chunk_tiles;
 
   // ---- rows of this wave ----
@@ -322,7 +329,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
         return ((static_cast<int64_t>(ring) * hkv + g) * W + kBlock * lb) * D;
       }
     } else {
-      const int cb = (first_ctile + tile - n_hist_tiles) * kStageBlocks + sb;  // chunk block
+      const int cb = c_first / kBlock + (tile - n_hist_tiles) * kStageBlocks + sb;  // chunk block
       if (kBlock * cb >= i_end) { valid = 0; return -1; }
       valid = min(kBlock, i_end - kBlock * cb);
       return ((stage_blk0 + cb) * hkv + g) * kBlock * D;  // K part; V part is offset by stage_blocks
@@ -336,16 +343,16 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
         return p < hist ? p : -1;
       } else {
         const int s = tile * kStageKeys + kk;             // ring slot
-        if (s >= W) return -1;
+        if (s >= W) return kNoKey;
         const int last = hist - 1;
         int d = (last - s) % W;
         if (d < 0) d += W;
         const int p = last - d;
-        return p >= 0 ? p : -1;
+        return p >= 0 ? p : kNoKey;
       }
     } else {
-      const int ci = (first_ctile + tile - n_hist_tiles) * kStageKeys + kk;
-      return (ci < i_end) ? hist + ci : -1;
+      const int ci = c_first + (tile - n_hist_tiles) * kStageKeys + kk;
+      return (ci < i_end) ? hist + ci : kNoKey;
     }
   };
 
@@ -447,7 +454,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
         exact = false;
       }
     } else {
-      const int c0 = (first_ctile + tile - n_hist_tiles) * kStageKeys + kTileKeys * sub;
+      const int c0 = c_first + (tile - n_hist_tiles) * kStageKeys + kTileKeys * sub;
       kmin = hist + c0;
       kmax = hist + min(c0 + kTileKeys, i_end) - 1;
       exact = c0 + kTileKeys <= i_end;
@@ -510,10 +517,15 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
       }
     }
 
-    if (visible_any) {
+    // One compute tile whose keys sit in its first NB blocks (NB < 4 only
+    // for the last chunk tile of an SWA window; the other blocks hold
+    // zeros and are not computed).
+    auto compute_tile = [&](auto nb_const) __attribute__((always_inline)) {
+      constexpr int NB = decltype(nb_const)::value;
+      constexpr int kPairs = (NB + 1) / 2;
       const u32x4* sk = sm.k[buf] + sub * kTileBlocks * (kBlk / 8);
       const u32x4* sv = sm.v[buf] + sub * (kTileBlocks / 2) * (DT / 2) * 2 * 64;
-      f32x4 s[kTileBlocks][kRowGroups];
+      f32x4 s[NB][kRowGroups];
       // S^T = K Q^T for the tile (then masked where needed).
       auto scores = [&]() __attribute__((always_inline)) {
         // Compiler-only fence: the recomputation must read K again rather
@@ -521,13 +533,13 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
         asm volatile("" ::: "memory");
         // K operands stream through a short register window: operand j
         // (block j / KS, reduction step j % KS) feeds one MFMA per row group.
-        constexpr int kKOps = kTileBlocks * KS;
-        constexpr int kAhead = kFull ? 5 : 8;   // K operands in flight
+        constexpr int kKOps = NB * KS;
+        constexpr int kAhead = (kFull ? 5 : 8) < kKOps ? (kFull ? 5 : 8) : kKOps;   // K operands in flight
         u32x4 kr[kKOps];
 #pragma unroll
         for (int j = 0; j < kKOps; ++j) kr[j] = sk[(j / KS) * (kBlk / 8) + 64 * (j % KS) + lane];
 #pragma unroll
-        for (int kb = 0; kb < kTileBlocks; ++kb)
+        for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
           for (int rg = 0; rg < kRowGroups; ++rg) s[kb][rg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -545,7 +557,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
 
         if (need_mask) {
 #pragma unroll
-          for (int kb = 0; kb < kTileBlocks; ++kb) {
+          for (int kb = 0; kb < NB; ++kb) {
             int kps[4];
             if constexpr (kFull) {
               // key kk of the tile sits at position kmin + kk, valid up to kmax
@@ -554,16 +566,30 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
                 const int kpos = kmin + kBlock * kb + 4 * q4 + r;
                 kps[r] = (kpos <= kmax && !((no_page_bits >> kb) & 1)) ? kpos : -1;
               }
-            } else {
+            } else if (tile < n_hist_tiles) {
+              // ring slots: their staged positions (kNoKey where a slot holds none)
               const int4 kp = sm.pos[buf][(sub * kTileBlocks + kb) * 4 + q4];
               kps[0] = kp.x; kps[1] = kp.y; kps[2] = kp.z; kps[3] = kp.w;
+            } else {
+              // chunk keys: contiguous from kmin, present up to kmax
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int kpos = kmin + kBlock * kb + 4 * q4 + r;
+                kps[r] = kpos <= kmax ? kpos : kNoKey;
+              }
             }
 #pragma unroll
             for (int rg = 0; rg < kRowGroups; ++rg) {
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
-                bool ok = kps[r] >= 0 && kps[r] <= qpos[rg];
-                if constexpr (!kFull) ok = ok && kps[r] > qpos[rg] - W;
+                bool ok;
+                if constexpr (kFull) {
+                  ok = kps[r] >= 0 && kps[r] <= qpos[rg];
+                } else {
+                  // in the window: 0 <= qpos - kpos < W, one unsigned compare
+                  // (a key after the query wraps to a large distance; kNoKey too)
+                  ok = static_cast<uint32_t>(qpos[rg]) - static_cast<uint32_t>(kps[r]) < static_cast<uint32_t>(W);
+                }
                 s[kb][rg][r] = ok ? s[kb][rg][r] : -INFINITY;
               }
             }
@@ -574,7 +600,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
 
       // Probabilities against the current reference m_run, in bf16 for the
       // matrix cores and summed in fp32 for l.
-      u32x4 pb[kTileBlocks / 2][kRowGroups];   // P^T for block pairs: B operands of P.V
+      u32x4 pb[kPairs][kRowGroups];   // P^T for block pairs: B operands of P.V
       float lsum[kRowGroups];
       auto probabilities = [&]() __attribute__((always_inline)) {
         float m_use[kRowGroups];
@@ -584,7 +610,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
           lsum[rg] = 0.0f;
         }
 #pragma unroll
-        for (int kb = 0; kb < kTileBlocks; ++kb) {
+        for (int kb = 0; kb < NB; ++kb) {
 #pragma unroll
           for (int rg = 0; rg < kRowGroups; ++rg) {
             float p[4];
@@ -601,6 +627,13 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
             }
           }
         }
+        if constexpr (NB & 1) {   // the last pair's second block has no keys: P = 0
+#pragma unroll
+          for (int rg = 0; rg < kRowGroups; ++rg) {
+            pb[NB / 2][rg].z = 0u;
+            pb[NB / 2][rg].w = 0u;
+          }
+        }
       };
       // Raise each row's reference to the max of its scores in this tile
       // (a cross-lane reduction) where that is higher, rescaling O and l.
@@ -609,7 +642,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
         for (int rg = 0; rg < kRowGroups; ++rg) {
           float mx = -INFINITY;
 #pragma unroll
-          for (int kb = 0; kb < kTileBlocks; ++kb)
+          for (int kb = 0; kb < NB; ++kb)
             mx = max_prop(mx, max_prop(max_prop(s[kb][rg][0], s[kb][rg][1]), max_prop(s[kb][rg][2], s[kb][rg][3])));
           const float m_new = max_prop(m_run[rg], group4_max(mx) * sl2);
           const float alpha = (m_new == -INFINITY || m_run[rg] == -INFINITY) ? 1.0f : fast_exp2(m_run[rg] - m_new);
@@ -648,7 +681,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
         for (int rg = 0; rg < kRowGroups; ++rg) {
           float mx = -INFINITY;
 #pragma unroll
-          for (int kb = 0; kb < kTileBlocks; ++kb)
+          for (int kb = 0; kb < NB; ++kb)
             mx = max_prop(mx, max_prop(max_prop(s[kb][rg][0], s[kb][rg][1]), max_prop(s[kb][rg][2], s[kb][rg][3])));
           tmax[rg] = group4_max(mx) * sl2;
           grow = grow || (tmax[rg] > m_run[rg] + kRescaleSlack);
@@ -673,7 +706,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
       // reduction slots 8q..8q+3 of a lane are keys 4q..4q+3 of block kb,
       // slots 8q+4..8q+7 the same keys of block kb+1, in both operands.
 #pragma unroll
-      for (int pair = 0; pair < kTileBlocks / 2; ++pair) {
+      for (int pair = 0; pair < kPairs; ++pair) {
 #pragma unroll
         for (int p = 0; p < DT / 2; ++p) {
           const u32x4 v0 = sv[((pair * (DT / 2) + p) * 2 + 0) * 64 + lane];   // dim tile 2p
@@ -691,11 +724,23 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
       constexpr int kVAhead = 2;
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVAhead, 1);
 #pragma unroll
-      for (int i = 0; i < (DT / 2) * (kTileBlocks / 2) - kVAhead; ++i) {
+      for (int i = 0; i < (DT / 2) * kPairs - kVAhead; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * kRowGroups, 1);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 2 * kRowGroups * kVAhead, 1);
+    };
+    if (visible_any) {
+      if constexpr (kFull) {
+        compute_tile(std::integral_constant<int, kTileBlocks>{});
+      } else {
+        // ring tiles use all four blocks; a chunk tile only those its keys reach
+        const int nb = tile < n_hist_tiles ? kTileBlocks : (kmax - kmin) / kBlock + 1;
+        if (nb >= 4) compute_tile(std::integral_constant<int, 4>{});
+        else if (nb == 3) compute_tile(std::integral_constant<int, 3>{});
+        else if (nb == 2) compute_tile(std::integral_constant<int, 2>{});
+        else compute_tile(std::integral_constant<int, 1>{});
+      }
     }
     if (sub + 1 < kSubTiles && has_next) {
       // next V phase: this one's loads (and the K loads before them) are done
