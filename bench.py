@@ -960,11 +960,22 @@ def run_ceilings(torch, shape, group, data, device):
         dt = timed(lambda: _lib.check(lib.ha_probe_mfma_bf16(wgs, iters, fsink.data_ptr(), sptr)), reps=5)
         best = max(best, (wgs * 4 * iters * 8 * 16384 / dt / 1e12, wgs))
     out["mfma_bf16_tflops"] = round(best[0], 1)
+    # Matrix cores beside vector work (two waves per SIMD, one workgroup per CU): how much of one
+    # wave's exp2/FMA work hides under another wave's products on the same SIMD.
+    csink = torch.empty(256 * 512, dtype=torch.float32, device=device)
+    cms = {}
+    for mode, name in enumerate(("matrix_only", "split_waves", "in_phase", "ping_pong", "vector_only")):
+        dt = timed(lambda m=mode: _lib.check(lib.ha_probe_coissue(m, 256, 2000, csink.data_ptr(), sptr)), reps=3)
+        cms[name] = round(dt * 1e3, 3)
+    out["coissue_ms"] = cms
     out["what"] = ("copy: dst = -src over 2 GiB; write_only: a fill of 2 GiB; decode_pattern_read: every K/V block of the decode "
                    f"workload's full pool ({nbytes} B) read as the full-layer decode kernel walks it, no "
                    "arithmetic (nt: non-temporal loads, as decode issues them); mfma: v_mfma_f32_16x16x32_bf16 "
-                   f"with register operands, best of 1, 2 and 4 waves per SIMD ({best[1] // 256} per SIMD)")
-    del sink, fsink
+                   f"with register operands, best of 1, 2 and 4 waves per SIMD ({best[1] // 256} per SIMD); "
+                   "coissue_ms: ha_probe_coissue modes 0-4 (96 MFMAs and 96 exp2/FMA pairs per wave and "
+                   "iteration, 2000 iterations, 8 waves per CU): matrix blocks only, waves 0-3 matrix next to "
+                   "waves 4-7 vector, both in phase between barriers, ping-pong, vector blocks only")
+    del sink, fsink, csink
     return out
 
 

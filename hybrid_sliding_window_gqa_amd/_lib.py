@@ -61,6 +61,7 @@ EXPORTS = (
     "ha_tree_stats",
     "ha_probe_paged_read",
     "ha_probe_mfma_bf16",
+    "ha_probe_coissue",
 )
 
 
@@ -156,6 +157,8 @@ def load() -> ctypes.CDLL:
     lib.ha_probe_paged_read.restype = i32
     lib.ha_probe_mfma_bf16.argtypes = [i32, i32, p, p]
     lib.ha_probe_mfma_bf16.restype = i32
+    lib.ha_probe_coissue.argtypes = [i32, i32, i32, p, p]
+    lib.ha_probe_coissue.restype = i32
     lib.ha_tree_destroy.argtypes = [p]
     lib.ha_tree_destroy.restype = None
     if lib.ha_abi_version() != ABI_VERSION:

@@ -81,6 +81,69 @@ __global__ __launch_bounds__(256) void mfma_kernel(int iterations, float* sink) 
   sink[static_cast<int64_t>(blockIdx.x) * 256 + t] = s;
 }
 
+
+// Matrix cores next to vector ALU work, 8 wavefronts (two per SIMD). A
+// matrix block is 12 x 8 products on register operands (8 chains); a vector
+// block is 6 x 16 dependent (FMA, exp2) pairs (16 chains), no memory.
+//   0: every wave matrix blocks only      1: waves 0-3 matrix, 4-7 vector
+//   2: every wave a matrix then a vector block, a barrier after each (in phase)
+//   3: waves 0-3 matrix then vector, 4-7 vector then matrix, same barriers
+//   4: every wave vector blocks only
+template <int kMode>
+__global__ __launch_bounds__(512, 1) void coissue_kernel(int iterations, float* sink) {
+  const uint32_t t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(t >> 6));
+  const u32x4 a = {0x3f803f80u ^ (t & 7u), 0x3f003f00u, 0x3e803e80u, 0x3f803f00u};
+  const u32x4 b = {0x3f003f80u, 0x3f803f80u, 0x3e803f00u ^ (t & 3u), 0x3f003f00u};
+  f32x4 c[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float x[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) x[j] = 1e-3f * static_cast<float>(t + j);
+  const float sc = 0.5f + 1e-7f * static_cast<float>(t);
+  auto matrix = [&]() {
+#pragma unroll
+    for (int i = 0; i < 12; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = mfma_16x16x32(a, b, c[j]);
+  };
+  auto vector = [&]() {
+#pragma unroll
+    for (int i = 0; i < 6; ++i)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) x[j] = fast_exp2(x[j] * sc - 1.0f);
+  };
+  for (int it = 0; it < iterations; ++it) {
+    if constexpr (kMode == 0) {
+      matrix();
+    } else if constexpr (kMode == 1) {
+      if (wave < 4) matrix();
+      else vector();
+    } else if constexpr (kMode == 2) {
+      matrix();
+      __syncthreads();
+      vector();
+      __syncthreads();
+    } else if constexpr (kMode == 3) {
+      if (wave < 4) matrix();
+      else vector();
+      __syncthreads();
+      if (wave < 4) vector();
+      else matrix();
+      __syncthreads();
+    } else {
+      vector();
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += c[j][0] + c[j][1] + c[j][2] + c[j][3];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) s += x[j];
+  sink[static_cast<int64_t>(blockIdx.x) * 512 + t] = s;
+}
+
 }  // namespace
 }  // namespace ha
 
@@ -128,6 +191,26 @@ ha_status ha_probe_mfma_bf16(int32_t workgroups, int32_t iterations, float* sink
   if (!sink) return ha::set_error(HA_ERR_NULL, "sink is NULL");
   hipLaunchKernelGGL(ha::mfma_kernel, dim3(workgroups), dim3(256), 0, static_cast<hipStream_t>(stream), iterations,
                      sink);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return ha::set_error(HA_ERR_HIP, "probe launch: %s", hipGetErrorString(e));
+  return ha::clear_error();
+}
+
+ha_status ha_probe_coissue(int32_t mode, int32_t workgroups, int32_t iterations, float* sink, void* stream) {
+  if (mode < 0 || mode > 4) return ha::set_error(HA_ERR_RANGE, "mode must be 0..4 (got %d)", mode);
+  if (workgroups < 1 || iterations < 1)
+    return ha::set_error(HA_ERR_RANGE, "workgroups and iterations must be >= 1 (got %d, %d)", workgroups,
+                         iterations);
+  if (!sink) return ha::set_error(HA_ERR_NULL, "sink is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(workgroups), block(512);
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(ha::coissue_kernel<0>, grid, block, 0, s, iterations, sink); break;
+    case 1: hipLaunchKernelGGL(ha::coissue_kernel<1>, grid, block, 0, s, iterations, sink); break;
+    case 2: hipLaunchKernelGGL(ha::coissue_kernel<2>, grid, block, 0, s, iterations, sink); break;
+    case 3: hipLaunchKernelGGL(ha::coissue_kernel<3>, grid, block, 0, s, iterations, sink); break;
+    default: hipLaunchKernelGGL(ha::coissue_kernel<4>, grid, block, 0, s, iterations, sink); break;
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return ha::set_error(HA_ERR_HIP, "probe launch: %s", hipGetErrorString(e));
   return ha::clear_error();

@@ -47,4 +47,8 @@ ha_status ha_probe_mfma_bf16(int32_t, int32_t, float*, void*) {
   return ha::set_error(HA_ERR_HIP, "no device (host-only sanitizer build)");
 }
 
+ha_status ha_probe_coissue(int32_t, int32_t, int32_t, float*, void*) {
+  return ha::set_error(HA_ERR_HIP, "no device (host-only sanitizer build)");
+}
+
 }  // extern "C"

@@ -47,6 +47,21 @@ ha_status ha_probe_paged_read(const ha_shape* shape, const ha_kv_view* pages, co
  *   sink float32 [workgroups * 256] device (written; content meaningless) */
 ha_status ha_probe_mfma_bf16(int32_t workgroups, int32_t iterations, float* sink, void* stream);
 
+/* Matrix cores beside vector ALU work: whether one wavefront's products and
+ * another's vector instructions on the same SIMD run at the same time, which
+ * decides how much of prefill's softmax can hide under its products.
+ * `workgroups` workgroups of 8 wavefronts (two per SIMD); per iteration a
+ * "matrix block" is 96 v_mfma_f32_16x16x32_bf16 on register operands and a
+ * "vector block" 96 dependent (FMA, exp2) pairs, no memory traffic.
+ *   mode 0  every wave: matrix blocks only
+ *   mode 1  waves 0-3: matrix blocks; waves 4-7: vector blocks
+ *   mode 2  every wave: a matrix block, barrier, a vector block, barrier
+ *   mode 3  waves 0-3 as mode 2; waves 4-7 vector first, then matrix
+ *   mode 4  every wave: vector blocks only
+ *   workgroups >= 1, iterations >= 1
+ *   sink float32 [workgroups * 512] device (written; content meaningless) */
+ha_status ha_probe_coissue(int32_t mode, int32_t workgroups, int32_t iterations, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -268,3 +268,8 @@ def test_probe_argument_errors(lib):
     assert lib.ha_probe_mfma_bf16(0, 10, FAKE, None) == _lib.HA_ERR_RANGE
     assert lib.ha_probe_mfma_bf16(4, 0, FAKE, None) == _lib.HA_ERR_RANGE
     assert lib.ha_probe_mfma_bf16(4, 10, None, None) == _lib.HA_ERR_NULL
+    assert lib.ha_probe_coissue(5, 4, 10, FAKE, None) == _lib.HA_ERR_RANGE
+    assert lib.ha_probe_coissue(-1, 4, 10, FAKE, None) == _lib.HA_ERR_RANGE
+    assert lib.ha_probe_coissue(0, 0, 10, FAKE, None) == _lib.HA_ERR_RANGE
+    assert lib.ha_probe_coissue(0, 4, 0, FAKE, None) == _lib.HA_ERR_RANGE
+    assert lib.ha_probe_coissue(2, 4, 10, None, None) == _lib.HA_ERR_NULL
