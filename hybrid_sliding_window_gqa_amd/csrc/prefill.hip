@@ -20,8 +20,9 @@
 //     (three 16-row MFMA column groups; 384 rows) share each staged tile, one
 //     workgroup per CU -- every wave reads the whole tile from LDS, so more
 //     rows per wave means fewer LDS bytes per MFMA, and staging per MFMA is a
-//     third of what 4 waves of 32 rows would need. SWA layers, bound by their
-//     Q reads and O writes: 4 waves of 32 rows, two workgroups per CU. Keys
+//     third of what 4 waves of 32 rows would need. SWA layers (three tiles
+//     or so per workgroup, bound by the latency of that short chain): 4
+//     waves of 32 rows, two workgroups per CU. Keys
 //     are consumed in 64-key tiles of four blocks and staged into LDS in
 //     stage tiles of 128 keys (full: one block per wave, two compute tiles
 //     per barrier) or 64 keys (SWA). The waves stage the next stage tile
@@ -43,7 +44,10 @@
 //     sums after the exp2s); only a tile that fails the check, or a row's
 //     first keys, takes the row max (a cross-lane reduction), rescales O and
 //     l and recomputes. SWA layers (a few tiles per row) take the row max
-//     every tile and raise the reference only past a slack.
+//     every tile and raise the reference only past a slack. Their chunk
+//     tiles start at the block holding the window's first key, and a tile's
+//     blocks that hold no key are not computed (a 16-position query block's
+//     143 keys take 9 blocks, not 12).
 //     Tiles a wave sees completely skip masking; tiles no row of the wave
 //     sees are skipped.
 //
@@ -69,9 +73,9 @@ constexpr int kTileBlocks = kTileKeys / kBlock;   // 4
 template <bool kFull>
 constexpr int stage_keys() { return kFull ? 128 : 64; }
 constexpr int kXcds = 8;
-// Full layers: 8 waves (256 rows) share each staged tile, one workgroup per
-// CU. SWA layers, bound by their Q reads and O writes: 4 waves (128 rows),
-// two workgroups per CU so one's prologue/epilogue overlaps the other.
+// Full layers: 8 waves (384 rows) share each staged tile, one workgroup per
+// CU. SWA layers: 4 waves (128 rows), two workgroups per CU so one's
+// prologue/epilogue overlaps the other.
 template <bool kFull>
 constexpr int waves_per_wg() { return kFull ? 8 : 4; }
 template <bool kFull>
