@@ -219,8 +219,11 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
   const int hkv = a.geo.hkv;
   const int hq = a.geo.hq;
   const int G = a.geo.group;
+  // The group is a power of two (1..16, checked at the boundary): row ->
+  // (position, head) by shift and mask, not by integer division.
+  const int gsh = __builtin_ctz(static_cast<unsigned>(G));
   const int W = a.geo.window;
-  const int QB = kRowsPerWg / G;        // query positions per workgroup
+  const int QB = kRowsPerWg >> gsh;     // query positions per workgroup
 
   // ---- workgroup -> (sequence, kv head, query block), XCD-aware ----
   const int npairs = a.batch * hkv;
@@ -271,8 +274,8 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
 
   // ---- rows of this wave ----
   const int row0 = wave * kRowsPerWave;
-  const int wave_i_lo = i0 + row0 / G;
-  const int wave_i_hi = min(i_end - 1, i0 + (row0 + kRowsPerWave - 1) / G);
+  const int wave_i_lo = i0 + (row0 >> gsh);
+  const int wave_i_hi = min(i_end - 1, i0 + ((row0 + kRowsPerWave - 1) >> gsh));
   const bool wave_live = wave_i_lo < i_end;
   const int qlo = hist + wave_i_lo;
   const int qhi = hist + wave_i_hi;
@@ -283,8 +286,8 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
 #pragma unroll
   for (int rg = 0; rg < kRowGroups; ++rg) {
     const int rho = row0 + 16 * rg + c16;
-    const int ci = i0 + rho / G;
-    const int hh = g * G + rho % G;
+    const int ci = i0 + (rho >> gsh);
+    const int hh = g * G + (rho & (G - 1));
     const bool ok = ci < i_end;
     qpos[rg] = hist + ci;
     const int64_t off = (static_cast<int64_t>(tok0 + (ok ? ci : 0)) * hq + hh) * D + 8 * q4;
@@ -783,10 +786,10 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
         *reinterpret_cast<f32x4*>(&slab[c16 * kPitch + 16 * d + 4 * q4]) = o[rg][d] * inv;
       {
         const int rho = row0 + 16 * rg + c16;
-        const int ci = i0 + rho / G;
+        const int ci = i0 + (rho >> gsh);
         if (q4 == 0 && ci < i_end) {
           const float mu = (m_run[rg] == -INFINITY) ? 0.0f : m_run[rg];
-          a.lse[static_cast<int64_t>(tok0 + ci) * hq + g * G + rho % G] = (mu + fast_log2(l)) * kLn2;
+          a.lse[static_cast<int64_t>(tok0 + ci) * hq + g * G + (rho & (G - 1))] = (mu + fast_log2(l)) * kLn2;
         }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);                          // lgkmcnt(0): the slab is written
@@ -796,9 +799,9 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
         const int col = 4 * (lane % kLanesPerRow);
         const f32x4 val = *reinterpret_cast<const f32x4*>(&slab[r * kPitch + col]);
         const int rho = row0 + 16 * rg + r;
-        const int ci = i0 + rho / G;
+        const int ci = i0 + (rho >> gsh);
         if (ci < i_end) {
-          const int64_t row = static_cast<int64_t>(tok0 + ci) * hq + g * G + rho % G;
+          const int64_t row = static_cast<int64_t>(tok0 + ci) * hq + g * G + (rho & (G - 1));
           __builtin_nontemporal_store(val, reinterpret_cast<f32x4*>(&a.out[row * D + col]));
         }
       }
@@ -809,9 +812,9 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
   for (int rg = 0; rg < kRowGroups; ++rg) {
     const float l = group4_sum(l_run[rg]);
     const int rho = row0 + 16 * rg + c16;
-    const int ci = i0 + rho / G;
+    const int ci = i0 + (rho >> gsh);
     if (ci >= i_end) continue;
-    const int hh = g * G + rho % G;
+    const int hh = g * G + (rho & (G - 1));
     const int64_t row = static_cast<int64_t>(tok0 + ci) * hq + hh;
     const float inv = 1.0f / l;
 #pragma unroll
