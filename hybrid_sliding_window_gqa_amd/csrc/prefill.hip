@@ -343,6 +343,8 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
     }
   };
 
+  // Ring slot of the newest history position (hist - 1) mod W, in [0, W).
+  const int last_slot = kFull ? 0 : ((hist - 1) % W + W) % W;
   auto key_position = [&](int tile, int kk) -> int {   // kk = key within the tile
     if (tile < n_hist_tiles) {
       if constexpr (kFull) {
@@ -351,10 +353,9 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
       } else {
         const int s = tile * kStageKeys + kk;             // ring slot
         if (s >= W) return kNoKey;
-        const int last = hist - 1;
-        int d = (last - s) % W;
+        int d = last_slot - s;                            // slots back from the newest
         if (d < 0) d += W;
-        const int p = last - d;
+        const int p = hist - 1 - d;
         return p >= 0 ? p : kNoKey;
       }
     } else {
@@ -563,8 +564,17 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
         __builtin_amdgcn_sched_group_barrier(0x008, kAhead * kRowGroups, 0);
 
         if (need_mask) {
+          // A block that every row of the wave sees in full keeps its scores
+          // (ring tiles: positions are not contiguous, always masked).
+          auto block_all_visible = [&](int kb) -> bool {
+            const int klo = kmin + kBlock * kb;
+            const int khi = klo + kBlock - 1;
+            if constexpr (kFull) return khi <= kmax && khi <= qlo && !((no_page_bits >> kb) & 1);
+            else return tile >= n_hist_tiles && khi <= kmax && khi <= qlo && klo > qhi - W;
+          };
 #pragma unroll
           for (int kb = 0; kb < NB; ++kb) {
+            if (block_all_visible(kb)) continue;
             int kps[4];
             if constexpr (kFull) {
               // key kk of the tile sits at position kmin + kk, valid up to kmax
@@ -775,12 +785,16 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
     constexpr int kPitch = D + 4;                                  // floats per LDS row
     static_assert(kWaves * 16 * kPitch * 4 <= sizeof(sm), "O slabs fit in the tile buffers");
     float* slab = reinterpret_cast<float*>(&sm) + wave * 16 * kPitch;
+    // Row rho of the workgroup is O row (tok0 + i0 + (rho >> gsh)) * hq + g * G + (rho & (G - 1)):
+    // one 64-bit base per workgroup, a small offset per row.
+    float* out_wg = a.out + (static_cast<int64_t>(tok0 + i0) * hq + g * G) * D;
+    float* lse_wg = a.lse + static_cast<int64_t>(tok0 + i0) * hq + g * G;
     constexpr int kLanesPerRow = D / 4;                           // 16-byte pieces per row
     constexpr int kRowsPerStore = 64 / kLanesPerRow;              // rows one instruction covers
 #pragma unroll
     for (int rg = 0; rg < kRowGroups; ++rg) {
       const float l = group4_sum(l_run[rg]);
-      const float inv = 1.0f / l;
+      const float inv = __builtin_amdgcn_rcpf(l);
 #pragma unroll
       for (int d = 0; d < DT; ++d)
         *reinterpret_cast<f32x4*>(&slab[c16 * kPitch + 16 * d + 4 * q4]) = o[rg][d] * inv;
@@ -789,7 +803,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
         const int ci = i0 + (rho >> gsh);
         if (q4 == 0 && ci < i_end) {
           const float mu = (m_run[rg] == -INFINITY) ? 0.0f : m_run[rg];
-          a.lse[static_cast<int64_t>(tok0 + ci) * hq + g * G + (rho & (G - 1))] = (mu + fast_log2(l)) * kLn2;
+          lse_wg[(rho >> gsh) * hq + (rho & (G - 1))] = (mu + fast_log2(l)) * kLn2;
         }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);                          // lgkmcnt(0): the slab is written
@@ -801,8 +815,8 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
         const int rho = row0 + 16 * rg + r;
         const int ci = i0 + (rho >> gsh);
         if (ci < i_end) {
-          const int64_t row = static_cast<int64_t>(tok0 + ci) * hq + g * G + (rho & (G - 1));
-          __builtin_nontemporal_store(val, reinterpret_cast<f32x4*>(&a.out[row * D + col]));
+          const int rel = (rho >> gsh) * hq + (rho & (G - 1));
+          __builtin_nontemporal_store(val, reinterpret_cast<f32x4*>(out_wg + static_cast<int64_t>(rel) * D + col));
         }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);                          // reads done before the slab is rewritten
@@ -816,7 +830,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
     if (ci >= i_end) continue;
     const int hh = g * G + (rho & (G - 1));
     const int64_t row = static_cast<int64_t>(tok0 + ci) * hq + hh;
-    const float inv = 1.0f / l;
+    const float inv = __builtin_amdgcn_rcpf(l);
 #pragma unroll
     for (int d = 0; d < DT; ++d)
       *reinterpret_cast<f32x4*>(&a.out[row * D + 16 * d + 4 * q4]) = o[rg][d] * inv;
