@@ -102,6 +102,10 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
   const int hq = a.geo.hq;
   const int hkv = a.geo.hkv;
   const int W = a.geo.window;
+  // The group is a power of two (1..16, checked at the boundary): column ->
+  // (token, head) by shift and mask, not by integer division.
+  const int gsh = __builtin_ctz(static_cast<unsigned>(G));
+  constexpr int kLog2D = D == 128 ? 7 : 6;
   const int nq = a.nq;
 
   const int len = a.kv_len[b];
@@ -115,15 +119,19 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
     // kv_len below nq: no valid query position; rows are zero, LSE -inf.
     if (split == 0) {
       for (int e = threadIdx.x; e < nq * G * D; e += blockDim.x) {
-        const int i = e / (G * D);
+        const int i = e >> (gsh + kLog2D);
         const int r = e - i * G * D;
         a.out[((static_cast<int64_t>(b) * nq + i) * hq + g * G) * D + r] = 0.0f;
       }
       for (int e = threadIdx.x; e < nq * G; e += blockDim.x)
-        a.lse[(static_cast<int64_t>(b) * nq + e / G) * hq + g * G + e % G] = -INFINITY;
+        a.lse[(static_cast<int64_t>(b) * nq + (e >> gsh)) * hq + g * G + (e & (G - 1))] = -INFINITY;
     }
     return;
   }
+
+  // Ring slots of the newest history position (t0 - 1) and of t0, in [0, W).
+  const int last_slot = kFull ? 0 : ((t0 - 1) % W + W) % W;
+  const int t0_slot = last_slot + 1 == W ? 0 : last_slot + 1;
 
   // History blocks of this split (pool blocks holding positions < t0).
   int first, last, nsplit;
@@ -164,10 +172,9 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
       return p < t0 ? p : -1;
     } else {
       const int s = kBlock * i + k;   // ring slot
-      const int last_p = t0 - 1;
-      int d = (last_p - s) % W;
+      int d = last_slot - s;          // slots back from the newest history position
       if (d < 0) d += W;
-      const int p = last_p - d;
+      const int p = t0 - 1 - d;
       return (p >= 0 && p > t0 - W) ? p : -1;
     }
   };
@@ -178,11 +185,11 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
 #pragma unroll
   for (int gr = 0; gr < NG; ++gr) {
     const int c = 16 * gr + c16;
-    const int i = c / G;
+    const int i = c >> gsh;
     const bool ok = i < nq;
     tcol[gr] = ok ? t0 + i : -0x40000000;
     if constexpr (kF32) {
-      const int64_t qoff = ((static_cast<int64_t>(b) * nq + (ok ? i : 0)) * hq + g * G + c % G) * D + 8 * q4;
+      const int64_t qoff = ((static_cast<int64_t>(b) * nq + (ok ? i : 0)) * hq + g * G + (c & (G - 1))) * D + 8 * q4;
 #pragma unroll
       for (int m = 0; m < KS; ++m) {
         qop[gr][m] = load8_as_bf16<kF32>(a.q, qoff + 32 * m);
@@ -194,7 +201,7 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
       // would wait for the load).
       const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const uint16_t*>(a.q) + static_cast<int64_t>(b) * nq * hq * D,
                                                   static_cast<uint32_t>(nq * hq * D * 2));
-      const uint32_t off = ok ? 2u * static_cast<uint32_t>((i * hq + g * G + c % G) * D + 8 * q4) : 0x40000000u;
+      const uint32_t off = ok ? 2u * static_cast<uint32_t>((i * hq + g * G + (c & (G - 1))) * D + 8 * q4) : 0x40000000u;
 #pragma unroll
       for (int m = 0; m < KS; ++m) qop[gr][m] = buf_load16(rq, off + 64 * m);
     }
@@ -433,7 +440,7 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
     const float inv = 1.0f / l;
 #pragma unroll
     for (int w = 0; w < kVerifyWaves; ++w) sm_f[w][c] = f[w] * inv;
-    const int64_t row = (static_cast<int64_t>(b) * nq + c / G) * hq + g * G + c % G;
+    const int64_t row = (static_cast<int64_t>(b) * nq + (c >> gsh)) * hq + g * G + (c & (G - 1));
     const float lse2 = mu + fast_log2(l);
     if (final_row) a.lse[row] = lse2 * kLn2;
     else a.part_lse[row * a.splits + split] = lse2;
@@ -446,7 +453,7 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < kVerifyWaves; ++w) acc += *reinterpret_cast<const f32x4*>(&sm_o[w][c][4 * d4]) * sm_f[w][c];
-    const int64_t row = (static_cast<int64_t>(b) * nq + c / G) * hq + g * G + c % G;
+    const int64_t row = (static_cast<int64_t>(b) * nq + (c >> gsh)) * hq + g * G + (c & (G - 1));
     float* dst = final_row ? a.out + row * D : a.part_o + (row * a.splits + split) * D;
     *reinterpret_cast<f32x4*>(dst + 4 * d4) = acc;
   }
@@ -464,7 +471,8 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
       blk = (static_cast<int64_t>(pg) * hkv + g) * kBlock * D;
     } else {
       if (ring < 0 || ring >= a.num_blocks) return;
-      const int s = p % W;
+      int s = t0_slot + j;            // (t0 + j) mod W: j < nq <= 16 <= W
+      if (s >= W) s -= W;
       blk = ((static_cast<int64_t>(ring) * hkv + g) * W + kBlock * (s / kBlock)) * D;
     }
     const int row = p % kBlock;
