@@ -95,7 +95,7 @@ def check_against_oracle(shape, kind, seqs, outs, lses, rows=None):
 # (the SWA kernel computes only the blocks of a tile that hold window keys: groups and windows
 # below give last tiles of 1 (64/8, W 128), 2 (4/1, W 128), 3 (8/1, W 32 and 16/8, W 48) and 4 blocks)
 @pytest.mark.parametrize("hq,hkv,d,window", [(4, 1, 64, 128), (64, 8, 128, 128), (32, 2, 64, 48), (16, 16, 128, 64),
-                                             (8, 1, 64, 32), (16, 8, 64, 48)])
+                                             (8, 1, 64, 32), (16, 8, 64, 48), (8, 8, 64, 16)])
 def test_one_shot_ragged_batch(kind, hq, hkv, d, window):
     shape = ha.HeadShape(hq, hkv, d, window=window)
     totals = [1, 15, 33, 130, 257, 700]

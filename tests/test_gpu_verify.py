@@ -87,7 +87,8 @@ def check(case, out, lse):
 
 @pytest.mark.parametrize("kind", [ha.HA_SWA, ha.HA_FULL])
 @pytest.mark.parametrize("hq,hkv,d,window,nq", [(64, 8, 128, 128, 4), (64, 8, 128, 128, 1), (64, 8, 128, 128, 3),
-                                                 (4, 1, 64, 128, 8), (16, 16, 128, 32, 16), (32, 2, 64, 64, 2)])
+                                                 (4, 1, 64, 128, 8), (16, 16, 128, 32, 16), (32, 2, 64, 64, 2),
+                                                 (16, 16, 64, 16, 16), (16, 8, 64, 48, 8)])
 def test_verify_matches_oracle_and_appends(kind, hq, hkv, d, window, nq):
     shape = ha.HeadShape(hq, hkv, d, window=window)
     lens = [n for n in LENS] + [nq - 1 if nq > 1 else 0]     # one row shorter than nq
