@@ -470,6 +470,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
   };
 
   // ---- main loop ----
+  bool have_ref = false;   // SWA: the wave has computed a tile (O and l may be nonzero)
   const float sl2 = a.geo.scale * kLog2e;
   float m_run[kRowGroups], l_run[kRowGroups];
   f32x4 o[kRowGroups][DT];
@@ -703,7 +704,12 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
           tmax[rg] = group4_max(mx) * sl2;
           grow = grow || (tmax[rg] > m_run[rg] + kRescaleSlack);
         }
-        if (__any(grow)) {
+        if (!have_ref) {
+          // the wave's first tile: O and l are still zero, nothing to rescale
+#pragma unroll
+          for (int rg = 0; rg < kRowGroups; ++rg) m_run[rg] = max_prop(m_run[rg], tmax[rg]);
+          have_ref = true;
+        } else if (__any(grow)) {
 #pragma unroll
           for (int rg = 0; rg < kRowGroups; ++rg) {
             const float m_new = max_prop(m_run[rg], tmax[rg]);
