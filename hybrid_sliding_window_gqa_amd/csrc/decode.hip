@@ -614,22 +614,29 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
   __syncthreads();
 
   const bool final_row = (nsplit == 1);
-  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
-    const int h = e / D;
-    const int dd = e - h * D;
-    float mx = sm_m[0][h];
+  // Each thread folds channels of one head, so that head's wave factors and
+  // l are computed once per thread, not once per channel. G and the thread
+  // count are powers of two, so the threads split evenly over the heads.
+  const int tph_shift = __builtin_ctz(static_cast<unsigned>(64 * kWaves)) - __builtin_ctz(static_cast<unsigned>(G));
+  const int h = static_cast<int>(threadIdx.x) >> tph_shift;
+  const int t_in_head = static_cast<int>(threadIdx.x) - (h << tph_shift);
+  float mx = sm_m[0][h];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) mx = max_prop(mx, sm_m[w][h]);
-    const float mu = (mx == -INFINITY) ? 0.0f : mx;
-    float l = 0.0f, acc = 0.0f;
+  for (int w = 1; w < kWaves; ++w) mx = max_prop(mx, sm_m[w][h]);
+  const float mu = (mx == -INFINITY) ? 0.0f : mx;
+  float f[kWaves];
+  float l = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = fast_exp2(sm_m[w][h] - mu);
-      l += sm_l[w][h] * f;
-      acc += sm_o[w][h][dd] * f;
-    }
-    const int64_t row = static_cast<int64_t>(b) * hq + g * G + h;
-    const float lse2 = mu + fast_log2(l);
+  for (int w = 0; w < kWaves; ++w) {
+    f[w] = fast_exp2(sm_m[w][h] - mu);
+    l += sm_l[w][h] * f[w];
+  }
+  const int64_t row = static_cast<int64_t>(b) * hq + g * G + h;
+  const float lse2 = mu + fast_log2(l);
+  for (int dd = t_in_head; dd < D; dd += 1 << tph_shift) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) acc += sm_o[w][h][dd] * f[w];
     if (final_row) {
       // l = 0: no valid key (an invalid ring id, or no valid page): O = 0, LSE = -inf
       a.out[row * D + dd] = l > 0.0f ? acc / l : 0.0f;
