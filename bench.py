@@ -669,7 +669,7 @@ def run_chunked(torch, ha, grp, synth, args, device, cpu_seconds=0.0):
             "unit": "TFLOP/s",
             "frac": flops["full"] / (full_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "traffic": profile_traffic(PREFILL_PROFILE),
-            "kernel": "hybrid_attn_prefill, full layer (stage_chunk_kernel + prefill_kernel<128,full>), "
+            "kernel": "hybrid_attn_prefill, full layer (stage_chunk_kernel + prefill_kernel<128,full> + prefill_merge_kernel), "
                       f"mean over the {nchunks} chunk calls",
             "flops_per_launch": flops["full"] / nchunks,
         },
@@ -782,7 +782,7 @@ def run_reuse(torch, ha, grp, synth, args, device, cpu_seconds=0.0):
         "full_layer_tflops": full_tf,
         "roofline": {"bound": "mfma", "achieved": full_tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": full_tf / MFMA_BF16_PEAK_TFLOPS, "traffic": profile_traffic(REUSE_PROFILE),
-                     "kernel": "hybrid_attn_prefill, full layer (stage_chunk_kernel + prefill_kernel<128,full>)",
+                     "kernel": "hybrid_attn_prefill, full layer (stage_chunk_kernel + prefill_kernel<128,full> + prefill_merge_kernel)",
                      "flops_per_launch": flops["full"]},
         "full_call_compulsory_bytes": int(t_new * hq * d * (2 + 4) + t_new * hq * 4
                                           + (t_new + int(reuse_len.sum())) * kv_bytes_per_token(shape)),

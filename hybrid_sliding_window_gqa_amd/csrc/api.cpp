@@ -152,10 +152,16 @@ ha_status read_common(const ha_shape* shape, const ha_kv_view* view, int32_t wan
   return hip_status(ha::launch_read(a, k_out, v_out, static_cast<hipStream_t>(stream)), "read launch");
 }
 
-size_t prefill_workspace(const ha::Geometry& geo, int batch, int num_tokens) {
+// Bytes of the staged chunk (K and V of every 16-token block, bf16), rounded
+// up to 256 so the full layers' partial rows that follow start aligned.
+size_t prefill_stage_bytes(const ha::Geometry& geo, int batch, int num_tokens) {
+  const size_t bytes = static_cast<size_t>(ha::prefill_stage_blocks(num_tokens, batch)) * geo.hkv * 16 * geo.d * 2 * 2;
+  return (bytes + 255) / 256 * 256;
+}
+
+size_t prefill_workspace(const ha::Geometry& geo, bool full, int batch, int num_tokens) {
   if (batch <= 0 || num_tokens <= 0) return 0;
-  // K and V of every staged 16-token block, bf16
-  return static_cast<size_t>(ha::prefill_stage_blocks(num_tokens, batch)) * geo.hkv * 16 * geo.d * 2 * 2;
+  return prefill_stage_bytes(geo, batch, num_tokens) + (full ? static_cast<size_t>(ha::prefill_partial_bytes(geo.d)) : 0);
 }
 
 size_t decode_workspace(const ha::Geometry& geo, bool full, int batch, int max_kv_len, int num_splits) {
@@ -351,7 +357,7 @@ ha_status hybrid_attn_prefill(const ha_shape* shape, const ha_kv_view* kv, const
   if (!hist_len || !cu_new) return fail(HA_ERR_NULL, "hist_len or cu_new is NULL");
   if (!q || !k_new || !v_new) return fail(HA_ERR_NULL, "q, k_new or v_new is NULL");
   if (!out || !lse) return fail(HA_ERR_NULL, "out or lse is NULL");
-  const size_t need = prefill_workspace(geo, batch, num_tokens);
+  const size_t need = prefill_workspace(geo, kv->kind == HA_FULL, batch, num_tokens);
   if (!workspace || workspace_bytes < need)
     return fail(HA_ERR_WORKSPACE, "prefill needs %zu workspace bytes, got %zu", need, workspace ? workspace_bytes : 0);
   ha::PrefillArgs a{};
@@ -375,6 +381,8 @@ ha_status hybrid_attn_prefill(const ha_shape* shape, const ha_kv_view* kv, const
   a.lse = lse;
   a.stage = static_cast<uint16_t*>(workspace);
   a.stage_blocks = ha::prefill_stage_blocks(num_tokens, batch);
+  a.part = a.full ? reinterpret_cast<float*>(static_cast<char*>(workspace) + prefill_stage_bytes(geo, batch, num_tokens))
+                  : nullptr;
   return hip_status(ha::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
 }
 
@@ -459,7 +467,7 @@ size_t hybrid_attn_workspace_size(const ha_shape* shape, int32_t kind, int32_t d
   ha::Geometry geo;
   if (check_shape(shape, &geo) != HA_OK) return 0;
   if ((kind != HA_SWA && kind != HA_FULL) || batch < 0 || max_kv_len < 0 || num_splits < 0) return 0;
-  if (!decode) return prefill_workspace(geo, batch, max_kv_len);
+  if (!decode) return prefill_workspace(geo, kind == HA_FULL, batch, max_kv_len);
   return decode_workspace(geo, kind == HA_FULL, batch, max_kv_len, num_splits);
 }
 

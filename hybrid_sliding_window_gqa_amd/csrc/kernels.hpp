@@ -81,6 +81,16 @@ struct PrefillArgs {
   float* lse;
   uint16_t* stage;        // workspace: chunk K/V re-laid as 16-token blocks
   int64_t stage_blocks;   // blocks the workspace holds
+  // Full layers: the last tail_items work items of each XCD's sequence run
+  // split by key tiles, the final tail_quads of them in four parts and the
+  // others in two, one workgroup per part. Each part writes normalised
+  // partial rows to its own entry of `part` (kPrefillPartEntries entries of
+  // kPrefillFullRows rows: O [entry][row][D], then LSE [entry][row] in the
+  // log2 domain) and prefill_merge_kernel combines an item's parts into
+  // out / lse.
+  int32_t tail_items;
+  int32_t tail_quads;
+  float* part;
 };
 
 // Multi-token verify decode: nq new tokens per sequence at positions
@@ -114,6 +124,20 @@ struct VerifyArgs {
 // (same layout as a pool page), sequence b's blocks starting at
 // ceil(cu_new[b] / 16) + b.
 int64_t prefill_stage_blocks(int num_tokens, int batch);
+
+// Full-layer prefill work items: 384 rows (query position x query head of
+// one kv head's group). The last items of each of the 8 XCDs' sequences may
+// run split by keys: at most kPrefillMaxTail per XCD, of which at most
+// kPrefillMaxQuads in four parts and the rest in two.
+constexpr int kPrefillFullRows = 384;
+constexpr int kPrefillMaxTail = 12;
+constexpr int kPrefillMaxQuads = 4;
+constexpr int kPrefillPartEntries = 8 * (2 * kPrefillMaxTail + 2 * kPrefillMaxQuads);
+// Split work items per XCD (tail) and how many of them run in four parts
+// (quads), for a call of `items_per_xcd` work items per XCD.
+void prefill_tail_policy(int64_t items_per_xcd, int* tail, int* quads);
+// Bytes of the partial rows of the split items (full layers), head dim d.
+int64_t prefill_partial_bytes(int d);
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 // Pool -> token-major rows (k_new / v_new of the args are the outputs).

@@ -8,7 +8,7 @@
 // "为什么选择 Hybrid SWA 架构"); chunked prefill is what the serving stack runs
 // for long requests (blog.hotdry.top 2026-06-09, section "PD 分离与长度分桶").
 //
-// Two kernels per call:
+// Two kernels per call, three when a full-layer call splits its tail:
 //  1. stage_chunk_kernel re-lays the chunk's K/V (bf16 or f32) into 16-token
 //     blocks in the workspace, in exactly the pools' block format (matrix-core
 //     operand order, common.hpp), zero-padded past the chunk's end. Every key
@@ -51,6 +51,12 @@
 //     Tiles a wave sees completely skip masking; tiles no row of the wave
 //     sees are skipped.
 //
+//  3. prefill_merge_kernel (full layers, calls of more than one round of
+//     work items per XCD): the last items of each XCD's sequence ran as two
+//     or four workgroups over parts of their key tiles, so that the final
+//     round is not a few whole items on otherwise idle CUs; it merges their
+//     partial rows (O, LSE) into the output.
+//
 // Grid order: workgroup i runs on XCD i % 8 (round-robin dispatch). All query
 // blocks of one (sequence, kv head) pair are placed on the same XCD and
 // dispatched back to back (heaviest, i.e. latest, first), so the workgroups
@@ -82,6 +88,24 @@ template <bool kFull>
 constexpr int rows_per_wave() { return kFull ? 48 : 32; }
 template <bool kFull>
 constexpr int rows_per_wg() { return rows_per_wave<kFull>() * waves_per_wg<kFull>(); }
+static_assert(rows_per_wg<true>() == kPrefillFullRows, "partial-row layout of split full-layer items");
+
+// Work item jj of an XCD's sequence: pairs on XCD x are x, x + 8, ...; each
+// pair's query blocks run back to back, latest (heaviest) first.
+__device__ __forceinline__ void work_item(int jj, int xcd, int qb_max, int& pair, int& qblk) {
+  pair = (jj / qb_max) * kXcds + xcd;
+  qblk = qb_max - 1 - jj % qb_max;
+}
+
+// Split tail of full layers (PrefillArgs::tail_items): the XCD's last
+// `tail` items run in parts, the first tail - quads of them in two, the
+// final `quads` in four. Tail item k (counted within the XCD's tail) has
+// tail_parts(k) parts, whose partial rows take consecutive entries from
+// xcd * (2 tail + 2 quads) + tail_first_entry(k).
+__device__ __forceinline__ int tail_parts(int k, int tail, int quads) { return k < tail - quads ? 2 : 4; }
+__device__ __forceinline__ int tail_first_entry(int k, int tail, int quads) {
+  return k < tail - quads ? 2 * k : 2 * (tail - quads) + 4 * (k - (tail - quads));
+}
 // SWA layers write O through LDS with full-row non-temporal stores (see the
 // kernel's epilogue): 2% faster SWA layers on the chunked workload; full
 // layers, whose epilogue is a small part of a workgroup's time, measured the
@@ -230,12 +254,35 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
   const int qb_max = (a.max_new + QB - 1) / QB;
   const int lin = blockIdx.x;
   const int xcd = lin % kXcds;
-  const int jj = lin / kXcds;
+  int jj = lin / kXcds;
+  // Full layers: the last tail_items items of the XCD's sequence run in
+  // parts (part key_part of key_parts takes that share of the item's key
+  // tiles), one workgroup each, which write partial rows to entry
+  // `part_entry` for prefill_merge_kernel.
+  int key_part = 0, key_parts_log2 = 0, part_entry = -1;
+  if constexpr (kFull) {
+    const int tail = a.tail_items, quads = a.tail_quads;
+    const int first_tail = qb_max * ((npairs + kXcds - 1) / kXcds) - tail;
+    if (tail > 0 && jj >= first_tail) {
+      const int r = jj - first_tail;            // workgroup within the XCD's tail
+      part_entry = xcd * (2 * tail + 2 * quads) + r;
+      if (r < 2 * (tail - quads)) {
+        jj = first_tail + (r >> 1);
+        key_part = r & 1;
+        key_parts_log2 = 1;
+      } else {
+        const int r4 = r - 2 * (tail - quads);
+        jj = first_tail + (tail - quads) + (r4 >> 2);
+        key_part = r4 & 3;
+        key_parts_log2 = 2;
+      }
+    }
+  }
   // Pair-major within an XCD: the workgroups resident on one XCD at a time
   // are consecutive query blocks of ONE pair, so they stream the same K/V
   // tiles at nearly the same time and the XCD's L2 serves most of them.
-  const int pair = (jj / qb_max) * kXcds + xcd;
-  const int qblk = qb_max - 1 - jj % qb_max;
+  int pair, qblk;
+  work_item(jj, xcd, qb_max, pair, qblk);
   if (pair >= npairs || qblk < 0) return;
   const int b = pair / hkv;
   const int g = pair - b * hkv;
@@ -271,6 +318,9 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
   if constexpr (!kFull) c_first = kBlock * (max(0, i0 - W + 1) / kBlock);
   const int n_chunk_tiles = (i_end - c_first + kStageKeys - 1) / kStageKeys;
   const int n_tiles = n_hist_tiles + n_chunk_tiles;
+  // Stage tiles this workgroup consumes: all, or its part's share.
+  const int t_begin = (key_part * n_tiles) >> key_parts_log2;
+  const int t_end = ((key_part + 1) * n_tiles) >> key_parts_log2;
 
   // ---- rows of this wave ----
   const int row0 = wave * kRowsPerWave;
@@ -300,8 +350,9 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
 
   // ---- staging: wave w moves block w of a tile ----
   // Page ids of this wave's history blocks, 64 tiles at a time: lane j holds
-  // the page of tile (batch_base + j). One vector load per 64 tiles; the
-  // per-tile id is a readlane (scalar), so the tile loop never waits on it.
+  // the page of tile (batch_base + j), batches counted from t_begin. One
+  // vector load per 64 tiles; the per-tile id is a readlane (scalar), so the
+  // tile loop never waits on it.
   // Wave w stages units [part * kStageUnits, +kStageUnits) of block sb.
   constexpr int kStageUnits = CPL / kWavesPerBlock;
   const int sb = wave / kWavesPerBlock;
@@ -315,7 +366,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
     }
   };
   auto page_for = [&](int tile) -> int {
-    if constexpr (kFull) return __builtin_amdgcn_readlane(pg_vec, tile & 63);
+    if constexpr (kFull) return __builtin_amdgcn_readlane(pg_vec, (tile - t_begin) & 63);
     else return -1;
   };
   // Element offset of this wave's block of tile `tile` (-1: nothing to load),
@@ -482,9 +533,9 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
     for (int d = 0; d < DT; ++d) o[rg][d] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  fetch_pages(0);
-  if (n_tiles > 0) {
-    load_tile(0, page_for(0), 0);
+  fetch_pages(t_begin);
+  if (t_end > t_begin) {
+    load_tile(t_begin, page_for(t_begin), 0);
 #pragma unroll
     for (int ph = 0; ph < kSubTiles; ++ph) {
       load_v(ph);
@@ -497,10 +548,10 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int buf = tile & 1;
-    const bool has_next = tile + 1 < n_tiles;
-    if (((tile + 1) & 63) == 0 && tile + 1 < n_hist_tiles) fetch_pages(tile + 1);
+  for (int tile = t_begin; tile < t_end; ++tile) {
+    const int buf = (tile - t_begin) & 1;
+    const bool has_next = tile + 1 < t_end;
+    if (((tile + 1 - t_begin) & 63) == 0 && tile + 1 < n_hist_tiles) fetch_pages(tile + 1);
     if (has_next) {
       load_tile(tile + 1, page_for(tile + 1), buf ^ 1);
       load_v(0);
@@ -827,6 +878,27 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);                          // reads done before the slab is rewritten
     }
+  } else if (part_entry >= 0) {
+    // A split item's partial rows: O normalised by this part's l, and the
+    // part's LSE (log2 domain); a row that saw no key here writes O = 0 and
+    // LSE = -inf, which the merge weighs as nothing.
+    float* po = a.part + static_cast<int64_t>(part_entry) * kRowsPerWg * D;
+    float* pl = a.part + static_cast<int64_t>(kPrefillPartEntries) * kRowsPerWg * D +
+                static_cast<int64_t>(part_entry) * kRowsPerWg;
+#pragma unroll
+    for (int rg = 0; rg < kRowGroups; ++rg) {
+      const float l = group4_sum(l_run[rg]);
+      const int rho = row0 + 16 * rg + c16;
+      if (i0 + (rho >> gsh) >= i_end) continue;
+      const float inv = l > 0.0f ? __builtin_amdgcn_rcpf(l) : 0.0f;
+#pragma unroll
+      for (int d = 0; d < DT; ++d)
+        *reinterpret_cast<f32x4*>(&po[rho * D + 16 * d + 4 * q4]) = o[rg][d] * inv;
+      if (q4 == 0) {
+        const float mu = (m_run[rg] == -INFINITY) ? 0.0f : m_run[rg];
+        pl[rho] = l > 0.0f ? mu + fast_log2(l) : -INFINITY;
+      }
+    }
   } else {
 #pragma unroll
   for (int rg = 0; rg < kRowGroups; ++rg) {
@@ -848,6 +920,65 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
   }
 }
 
+// ---- 3. merge of split full-layer items ----
+// Workgroup (tail item, row group): rows of one split item, one thread per 4
+// channels. With each part's partial O_p (normalised by its own l_p) and
+// LSE_p = log2 of its weight, the item's row is O = sum_p 2^(LSE_p - LSE) O_p
+// with LSE = log2 sum_p 2^LSE_p.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a) {
+  constexpr int kRows = kPrefillFullRows;
+  constexpr int kLanesPerRow = D / 4;
+  constexpr int kRowsPerBlock = 256 / kLanesPerRow;
+  const int tail = a.tail_items, quads = a.tail_quads;
+  const int xcd = blockIdx.x / tail;
+  const int k = blockIdx.x - xcd * tail;       // tail item of the XCD
+  const int G = a.geo.group;
+  const int hq = a.geo.hq;
+  const int gsh = __builtin_ctz(static_cast<unsigned>(G));
+  const int QB = kRows >> gsh;
+  const int npairs = a.batch * a.geo.hkv;
+  const int qb_max = (a.max_new + QB - 1) / QB;
+  const int items = qb_max * ((npairs + kXcds - 1) / kXcds);
+  int pair, qblk;
+  work_item(items - tail + k, xcd, qb_max, pair, qblk);
+  if (pair >= npairs || qblk < 0) return;
+  const int b = pair / a.geo.hkv;
+  const int g = pair - b * a.geo.hkv;
+  const int tok0 = a.cu_new[b];
+  const int n = min(a.cu_new[b + 1], a.num_tokens) - tok0;
+  const int i0 = qblk * QB;
+  if (tok0 < 0 || i0 >= n) return;
+  const int rho = blockIdx.y * kRowsPerBlock + static_cast<int>(threadIdx.x) / kLanesPerRow;
+  const int col = 4 * (static_cast<int>(threadIdx.x) % kLanesPerRow);
+  const int ci = i0 + (rho >> gsh);
+  if (rho >= kRows || ci >= min(n, i0 + QB)) return;
+  const int parts = tail_parts(k, tail, quads);
+  const int e0 = xcd * (2 * tail + 2 * quads) + tail_first_entry(k, tail, quads);
+  const float* pl = a.part + static_cast<int64_t>(kPrefillPartEntries) * kRows * D;
+  float lp[4];
+  float mx = -INFINITY;
+  for (int p = 0; p < parts; ++p) {
+    lp[p] = pl[(e0 + p) * kRows + rho];
+    mx = fmaxf(mx, lp[p]);
+  }
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  float lse = -INFINITY;
+  if (mx != -INFINITY) {
+    float wsum = 0.0f;
+    for (int p = 0; p < parts; ++p) {
+      const float w = fast_exp2(lp[p] - mx);
+      wsum += w;
+      o += *reinterpret_cast<const f32x4*>(a.part + (static_cast<int64_t>(e0 + p) * kRows + rho) * D + col) * w;
+    }
+    o *= __builtin_amdgcn_rcpf(wsum);
+    lse = (mx + fast_log2(wsum)) * kLn2;
+  }
+  const int64_t row = static_cast<int64_t>(tok0 + ci) * hq + g * G + (rho & (G - 1));
+  *reinterpret_cast<f32x4*>(a.out + row * D + col) = o;
+  if (col == 0) a.lse[row] = lse;
+}
+
 template <int D>
 static void launch_prefill_d(const PrefillArgs& a, dim3 grid, hipStream_t stream) {
   const dim3 sgrid((a.max_new + kBlock - 1) / kBlock, a.batch);
@@ -861,15 +992,24 @@ static void launch_prefill_d(const PrefillArgs& a, dim3 grid, hipStream_t stream
     if (a.full) hipLaunchKernelGGL((prefill_kernel<D, true, false>), grid, bfull, 0, stream, a);
     else hipLaunchKernelGGL((prefill_kernel<D, false, false>), grid, bswa, 0, stream, a);
   }
+  if (a.full && a.tail_items > 0) {
+    const dim3 mgrid(kXcds * a.tail_items, (kPrefillFullRows * (D / 4) + 255) / 256);
+    hipLaunchKernelGGL((prefill_merge_kernel<D>), mgrid, dim3(256), 0, stream, a);
+  }
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-  if (a.batch == 0 || a.max_new == 0) return hipSuccess;
+hipError_t launch_prefill(const PrefillArgs& args, hipStream_t stream) {
+  if (args.batch == 0 || args.max_new == 0) return hipSuccess;
+  PrefillArgs a = args;
   const int qb = (a.full ? rows_per_wg<true>() : rows_per_wg<false>()) / a.geo.group;
   const int64_t qb_max = (a.max_new + qb - 1) / qb;
   const int64_t npairs = static_cast<int64_t>(a.batch) * a.geo.hkv;
   const int64_t ppx = (npairs + kXcds - 1) / kXcds;
-  const int64_t blocks = qb_max * ppx * kXcds;
+  const int64_t items = qb_max * ppx;     // work items per XCD
+  a.tail_items = a.tail_quads = 0;
+  if (a.full && a.part != nullptr) prefill_tail_policy(items, &a.tail_items, &a.tail_quads);
+  // a split item adds one workgroup per part beyond the first
+  const int64_t blocks = (items + a.tail_items + 2 * a.tail_quads) * kXcds;
   if (blocks > 0x7fffffff || a.batch > 65535) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks));
   if (a.geo.d == 64) launch_prefill_d<64>(a, grid, stream);

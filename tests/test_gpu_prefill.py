@@ -256,3 +256,29 @@ def test_swa_long_chunks_match_oracle(boundaries):
     seqs = Seqs(shape, totals, seed=123)
     outs, lses = run_chunks(shape, ha.HA_SWA, seqs, boundaries)
     check_against_oracle(shape, ha.HA_SWA, seqs, outs, lses)
+
+
+def _tail_items(shape, batch, max_new):
+    """Split work items per XCD of a full-layer call (the library's tail policy:
+    none up to 32 items per XCD, else min(12, items / 4), a third of them in
+    four parts and the rest in two)."""
+    qb = 384 // (shape.num_q_heads // shape.num_kv_heads)
+    items = -(-max_new // qb) * -(-batch * shape.num_kv_heads // 8)
+    return 0 if items <= 32 else min(12, items // 4)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(16, 1, 64), (64, 8, 128)])
+def test_full_prefill_split_tail_items(hq, hkv, d):
+    # Calls of more than 32 work items per XCD run each XCD's last items in two
+    # or four key parts plus a merge. These batches make those items the first
+    # query blocks of the last pairs, including blocks whose early parts hold
+    # no tile (history 0, one tile) and tail items with no pair at all.
+    shape = ha.HeadShape(hq, hkv, d)
+    bounds = [[0, 900], [0, 333, 1200], [0, 870, 1700]] if hkv == 1 else [[0, 700], [0, 61, 650], [0, 400, 690]]
+    totals = [b[-1] for b in bounds]
+    steps = [[bd[min(s, len(bd) - 1)] for bd in bounds] for s in range(3)]
+    for lo, hi in zip(steps, steps[1:]):
+        assert _tail_items(shape, len(totals), max(h - l for l, h in zip(lo, hi))) > 0
+    seqs = Seqs(shape, totals, seed=hq + d)
+    outs, lses = run_chunks(shape, ha.HA_FULL, seqs, bounds)
+    check_against_oracle(shape, ha.HA_FULL, seqs, outs, lses)
