@@ -55,14 +55,22 @@ int64_t prefill_partial_bytes(int d) {
 // ragged batches still spread over the chip. (Ragged decode workload, 24
 // sequences of 1K to 1M tokens, full-layer call on one MI355X: 224 splits
 // of up to 256 blocks 2651 us; 255 to 320 splits 2547 to 2575 us.)
+// Batches with enough pairs for every CU are capped at 1024 blocks (8 MiB)
+// per workgroup. The policy sees only the longest sequence, and a batch of
+// many short sequences plus one long one would otherwise leave the long
+// sequence to its own Hkv workgroups (one MI355X: 255 one-token sequences
+// and one of 900K tokens took 14.9 ms in one split per sequence, 0.79 ms
+// with the cap (55 splits), 0.63 ms for the long sequence alone); the
+// decode workload's 513-block sequences stay at one split.
 int decode_split_blocks(bool full, int window, int max_kv_len, int batch, int hkv, int requested_splits) {
   if (!full) return window / kBlockTokens;
   const int nblk = (max_of(max_kv_len, 1) + kBlockTokens - 1) / kBlockTokens;
   if (requested_splits > 0) return max_of(1, (nblk + requested_splits - 1) / requested_splits);
   constexpr int64_t kSlots = 256 * 2;
-  constexpr int kMaxBlocks = 208, kMinBlocks = 4, kFixedCost = 4, kMergeCost = 8;
+  constexpr int kMaxBlocks = 208, kMaxBlocksFilled = 1024, kMinBlocks = 4, kFixedCost = 4, kMergeCost = 8;
   const int64_t pairs = static_cast<int64_t>(max_of(batch, 1)) * max_of(hkv, 1);
-  const int s_lo = pairs >= kSlots ? 1 : max_of(1, (nblk + kMaxBlocks - 1) / kMaxBlocks);
+  const int cap = pairs >= kSlots ? kMaxBlocksFilled : kMaxBlocks;
+  const int s_lo = max_of(1, (nblk + cap - 1) / cap);
   const int s_hi = min_of(max_of(s_lo, nblk / kMinBlocks), s_lo + 512);
   int best_sb = (nblk + s_lo - 1) / s_lo;
   int64_t best_cost = INT64_MAX;

@@ -121,6 +121,11 @@ def test_decode_workspace_checked(lib):
     assert lib.hybrid_attn_workspace_size(ctypes.byref(s), _lib.HA_FULL, 0, 64, 8193, 0) == \
         stage + 8 * (2 * 12 + 2 * 4) * 384 * (128 + 1) * 4
     assert lib.hybrid_attn_decode_splits(ctypes.byref(s), _lib.HA_SWA, 64, 8193, 0) == 1
+    # a filled batch still splits a long sequence: at most 1024 blocks per workgroup
+    # (a batch of short sequences and one of 900K tokens must not leave the long one
+    # to its 8 workgroups)
+    splits = lib.hybrid_attn_decode_splits(ctypes.byref(s), _lib.HA_FULL, 256, 900000, 0)
+    assert splits > 1 and -(-(-(-900000 // 16)) // splits) <= 1024
     # explicit split count is honoured
     assert lib.hybrid_attn_decode_splits(ctypes.byref(s), _lib.HA_FULL, 64, 8193, 4) == 4
 

@@ -93,6 +93,20 @@ def test_decode_split_counts_agree(splits):
     assert_close(host(out), host(lse), ref_o, ref_l, f"splits={splits}")
 
 
+def test_filled_batch_with_one_long_sequence_splits():
+    # 64 sequences x 8 kv heads give every CU two workgroups, but one sequence
+    # is much longer than the rest: workgroups are capped at 1024 blocks, so
+    # its keys still split (here in two), and the merge matches the oracle.
+    shape = ha.HeadShape(64, 8, 128)
+    lens = [3] * 40 + [17] * 22 + [600, 20000]
+    assert ha.hybrid_attn_decode_splits(shape, ha.HA_FULL, len(lens), max(lens)) == 2
+    seq, q, pool, view = build(shape, ha.HA_FULL, lens, seed=21)
+    out, lse = ha.hybrid_attn_decode(shape, view, i32(lens), q, max(lens))
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_decode(shape, ha.HA_FULL, seq, q, lens)
+    assert_close(host(out), host(lse), ref_o, ref_l, "filled batch, one long sequence")
+
+
 def test_empty_rows_and_float32_queries():
     shape = ha.HeadShape(4, 1, 64, softmax_scale=1.0 / 8.0)
     lens = [0, 40, 0, 129]
