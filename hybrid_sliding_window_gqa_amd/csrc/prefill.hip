@@ -61,6 +61,9 @@
 // blocks of one (sequence, kv head) pair are placed on the same XCD and
 // dispatched back to back (heaviest, i.e. latest, first), so the workgroups
 // resident on an XCD stream one pair's K/V in near lockstep through its L2.
+// When the pairs are not a multiple of 8 (few kv heads, small batches), each
+// pair's blocks are dealt into 8 / gcd(pairs, 8) units placed the same way,
+// so every XCD gets the same number of units of about equal work.
 #include <cmath>
 #include <type_traits>
 
@@ -90,11 +93,19 @@ template <bool kFull>
 constexpr int rows_per_wg() { return rows_per_wave<kFull>() * waves_per_wg<kFull>(); }
 static_assert(rows_per_wg<true>() == kPrefillFullRows, "partial-row layout of split full-layer items");
 
-// Work item jj of an XCD's sequence: pairs on XCD x are x, x + 8, ...; each
-// pair's query blocks run back to back, latest (heaviest) first.
-__device__ __forceinline__ void work_item(int jj, int xcd, int qb_max, int& pair, int& qblk) {
-  pair = (jj / qb_max) * kXcds + xcd;
-  qblk = qb_max - 1 - jj % qb_max;
+// Work units: each (sequence, kv head) pair's query blocks, latest
+// (heaviest) first, dealt into 2^rsh units of qb_sub blocks (unit r of a
+// pair takes its blocks r, r + 2^rsh, ...), where 2^rsh = 8 / gcd(pairs, 8)
+// makes the unit count a multiple of the 8 XCDs (one unit per pair when the
+// pairs already are). Dealt rather than cut into ranges, a pair's units
+// carry equal work: causal blocks grow with their position. Units on XCD x
+// are x, x + 8, ...; item jj of an XCD's sequence is block jj % qb_sub of
+// its unit jj / qb_sub, so a unit's blocks run back to back on one XCD.
+__device__ __forceinline__ int unit_shift(int npairs) { return 3 - min(__builtin_ctz(static_cast<unsigned>(npairs)), 3); }
+__device__ __forceinline__ void work_item(int jj, int xcd, int qb_max, int qb_sub, int rsh, int& pair, int& qblk) {
+  const int unit = (jj / qb_sub) * kXcds + xcd;
+  pair = unit >> rsh;
+  qblk = qb_max - 1 - (((jj % qb_sub) << rsh) + (unit & ((1 << rsh) - 1)));
 }
 
 // Split tail of full layers (PrefillArgs::tail_items): the XCD's last
@@ -252,6 +263,9 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
   // ---- workgroup -> (sequence, kv head, query block), XCD-aware ----
   const int npairs = a.batch * hkv;
   const int qb_max = (a.max_new + QB - 1) / QB;
+  const int rsh = unit_shift(npairs);
+  const int qb_sub = (qb_max + (1 << rsh) - 1) >> rsh;
+  const int items = qb_sub * ((npairs << rsh) / kXcds);   // work items per XCD
   const int lin = blockIdx.x;
   const int xcd = lin % kXcds;
   int jj = lin / kXcds;
@@ -262,7 +276,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
   int key_part = 0, key_parts_log2 = 0, part_entry = -1;
   if constexpr (kFull) {
     const int tail = a.tail_items, quads = a.tail_quads;
-    const int first_tail = qb_max * ((npairs + kXcds - 1) / kXcds) - tail;
+    const int first_tail = items - tail;
     if (tail > 0 && jj >= first_tail) {
       const int r = jj - first_tail;            // workgroup within the XCD's tail
       part_entry = xcd * (2 * tail + 2 * quads) + r;
@@ -278,11 +292,11 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
       }
     }
   }
-  // Pair-major within an XCD: the workgroups resident on one XCD at a time
+  // Unit-major within an XCD: the workgroups resident on one XCD at a time
   // are consecutive query blocks of ONE pair, so they stream the same K/V
   // tiles at nearly the same time and the XCD's L2 serves most of them.
   int pair, qblk;
-  work_item(jj, xcd, qb_max, pair, qblk);
+  work_item(jj, xcd, qb_max, qb_sub, rsh, pair, qblk);
   if (pair >= npairs || qblk < 0) return;
   const int b = pair / hkv;
   const int g = pair - b * hkv;
@@ -939,9 +953,11 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a) {
   const int QB = kRows >> gsh;
   const int npairs = a.batch * a.geo.hkv;
   const int qb_max = (a.max_new + QB - 1) / QB;
-  const int items = qb_max * ((npairs + kXcds - 1) / kXcds);
+  const int rsh = unit_shift(npairs);
+  const int qb_sub = (qb_max + (1 << rsh) - 1) >> rsh;
+  const int items = qb_sub * ((npairs << rsh) / kXcds);
   int pair, qblk;
-  work_item(items - tail + k, xcd, qb_max, pair, qblk);
+  work_item(items - tail + k, xcd, qb_max, qb_sub, rsh, pair, qblk);
   if (pair >= npairs || qblk < 0) return;
   const int b = pair / a.geo.hkv;
   const int g = pair - b * a.geo.hkv;
@@ -1004,8 +1020,11 @@ hipError_t launch_prefill(const PrefillArgs& args, hipStream_t stream) {
   const int qb = (a.full ? rows_per_wg<true>() : rows_per_wg<false>()) / a.geo.group;
   const int64_t qb_max = (a.max_new + qb - 1) / qb;
   const int64_t npairs = static_cast<int64_t>(a.batch) * a.geo.hkv;
-  const int64_t ppx = (npairs + kXcds - 1) / kXcds;
-  const int64_t items = qb_max * ppx;     // work items per XCD
+  // Work units as in the kernel: each pair dealt into 8 / gcd(pairs, 8) units.
+  int rsh = 3;
+  for (int64_t p = npairs; rsh > 0 && (p & 1) == 0; p >>= 1) --rsh;
+  const int64_t qb_sub = (qb_max + (int64_t{1} << rsh) - 1) >> rsh;
+  const int64_t items = qb_sub * ((npairs << rsh) / kXcds);   // work items per XCD
   a.tail_items = a.tail_quads = 0;
   if (a.full && a.part != nullptr) prefill_tail_policy(items, &a.tail_items, &a.tail_quads);
   // a split item adds one workgroup per part beyond the first

@@ -3,6 +3,8 @@ the oracle for one-shot, chunked and ragged batches, histories that do not
 start on a page edge, float32 inputs, and windows of several sizes; chunked
 prefill agrees with one-shot prefill and decode row t with prefill row t."""
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -261,20 +263,24 @@ def test_swa_long_chunks_match_oracle(boundaries):
 def _tail_items(shape, batch, max_new):
     """Split work items per XCD of a full-layer call (the library's tail policy:
     none up to 32 items per XCD, else min(12, items / 4), a third of them in
-    four parts and the rest in two)."""
+    four parts and the rest in two). Items per XCD: each pair's query blocks
+    dealt into 8 / gcd(pairs, 8) units, spread evenly over the 8 XCDs."""
     qb = 384 // (shape.num_q_heads // shape.num_kv_heads)
-    items = -(-max_new // qb) * -(-batch * shape.num_kv_heads // 8)
+    pairs = batch * shape.num_kv_heads
+    ranges = 8 // math.gcd(pairs, 8)
+    items = -(-(-(-max_new // qb)) // ranges) * (pairs * ranges // 8)
     return 0 if items <= 32 else min(12, items // 4)
 
 
-@pytest.mark.parametrize("hq,hkv,d", [(16, 1, 64), (64, 8, 128)])
+@pytest.mark.parametrize("hq,hkv,d", [(32, 2, 64), (64, 8, 128)])
 def test_full_prefill_split_tail_items(hq, hkv, d):
     # Calls of more than 32 work items per XCD run each XCD's last items in two
     # or four key parts plus a merge. These batches make those items the first
     # query blocks of the last pairs, including blocks whose early parts hold
-    # no tile (history 0, one tile) and tail items with no pair at all.
+    # no tile (history 0, one tile).
     shape = ha.HeadShape(hq, hkv, d)
-    bounds = [[0, 900], [0, 333, 1200], [0, 870, 1700]] if hkv == 1 else [[0, 700], [0, 61, 650], [0, 400, 690]]
+    bounds = ([[0, 900], [0, 333, 1200], [0, 870, 1700], [0, 100, 800]] if hkv == 2
+              else [[0, 700], [0, 61, 650], [0, 400, 690]])
     totals = [b[-1] for b in bounds]
     steps = [[bd[min(s, len(bd) - 1)] for bd in bounds] for s in range(3)]
     for lo, hi in zip(steps, steps[1:]):
@@ -282,3 +288,18 @@ def test_full_prefill_split_tail_items(hq, hkv, d):
     seqs = Seqs(shape, totals, seed=hq + d)
     outs, lses = run_chunks(shape, ha.HA_FULL, seqs, bounds)
     check_against_oracle(shape, ha.HA_FULL, seqs, outs, lses)
+
+
+@pytest.mark.parametrize("kind", [ha.HA_SWA, ha.HA_FULL])
+@pytest.mark.parametrize("totals", [[6400], [900, 40, 1300]])
+def test_prefill_with_fewer_pairs_than_xcds(kind, totals):
+    # One kv head and one or three sequences: each pair's query blocks are
+    # dealt into 8 units so that all 8 XCDs get work; with one 6400-token
+    # sequence the full layer also splits its tail (units of 34 blocks).
+    shape = ha.HeadShape(16, 1, 64)
+    if kind == ha.HA_FULL and len(totals) == 1:
+        assert _tail_items(shape, 1, totals[0]) > 0
+    seqs = Seqs(shape, totals, seed=len(totals) + kind)
+    outs, lses = run_chunks(shape, kind, seqs, [[0, t] for t in totals])
+    rows = (lambda t: range(0, t, 3)) if max(totals) > 2000 else None
+    check_against_oracle(shape, kind, seqs, outs, lses, rows=rows)
