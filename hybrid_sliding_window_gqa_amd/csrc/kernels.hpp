@@ -81,15 +81,15 @@ struct PrefillArgs {
   float* lse;
   uint16_t* stage;        // workspace: chunk K/V re-laid as 16-token blocks
   int64_t stage_blocks;   // blocks the workspace holds
-  // Full layers: the last tail_items work items of each XCD's sequence run
-  // split by key tiles, the final tail_quads of them in four parts and the
-  // others in two, one workgroup per part. Each part writes normalised
-  // partial rows to its own entry of `part` (kPrefillPartEntries entries of
-  // kPrefillFullRows rows: O [entry][row][D], then LSE [entry][row] in the
-  // log2 domain) and prefill_merge_kernel combines an item's parts into
-  // out / lse.
-  int32_t tail_items;
-  int32_t tail_quads;
+  // Full layers: an XCD's sequence of work items ends in split_n1 items run
+  // in split_p1 parts each, then split_n2 items in split_p2 parts (one
+  // workgroup per part, over that share of the item's key tiles). A part
+  // writes normalised partial rows to its entry of `part` (kPrefillPartEntries
+  // entries of kPrefillFullRows rows: O [entry][row][D], then LSE
+  // [entry][row] in the log2 domain) and prefill_merge_kernel combines an
+  // item's parts into out / lse; parts without a key tile write nothing, and
+  // an item with a single tile is written by its one part directly.
+  int32_t split_n1, split_p1, split_n2, split_p2;
   float* part;
 };
 
@@ -126,16 +126,15 @@ struct VerifyArgs {
 int64_t prefill_stage_blocks(int num_tokens, int batch);
 
 // Full-layer prefill work items: 384 rows (query position x query head of
-// one kv head's group). The last items of each of the 8 XCDs' sequences may
-// run split by keys: at most kPrefillMaxTail per XCD, of which at most
-// kPrefillMaxQuads in four parts and the rest in two.
+// one kv head's group). Items of each of the 8 XCDs' sequences may run split
+// by keys, in at most kPrefillPartsPerXcd workgroups per XCD.
 constexpr int kPrefillFullRows = 384;
-constexpr int kPrefillMaxTail = 12;
-constexpr int kPrefillMaxQuads = 4;
-constexpr int kPrefillPartEntries = 8 * (2 * kPrefillMaxTail + 2 * kPrefillMaxQuads);
-// Split work items per XCD (tail) and how many of them run in four parts
-// (quads), for a call of `items_per_xcd` work items per XCD.
-void prefill_tail_policy(int64_t items_per_xcd, int* tail, int* quads);
+constexpr int kPrefillPartsPerXcd = 32;
+constexpr int kPrefillPartEntries = 8 * kPrefillPartsPerXcd;
+// How a call of `items_per_xcd` work items per XCD splits them: the last n1
+// items of each XCD's sequence in p1 parts, then n2 items in p2 parts
+// (n1 * p1 + n2 * p2 <= kPrefillPartsPerXcd; all zero: no split).
+void prefill_split_policy(int64_t items_per_xcd, int* n1, int* p1, int* n2, int* p2);
 // Bytes of the partial rows of the split items (full layers), head dim d.
 int64_t prefill_partial_bytes(int d);
 

@@ -8,7 +8,7 @@
 // "为什么选择 Hybrid SWA 架构"); chunked prefill is what the serving stack runs
 // for long requests (blog.hotdry.top 2026-06-09, section "PD 分离与长度分桶").
 //
-// Two kernels per call, three when a full-layer call splits its tail:
+// Two kernels per call, three when a full-layer call splits work items:
 //  1. stage_chunk_kernel re-lays the chunk's K/V (bf16 or f32) into 16-token
 //     blocks in the workspace, in exactly the pools' block format (matrix-core
 //     operand order, common.hpp), zero-padded past the chunk's end. Every key
@@ -51,11 +51,13 @@
 //     Tiles a wave sees completely skip masking; tiles no row of the wave
 //     sees are skipped.
 //
-//  3. prefill_merge_kernel (full layers, calls of more than one round of
-//     work items per XCD): the last items of each XCD's sequence ran as two
-//     or four workgroups over parts of their key tiles, so that the final
-//     round is not a few whole items on otherwise idle CUs; it merges their
-//     partial rows (O, LSE) into the output.
+//  3. prefill_merge_kernel (full layers). Some items ran as several
+//     workgroups over parts of their key tiles, and this merges their
+//     partial rows (O, LSE) into the output: in calls of more than one round
+//     of items per XCD, the last items of each XCD's sequence (two or four
+//     parts), so that the final round is not a few whole items on otherwise
+//     idle CUs; in calls of at most 16 items per XCD (short chunks of few
+//     sequences over long histories), every item, 32 workgroups per XCD.
 //
 // Grid order: workgroup i runs on XCD i % 8 (round-robin dispatch). All query
 // blocks of one (sequence, kv head) pair are placed on the same XCD and
@@ -108,14 +110,20 @@ __device__ __forceinline__ void work_item(int jj, int xcd, int qb_max, int qb_su
   qblk = qb_max - 1 - (((jj % qb_sub) << rsh) + (unit & ((1 << rsh) - 1)));
 }
 
-// Split tail of full layers (PrefillArgs::tail_items): the XCD's last
-// `tail` items run in parts, the first tail - quads of them in two, the
-// final `quads` in four. Tail item k (counted within the XCD's tail) has
-// tail_parts(k) parts, whose partial rows take consecutive entries from
-// xcd * (2 tail + 2 quads) + tail_first_entry(k).
-__device__ __forceinline__ int tail_parts(int k, int tail, int quads) { return k < tail - quads ? 2 : 4; }
-__device__ __forceinline__ int tail_first_entry(int k, int tail, int quads) {
-  return k < tail - quads ? 2 * k : 2 * (tail - quads) + 4 * (k - (tail - quads));
+// Split items of full layers (PrefillArgs::split_*): an XCD's sequence ends
+// in n1 items of p1 parts, then n2 items of p2 parts. Split item k (counted
+// from the first split item) has split_parts(k) parts, whose partial rows
+// take consecutive entries from xcd * kPrefillPartsPerXcd + split_entry(k).
+__device__ __forceinline__ int split_parts(const PrefillArgs& a, int k) { return k < a.split_n1 ? a.split_p1 : a.split_p2; }
+__device__ __forceinline__ int split_entry(const PrefillArgs& a, int k) {
+  return k < a.split_n1 ? k * a.split_p1 : a.split_n1 * a.split_p1 + (k - a.split_n1) * a.split_p2;
+}
+// Stage tiles of a full-layer work item: history tiles (128 keys of the
+// pages, up to the page-table row), then chunk tiles up to the block's end.
+__device__ __forceinline__ int full_item_tiles(int hist, int i_end, int table_stride, int stage_keys) {
+  const int hist_blocks = min((hist + kBlock - 1) / kBlock, table_stride);
+  const int blocks_per_tile = stage_keys / kBlock;
+  return (hist_blocks + blocks_per_tile - 1) / blocks_per_tile + (i_end + stage_keys - 1) / stage_keys;
 }
 // SWA layers write O through LDS with full-row non-temporal stores (see the
 // kernel's epilogue): 2% faster SWA layers on the chunked workload; full
@@ -269,27 +277,29 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
   const int lin = blockIdx.x;
   const int xcd = lin % kXcds;
   int jj = lin / kXcds;
-  // Full layers: the last tail_items items of the XCD's sequence run in
+  // Full layers: the split items at the end of the XCD's sequence run in
   // parts (part key_part of key_parts takes that share of the item's key
   // tiles), one workgroup each, which write partial rows to entry
   // `part_entry` for prefill_merge_kernel.
-  int key_part = 0, key_parts_log2 = 0, part_entry = -1;
+  int key_part = 0, key_parts = 1, part_entry = -1;
   if constexpr (kFull) {
-    const int tail = a.tail_items, quads = a.tail_quads;
-    const int first_tail = items - tail;
-    if (tail > 0 && jj >= first_tail) {
-      const int r = jj - first_tail;            // workgroup within the XCD's tail
-      part_entry = xcd * (2 * tail + 2 * quads) + r;
-      if (r < 2 * (tail - quads)) {
-        jj = first_tail + (r >> 1);
-        key_part = r & 1;
-        key_parts_log2 = 1;
+    const int n1 = a.split_n1, p1 = a.split_p1, n2 = a.split_n2, p2 = a.split_p2;
+    const int first_split = items - n1 - n2;
+    if (n1 + n2 > 0 && jj >= first_split) {
+      const int r = jj - first_split;            // workgroup within the XCD's split region
+      part_entry = xcd * kPrefillPartsPerXcd + r;
+      int k;
+      if (r < n1 * p1) {
+        k = r / p1;
+        key_part = r - k * p1;
+        key_parts = p1;
       } else {
-        const int r4 = r - 2 * (tail - quads);
-        jj = first_tail + (tail - quads) + (r4 >> 2);
-        key_part = r4 & 3;
-        key_parts_log2 = 2;
+        const int r2 = r - n1 * p1;
+        k = n1 + r2 / p2;
+        key_part = r2 - (k - n1) * p2;
+        key_parts = p2;
       }
+      jj = first_split + k;
     }
   }
   // Unit-major within an XCD: the workgroups resident on one XCD at a time
@@ -331,10 +341,15 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
   int c_first = 0;
   if constexpr (!kFull) c_first = kBlock * (max(0, i0 - W + 1) / kBlock);
   const int n_chunk_tiles = (i_end - c_first + kStageKeys - 1) / kStageKeys;
-  const int n_tiles = n_hist_tiles + n_chunk_tiles;
-  // Stage tiles this workgroup consumes: all, or its part's share.
-  const int t_begin = (key_part * n_tiles) >> key_parts_log2;
-  const int t_end = ((key_part + 1) * n_tiles) >> key_parts_log2;
+  // (full layers: the count prefill_merge_kernel recomputes for split items)
+  const int n_tiles = kFull ? full_item_tiles(hist, i_end, a.table_stride, kStageKeys) : n_hist_tiles + n_chunk_tiles;
+  // Stage tiles this workgroup consumes: all, or its part's share. A part
+  // with no tile writes nothing; an item of one tile is written, as if
+  // whole, by the one part that has it.
+  const int t_begin = key_part * n_tiles / key_parts;
+  const int t_end = (key_part + 1) * n_tiles / key_parts;
+  if (t_begin == t_end && key_parts > 1) return;
+  if (n_tiles <= 1) part_entry = -1;
 
   // ---- rows of this wave ----
   const int row0 = wave * kRowsPerWave;
@@ -935,18 +950,19 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
 }
 
 // ---- 3. merge of split full-layer items ----
-// Workgroup (tail item, row group): rows of one split item, one thread per 4
-// channels. With each part's partial O_p (normalised by its own l_p) and
+// Workgroup (split item, row group): rows of one split item, one thread per
+// 4 channels. With each part's partial O_p (normalised by its own l_p) and
 // LSE_p = log2 of its weight, the item's row is O = sum_p 2^(LSE_p - LSE) O_p
-// with LSE = log2 sum_p 2^LSE_p.
+// with LSE = log2 sum_p 2^LSE_p, over the parts that hold a key tile (the
+// others wrote nothing). Items of one tile were written by their one part.
 template <int D>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a) {
   constexpr int kRows = kPrefillFullRows;
   constexpr int kLanesPerRow = D / 4;
   constexpr int kRowsPerBlock = 256 / kLanesPerRow;
-  const int tail = a.tail_items, quads = a.tail_quads;
-  const int xcd = blockIdx.x / tail;
-  const int k = blockIdx.x - xcd * tail;       // tail item of the XCD
+  const int n_split = a.split_n1 + a.split_n2;
+  const int xcd = blockIdx.x / n_split;
+  const int k = blockIdx.x - xcd * n_split;     // split item of the XCD
   const int G = a.geo.group;
   const int hq = a.geo.hq;
   const int gsh = __builtin_ctz(static_cast<unsigned>(G));
@@ -957,7 +973,7 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a) {
   const int qb_sub = (qb_max + (1 << rsh) - 1) >> rsh;
   const int items = qb_sub * ((npairs << rsh) / kXcds);
   int pair, qblk;
-  work_item(items - tail + k, xcd, qb_max, qb_sub, rsh, pair, qblk);
+  work_item(items - n_split + k, xcd, qb_max, qb_sub, rsh, pair, qblk);
   if (pair >= npairs || qblk < 0) return;
   const int b = pair / a.geo.hkv;
   const int g = pair - b * a.geo.hkv;
@@ -965,25 +981,27 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a) {
   const int n = min(a.cu_new[b + 1], a.num_tokens) - tok0;
   const int i0 = qblk * QB;
   if (tok0 < 0 || i0 >= n) return;
+  const int i_end = min(n, i0 + QB);
+  const int n_tiles = full_item_tiles(max(a.hist_len[b], 0), i_end, a.table_stride, stage_keys<true>());
+  if (n_tiles <= 1) return;
   const int rho = blockIdx.y * kRowsPerBlock + static_cast<int>(threadIdx.x) / kLanesPerRow;
   const int col = 4 * (static_cast<int>(threadIdx.x) % kLanesPerRow);
   const int ci = i0 + (rho >> gsh);
-  if (rho >= kRows || ci >= min(n, i0 + QB)) return;
-  const int parts = tail_parts(k, tail, quads);
-  const int e0 = xcd * (2 * tail + 2 * quads) + tail_first_entry(k, tail, quads);
+  if (rho >= kRows || ci >= i_end) return;
+  const int parts = split_parts(a, k);
+  const int e0 = xcd * kPrefillPartsPerXcd + split_entry(a, k);
   const float* pl = a.part + static_cast<int64_t>(kPrefillPartEntries) * kRows * D;
-  float lp[4];
+  auto has_tile = [&](int p) { return p * n_tiles / parts < (p + 1) * n_tiles / parts; };
   float mx = -INFINITY;
-  for (int p = 0; p < parts; ++p) {
-    lp[p] = pl[(e0 + p) * kRows + rho];
-    mx = fmaxf(mx, lp[p]);
-  }
+  for (int p = 0; p < parts; ++p)
+    if (has_tile(p)) mx = fmaxf(mx, pl[(e0 + p) * kRows + rho]);
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
   float lse = -INFINITY;
   if (mx != -INFINITY) {
     float wsum = 0.0f;
     for (int p = 0; p < parts; ++p) {
-      const float w = fast_exp2(lp[p] - mx);
+      if (!has_tile(p)) continue;
+      const float w = fast_exp2(pl[(e0 + p) * kRows + rho] - mx);
       wsum += w;
       o += *reinterpret_cast<const f32x4*>(a.part + (static_cast<int64_t>(e0 + p) * kRows + rho) * D + col) * w;
     }
@@ -1008,8 +1026,8 @@ static void launch_prefill_d(const PrefillArgs& a, dim3 grid, hipStream_t stream
     if (a.full) hipLaunchKernelGGL((prefill_kernel<D, true, false>), grid, bfull, 0, stream, a);
     else hipLaunchKernelGGL((prefill_kernel<D, false, false>), grid, bswa, 0, stream, a);
   }
-  if (a.full && a.tail_items > 0) {
-    const dim3 mgrid(kXcds * a.tail_items, (kPrefillFullRows * (D / 4) + 255) / 256);
+  if (a.full && a.split_n1 + a.split_n2 > 0) {
+    const dim3 mgrid(kXcds * (a.split_n1 + a.split_n2), (kPrefillFullRows * (D / 4) + 255) / 256);
     hipLaunchKernelGGL((prefill_merge_kernel<D>), mgrid, dim3(256), 0, stream, a);
   }
 }
@@ -1025,10 +1043,11 @@ hipError_t launch_prefill(const PrefillArgs& args, hipStream_t stream) {
   for (int64_t p = npairs; rsh > 0 && (p & 1) == 0; p >>= 1) --rsh;
   const int64_t qb_sub = (qb_max + (int64_t{1} << rsh) - 1) >> rsh;
   const int64_t items = qb_sub * ((npairs << rsh) / kXcds);   // work items per XCD
-  a.tail_items = a.tail_quads = 0;
-  if (a.full && a.part != nullptr) prefill_tail_policy(items, &a.tail_items, &a.tail_quads);
+  a.split_n1 = a.split_p1 = a.split_n2 = a.split_p2 = 0;
+  if (a.full && a.part != nullptr) prefill_split_policy(items, &a.split_n1, &a.split_p1, &a.split_n2, &a.split_p2);
   // a split item adds one workgroup per part beyond the first
-  const int64_t blocks = (items + a.tail_items + 2 * a.tail_quads) * kXcds;
+  const int64_t blocks =
+      (items + a.split_n1 * (a.split_p1 - 1) + a.split_n2 * (a.split_p2 - 1)) * kXcds;
   if (blocks > 0x7fffffff || a.batch > 65535) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks));
   if (a.geo.d == 64) launch_prefill_d<64>(a, grid, stream);

@@ -22,21 +22,40 @@ int64_t prefill_stage_blocks(int num_tokens, int batch) {
   return (static_cast<int64_t>(num_tokens) + kBlockTokens - 1) / kBlockTokens + batch;
 }
 
-// Full-layer prefill tail. A call's work items are whole query blocks of
-// different key counts, list-scheduled over each XCD's 32 CUs, so the last
-// round leaves CUs idle while the final items finish. A simulation with the
-// kernel's measured per-item and per-tile costs puts that at about 2% of the
-// full layers of the chunked workload (4 x 32768 tokens, 8192-token chunks).
-// Running each XCD's last 12 items in two key parts, the final 4 of them in
-// four, brings it to 0.4%; over chunk sizes of 3000 to 16384 tokens and 2 or
-// 4 sequences the same rule averaged 1.3% against 2.6% unsplit (every split
-// part counted with the per-item fixed cost). Calls of at most one round per
-// XCD keep whole items: there the makespan is the largest item, which
-// splitting the last (lightest) ones does not shorten.
-void prefill_tail_policy(int64_t items_per_xcd, int* tail, int* quads) {
-  constexpr int64_t kCusPerXcd = 32;
-  *tail = items_per_xcd <= kCusPerXcd ? 0 : static_cast<int>(min_of<int64_t>(kPrefillMaxTail, items_per_xcd / 4));
-  *quads = min_of(kPrefillMaxQuads, *tail / 3);
+// Full-layer prefill split. A call's work items are whole query blocks of
+// different key counts, list-scheduled over each XCD's 32 CUs.
+//  * More than 32 items per XCD: the last round leaves CUs idle while the
+//    final items finish. A simulation with the kernel's measured per-item and
+//    per-tile costs puts that at about 2% of the full layers of the chunked
+//    workload (4 x 32768 tokens, 8192-token chunks). Running each XCD's last
+//    12 items in two key parts, the final 4 of them in four, brings it to
+//    0.4%; over chunk sizes of 3000 to 16384 tokens and 2 or 4 sequences the
+//    same rule averaged 1.3% against 2.6% unsplit (every split part counted
+//    with the per-item fixed cost).
+//  * At most 16 items per XCD (short chunks, few sequences): most CUs would
+//    have no item at all, so every item is split, into 32 / items parts or
+//    one more for the first (heaviest) ones, one round of 32 workgroups.
+//  * 17 to 32 items: one round already; splitting some items does not
+//    shorten the largest, so items stay whole.
+void prefill_split_policy(int64_t items_per_xcd, int* n1, int* p1, int* n2, int* p2) {
+  constexpr int64_t kCusPerXcd = kPrefillPartsPerXcd;
+  *n1 = *p1 = *n2 = *p2 = 0;
+  if (items_per_xcd <= 0) return;
+  if (items_per_xcd <= kCusPerXcd / 2) {
+    const int items = static_cast<int>(items_per_xcd);
+    const int parts = static_cast<int>(kCusPerXcd) / items;      // >= 2
+    *n1 = static_cast<int>(kCusPerXcd) - items * parts;           // heaviest items get one more part
+    *p1 = parts + 1;
+    *n2 = items - *n1;
+    *p2 = parts;
+  } else if (items_per_xcd > kCusPerXcd) {
+    const int tail = static_cast<int>(min_of<int64_t>(12, items_per_xcd / 4));
+    const int quads = tail / 3;
+    *n1 = tail - quads;
+    *p1 = 2;
+    *n2 = quads;
+    *p2 = 4;
+  }
 }
 
 int64_t prefill_partial_bytes(int d) {

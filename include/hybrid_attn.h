@@ -222,8 +222,9 @@ ha_status window_safe_match(const int32_t* req_tokens, int64_t req_len, const in
  *   out float32 [num_tokens][Hq][D], lse float32 [num_tokens][Hq] (natural log)
  *   workspace: hybrid_attn_workspace_size(shape, kind, 0, batch, num_tokens, 0)
  *   bytes of device memory (the chunk's K/V re-laid as 16-token blocks; for
- *   full layers also the partial rows of work items split by keys to even
- *   out the end of the launch, merged into out/lse by a third kernel);
+ *   full layers also the partial rows of work items split by keys, at the
+ *   end of large calls and throughout calls of few items, merged into
+ *   out/lse by a third kernel);
  *   it is scratch for this call only. */
 ha_status hybrid_attn_prefill(const ha_shape* shape, const ha_kv_view* kv, const int32_t* hist_len,
                               const int32_t* cu_new, int32_t batch, int32_t num_tokens, int32_t max_new,

@@ -260,20 +260,22 @@ def test_swa_long_chunks_match_oracle(boundaries):
     check_against_oracle(shape, ha.HA_SWA, seqs, outs, lses)
 
 
-def _tail_items(shape, batch, max_new):
-    """Split work items per XCD of a full-layer call (the library's tail policy:
-    none up to 32 items per XCD, else min(12, items / 4), a third of them in
-    four parts and the rest in two). Items per XCD: each pair's query blocks
-    dealt into 8 / gcd(pairs, 8) units, spread evenly over the 8 XCDs."""
+def _split_items(shape, batch, max_new):
+    """Split work items per XCD of a full-layer call, by the library's policy:
+    every item when there are at most 16 items per XCD, none for 17 to 32,
+    else min(12, items / 4) at the end. Items per XCD: each pair's query
+    blocks dealt into 8 / gcd(pairs, 8) units, spread evenly over the 8 XCDs."""
     qb = 384 // (shape.num_q_heads // shape.num_kv_heads)
     pairs = batch * shape.num_kv_heads
     ranges = 8 // math.gcd(pairs, 8)
     items = -(-(-(-max_new // qb)) // ranges) * (pairs * ranges // 8)
+    if items <= 16:
+        return items
     return 0 if items <= 32 else min(12, items // 4)
 
 
 @pytest.mark.parametrize("hq,hkv,d", [(32, 2, 64), (64, 8, 128)])
-def test_full_prefill_split_tail_items(hq, hkv, d):
+def test_full_prefill_split_split_items(hq, hkv, d):
     # Calls of more than 32 work items per XCD run each XCD's last items in two
     # or four key parts plus a merge. These batches make those items the first
     # query blocks of the last pairs, including blocks whose early parts hold
@@ -284,7 +286,7 @@ def test_full_prefill_split_tail_items(hq, hkv, d):
     totals = [b[-1] for b in bounds]
     steps = [[bd[min(s, len(bd) - 1)] for bd in bounds] for s in range(3)]
     for lo, hi in zip(steps, steps[1:]):
-        assert _tail_items(shape, len(totals), max(h - l for l, h in zip(lo, hi))) > 0
+        assert _split_items(shape, len(totals), max(h - l for l, h in zip(lo, hi))) > 0
     seqs = Seqs(shape, totals, seed=hq + d)
     outs, lses = run_chunks(shape, ha.HA_FULL, seqs, bounds)
     check_against_oracle(shape, ha.HA_FULL, seqs, outs, lses)
@@ -298,8 +300,29 @@ def test_prefill_with_fewer_pairs_than_xcds(kind, totals):
     # sequence the full layer also splits its tail (units of 34 blocks).
     shape = ha.HeadShape(16, 1, 64)
     if kind == ha.HA_FULL and len(totals) == 1:
-        assert _tail_items(shape, 1, totals[0]) > 0
+        assert _split_items(shape, 1, totals[0]) > 0
     seqs = Seqs(shape, totals, seed=len(totals) + kind)
     outs, lses = run_chunks(shape, kind, seqs, [[0, t] for t in totals])
     rows = (lambda t: range(0, t, 3)) if max(totals) > 2000 else None
     check_against_oracle(shape, kind, seqs, outs, lses, rows=rows)
+
+
+@pytest.mark.parametrize("hq,hkv,d,bounds", [
+    (64, 8, 128, [[0, 3000, 3100]]),            # 3 items per XCD: 11, 11 and 10 key parts
+    (64, 8, 128, [[0, 300, 320]]),              # 1 item of 4 tiles in 32 parts: 28 parts without a tile
+    (64, 8, 128, [[0, 40]]),                    # 1 item of 1 tile: written by its one part
+    (16, 1, 64, [[0, 5000, 5060]]),             # 1 pair dealt into 8 units, 3 of them with an item
+    (32, 4, 128, [[0, 2000, 2050], [0, 700, 760]]),
+])
+def test_full_prefill_short_chunks_over_long_history(hq, hkv, d, bounds):
+    # Calls of at most 16 work items per XCD split every item by keys over
+    # the XCD's 32 CUs and merge the parts; the last step of each batch (a
+    # short chunk over the history the earlier step wrote) is such a call.
+    shape = ha.HeadShape(hq, hkv, d)
+    totals = [b[-1] for b in bounds]
+    last = max(bd[-1] - (bd[-2] if len(bd) > 2 else 0) for bd in bounds)
+    assert 0 < _split_items(shape, len(totals), last) <= 16
+    seqs = Seqs(shape, totals, seed=hq + hkv + totals[0])
+    outs, lses = run_chunks(shape, ha.HA_FULL, seqs, bounds)
+    rows = lambda t: list(range(0, t, 29)) + list(range(max(0, t - 120), t))
+    check_against_oracle(shape, ha.HA_FULL, seqs, outs, lses, rows=rows)
