@@ -127,9 +127,10 @@ int64_t prefill_stage_blocks(int num_tokens, int batch);
 
 // Full-layer prefill work items: 384 rows (query position x query head of
 // one kv head's group). Items of each of the 8 XCDs' sequences may run split
-// by keys, in at most kPrefillPartsPerXcd workgroups per XCD.
+// by keys, in at most kPrefillPartsPerXcd workgroups per XCD (two rounds of
+// its 32 CUs).
 constexpr int kPrefillFullRows = 384;
-constexpr int kPrefillPartsPerXcd = 32;
+constexpr int kPrefillPartsPerXcd = 64;
 constexpr int kPrefillPartEntries = 8 * kPrefillPartsPerXcd;
 // How a call of `items_per_xcd` work items per XCD splits them: the last n1
 // items of each XCD's sequence in p1 parts, then n2 items in p2 parts

@@ -56,8 +56,9 @@
 //     partial rows (O, LSE) into the output: in calls of more than one round
 //     of items per XCD, the last items of each XCD's sequence (two or four
 //     parts), so that the final round is not a few whole items on otherwise
-//     idle CUs; in calls of at most 16 items per XCD (short chunks of few
-//     sequences over long histories), every item, 32 workgroups per XCD.
+//     idle CUs; in calls of at most 21 items per XCD (short chunks of few
+//     sequences over long histories), every item, so that all 32 CUs of an
+//     XCD have work.
 //
 // Grid order: workgroup i runs on XCD i % 8 (round-robin dispatch). All query
 // blocks of one (sequence, kv head) pair are placed on the same XCD and

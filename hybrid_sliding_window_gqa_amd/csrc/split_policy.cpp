@@ -32,24 +32,31 @@ int64_t prefill_stage_blocks(int num_tokens, int batch) {
 //    0.4%; over chunk sizes of 3000 to 16384 tokens and 2 or 4 sequences the
 //    same rule averaged 1.3% against 2.6% unsplit (every split part counted
 //    with the per-item fixed cost).
-//  * At most 16 items per XCD (short chunks, few sequences): most CUs would
-//    have no item at all, so every item is split, into 32 / items parts or
-//    one more for the first (heaviest) ones, one round of 32 workgroups.
-//  * 17 to 32 items: one round already; splitting some items does not
-//    shorten the largest, so items stay whole.
+//  * At most 16 items per XCD (short chunks of few sequences over long
+//    histories): most CUs would have no item at all, so every item is split,
+//    into 32 / items parts (the first, heaviest, one more): one round of 32
+//    workgroups.
+//  * 17 to 21 items: one round of whole items leaves 11 to 15 CUs idle, and
+//    the round lasts a whole item. In three parts each, the items take two
+//    rounds of a third: 2/3 of the time.
+//  * 22 to 32 items: two rounds of parts would need more than three parts
+//    for some items, or end no earlier than a whole item; items stay whole.
 void prefill_split_policy(int64_t items_per_xcd, int* n1, int* p1, int* n2, int* p2) {
-  constexpr int64_t kCusPerXcd = kPrefillPartsPerXcd;
+  constexpr int kCusPerXcd = 32;
   *n1 = *p1 = *n2 = *p2 = 0;
   if (items_per_xcd <= 0) return;
-  if (items_per_xcd <= kCusPerXcd / 2) {
-    const int items = static_cast<int>(items_per_xcd);
-    const int parts = static_cast<int>(kCusPerXcd) / items;      // >= 2
-    *n1 = static_cast<int>(kCusPerXcd) - items * parts;           // heaviest items get one more part
+  const int items = static_cast<int>(min_of<int64_t>(items_per_xcd, 1 << 20));
+  if (items <= kCusPerXcd / 2) {
+    const int parts = kCusPerXcd / items;              // >= 2
+    *n1 = kCusPerXcd - items * parts;                  // heaviest items get one more part
     *p1 = parts + 1;
     *n2 = items - *n1;
     *p2 = parts;
-  } else if (items_per_xcd > kCusPerXcd) {
-    const int tail = static_cast<int>(min_of<int64_t>(12, items_per_xcd / 4));
+  } else if (3 * items <= kPrefillPartsPerXcd) {
+    *n2 = items;
+    *p2 = 3;
+  } else if (items > kCusPerXcd) {
+    const int tail = min_of(12, items / 4);
     const int quads = tail / 3;
     *n1 = tail - quads;
     *p1 = 2;

@@ -114,12 +114,12 @@ def test_decode_workspace_checked(lib):
     # SWA decode and prefill need none
     assert lib.hybrid_attn_workspace_size(ctypes.byref(s), _lib.HA_SWA, 1, 64, 8193, 0) == 0
     # prefill: the staged chunk (K and V of every 16-token block); full layers add the
-    # partial rows of the split tail items: per XCD 12 items, 8 in two parts and 4 in
-    # four, 384 rows x (D + 1) floats per part
+    # partial rows of work items split by keys: up to 64 parts per XCD, 384 rows x
+    # (D + 1) floats each
     stage = ((8193 + 15) // 16 + 64) * 8 * 16 * 128 * 2 * 2
     assert lib.hybrid_attn_workspace_size(ctypes.byref(s), _lib.HA_SWA, 0, 64, 8193, 0) == stage
     assert lib.hybrid_attn_workspace_size(ctypes.byref(s), _lib.HA_FULL, 0, 64, 8193, 0) == \
-        stage + 8 * (2 * 12 + 2 * 4) * 384 * (128 + 1) * 4
+        stage + 8 * 64 * 384 * (128 + 1) * 4
     assert lib.hybrid_attn_decode_splits(ctypes.byref(s), _lib.HA_SWA, 64, 8193, 0) == 1
     # a filled batch still splits a long sequence: at most 1024 blocks per workgroup
     # (a batch of short sequences and one of 900K tokens must not leave the long one

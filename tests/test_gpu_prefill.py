@@ -262,14 +262,15 @@ def test_swa_long_chunks_match_oracle(boundaries):
 
 def _split_items(shape, batch, max_new):
     """Split work items per XCD of a full-layer call, by the library's policy:
-    every item when there are at most 16 items per XCD, none for 17 to 32,
-    else min(12, items / 4) at the end. Items per XCD: each pair's query
-    blocks dealt into 8 / gcd(pairs, 8) units, spread evenly over the 8 XCDs."""
+    every item when there are at most 21 items per XCD (up to 16: 32 parts
+    in all; 17 to 21: three parts each), none for 22 to 32, else
+    min(12, items / 4) at the end. Items per XCD: each pair's query blocks
+    dealt into 8 / gcd(pairs, 8) units, spread evenly over the 8 XCDs."""
     qb = 384 // (shape.num_q_heads // shape.num_kv_heads)
     pairs = batch * shape.num_kv_heads
     ranges = 8 // math.gcd(pairs, 8)
     items = -(-(-(-max_new // qb)) // ranges) * (pairs * ranges // 8)
-    if items <= 16:
+    if items <= 21:
         return items
     return 0 if items <= 32 else min(12, items // 4)
 
@@ -313,15 +314,16 @@ def test_prefill_with_fewer_pairs_than_xcds(kind, totals):
     (64, 8, 128, [[0, 40]]),                    # 1 item of 1 tile: written by its one part
     (16, 1, 64, [[0, 5000, 5060]]),             # 1 pair dealt into 8 units, 3 of them with an item
     (32, 4, 128, [[0, 2000, 2050], [0, 700, 760]]),
+    (64, 8, 128, [[0, 1000, 1900]]),            # 19 items per XCD: three parts each, two rounds
 ])
 def test_full_prefill_short_chunks_over_long_history(hq, hkv, d, bounds):
-    # Calls of at most 16 work items per XCD split every item by keys over
+    # Calls of at most 21 work items per XCD split every item by keys over
     # the XCD's 32 CUs and merge the parts; the last step of each batch (a
     # short chunk over the history the earlier step wrote) is such a call.
     shape = ha.HeadShape(hq, hkv, d)
     totals = [b[-1] for b in bounds]
     last = max(bd[-1] - (bd[-2] if len(bd) > 2 else 0) for bd in bounds)
-    assert 0 < _split_items(shape, len(totals), last) <= 16
+    assert 0 < _split_items(shape, len(totals), last) <= 21
     seqs = Seqs(shape, totals, seed=hq + hkv + totals[0])
     outs, lses = run_chunks(shape, ha.HA_FULL, seqs, bounds)
     rows = lambda t: list(range(0, t, 29)) + list(range(max(0, t - 120), t))
