@@ -304,8 +304,9 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
     }
   }
   // Unit-major within an XCD: the workgroups resident on one XCD at a time
-  // are consecutive query blocks of ONE pair, so they stream the same K/V
-  // tiles at nearly the same time and the XCD's L2 serves most of them.
+  // are query blocks of ONE pair (of one unit of it), so they stream the
+  // same K/V tiles at nearly the same time and the XCD's L2 serves most of
+  // them.
   int pair, qblk;
   work_item(jj, xcd, qb_max, qb_sub, rsh, pair, qblk);
   if (pair >= npairs || qblk < 0) return;
