@@ -4,7 +4,7 @@ for AMD Instinct MI355X (gfx950).
 The compute path is libhybridattn.so (hand-written HIP kernels behind a C
 ABI, include/hybrid_attn.h); this package is its Python binding plus the
 host-side pool bookkeeping (pool tensors, page free list) and the 6:1 layer
-group driver. Importing the package does not load the library; the first
+group step plans. Importing the package does not load the library; the first
 call does, and fails loudly if it has not been built.
 """
 

@@ -1,5 +1,5 @@
 """The five synthetic workloads at full size, in the launch configuration the
-bench uses (7-layer 6:1 groups through the plan driver), checked against the
+bench uses (7-layer 6:1 groups through the step plans), checked against the
 fp64 oracle on sampled rows (bf16 inputs, fp32 accumulation: max |O| error
 <= 1e-2, max |LSE| error <= 1e-3).
 
