@@ -27,7 +27,7 @@ HA_FULL = 1
 HA_KV_BF16 = 0
 HA_KV_INT8 = 1
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 # Bytes of the library-owned scratch array of hybrid_attn_decode_noalloc.
 HA_DECODE_SCRATCH_BYTES = 64 << 20

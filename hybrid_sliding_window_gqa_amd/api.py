@@ -107,16 +107,17 @@ class _PoolStorage:
 class SwaRingPool(_PoolStorage):
     """SWA pool of one layer: W slots per (ring, kv head).
 
-    K and V are [rings, Hkv, W/16, 16*D]: 16-slot blocks stored in the
-    library's matrix-core operand order (include/hybrid_attn.h); int8 pools
-    add k_scale / v_scale [rings, Hkv, W/16, 16]."""
+    K and V are [rings, Hkv, ceil(W/16), 16*D]: 16-slot blocks stored in the
+    library's matrix-core operand order (include/hybrid_attn.h), the last
+    block's slots past W unused; int8 pools add k_scale / v_scale
+    [rings, Hkv, ceil(W/16), 16]."""
 
     def __init__(self, shape: HeadShape, num_rings: int, device, fill: float | None = None,
                  kv_dtype: str = "bf16"):
         w, d, h = shape.window, shape.head_dim, shape.num_kv_heads
         self.shape = shape
         self.num_rings = num_rings
-        self._alloc((num_rings, h, w // BLOCK), d, device, kv_dtype, fill)
+        self._alloc((num_rings, h, -(-w // BLOCK)), d, device, kv_dtype, fill)
 
     def view(self, ring_id: torch.Tensor) -> KvView:
         _check_table(ring_id, 1, self.k.device)

@@ -44,14 +44,15 @@ ha_status check_shape(const ha_shape* s, ha::Geometry* geo) {
     return fail(HA_ERR_SHAPE, "query heads per kv head must be 1, 2, 4, 8 or 16 (got %d)", group);
   if (s->head_dim != 64 && s->head_dim != 128)
     return fail(HA_ERR_SHAPE, "head_dim must be 64 or 128 (got %d)", s->head_dim);
-  if (s->window < 16 || s->window % 16 != 0)
-    return fail(HA_ERR_SHAPE, "window must be a positive multiple of 16 (got %d)", s->window);
+  if (s->window < 1 || s->window > (1 << 24))
+    return fail(HA_ERR_SHAPE, "window must be in [1, 2^24] (got %d)", s->window);
   if (s->page_size != 16) return fail(HA_ERR_SHAPE, "page_size must be 16 (got %d)", s->page_size);
   if (!(std::isfinite(s->softmax_scale))) return fail(HA_ERR_SHAPE, "softmax_scale is not finite");
   geo->hq = s->num_q_heads;
   geo->hkv = s->num_kv_heads;
   geo->d = s->head_dim;
   geo->window = s->window;
+  geo->ring = (s->window + 15) / 16 * 16;
   geo->group = group;
   geo->scale = s->softmax_scale > 0.0f ? s->softmax_scale : 1.0f / std::sqrt(static_cast<float>(s->head_dim));
   return HA_OK;

@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const int r = a.table[b];
     if (r < 0 || r >= a.num_blocks) return;
     const int s = static_cast<int>(p % w);
-    block_base = ((static_cast<int64_t>(r) * hkv + g) * w + (s & ~(kBlock - 1))) * d;
+    block_base = ((static_cast<int64_t>(r) * hkv + g) * a.geo.ring + (s & ~(kBlock - 1))) * d;
     in_blk = s & (kBlock - 1);
   } else {
     const int64_t lp = p >> 4;
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void append8_kernel(AppendArgs a) {
     const int r = a.table[b];
     if (r < 0 || r >= a.num_blocks) return;
     const int s = static_cast<int>(p % w);
-    block_base = ((static_cast<int64_t>(r) * hkv + g) * w + (s & ~(kBlock - 1))) * d;
+    block_base = ((static_cast<int64_t>(r) * hkv + g) * a.geo.ring + (s & ~(kBlock - 1))) * d;
     in_blk = s & (kBlock - 1);
   } else {
     const int64_t lp = p >> 4;
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256) void read_kernel(AppendArgs a, uint16_t* k_out
     const int r = a.table[b];
     if (r < 0 || r >= a.num_blocks) return;
     const int s = static_cast<int>(p % w);
-    block_base = ((static_cast<int64_t>(r) * hkv + g) * w + (s & ~(kBlock - 1))) * d;
+    block_base = ((static_cast<int64_t>(r) * hkv + g) * a.geo.ring + (s & ~(kBlock - 1))) * d;
     in_blk = s & (kBlock - 1);
   } else {
     const int64_t lp = p >> 4;

@@ -85,8 +85,9 @@ __device__ __forceinline__ void load_block(BlockOps<D>& ops, const uint16_t* kp,
   }
 }
 
-// One 16-token block: scores, masking of keys past `t` (when `partial`),
-// online-softmax update and the P.V accumulation.
+// One 16-token block: scores, masking of keys past index `t` (the last
+// position or ring slot that holds a key; when `partial`), online-softmax
+// update and the P.V accumulation.
 template <int D>
 __device__ __forceinline__ void consume_block(BlockOps<D>& ops, const u32x4* qop, int first_key, int t,
                                               bool partial, float sl2, float& m_run, float& l_run, f32x4* o,
@@ -179,9 +180,14 @@ __device__ __forceinline__ void widen_block8(const RawBlock8<D>& raw, BlockOps<D
 }
 
 // consume_block for INT8 pools: score = k_scale * (q . code), and the V scale
-// of each key multiplies its probability before the bf16 cast (P'V = P
-// (scale * code)); l keeps the unscaled probabilities. Masked keys get a zero
-// V scale so an unwritten slot's scale cannot reach O.
+// of each key multiplies its probability (P'V = P (scale * code)); l keeps
+// the unscaled probabilities. Masked keys get a zero V scale so an unwritten
+// slot's scale cannot reach O. P' goes to the matrix cores as two bf16 parts,
+// hi = bf16(P') and lo = bf16(P' - hi), in one v_mfma_f32_16x16x32_bf16 per
+// dim tile whose A operand holds the block's codes twice (codes are exact in
+// bf16): a single bf16 P' would carry a 2^-9 relative error on every term,
+// also on a row's dominant key, whose probability times an arbitrary scale
+// is no longer 1. The 32-deep product takes the cycles of the 16-deep one.
 template <int D>
 __device__ __forceinline__ void consume_block8(const RawBlock8<D>& raw, const u32x4* qop, int first_key, int t,
                                                bool partial, float sl2, float& m_run, float& l_run, f32x4* o,
@@ -225,9 +231,15 @@ __device__ __forceinline__ void consume_block8(const RawBlock8<D>& raw, const u3
 #pragma unroll
   for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s[r] * sl2 - m_use);
   l_run += (p[0] + p[1]) + (p[2] + p[3]);
-  const u32x2 pb = {pack_bf16x2(p[0] * vs[0], p[1] * vs[1]), pack_bf16x2(p[2] * vs[2], p[3] * vs[3])};
+  float pv[4];
 #pragma unroll
-  for (int d = 0; d < DT; ++d) o[d] = mfma_16x16x16(ops.v[d], pb, o[d]);
+  for (int r = 0; r < 4; ++r) pv[r] = p[r] * vs[r];
+  const uint32_t h01 = pack_bf16x2(pv[0], pv[1]), h23 = pack_bf16x2(pv[2], pv[3]);
+  const uint32_t l01 = pack_bf16x2(pv[0] - bf16_bits_to_f32(h01 & 0xffffu), pv[1] - bf16_bits_to_f32(h01 >> 16));
+  const uint32_t l23 = pack_bf16x2(pv[2] - bf16_bits_to_f32(h23 & 0xffffu), pv[3] - bf16_bits_to_f32(h23 >> 16));
+  const u32x4 pb = {h01, h23, l01, l23};
+#pragma unroll
+  for (int d = 0; d < DT; ++d) o[d] = mfma_16x16x32(u32x4{ops.v[d].x, ops.v[d].y, ops.v[d].x, ops.v[d].y}, pb, o[d]);
 }
 
 // One block's operands in the pool's format.
@@ -337,6 +349,9 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
     return;
   }
   const int t = len - 1;  // query position
+  // Last pool index holding a key: position t (full), or ring slot
+  // min(t, W - 1) (slots past W - 1 of the last ring block hold none).
+  const int key_last = kFull ? t : min(t, W - 1);
 
   int first, last, nsplit;
   if constexpr (kFull) {
@@ -347,8 +362,9 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
     first = split * a.split_blocks;
     last = min(nblk, first + a.split_blocks);
   } else {
-    // Ring blocks holding at least one written slot: all of them once t >= W-1.
-    const int nrb = (t >= W - 1) ? W / kBlock : (t + kBlock) / kBlock;
+    // Ring blocks holding at least one written slot: all of them once
+    // t >= W-1 (the last one partly, when W is not a multiple of 16).
+    const int nrb = (t >= W - 1) ? a.geo.ring / kBlock : (t + kBlock) / kBlock;
     nsplit = 1;
     first = 0;
     last = nrb;
@@ -369,12 +385,12 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
       return (static_cast<int64_t>(pg) * hkv + g) * kBlock * D;
     } else {
       if (i >= last) return -1;
-      return ((static_cast<int64_t>(ring) * hkv + g) * W + kBlock * i) * D;
+      return ((static_cast<int64_t>(ring) * hkv + g) * a.geo.ring + kBlock * i) * D;
     }
   };
   auto is_partial = [&](int i) -> bool {
     if constexpr (kFull) return kBlock * i + kBlock - 1 > t;
-    else return (t < W - 1) && (kBlock * i + kBlock - 1 > t);
+    else return kBlock * i + kBlock - 1 > key_last;
   };
 
   // Q^T as the B operand: column c16 = query head g*G + c16 (zero past the group).
@@ -394,8 +410,9 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
   // Fused append: block of position t, its row in the block, and whether
   // this wave consumes that block.
   const bool fuse = a.k_new != nullptr;
-  const int new_blk = kFull ? (t >> 4) : ((t % W) >> 4);
-  const int new_row = t & (kBlock - 1);
+  const int new_slot = kFull ? t : t % W;
+  const int new_blk = new_slot >> 4;
+  const int new_row = new_slot & (kBlock - 1);
   const bool new_mine = fuse && new_blk >= first && new_blk < last && (new_blk - first) % kWaves == wave;
   NewToken<D> nt;
   NewToken8<D> n8;
@@ -554,13 +571,13 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
       if (i < last) {
         load_buf<D, kKv8>(A, a, base_of(i, 0), q4, c16);
         patch_new(A, i);
-        consume_buf<D, kKv8>(A, qop, kBlock * i, t, is_partial(i), sl2, m_run, l_run, o, q4);
+        consume_buf<D, kKv8>(A, qop, kBlock * i, key_last, is_partial(i), sl2, m_run, l_run, o, q4);
       }
     } else {
       for (int i = first + wave; i < last; i += kWaves) {
         load_buf<D, kKv8>(A, a, base_of(i, 0), q4, c16);
         patch_new(A, i);
-        consume_buf<D, kKv8>(A, qop, kBlock * i, t, is_partial(i), sl2, m_run, l_run, o, q4);
+        consume_buf<D, kKv8>(A, qop, kBlock * i, key_last, is_partial(i), sl2, m_run, l_run, o, q4);
       }
     }
   } else {

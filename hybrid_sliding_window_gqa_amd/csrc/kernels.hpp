@@ -10,6 +10,7 @@ namespace ha {
 // Geometry after validation.
 struct Geometry {
   int hq, hkv, d, window, group;  // group = hq / hkv
+  int ring;                       // slots per (ring, kv head): window rounded up to 16-slot blocks
   float scale;                    // softmax scale (natural units)
 };
 

@@ -333,7 +333,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
   } else {
     ring = a.table[b];
     const bool ring_ok = ring >= 0 && ring < a.num_blocks;
-    hist_blocks = W / kBlock;
+    hist_blocks = a.geo.ring / kBlock;
     if (ring_ok && hist > 0 && t_first - W + 1 < hist) n_hist_tiles = (hist_blocks + kStageBlocks - 1) / kStageBlocks;
   }
   // Chunk tiles start at chunk index c_first: 0 for full layers; for SWA
@@ -414,8 +414,9 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
         if (pg < 0 || pg >= a.num_blocks) { valid = 0; no_page = true; return -1; }
         return (static_cast<int64_t>(pg) * hkv + g) * kBlock * D;
       } else {
-        valid = hist >= W ? kBlock : min(kBlock, max(0, hist - lb * kBlock));  // unwritten slots
-        return ((static_cast<int64_t>(ring) * hkv + g) * W + kBlock * lb) * D;
+        // leading slots holding a position: min(hist, W) of the ring's slots
+        valid = min(kBlock, max(0, min(hist, W) - lb * kBlock));
+        return ((static_cast<int64_t>(ring) * hkv + g) * a.geo.ring + kBlock * lb) * D;
       }
     } else {
       const int cb = c_first / kBlock + (tile - n_hist_tiles) * kStageBlocks + sb;  // chunk block

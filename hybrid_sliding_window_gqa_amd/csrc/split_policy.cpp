@@ -89,7 +89,7 @@ int64_t prefill_partial_bytes(int d) {
 // with the cap (55 splits), 0.63 ms for the long sequence alone); the
 // decode workload's 513-block sequences stay at one split.
 int decode_split_blocks(bool full, int window, int max_kv_len, int batch, int hkv, int requested_splits) {
-  if (!full) return window / kBlockTokens;
+  if (!full) return (window + kBlockTokens - 1) / kBlockTokens;
   const int nblk = (max_of(max_kv_len, 1) + kBlockTokens - 1) / kBlockTokens;
   if (requested_splits > 0) return max_of(1, (nblk + requested_splits - 1) / requested_splits);
   constexpr int64_t kSlots = 256 * 2;

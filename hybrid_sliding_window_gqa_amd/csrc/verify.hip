@@ -129,9 +129,8 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
     return;
   }
 
-  // Ring slots of the newest history position (t0 - 1) and of t0, in [0, W).
+  // Ring slot of the newest history position (t0 - 1), in [0, W).
   const int last_slot = kFull ? 0 : ((t0 - 1) % W + W) % W;
-  const int t0_slot = last_slot + 1 == W ? 0 : last_slot + 1;
 
   // History blocks of this split (pool blocks holding positions < t0).
   int first, last, nsplit;
@@ -143,7 +142,7 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
   } else {
     nsplit = 1;
     first = 0;
-    last = (t0 >= W) ? W / kBlock : (t0 + kBlock - 1) / kBlock;   // ring blocks with a written slot
+    last = (t0 >= W) ? a.geo.ring / kBlock : (t0 + kBlock - 1) / kBlock;   // ring blocks with a written slot
   }
   if (split >= nsplit) return;
   const int ring = ring_id;
@@ -158,7 +157,7 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
       if (pg < 0 || pg >= a.num_blocks) return -1;
       return (static_cast<int64_t>(pg) * hkv + g) * kBlock * D;
     } else {
-      return ((static_cast<int64_t>(ring) * hkv + g) * W + kBlock * i) * D;
+      return ((static_cast<int64_t>(ring) * hkv + g) * a.geo.ring + kBlock * i) * D;
     }
   };
   // Position of key k (0..15) of history block i, or -1 if that slot holds
@@ -172,6 +171,7 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
       return p < t0 ? p : -1;
     } else {
       const int s = kBlock * i + k;   // ring slot
+      if (s >= W) return -1;          // padding slots of the last ring block
       int d = last_slot - s;          // slots back from the newest history position
       if (d < 0) d += W;
       const int p = t0 - 1 - d;
@@ -464,18 +464,20 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
     const int dd = e - j * D;
     const int p = t0 + j;
     int64_t blk;
+    int row;
     if constexpr (kFull) {
       const int lb = p / kBlock;
       const int pg = lb < a.table_stride ? page_row[lb] : -1;
       if (pg < 0 || pg >= a.num_blocks) return;
       blk = (static_cast<int64_t>(pg) * hkv + g) * kBlock * D;
+      row = p % kBlock;
     } else {
       if (ring < 0 || ring >= a.num_blocks) return;
-      int s = t0_slot + j;            // (t0 + j) mod W: j < nq <= 16 <= W
-      if (s >= W) s -= W;
-      blk = ((static_cast<int64_t>(ring) * hkv + g) * W + kBlock * (s / kBlock)) * D;
+      if (j < nq - W) return;         // its slot is written again by a later token of this call
+      const int s = p % W;
+      blk = ((static_cast<int64_t>(ring) * hkv + g) * a.geo.ring + kBlock * (s / kBlock)) * D;
+      row = s % kBlock;
     }
-    const int row = p % kBlock;
     a.k_pool_w[blk + k_elem(row, dd)] = static_cast<uint16_t>(kv);
     a.v_pool_w[blk + v_elem(row, dd)] = static_cast<uint16_t>(vv);
   };

@@ -53,8 +53,9 @@
  *
  * Pool layouts (bfloat16, per layer). Both pools are made of blocks of 16
  * tokens x D channels (D = head_dim) of one kv head, 16*D values each:
- *   SWA ring pool, W slots per (ring, kv head), W a multiple of 16:
- *     K, V  [num_rings][Hkv][W/16][16*D]        ring slot s in block s/16, token s%16
+ *   SWA ring pool, W slots per (ring, kv head), stored as ceil(W/16) blocks
+ *   (the last block's slots past W are never written nor read as keys):
+ *     K, V  [num_rings][Hkv][ceil(W/16)][16*D]  ring slot s in block s/16, token s%16
  *   Full page pool, one block per (page, kv head):
  *     K, V  [num_pages][Hkv][16*D]
  *   Position p of a sequence lives in ring slot p mod W, or in page
@@ -81,7 +82,7 @@
  *   so a lane's K chunks of two 32-channel slices and its V values of four
  *   16-channel tiles are each one 16-byte load.
  *   Scales: k_scale / v_scale float32 [num_blocks][Hkv][16] for pages and
- *   [rings][Hkv][W/16][16] for rings, i.e. the scale of the value at element
+ *   [rings][Hkv][ceil(W/16)][16] for rings, i.e. the scale of the value at element
  *   offset e of the codes is at e / (16*D) * 16 + token. */
 #ifndef HYBRID_ATTN_H
 #define HYBRID_ATTN_H
@@ -93,16 +94,16 @@
 extern "C" {
 #endif
 
-#define HA_ABI_VERSION 7
+#define HA_ABI_VERSION 8
 
 typedef enum ha_status {
   HA_OK = 0,
   HA_ERR_NULL = 1,        /* a required pointer is NULL                        */
   HA_ERR_SHAPE = 2,       /* unsupported geometry: Hq % Hkv != 0, group not in
-                             {1,2,4,8,16}, head_dim not 64 or 128, window not a
-                             positive multiple of 16 (the ring is made of
-                             16-slot blocks), page_size != 16, or a
-                             non-finite softmax_scale                         */
+                             {1,2,4,8,16}, head_dim not 64 or 128, window
+                             outside [1, 2^24], page_size != 16 (pages are
+                             the 16-token blocks), or a non-finite
+                             softmax_scale                                    */
   HA_ERR_RANGE = 3,       /* negative or inconsistent sizes                    */
   HA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required        */
   HA_ERR_UNSUPPORTED = 5, /* dtype or layer kind not supported                 */
@@ -120,8 +121,8 @@ typedef enum ha_kv_dtype { HA_KV_BF16 = 0, HA_KV_INT8 = 1 } ha_kv_dtype;
  * the kernels and by window_safe_match cannot drift apart ([HD12] notes that
  * changing W must change the window-safe rule with it).
  *   num_q_heads % num_kv_heads == 0, group = num_q_heads / num_kv_heads in
- *   {1, 2, 4, 8, 16}; head_dim in {64, 128}; window >= 16 and a multiple of
- *   16; page_size == 16; softmax_scale <= 0 selects 1/sqrt(head_dim). */
+ *   {1, 2, 4, 8, 16}; head_dim in {64, 128}; 1 <= window <= 2^24;
+ *   page_size == 16; softmax_scale <= 0 selects 1/sqrt(head_dim). */
 typedef struct ha_shape {
   int32_t num_q_heads;
   int32_t num_kv_heads;

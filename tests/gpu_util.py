@@ -86,7 +86,8 @@ def page_blocks(pool: ha.FullPagePool, g):
 
 
 def check_ring(pool, ring, seq_k, seq_v, appended_positions, window):
-    """Ring contents equal the oracle ring model, bit-exact; untouched slots stay NaN."""
+    """Ring contents equal the oracle ring model, bit-exact; untouched slots,
+    and the last block's slots past W, stay NaN."""
     model = ring_contents(appended_positions, window)
     for g in range(seq_k.shape[1]):
         k, v = ring_slots(pool, ring, g)
@@ -96,6 +97,7 @@ def check_ring(pool, ring, seq_k, seq_v, appended_positions, window):
             else:
                 np.testing.assert_array_equal(k[s], seq_k[p, g])
                 np.testing.assert_array_equal(v[s], seq_v[p, g])
+        assert np.isnan(k[window:]).all() and np.isnan(v[window:]).all(), (ring, g, "padding slots")
 
 
 def check_pages(pool, table_row, seq_k, seq_v, length, page_size=16):

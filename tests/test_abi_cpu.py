@@ -70,8 +70,9 @@ def decode_call(lib, shape, kv, batch=2, max_len=100, q=FAKE, dtype=0, splits=0,
         (dict(num_q_heads=8 * 32), _lib.HA_ERR_SHAPE),      # group 32 unsupported
         (dict(num_q_heads=24), _lib.HA_ERR_SHAPE),          # group 3 unsupported
         (dict(head_dim=96), _lib.HA_ERR_SHAPE),
-        (dict(window=100), _lib.HA_ERR_SHAPE),
         (dict(window=0), _lib.HA_ERR_SHAPE),
+        (dict(window=-16), _lib.HA_ERR_SHAPE),
+        (dict(window=(1 << 24) + 1), _lib.HA_ERR_SHAPE),
         (dict(page_size=32), _lib.HA_ERR_SHAPE),
         (dict(num_kv_heads=0), _lib.HA_ERR_SHAPE),
         (dict(softmax_scale=float("nan")), _lib.HA_ERR_SHAPE),
@@ -80,6 +81,13 @@ def decode_call(lib, shape, kv, batch=2, max_len=100, q=FAKE, dtype=0, splits=0,
 def test_shape_errors(lib, shape_kw, status):
     assert decode_call(lib, good_shape(**shape_kw), view()) == status
     assert "" != lib.ha_last_error().decode()
+
+
+@pytest.mark.parametrize("window", [1, 3, 16, 100, 1 << 24])
+def test_any_window_from_one_is_accepted(lib, window):
+    # the ring is stored as ceil(W / 16) blocks, so W need not be a multiple of
+    # 16; validation then reaches the next argument (a NULL q)
+    assert decode_call(lib, good_shape(window=window), view(), q=None) == _lib.HA_ERR_NULL
 
 
 def test_null_and_range_errors(lib):

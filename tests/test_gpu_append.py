@@ -48,6 +48,28 @@ def test_ring_append_sequence_of_calls(window, hkv, d, src):
         assert torch.isnan(pool.k[r].float()).all() and torch.isnan(pool.v[r].float()).all()
 
 
+@pytest.mark.parametrize("window,hkv,d", [(1, 2, 64), (3, 1, 64), (24, 2, 128), (100, 8, 64)])
+def test_ring_append_windows_not_a_multiple_of_16(window, hkv, d):
+    # the ring is ceil(W / 16) blocks; slot p mod W, padding slots never written
+    shape = ha.HeadShape(hkv * 2, hkv, d, window=window)
+    gen = make_generator(303 + window)
+    lens = [1, window + 2, 3 * window + 5, 50]
+    seq = [(randn_bf16(gen, n, hkv, d), randn_bf16(gen, n, hkv, d)) for n in lens]
+    pool = ha.SwaRingPool(shape, num_rings=len(lens) + 2, device="cuda", fill=float("nan"))
+    ring_id = [3, 0, 5, 1]
+    view = pool.view(i32(ring_id))
+    cuts = [sorted({0, min(n, 2), min(n, window + 1), n}) for n in lens]
+    for step in range(max(len(c) for c in cuts) - 1):
+        starts = [c[min(step, len(c) - 1)] for c in cuts]
+        ends = [c[min(step + 1, len(c) - 1)] for c in cuts]
+        append_history(shape, view, seq, starts, ends)
+    torch.cuda.synchronize()
+    for b, n in enumerate(lens):
+        check_ring(pool, ring_id[b], host(seq[b][0]), host(seq[b][1]), list(range(n)), window)
+    for r in set(range(pool.num_rings)) - set(ring_id):
+        assert torch.isnan(pool.k[r].float()).all() and torch.isnan(pool.v[r].float()).all()
+
+
 @pytest.mark.parametrize("hkv,d", [(1, 64), (8, 128)])
 def test_page_append_permuted_table(hkv, d):
     shape = ha.HeadShape(hkv * 4, hkv, d)

@@ -68,7 +68,9 @@ def oracle_decode(shape, kind, seq, q, lens):
 
 @pytest.mark.parametrize("kind", [ha.HA_SWA, ha.HA_FULL])
 @pytest.mark.parametrize("hq,hkv,d,window", [(4, 1, 64, 128), (64, 8, 128, 128), (16, 16, 128, 32), (32, 2, 64, 64),
-                                              (16, 2, 128, 256), (8, 8, 64, 512)])
+                                              (16, 2, 128, 256), (8, 8, 64, 512),
+                                              # windows that are not a multiple of 16
+                                              (8, 2, 64, 1), (8, 1, 64, 3), (16, 2, 128, 24), (32, 4, 64, 100)])
 def test_decode_matches_oracle(kind, hq, hkv, d, window):
     shape = ha.HeadShape(hq, hkv, d, window=window)
     seq, q, pool, view = build(shape, kind, LENS, seed=hq * 7 + d)
@@ -171,7 +173,8 @@ def pool_bits(pool):
 
 @pytest.mark.parametrize("kind", [ha.HA_SWA, ha.HA_FULL])
 @pytest.mark.parametrize("hq,hkv,d,window,splits", [(64, 8, 128, 128, 0), (4, 1, 64, 32, 0), (64, 8, 128, 128, 7),
-                                                      (32, 2, 64, 64, 3), (16, 2, 128, 256, 0)])
+                                                      (32, 2, 64, 64, 3), (16, 2, 128, 256, 0),
+                                                      (8, 2, 64, 24, 0), (8, 2, 64, 3, 0)])
 def test_fused_append_equals_append_then_decode(kind, hq, hkv, d, window, splits):
     """Passing the new token's K/V appends it in the same launch: outputs and
     the pool afterwards are bit-identical to append-then-decode."""

@@ -60,7 +60,8 @@ def make_pools(shape, kind, lens, seed=0):
 
 
 @pytest.mark.parametrize("kind", [ha.HA_SWA, ha.HA_FULL])
-@pytest.mark.parametrize("d,window,src", [(128, 128, None), (64, 32, torch.float32), (128, 32, None)])
+@pytest.mark.parametrize("d,window,src", [(128, 128, None), (64, 32, torch.float32), (128, 32, None),
+                                          (64, 24, None), (64, 3, None)])
 def test_append_writes_the_oracle_codes(kind, d, window, src):
     shape = ha.HeadShape(8, 2, d, window=window)
     lens = [1, 15, 16, 17, 130, 300]
@@ -116,7 +117,8 @@ def oracle_decode(q_row, k_seq, v_seq, n, kind, window):
 @pytest.mark.parametrize("kind", [ha.HA_SWA, ha.HA_FULL])
 @pytest.mark.parametrize("hq,hkv,d,window,splits,qsrc", [(64, 8, 128, 128, 0, None), (16, 2, 64, 32, 3, None),
                                                           (32, 4, 128, 64, 7, torch.float32),
-                                                          (8, 8, 128, 128, 1, None)])
+                                                          (8, 8, 128, 128, 1, None),
+                                                          (16, 2, 64, 24, 0, None), (8, 2, 64, 3, 0, None)])
 def test_decode_matches_oracle_over_dequantized_kv(kind, hq, hkv, d, window, splits, qsrc):
     shape = ha.HeadShape(hq, hkv, d, window=window)
     lens = [1, 2, 15, 16, 17, window - 1, window, window + 1, 300, 1029, 2500]
@@ -194,7 +196,7 @@ def test_decode_workload_with_int8_pools_sampled_sequences():
 
 
 @pytest.mark.parametrize("kind", [ha.HA_SWA, ha.HA_FULL])
-@pytest.mark.parametrize("d,window,qsrc", [(128, 128, None), (64, 32, torch.float32)])
+@pytest.mark.parametrize("d,window,qsrc", [(128, 128, None), (64, 32, torch.float32), (64, 24, None)])
 def test_fused_append_equals_append_then_decode(kind, d, window, qsrc):
     """Decode with the new token's K/V quantizes and appends it in the same
     launch: pools and outputs bit-identical to append8 followed by decode."""

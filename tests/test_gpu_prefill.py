@@ -97,7 +97,9 @@ def check_against_oracle(shape, kind, seqs, outs, lses, rows=None):
 # (the SWA kernel computes only the blocks of a tile that hold window keys: groups and windows
 # below give last tiles of 1 (64/8, W 128), 2 (4/1, W 128), 3 (8/1, W 32 and 16/8, W 48) and 4 blocks)
 @pytest.mark.parametrize("hq,hkv,d,window", [(4, 1, 64, 128), (64, 8, 128, 128), (32, 2, 64, 48), (16, 16, 128, 64),
-                                             (8, 1, 64, 32), (16, 8, 64, 48), (8, 8, 64, 16)])
+                                             (8, 1, 64, 32), (16, 8, 64, 48), (8, 8, 64, 16),
+                                             # windows that are not a multiple of 16
+                                             (8, 2, 64, 1), (8, 1, 64, 3), (16, 2, 128, 24), (32, 4, 64, 100)])
 def test_one_shot_ragged_batch(kind, hq, hkv, d, window):
     shape = ha.HeadShape(hq, hkv, d, window=window)
     totals = [1, 15, 33, 130, 257, 700]
@@ -328,3 +330,35 @@ def test_full_prefill_short_chunks_over_long_history(hq, hkv, d, bounds):
     outs, lses = run_chunks(shape, ha.HA_FULL, seqs, bounds)
     rows = lambda t: list(range(0, t, 29)) + list(range(max(0, t - 120), t))
     check_against_oracle(shape, ha.HA_FULL, seqs, outs, lses, rows=rows)
+
+
+def test_window_one_is_self_attention():
+    # W = 1, the window's closed form: every row sees only its own key, so
+    # o_t = v_t and lse_t = scale * q_t . k_t, in one-shot and chunked prefill
+    # and in decode (its query's key appended in the same launch). O differs
+    # from v_t only by the rounding of p = exp2(s - m) near 1 and of 1 / l.
+    shape = ha.HeadShape(8, 2, 64, window=1)
+    totals = [1, 17, 100]
+    seqs = Seqs(shape, totals, seed=41)
+    heads = np.arange(8) // 4                       # kv head of each query head
+    outs, lses = run_chunks(shape, ha.HA_SWA, seqs, [[0, 40, t] if t > 40 else [0, t] for t in totals])
+    for b, t in enumerate(totals):
+        q, k, v = host(seqs.q[b]), host(seqs.k[b]), host(seqs.v[b])
+        ref_o = v[:, heads, :]
+        ref_l = 0.125 * np.einsum("thd,thd->th", q.astype(np.float64), k[:, heads, :].astype(np.float64))
+        assert np.abs(outs[b] - ref_o).max() <= 1e-5 * max(1.0, np.abs(ref_o).max()), f"prefill seq {b}"
+        assert np.abs(lses[b] - ref_l).max() <= 1e-4, f"prefill seq {b}"
+    pool = ha.SwaRingPool(shape, len(totals), "cuda", fill=float("nan"))
+    view = pool.view(i32(list(range(len(totals)))))
+    append_history(shape, view, list(zip(seqs.k, seqs.v)), [0] * len(totals), [t - 1 for t in totals])
+    q_last = torch.stack([x[t - 1] for x, t in zip(seqs.q, totals)]).contiguous()
+    k_last = torch.stack([x[t - 1] for x, t in zip(seqs.k, totals)]).contiguous()
+    v_last = torch.stack([x[t - 1] for x, t in zip(seqs.v, totals)]).contiguous()
+    out, lse = ha.hybrid_attn_decode(shape, view, i32(totals), q_last, max(totals), k_new=k_last, v_new=v_last)
+    torch.cuda.synchronize()
+    o, l = host(out), host(lse)
+    for b, t in enumerate(totals):
+        ref_o = host(seqs.v[b])[t - 1][heads]
+        ref_l = 0.125 * (host(seqs.q[b])[t - 1].astype(np.float64) * host(seqs.k[b])[t - 1][heads]).sum(-1)
+        assert np.abs(o[b] - ref_o).max() <= 1e-5 * max(1.0, np.abs(ref_o).max()), f"decode seq {b}"
+        assert np.abs(l[b] - ref_l).max() <= 1e-4, f"decode seq {b}"

@@ -88,7 +88,10 @@ def check(case, out, lse):
 @pytest.mark.parametrize("kind", [ha.HA_SWA, ha.HA_FULL])
 @pytest.mark.parametrize("hq,hkv,d,window,nq", [(64, 8, 128, 128, 4), (64, 8, 128, 128, 1), (64, 8, 128, 128, 3),
                                                  (4, 1, 64, 128, 8), (16, 16, 128, 32, 16), (32, 2, 64, 64, 2),
-                                                 (16, 16, 64, 16, 16), (16, 8, 64, 48, 8)])
+                                                 (16, 16, 64, 16, 16), (16, 8, 64, 48, 8),
+                                                 # windows that are not a multiple of 16, some below nq
+                                                 (8, 2, 64, 3, 4), (8, 1, 64, 1, 2), (16, 2, 128, 24, 4),
+                                                 (32, 4, 64, 100, 3)])
 def test_verify_matches_oracle_and_appends(kind, hq, hkv, d, window, nq):
     shape = ha.HeadShape(hq, hkv, d, window=window)
     lens = [n for n in LENS] + [nq - 1 if nq > 1 else 0]     # one row shorter than nq
