@@ -125,18 +125,22 @@ class SwaRingPool(_PoolStorage):
 
 
 class FullPagePool(_PoolStorage):
-    """Full pool of one layer: 16-token pages.
+    """Full pool of one layer: pages of shape.page_size tokens (16, 32, ...).
 
-    K and V are [pages, Hkv, 16*D]: each page is one 16-token block per kv
-    head in the library's matrix-core operand order (include/hybrid_attn.h);
-    int8 pools add k_scale / v_scale [pages, Hkv, 16]."""
+    K and V are [pages, Hkv, page_size/16, 16*D]: each page holds
+    page_size/16 16-token blocks per kv head in the library's matrix-core
+    operand order (include/hybrid_attn.h); int8 pools add k_scale / v_scale
+    [pages, Hkv, page_size/16, 16]."""
 
     def __init__(self, shape: HeadShape, num_pages: int, device, fill: float | None = None,
                  kv_dtype: str = "bf16"):
         d, h = shape.head_dim, shape.num_kv_heads
+        ps = shape.page_size
+        if ps < BLOCK or ps & (ps - 1):
+            raise ValueError(f"page_size must be a power of two >= {BLOCK}, got {shape.page_size}")
         self.shape = shape
         self.num_pages = num_pages
-        self._alloc((num_pages, h), d, device, kv_dtype, fill)
+        self._alloc((num_pages, h, shape.page_size // BLOCK), d, device, kv_dtype, fill)
 
     def view(self, page_table: torch.Tensor) -> KvView:
         _check_table(page_table, 2, self.k.device)

@@ -46,19 +46,21 @@ ha_status check_shape(const ha_shape* s, ha::Geometry* geo) {
     return fail(HA_ERR_SHAPE, "head_dim must be 64 or 128 (got %d)", s->head_dim);
   if (s->window < 1 || s->window > (1 << 24))
     return fail(HA_ERR_SHAPE, "window must be in [1, 2^24] (got %d)", s->window);
-  if (s->page_size != 16) return fail(HA_ERR_SHAPE, "page_size must be 16 (got %d)", s->page_size);
+  if (s->page_size < 16 || s->page_size > (1 << 20) || (s->page_size & (s->page_size - 1)) != 0)
+    return fail(HA_ERR_SHAPE, "page_size must be a power of two in [16, 2^20] (got %d)", s->page_size);
   if (!(std::isfinite(s->softmax_scale))) return fail(HA_ERR_SHAPE, "softmax_scale is not finite");
   geo->hq = s->num_q_heads;
   geo->hkv = s->num_kv_heads;
   geo->d = s->head_dim;
   geo->window = s->window;
   geo->ring = (s->window + 15) / 16 * 16;
+  geo->page_shift = __builtin_ctz(static_cast<unsigned>(s->page_size)) - 4;
   geo->group = group;
   geo->scale = s->softmax_scale > 0.0f ? s->softmax_scale : 1.0f / std::sqrt(static_cast<float>(s->head_dim));
   return HA_OK;
 }
 
-ha_status check_view(const ha_kv_view* kv, int batch) {
+ha_status check_view(const ha_kv_view* kv, int batch, const ha::Geometry& geo) {
   if (!kv) return fail(HA_ERR_NULL, "kv view is NULL");
   if (kv->kind != HA_SWA && kv->kind != HA_FULL) return fail(HA_ERR_UNSUPPORTED, "unknown layer kind %d", kv->kind);
   if (kv->num_blocks < 0) return fail(HA_ERR_RANGE, "num_blocks is negative");
@@ -71,6 +73,10 @@ ha_status check_view(const ha_kv_view* kv, int batch) {
     if (!kv->table) return fail(HA_ERR_NULL, "%s is NULL", kv->kind == HA_SWA ? "ring id table" : "page table");
     if (kv->kind == HA_FULL && kv->table_stride <= 0)
       return fail(HA_ERR_RANGE, "page table stride must be positive (got %d)", kv->table_stride);
+    // a row's 16-token blocks are counted in int; positions are int32, so
+    // rows past 2^27 blocks could never be reached anyway
+    if (kv->kind == HA_FULL && (static_cast<int64_t>(kv->table_stride) << geo.page_shift) > (int64_t{1} << 27))
+      return fail(HA_ERR_RANGE, "page table stride %d x page_size covers more than 2^31 tokens", kv->table_stride);
   }
   return HA_OK;
 }
@@ -92,7 +98,7 @@ ha_status append_common(const ha_shape* shape, const ha_kv_view* view, int32_t w
   ha_status st = check_shape(shape, &geo);
   if (st != HA_OK) return st;
   if (batch < 0 || num_tokens < 0) return fail(HA_ERR_RANGE, "batch and num_tokens must be >= 0");
-  st = check_view(view, batch);
+  st = check_view(view, batch, geo);
   if (st != HA_OK) return st;
   if (view->kind != want_kind)
     return fail(HA_ERR_UNSUPPORTED, "%s needs a %s view", want_kind == HA_SWA ? "swa_ring_append" : "full_pool_append",
@@ -129,7 +135,7 @@ ha_status read_common(const ha_shape* shape, const ha_kv_view* view, int32_t wan
   ha_status st = check_shape(shape, &geo);
   if (st != HA_OK) return st;
   if (batch < 0 || num_tokens < 0) return fail(HA_ERR_RANGE, "batch and num_tokens must be >= 0");
-  st = check_view(view, batch);
+  st = check_view(view, batch, geo);
   if (st != HA_OK) return st;
   if (view->kind != want_kind)
     return fail(HA_ERR_UNSUPPORTED, "%s needs a %s view", want_kind == HA_SWA ? "swa_ring_read" : "full_pool_read",
@@ -200,7 +206,7 @@ ha_status decode_common(const ha_shape* shape, const ha_kv_view* kv, const int32
   if (st != HA_OK) return st;
   if (batch < 0 || max_kv_len < 0 || num_splits < 0)
     return fail(HA_ERR_RANGE, "batch, max_kv_len and num_splits must be >= 0");
-  if ((st = check_view(kv, batch)) != HA_OK) return st;
+  if ((st = check_view(kv, batch, geo)) != HA_OK) return st;
   if ((st = check_dtype(in_dtype)) != HA_OK) return st;
   if (batch == 0) return ok();
   if (batch > 65535) return fail(HA_ERR_RANGE, "decode batch %d exceeds 65535", batch);
@@ -350,7 +356,7 @@ ha_status hybrid_attn_prefill(const ha_shape* shape, const ha_kv_view* kv, const
   if (st != HA_OK) return st;
   if (batch < 0 || num_tokens < 0 || max_new < 0)
     return fail(HA_ERR_RANGE, "batch, num_tokens and max_new must be >= 0");
-  if ((st = check_view(kv, batch)) != HA_OK) return st;
+  if ((st = check_view(kv, batch, geo)) != HA_OK) return st;
   if (kv->kv_dtype != HA_KV_BF16) return fail(HA_ERR_UNSUPPORTED, "prefill reads bf16 pools only");
   if ((st = check_dtype(in_dtype)) != HA_OK) return st;
   if (batch == 0 || num_tokens == 0 || max_new == 0) return ok();
@@ -413,7 +419,7 @@ ha_status hybrid_attn_verify(const ha_shape* shape, const ha_kv_view* kv, const 
   if (batch < 0 || max_kv_len < 0 || num_splits < 0)
     return fail(HA_ERR_RANGE, "batch, max_kv_len and num_splits must be >= 0");
   if ((st = check_nq(geo, nq)) != HA_OK) return st;
-  if ((st = check_view(kv, batch)) != HA_OK) return st;
+  if ((st = check_view(kv, batch, geo)) != HA_OK) return st;
   if (kv->kv_dtype != HA_KV_BF16) return fail(HA_ERR_UNSUPPORTED, "verify reads bf16 pools only");
   if ((st = check_dtype(in_dtype)) != HA_OK) return st;
   if (batch == 0) return ok();

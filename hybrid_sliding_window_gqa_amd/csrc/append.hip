@@ -57,11 +57,13 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     block_base = ((static_cast<int64_t>(r) * hkv + g) * a.geo.ring + (s & ~(kBlock - 1))) * d;
     in_blk = s & (kBlock - 1);
   } else {
-    const int64_t lp = p >> 4;
+    const int64_t lb = p >> 4;                    // 16-token block of the sequence
+    const int64_t lp = lb >> a.geo.page_shift;    // its page in the table row
     if (lp >= a.table_stride) return;
     const int pg = a.table[static_cast<int64_t>(b) * a.table_stride + lp];
     if (pg < 0 || pg >= a.num_blocks) return;
-    block_base = (static_cast<int64_t>(pg) * hkv + g) * kBlock * d;
+    block_base = page_block_offset(pg, g, hkv, static_cast<int>(lb & ((1 << a.geo.page_shift) - 1)),
+                                   a.geo.page_shift, kBlock * d);
     in_blk = static_cast<int>(p & (kBlock - 1));
   }
 
@@ -100,17 +102,19 @@ __global__ __launch_bounds__(256) void append_pages_kernel(AppendArgs a) {
   const int64_t start = p0 > 0 ? p0 : 0;       // positions below 0 are dropped
   const int64_t end = p0 + n;
   if (tok_b < 0 || start >= end) return;
-  const int64_t jb = (start >> 4) + blockIdx.x; // page index in the table row
+  const int64_t jb = (start >> 4) + blockIdx.x; // 16-token block of the sequence
   const int64_t lo = max(start, jb * kBlock), hi = min(end, jb * kBlock + kBlock);
-  if (lo >= hi || jb >= a.table_stride) return;
-  const int pg = a.table[static_cast<int64_t>(b) * a.table_stride + jb];
+  const int64_t jp = jb >> a.geo.page_shift;    // its page in the table row
+  if (lo >= hi || jp >= a.table_stride) return;
+  const int pg = a.table[static_cast<int64_t>(b) * a.table_stride + jp];
   if (pg < 0 || pg >= a.num_blocks) return;
+  const int sub = static_cast<int>(jb & ((1 << a.geo.page_shift) - 1));
   const int first = static_cast<int>(lo - jb * kBlock);   // slots [first, last) are appended
   const int last = static_cast<int>(hi - jb * kBlock);
   const int64_t tok_slot0 = tok_b + (jb * kBlock - p0);   // token index of slot 0
   const int tid = threadIdx.x;
   for (int g = 0; g < hkv; ++g) {
-    const int64_t blk = (static_cast<int64_t>(pg) * hkv + g) * kBlock * d;
+    const int64_t blk = page_block_offset(pg, g, hkv, sub, a.geo.page_shift, kBlock * d);
     for (int e = tid; e < kBlock * cpr; e += blockDim.x) {
       const int key = e / cpr;
       const int col = e - key * cpr;
@@ -199,11 +203,13 @@ __global__ __launch_bounds__(256) void append8_kernel(AppendArgs a) {
     block_base = ((static_cast<int64_t>(r) * hkv + g) * a.geo.ring + (s & ~(kBlock - 1))) * d;
     in_blk = s & (kBlock - 1);
   } else {
-    const int64_t lp = p >> 4;
+    const int64_t lb = p >> 4;                    // 16-token block of the sequence
+    const int64_t lp = lb >> a.geo.page_shift;    // its page in the table row
     if (lp >= a.table_stride) return;
     const int pg = a.table[static_cast<int64_t>(b) * a.table_stride + lp];
     if (pg < 0 || pg >= a.num_blocks) return;
-    block_base = (static_cast<int64_t>(pg) * hkv + g) * kBlock * d;
+    block_base = page_block_offset(pg, g, hkv, static_cast<int>(lb & ((1 << a.geo.page_shift) - 1)),
+                                   a.geo.page_shift, kBlock * d);
     in_blk = static_cast<int>(p & (kBlock - 1));
   }
   // Every early return above is uniform over the lanes of one row, so the
@@ -286,11 +292,13 @@ __global__ __launch_bounds__(256) void read_kernel(AppendArgs a, uint16_t* k_out
     block_base = ((static_cast<int64_t>(r) * hkv + g) * a.geo.ring + (s & ~(kBlock - 1))) * d;
     in_blk = s & (kBlock - 1);
   } else {
-    const int64_t lp = p >> 4;
+    const int64_t lb = p >> 4;                    // 16-token block of the sequence
+    const int64_t lp = lb >> a.geo.page_shift;    // its page in the table row
     if (lp >= a.table_stride) return;
     const int pg = a.table[static_cast<int64_t>(b) * a.table_stride + lp];
     if (pg < 0 || pg >= a.num_blocks) return;
-    block_base = (static_cast<int64_t>(pg) * hkv + g) * kBlock * d;
+    block_base = page_block_offset(pg, g, hkv, static_cast<int>(lb & ((1 << a.geo.page_shift) - 1)),
+                                   a.geo.page_shift, kBlock * d);
     in_blk = static_cast<int>(p & (kBlock - 1));
   }
   const int64_t dst = (static_cast<int64_t>(tok) * hkv + g) * d + c * 8;

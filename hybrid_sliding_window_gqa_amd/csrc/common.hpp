@@ -76,6 +76,14 @@ __device__ __forceinline__ f32x4 mfma_16x16x16(const u32x2& a, const u32x2& b, c
                                                    __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
+// Element offset of 16-token block `sub` of page `pg`, kv head g, in a Full
+// pool whose pages hold 1 << page_shift blocks per kv head
+// ([pages][Hkv][1 << page_shift][block_elems]).
+__device__ __forceinline__ int64_t page_block_offset(int pg, int g, int hkv, int sub, int page_shift,
+                                                     int block_elems) {
+  return ((((static_cast<int64_t>(pg) * hkv + g) << page_shift) + sub) * block_elems);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }

@@ -357,7 +357,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
   if constexpr (kFull) {
     // Blocks past the page-table row or past the split grid (kv_len larger
     // than the caller's bounds) are dropped rather than read out of range.
-    const int nblk = min((len + kBlock - 1) / kBlock, a.table_stride);
+    const int nblk = min((len + kBlock - 1) / kBlock, a.table_stride << a.geo.page_shift);
     nsplit = min((nblk + a.split_blocks - 1) / a.split_blocks, a.splits);
     first = split * a.split_blocks;
     last = min(nblk, first + a.split_blocks);
@@ -378,11 +378,12 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
   const int32_t* page_row = a.table + static_cast<int64_t>(b) * a.table_stride;
 
   // Page id of block `i` and element offset of its K/V (-1: nothing to read).
-  auto page_of = [&](int i) -> int { return (i < last) ? page_row[i] : -1; };
+  const int psh = a.geo.page_shift;
+  auto page_of = [&](int i) -> int { return (i < last) ? page_row[i >> psh] : -1; };
   auto base_of = [&](int i, int pg) -> int64_t {
     if constexpr (kFull) {
       if (i >= last || pg < 0 || pg >= a.num_blocks) return -1;
-      return (static_cast<int64_t>(pg) * hkv + g) * kBlock * D;
+      return page_block_offset(pg, g, hkv, i & ((1 << psh) - 1), psh, kBlock * D);
     } else {
       if (i >= last) return -1;
       return ((static_cast<int64_t>(ring) * hkv + g) * a.geo.ring + kBlock * i) * D;
@@ -522,7 +523,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
   // the stores made the SWA call about 1 us slower.)
   auto store_new = [&]() {
     if (kKv8 && new_mine) {
-      const int64_t nb = base_of(new_blk, kFull ? page_row[new_blk] : 0);
+      const int64_t nb = base_of(new_blk, kFull ? page_row[new_blk >> psh] : 0);
       if (nb >= 0) {
         uint8_t* kb = reinterpret_cast<uint8_t*>(a.k_pool_w) + nb;
         uint8_t* vb = reinterpret_cast<uint8_t*>(a.v_pool_w) + nb;
@@ -541,7 +542,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
         }
       }
     } else if (new_mine) {
-      const int64_t nb = base_of(new_blk, kFull ? page_row[new_blk] : 0);
+      const int64_t nb = base_of(new_blk, kFull ? page_row[new_blk >> psh] : 0);
       if (nb >= 0) {
         if (c16 == new_row) {
 #pragma unroll
@@ -677,7 +678,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
   if (e >= a.geo.hq * D) return;
   const int len = a.kv_len[b];
   if (len <= 0) return;
-  const int nblk = min((len + kBlock - 1) / kBlock, a.table_stride);
+  const int nblk = min((len + kBlock - 1) / kBlock, a.table_stride << a.geo.page_shift);
   const int nsplit = min((nblk + a.split_blocks - 1) / a.split_blocks, a.splits);
   if (nsplit <= 1) return;
   const int h = e / D;

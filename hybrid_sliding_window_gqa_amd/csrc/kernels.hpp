@@ -11,6 +11,7 @@ namespace ha {
 struct Geometry {
   int hq, hkv, d, window, group;  // group = hq / hkv
   int ring;                       // slots per (ring, kv head): window rounded up to 16-slot blocks
+  int page_shift;                 // log2(page_size / 16): a page holds 1 << page_shift 16-token blocks
   float scale;                    // softmax scale (natural units)
 };
 

@@ -120,9 +120,10 @@ __device__ __forceinline__ int split_entry(const PrefillArgs& a, int k) {
   return k < a.split_n1 ? k * a.split_p1 : a.split_n1 * a.split_p1 + (k - a.split_n1) * a.split_p2;
 }
 // Stage tiles of a full-layer work item: history tiles (128 keys of the
-// pages, up to the page-table row), then chunk tiles up to the block's end.
-__device__ __forceinline__ int full_item_tiles(int hist, int i_end, int table_stride, int stage_keys) {
-  const int hist_blocks = min((hist + kBlock - 1) / kBlock, table_stride);
+// pages, up to the page-table row's `row_blocks` 16-token blocks), then chunk
+// tiles up to the block's end.
+__device__ __forceinline__ int full_item_tiles(int hist, int i_end, int row_blocks, int stage_keys) {
+  const int hist_blocks = min((hist + kBlock - 1) / kBlock, row_blocks);
   const int blocks_per_tile = stage_keys / kBlock;
   return (hist_blocks + blocks_per_tile - 1) / blocks_per_tile + (i_end + stage_keys - 1) / stage_keys;
 }
@@ -328,7 +329,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
   const int32_t* page_row = a.table + static_cast<int64_t>(b) * a.table_stride;
   int hist_blocks = 0;
   if constexpr (kFull) {
-    hist_blocks = min((hist + kBlock - 1) / kBlock, a.table_stride);
+    hist_blocks = min((hist + kBlock - 1) / kBlock, a.table_stride << a.geo.page_shift);
     n_hist_tiles = (hist_blocks + kStageBlocks - 1) / kStageBlocks;
   } else {
     ring = a.table[b];
@@ -344,7 +345,8 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
   if constexpr (!kFull) c_first = kBlock * (max(0, i0 - W + 1) / kBlock);
   const int n_chunk_tiles = (i_end - c_first + kStageKeys - 1) / kStageKeys;
   // (full layers: the count prefill_merge_kernel recomputes for split items)
-  const int n_tiles = kFull ? full_item_tiles(hist, i_end, a.table_stride, kStageKeys) : n_hist_tiles + n_chunk_tiles;
+  const int n_tiles =
+      kFull ? full_item_tiles(hist, i_end, a.table_stride << a.geo.page_shift, kStageKeys) : n_hist_tiles + n_chunk_tiles;
   // Stage tiles this workgroup consumes: all, or its part's share. A part
   // with no tile writes nothing; an item of one tile is written, as if
   // whole, by the one part that has it.
@@ -393,7 +395,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
     if constexpr (kFull) {
       const int t = batch_base + lane;
       const int lb = t * kStageBlocks + sb;
-      pg_vec = (t < n_hist_tiles && lb < hist_blocks) ? page_row[lb] : -1;
+      pg_vec = (t < n_hist_tiles && lb < hist_blocks) ? page_row[lb >> a.geo.page_shift] : -1;
     }
   };
   auto page_for = [&](int tile) -> int {
@@ -412,7 +414,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
       if constexpr (kFull) {
         valid = min(kBlock, hist - lb * kBlock);
         if (pg < 0 || pg >= a.num_blocks) { valid = 0; no_page = true; return -1; }
-        return (static_cast<int64_t>(pg) * hkv + g) * kBlock * D;
+        return page_block_offset(pg, g, hkv, lb & ((1 << a.geo.page_shift) - 1), a.geo.page_shift, kBlock * D);
       } else {
         // leading slots holding a position: min(hist, W) of the ring's slots
         valid = min(kBlock, max(0, min(hist, W) - lb * kBlock));
@@ -985,7 +987,8 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a) {
   const int i0 = qblk * QB;
   if (tok0 < 0 || i0 >= n) return;
   const int i_end = min(n, i0 + QB);
-  const int n_tiles = full_item_tiles(max(a.hist_len[b], 0), i_end, a.table_stride, stage_keys<true>());
+  const int n_tiles =
+      full_item_tiles(max(a.hist_len[b], 0), i_end, a.table_stride << a.geo.page_shift, stage_keys<true>());
   if (n_tiles <= 1) return;
   const int rho = blockIdx.y * kRowsPerBlock + static_cast<int>(threadIdx.x) / kLanesPerRow;
   const int col = 4 * (static_cast<int>(threadIdx.x) % kLanesPerRow);

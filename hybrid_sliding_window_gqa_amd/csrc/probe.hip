@@ -156,6 +156,8 @@ ha_status ha_probe_paged_read(const ha_shape* shape, const ha_kv_view* pages, co
     return ha::set_error(HA_ERR_SHAPE, "head_dim must be 64 or 128 (got %d)", shape->head_dim);
   if (shape->num_kv_heads <= 0 || shape->num_kv_heads > 65535)
     return ha::set_error(HA_ERR_SHAPE, "num_kv_heads out of range (%d)", shape->num_kv_heads);
+  if (shape->page_size != 16)
+    return ha::set_error(HA_ERR_SHAPE, "the paged read probe walks 16-token pages (page_size %d)", shape->page_size);
   if (pages->kind != HA_FULL || pages->kv_dtype != HA_KV_BF16)
     return ha::set_error(HA_ERR_UNSUPPORTED, "the paged read probe takes a bf16 HA_FULL view");
   if (batch < 0 || batch > 65535) return ha::set_error(HA_ERR_RANGE, "batch out of range (%d)", batch);

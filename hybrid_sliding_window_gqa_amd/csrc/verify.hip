@@ -135,7 +135,7 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
   // History blocks of this split (pool blocks holding positions < t0).
   int first, last, nsplit;
   if constexpr (kFull) {
-    const int nblk = min((t0 + kBlock - 1) / kBlock, a.table_stride);
+    const int nblk = min((t0 + kBlock - 1) / kBlock, a.table_stride << a.geo.page_shift);
     nsplit = max(1, min((nblk + a.split_blocks - 1) / a.split_blocks, a.splits));
     first = split * a.split_blocks;
     last = min(nblk, first + a.split_blocks);
@@ -150,12 +150,13 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
     if (ring < 0 || ring >= a.num_blocks) last = first;  // invalid ring id: no history
   }
   const int32_t* page_row = a.table + static_cast<int64_t>(b) * a.table_stride;
-  auto page_of = [&](int i) -> int { return (kFull && i < last) ? page_row[i] : -1; };
+  const int psh = a.geo.page_shift;
+  auto page_of = [&](int i) -> int { return (kFull && i < last) ? page_row[i >> psh] : -1; };
   auto base_of = [&](int i, int pg) -> int64_t {
     if (i >= last) return -1;
     if constexpr (kFull) {
       if (pg < 0 || pg >= a.num_blocks) return -1;
-      return (static_cast<int64_t>(pg) * hkv + g) * kBlock * D;
+      return page_block_offset(pg, g, hkv, i & ((1 << psh) - 1), psh, kBlock * D);
     } else {
       return ((static_cast<int64_t>(ring) * hkv + g) * a.geo.ring + kBlock * i) * D;
     }
@@ -467,9 +468,9 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
     int row;
     if constexpr (kFull) {
       const int lb = p / kBlock;
-      const int pg = lb < a.table_stride ? page_row[lb] : -1;
+      const int pg = (lb >> psh) < a.table_stride ? page_row[lb >> psh] : -1;
       if (pg < 0 || pg >= a.num_blocks) return;
-      blk = (static_cast<int64_t>(pg) * hkv + g) * kBlock * D;
+      blk = page_block_offset(pg, g, hkv, lb & ((1 << psh) - 1), psh, kBlock * D);
       row = p % kBlock;
     } else {
       if (ring < 0 || ring >= a.num_blocks) return;
@@ -505,7 +506,7 @@ __global__ __launch_bounds__(256) void verify_reduce_kernel(VerifyArgs a) {
   if (e >= nq * a.geo.hq * D) return;
   const int t0 = a.kv_len[b] - nq;
   if (t0 < 0) return;
-  const int nblk = min((t0 + kBlock - 1) / kBlock, a.table_stride);
+  const int nblk = min((t0 + kBlock - 1) / kBlock, a.table_stride << a.geo.page_shift);
   const int nsplit = max(1, min((nblk + a.split_blocks - 1) / a.split_blocks, a.splits));
   if (nsplit <= 1) return;
   const int r = e / D;               // row of the sequence: token * hq + head

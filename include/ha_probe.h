@@ -31,7 +31,7 @@ extern "C" {
  * workgroup = (kv head, sequence), 4 wavefronts, wave w takes blocks w, w+4,
  * ..., two blocks in flight, 1 KiB contiguous per load instruction, page ids
  * through the page table. No arithmetic beyond an XOR per loaded word.
- *   pages      HA_FULL view, kv_dtype HA_KV_BF16
+ *   pages      HA_FULL view, kv_dtype HA_KV_BF16, shape->page_size 16
  *   kv_len     int32 [batch] device
  *   sink       uint32 [batch * Hkv * 256] device (written; content meaningless)
  *   nontemporal != 0: the loads carry the non-temporal bit, as decode's do.

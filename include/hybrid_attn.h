@@ -56,10 +56,11 @@
  *   SWA ring pool, W slots per (ring, kv head), stored as ceil(W/16) blocks
  *   (the last block's slots past W are never written nor read as keys):
  *     K, V  [num_rings][Hkv][ceil(W/16)][16*D]  ring slot s in block s/16, token s%16
- *   Full page pool, one block per (page, kv head):
- *     K, V  [num_pages][Hkv][16*D]
+ *   Full page pool, page_size/16 blocks per (page, kv head) (PS = page_size,
+ *   a power of two >= 16):
+ *     K, V  [num_pages][Hkv][PS/16][16*D]  page token r in block r/16, token r%16
  *   Position p of a sequence lives in ring slot p mod W, or in page
- *   page_table[b][p / 16] at token p mod 16.
+ *   page_table[b][p / PS] at page token p mod PS.
  *   Inside a block, values sit in matrix-core operand order: 16-byte units,
  *   unit u = 64a + 16q + c (a < D/32, q < 4, c < 16):
  *     K unit u = K[token c][channels 32a + 8q .. 32a + 8q + 7]
@@ -81,8 +82,8 @@
  *   V(t, ch) is byte ((ch/64)*64 + (t/4)*16 + ch%16)*16 + ((ch/16)%4)*4 + t%4,
  *   so a lane's K chunks of two 32-channel slices and its V values of four
  *   16-channel tiles are each one 16-byte load.
- *   Scales: k_scale / v_scale float32 [num_blocks][Hkv][16] for pages and
- *   [rings][Hkv][ceil(W/16)][16] for rings, i.e. the scale of the value at element
+ *   Scales: k_scale / v_scale float32 [num_blocks][Hkv][PS/16][16] for pages
+ *   and [rings][Hkv][ceil(W/16)][16] for rings, i.e. the scale of the value at element
  *   offset e of the codes is at e / (16*D) * 16 + token. */
 #ifndef HYBRID_ATTN_H
 #define HYBRID_ATTN_H
@@ -101,10 +102,12 @@ typedef enum ha_status {
   HA_ERR_NULL = 1,        /* a required pointer is NULL                        */
   HA_ERR_SHAPE = 2,       /* unsupported geometry: Hq % Hkv != 0, group not in
                              {1,2,4,8,16}, head_dim not 64 or 128, window
-                             outside [1, 2^24], page_size != 16 (pages are
-                             the 16-token blocks), or a non-finite
+                             outside [1, 2^24], page_size not a power of
+                             two in [16, 2^20], or a non-finite
                              softmax_scale                                    */
-  HA_ERR_RANGE = 3,       /* negative or inconsistent sizes                    */
+  HA_ERR_RANGE = 3,       /* negative or inconsistent sizes, or a page-table
+                             row (table_stride x page_size) of more than
+                             2^31 tokens                                      */
   HA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required        */
   HA_ERR_UNSUPPORTED = 5, /* dtype or layer kind not supported                 */
   HA_ERR_HIP = 6          /* a HIP launch failed (message has the HIP error)   */
@@ -122,7 +125,10 @@ typedef enum ha_kv_dtype { HA_KV_BF16 = 0, HA_KV_INT8 = 1 } ha_kv_dtype;
  * changing W must change the window-safe rule with it).
  *   num_q_heads % num_kv_heads == 0, group = num_q_heads / num_kv_heads in
  *   {1, 2, 4, 8, 16}; head_dim in {64, 128}; 1 <= window <= 2^24;
- *   page_size == 16; softmax_scale <= 0 selects 1/sqrt(head_dim). */
+ *   page_size a power of two in [16, 2^20] (tokens per Full page: pages of
+ *   more than 16 tokens hold several 16-token blocks per kv head, which lets
+ *   a caller's allocator hand out fewer, larger pages); softmax_scale <= 0
+ *   selects 1/sqrt(head_dim). */
 typedef struct ha_shape {
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -172,10 +178,10 @@ ha_status swa_ring_append(const ha_shape* shape, const ha_kv_view* ring, const i
 
 /* ---- a2: Full pool append ([YLY] KVCache系统重构: grows on demand) --------
  * Writes token i of sequence b (position p = pos0[b] + i) to page
- * pages->table[b][p / 16], offset p mod 16. The caller allocates the pages
- * (the pool grows by the caller handing out more page ids). Arguments as for
- * swa_ring_append; every page id used must be < pages->num_blocks and
- * p / 16 < table_stride. */
+ * pages->table[b][p / page_size], page token p mod page_size. The caller
+ * allocates the pages (the pool grows by the caller handing out more page
+ * ids). Arguments as for swa_ring_append; every page id used must be
+ * < pages->num_blocks and p / page_size < table_stride. */
 ha_status full_pool_append(const ha_shape* shape, const ha_kv_view* pages, const int32_t* pos0,
                            const int32_t* cu_new, int32_t batch, int32_t num_tokens,
                            const void* k_new, const void* v_new, int32_t src_dtype, void* stream);

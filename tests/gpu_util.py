@@ -80,9 +80,11 @@ def ring_slots(pool: ha.SwaRingPool, ring, g):
 
 
 def page_blocks(pool: ha.FullPagePool, g):
-    """Host copies of every page of kv head g: K, V each [num_pages, 16, D]."""
-    d = pool.shape.head_dim
-    return block_k(host(pool.k[:, g]), d), block_v(host(pool.v[:, g]), d)
+    """Host copies of every page of kv head g: K, V each [num_pages, page_size, D]."""
+    d, ps = pool.shape.head_dim, pool.shape.page_size
+    k = block_k(host(pool.k[:, g]), d).reshape(-1, ps, d)
+    v = block_v(host(pool.v[:, g]), d).reshape(-1, ps, d)
+    return k, v
 
 
 def check_ring(pool, ring, seq_k, seq_v, appended_positions, window):
@@ -100,12 +102,12 @@ def check_ring(pool, ring, seq_k, seq_v, appended_positions, window):
         assert np.isnan(k[window:]).all() and np.isnan(v[window:]).all(), (ring, g, "padding slots")
 
 
-def check_pages(pool, table_row, seq_k, seq_v, length, page_size=16):
+def check_pages(pool, table_row, seq_k, seq_v, length):
     """Positions [0, length) sit at the oracle page model's (page, offset), bit-exact."""
     pos = np.arange(length)
-    pages, offs = page_location(table_row, pos, page_size)
+    pages, offs = page_location(table_row, pos, pool.shape.page_size)
     for g in range(seq_k.shape[1]):
-        k, v = page_blocks(pool, g)                  # [P, 16, D] each
+        k, v = page_blocks(pool, g)                  # [P, page_size, D] each
         np.testing.assert_array_equal(k[pages, offs], seq_k[:length, g])
         np.testing.assert_array_equal(v[pages, offs], seq_v[:length, g])
 

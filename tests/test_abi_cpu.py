@@ -73,7 +73,10 @@ def decode_call(lib, shape, kv, batch=2, max_len=100, q=FAKE, dtype=0, splits=0,
         (dict(window=0), _lib.HA_ERR_SHAPE),
         (dict(window=-16), _lib.HA_ERR_SHAPE),
         (dict(window=(1 << 24) + 1), _lib.HA_ERR_SHAPE),
-        (dict(page_size=32), _lib.HA_ERR_SHAPE),
+        (dict(page_size=8), _lib.HA_ERR_SHAPE),           # pages hold whole 16-token blocks
+        (dict(page_size=48), _lib.HA_ERR_SHAPE),          # not a power of two
+        (dict(page_size=0), _lib.HA_ERR_SHAPE),
+        (dict(page_size=1 << 21), _lib.HA_ERR_SHAPE),
         (dict(num_kv_heads=0), _lib.HA_ERR_SHAPE),
         (dict(softmax_scale=float("nan")), _lib.HA_ERR_SHAPE),
     ],
@@ -88,6 +91,18 @@ def test_any_window_from_one_is_accepted(lib, window):
     # the ring is stored as ceil(W / 16) blocks, so W need not be a multiple of
     # 16; validation then reaches the next argument (a NULL q)
     assert decode_call(lib, good_shape(window=window), view(), q=None) == _lib.HA_ERR_NULL
+
+
+@pytest.mark.parametrize("page_size", [16, 32, 64, 1 << 20])
+def test_power_of_two_page_sizes_are_accepted(lib, page_size):
+    assert decode_call(lib, good_shape(page_size=page_size), view(), q=None) == _lib.HA_ERR_NULL
+
+
+def test_page_table_row_beyond_int32_positions_is_rejected(lib):
+    # a row of stride pages x page_size tokens must stay below 2^31 tokens
+    s = good_shape(page_size=1 << 20)
+    assert decode_call(lib, s, view(stride=1 << 11), q=None) == _lib.HA_ERR_NULL
+    assert decode_call(lib, s, view(stride=(1 << 11) + 1)) == _lib.HA_ERR_RANGE
 
 
 def test_null_and_range_errors(lib):

@@ -70,13 +70,15 @@ def test_ring_append_windows_not_a_multiple_of_16(window, hkv, d):
         assert torch.isnan(pool.k[r].float()).all() and torch.isnan(pool.v[r].float()).all()
 
 
+@pytest.mark.parametrize("page_size", [16, 64])
 @pytest.mark.parametrize("hkv,d", [(1, 64), (8, 128)])
-def test_page_append_permuted_table(hkv, d):
-    shape = ha.HeadShape(hkv * 4, hkv, d)
+def test_page_append_permuted_table(hkv, d, page_size):
+    # a page of 64 tokens holds four 16-token blocks per kv head
+    shape = ha.HeadShape(hkv * 4, hkv, d, page_size=page_size)
     gen = make_generator(202)
     rng = np.random.default_rng(5)
     lens = [5, 16, 33, 300]
-    pages_per = [-(-n // 16) for n in lens]
+    pages_per = [-(-n // page_size) for n in lens]
     num_pages = sum(pages_per) + 9
     perm = rng.permutation(num_pages)
     stride = max(pages_per) + 2
@@ -99,7 +101,7 @@ def test_page_append_permuted_table(hkv, d):
         used |= set(table[b, :pages_per[b]].tolist())
         # tail of the last page is untouched
         last = table[b, pages_per[b] - 1]
-        tail = n - 16 * (pages_per[b] - 1)
+        tail = n - page_size * (pages_per[b] - 1)
         for g in range(hkv):
             kb, vb = page_blocks(pool, g)
             assert np.isnan(kb[last, tail:]).all() and np.isnan(vb[last, tail:]).all()
@@ -125,23 +127,25 @@ def test_out_of_range_ids_are_dropped():
     assert torch.isnan(ring.k.float()).all()
 
 
+@pytest.mark.parametrize("page_size", [16, 32])
 @pytest.mark.parametrize("src", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("hkv,d", [(2, 64), (8, 128)])
-def test_page_block_append_matches_row_append(src, hkv, d):
+def test_page_block_append_matches_row_append(src, hkv, d, page_size):
     """A full-pool call that brings at least 16 tokens per sequence on average
     is written page block by page block; the same call with the batch padded
     by empty sequences takes the per-row path. Both must write the same
     slots with the same bits (untouched slots keep their NaN), and those
     slots must be where the oracle's page model puts each position.
     Starts are unaligned, page-aligned and negative (positions below 0 are
-    dropped); float32 sources are rounded to bfloat16 on the way."""
-    shape = ha.HeadShape(hkv * 4, hkv, d)
+    dropped); float32 sources are rounded to bfloat16 on the way. Pages of
+    32 tokens hold two 16-token blocks per kv head."""
+    shape = ha.HeadShape(hkv * 4, hkv, d, page_size=page_size)
     gen = make_generator(404 + d + hkv)
     rng = np.random.default_rng(9)
     starts = [0, 5, 16, 37, -3]
     counts = [40, 11, 64, 100, 30]
     ends = [s + c for s, c in zip(starts, counts)]
-    pages_per = [-(-max(e, 0) // 16) for e in ends]
+    pages_per = [-(-max(e, 0) // page_size) for e in ends]
     num_pages = sum(pages_per) + 5
     perm = rng.permutation(num_pages)
     stride = max(pages_per) + 1
@@ -170,12 +174,12 @@ def test_page_block_append_matches_row_append(src, hkv, d):
     a, b_ = pools
     assert torch.equal(a.k.view(torch.int16), b_.k.view(torch.int16))
     assert torch.equal(a.v.view(torch.int16), b_.v.view(torch.int16))
-    written = np.zeros((num_pages, 16), bool)
+    written = np.zeros((num_pages, page_size), bool)
     for g in range(hkv):
         kb, vb = page_blocks(a, g)
         for b in range(len(starts)):
             pos = np.arange(max(starts[b], 0), ends[b])
-            pages, offs = page_location(table[b], pos, 16)
+            pages, offs = page_location(table[b], pos, page_size)
             rows = cu[b] + (pos - starts[b])
             np.testing.assert_array_equal(kb[pages, offs], expect_k[rows, g])
             np.testing.assert_array_equal(vb[pages, offs], expect_v[rows, g])

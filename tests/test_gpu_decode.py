@@ -37,7 +37,7 @@ def build(shape, kind, lens, seed, table_perm_seed=0, ring_order=None, appended=
         view = pool.view(i32(ids))
     else:
         rng = np.random.default_rng(table_perm_seed)
-        per = [-(-n // 16) for n in lens]
+        per = [-(-n // shape.page_size) for n in lens]
         num_pages = sum(per) + 5
         perm = rng.permutation(num_pages)
         table = np.full((len(lens), max(per) + 1), -1, np.int32)
@@ -78,6 +78,28 @@ def test_decode_matches_oracle(kind, hq, hkv, d, window):
     torch.cuda.synchronize()
     ref_o, ref_l = oracle_decode(shape, kind, seq, q, LENS)
     assert_close(host(out), host(lse), ref_o, ref_l, f"kind={kind} shape={shape}")
+
+
+@pytest.mark.parametrize("page_size", [32, 64, 256])
+@pytest.mark.parametrize("splits", [0, 3, 40])
+def test_decode_larger_pages(page_size, splits):
+    """Pages of several 16-token blocks: a split may start and end inside a
+    page, and the fused append writes the new token into the right block of
+    its page."""
+    shape = ha.HeadShape(16, 2, 128, page_size=page_size)
+    seq, q, pool, view = build(shape, ha.HA_FULL, LENS, seed=61 + page_size)
+    out, lse = ha.hybrid_attn_decode(shape, view, i32(LENS), q, max(LENS), num_splits=splits)
+    _, _, pool_b, view_b = build(shape, ha.HA_FULL, LENS, seed=61 + page_size, appended=[n - 1 for n in LENS])
+    k_new = torch.stack([seq[b][0][n - 1] for b, n in enumerate(LENS)]).contiguous()
+    v_new = torch.stack([seq[b][1][n - 1] for b, n in enumerate(LENS)]).contiguous()
+    ob, lb = ha.hybrid_attn_decode(shape, view_b, i32(LENS), q, max(LENS), num_splits=splits,
+                                   k_new=k_new, v_new=v_new)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_decode(shape, ha.HA_FULL, seq, q, LENS)
+    assert_close(host(out), host(lse), ref_o, ref_l, f"page_size={page_size} splits={splits}")
+    assert torch.equal(out, ob) and torch.equal(lse, lb)
+    assert torch.equal(pool.k.view(torch.int16), pool_b.k.view(torch.int16))
+    assert torch.equal(pool.v.view(torch.int16), pool_b.v.view(torch.int16))
 
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 40])

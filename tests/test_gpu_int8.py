@@ -48,7 +48,7 @@ def make_pools(shape, kind, lens, seed=0):
     if kind == ha.HA_SWA:
         pool = ha.SwaRingPool(shape, b + 1, DEV, fill=float("nan"), kv_dtype="int8")
         return pool, pool.view(i32(list(range(b))[::-1])), None
-    per = [-(-max(n, 1) // 16) for n in lens]
+    per = [-(-max(n, 1) // shape.page_size) for n in lens]
     perm = np.random.default_rng(seed).permutation(sum(per) + 3)
     table = np.full((b, max(per)), -1, np.int32)
     off = 0
@@ -63,7 +63,16 @@ def make_pools(shape, kind, lens, seed=0):
 @pytest.mark.parametrize("d,window,src", [(128, 128, None), (64, 32, torch.float32), (128, 32, None),
                                           (64, 24, None), (64, 3, None)])
 def test_append_writes_the_oracle_codes(kind, d, window, src):
-    shape = ha.HeadShape(8, 2, d, window=window)
+    check_append_codes(kind, d, window, src, 16)
+
+
+@pytest.mark.parametrize("page_size", [32, 64])
+def test_append_codes_into_larger_pages(page_size):
+    check_append_codes(ha.HA_FULL, 128, 128, None, page_size)
+
+
+def check_append_codes(kind, d, window, src, page_size):
+    shape = ha.HeadShape(8, 2, d, window=window, page_size=page_size)
     lens = [1, 15, 16, 17, 130, 300]
     gen = make_generator(3 + d + window)
     k = [randn_bf16(gen, n, 2, d) * 3 for n in lens]
@@ -98,7 +107,10 @@ def test_append_writes_the_oracle_codes(kind, d, window, src):
                     np.testing.assert_array_equal(got[1], qv[p, g])
                     assert got[2] == sk[p, g] and got[3] == sv[p, g]
             else:
-                pages, offs = page_location(table[s], np.arange(n), 16)
+                # [pages, Hkv, page_size / 16, 16, ...] -> token offsets within a page
+                kc, vc = (x.reshape(x.shape[0], x.shape[1], page_size, d) for x in (kc, vc))
+                ks, vs = (x.reshape(x.shape[0], x.shape[1], page_size) for x in (ks, vs))
+                pages, offs = page_location(table[s], np.arange(n), page_size)
                 np.testing.assert_array_equal(kc[pages, g, offs], qk[:, g])
                 np.testing.assert_array_equal(vc[pages, g, offs], qv[:, g])
                 np.testing.assert_array_equal(ks[pages, g, offs], sk[:, g])
@@ -120,7 +132,16 @@ def oracle_decode(q_row, k_seq, v_seq, n, kind, window):
                                                           (8, 8, 128, 128, 1, None),
                                                           (16, 2, 64, 24, 0, None), (8, 2, 64, 3, 0, None)])
 def test_decode_matches_oracle_over_dequantized_kv(kind, hq, hkv, d, window, splits, qsrc):
-    shape = ha.HeadShape(hq, hkv, d, window=window)
+    check_decode(kind, hq, hkv, d, window, splits, qsrc, 16)
+
+
+@pytest.mark.parametrize("page_size,splits", [(32, 0), (64, 3), (128, 40)])
+def test_decode_over_larger_int8_pages(page_size, splits):
+    check_decode(ha.HA_FULL, 16, 2, 128, 128, splits, None, page_size)
+
+
+def check_decode(kind, hq, hkv, d, window, splits, qsrc, page_size):
+    shape = ha.HeadShape(hq, hkv, d, window=window, page_size=page_size)
     lens = [1, 2, 15, 16, 17, window - 1, window, window + 1, 300, 1029, 2500]
     gen = make_generator(hq + d + window + splits)
     k = [randn_bf16(gen, n, hkv, d) for n in lens]

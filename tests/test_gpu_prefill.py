@@ -41,7 +41,7 @@ def make_pool(shape, kind, totals, perm_seed=0):
     if kind == ha.HA_SWA:
         pool = ha.SwaRingPool(shape, b + 1, "cuda", fill=float("nan"))
         return pool, pool.view(i32(list(range(b))[::-1]))
-    per = [-(-t // 16) for t in totals]
+    per = [-(-t // shape.page_size) for t in totals]
     num_pages = sum(per) + 3
     perm = np.random.default_rng(perm_seed).permutation(num_pages)
     table = np.full((b, max(per) + 1), -1, np.int32)
@@ -329,6 +329,22 @@ def test_full_prefill_short_chunks_over_long_history(hq, hkv, d, bounds):
     seqs = Seqs(shape, totals, seed=hq + hkv + totals[0])
     outs, lses = run_chunks(shape, ha.HA_FULL, seqs, bounds)
     rows = lambda t: list(range(0, t, 29)) + list(range(max(0, t - 120), t))
+    check_against_oracle(shape, ha.HA_FULL, seqs, outs, lses, rows=rows)
+
+
+@pytest.mark.parametrize("page_size", [32, 64, 256])
+def test_full_prefill_over_larger_pages(page_size):
+    # Pages of 2, 4 or 16 blocks per kv head: a 128-key stage tile covers
+    # parts of several pages or part of one; chunk boundaries fall inside
+    # pages, and the last step (a short chunk over the history) splits its
+    # items by keys.
+    shape = ha.HeadShape(32, 4, 128, page_size=page_size)
+    bounds = [[0, 700, 1500, 1530], [0, 33, 1100, 1111], [0, 5, 300, 310]]
+    totals = [b[-1] for b in bounds]
+    assert 0 < _split_items(shape, len(totals), 30) <= 21
+    seqs = Seqs(shape, totals, seed=5 + page_size)
+    outs, lses = run_chunks(shape, ha.HA_FULL, seqs, bounds)
+    rows = lambda t: list(range(0, t, 7)) + list(range(max(0, t - 40), t))
     check_against_oracle(shape, ha.HA_FULL, seqs, outs, lses, rows=rows)
 
 

@@ -23,7 +23,7 @@ def make_pool(shape, kind, lens, perm_seed=0):
     if kind == ha.HA_SWA:
         pool = ha.SwaRingPool(shape, b + 2, "cuda", fill=float("nan"))
         return pool, pool.view(i32(list(range(b))[::-1]))
-    per = [-(-max(n, 1) // 16) for n in lens]
+    per = [-(-max(n, 1) // shape.page_size) for n in lens]
     num_pages = sum(per) + 5
     perm = np.random.default_rng(perm_seed).permutation(num_pages)
     table = np.full((b, max(per) + 1), -1, np.int32)
@@ -102,6 +102,21 @@ def test_verify_matches_oracle_and_appends(kind, hq, hkv, d, window, nq):
     ref_pool, ref_view = make_pool(shape, kind, lens)
     append_history(shape, ref_view, list(zip(case.k, case.v)), [0] * len(lens),
                    [n if n >= nq else 0 for n in lens])
+    torch.cuda.synchronize()
+    assert torch.equal(case.pool.k.view(torch.int16), ref_pool.k.view(torch.int16))
+    assert torch.equal(case.pool.v.view(torch.int16), ref_pool.v.view(torch.int16))
+
+
+@pytest.mark.parametrize("page_size,nq,splits", [(32, 4, 0), (64, 7, 3), (256, 16, 40)])
+def test_verify_over_larger_pages(page_size, nq, splits):
+    # the new tokens start inside a page of several 16-token blocks, and
+    # splits start and end inside pages (group 2: nq x group <= 32)
+    shape = ha.HeadShape(8, 4, 128, page_size=page_size)
+    case = Case(shape, ha.HA_FULL, LENS, nq, seed=page_size + nq)
+    out, lse = case.run(num_splits=splits)
+    check(case, out, lse)
+    ref_pool, ref_view = make_pool(shape, ha.HA_FULL, LENS)
+    append_history(shape, ref_view, list(zip(case.k, case.v)), [0] * len(LENS), [n if n >= nq else 0 for n in LENS])
     torch.cuda.synchronize()
     assert torch.equal(case.pool.k.view(torch.int16), ref_pool.k.view(torch.int16))
     assert torch.equal(case.pool.v.view(torch.int16), ref_pool.v.view(torch.int16))
