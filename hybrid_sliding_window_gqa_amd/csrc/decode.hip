@@ -26,10 +26,12 @@
 //     accumulates O^T += V^T P^T, where P^T is the softmax tile in exactly the
 //     accumulator layout.
 // INT8 pools (include/hybrid_attn.h) take half the bytes per block: the
-// raw codes and the block's scales are what the ping-pong buffers hold, and
-// a block is widened to the same bf16 operands right before it is consumed
-// (codes are exact in bf16), the K scale multiplying the scores and the V
-// scale folded into the probabilities. A fused append quantizes the token in
+// raw codes and the block's scales are what the ping-pong buffers hold. In
+// full layers the K codes go to the int8 matrix cores as loaded, against Q
+// split into three int8 parts per head; V codes (and the K codes of SWA
+// layers) are widened to the same bf16 operands the bf16 path loads right
+// before the block is consumed (codes are exact in bf16). The K scale
+// multiplies the scores and the V scale is folded into the probabilities. A fused append quantizes the token in
 // the owning wave with append8_kernel's arithmetic (absmax butterflies over
 // the lanes that hold the K row and the V row) and patches codes and scales
 // into the raw operands.
@@ -163,48 +165,137 @@ __device__ __forceinline__ void load_block8(RawBlock8<D>& raw, const DecodeArgs&
   raw.vs = __builtin_bit_cast(f32x4, buf_load16_stream(rvs, 16 * q4));
 }
 
-// Codes -> the same bf16 operands the bf16 path loads.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4 mfma_i8_16x16x64(const u32x4& a, const u32x4& b, const i32x4& c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0, 0,
+                                               0);
+}
+
+// INT8 pools: Q^T as operands of the int8 matrix cores, so the K codes are
+// multiplied as they are loaded, with no widening. Each head's query row
+// (the bf16 values the bf16 path uses) is split into kQParts int8 parts
+// against a per-head step sq = amax / 127: q = sq * (c0 + c1 / 254 +
+// c2 / 254^2) up to sq / (2 * 254^2), about amax * 6e-8. The integer
+// products are exact. Two parts (about amax * 1.5e-5) are not enough: the
+// error of a score grows with |k|, and keys 40 times the typical size then
+// moved LSE by 2.5e-3. In lane (q4, c16), the operand of 64-channel group j
+// holds the channels of bf16 operands 2j (bytes 0-7) and 2j + 1 (bytes 8-15),
+// the byte order of the pool's K units; part p goes to q8[p * D/64 + j].
+// Returns sq (1 for a zero row, such as the heads past the group; NaN for a
+// NaN row, which then reaches the row's output).
+constexpr int kQParts = 3;
 template <int D>
-__device__ __forceinline__ void widen_block8(const RawBlock8<D>& raw, BlockOps<D>& ops) {
+__device__ __forceinline__ float split_q8(const u32x4* qop, u32x4* q8) {
+  constexpr int KS = D / 32;
+  float x[KS][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int m = 0; m < KS; ++m) {
+    const uint32_t w4[4] = {qop[m].x, qop[m].y, qop[m].z, qop[m].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[m][2 * j] = __uint_as_float(w4[j] << 16);
+      x[m][2 * j + 1] = __uint_as_float(w4[j] & 0xffff0000u);
+      amax = max_prop(amax, max_prop(fabsf(x[m][2 * j]), fabsf(x[m][2 * j + 1])));
+    }
+  }
+  amax = max_prop(amax, __shfl_xor(amax, 16));   // the 4 lanes of column c16
+  amax = max_prop(amax, __shfl_xor(amax, 32));
+  const float sq = (amax == 0.0f) ? 1.0f : amax / 127.0f;
+  const float inv = 1.0f / sq;
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) {
+    uint32_t c[kQParts][4] = {};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float r = x[2 * j + (e >> 3)][e & 7];
+      float step = sq, inv_step = inv;
+#pragma unroll
+      for (int p = 0; p < kQParts; ++p) {
+        const float cv = fminf(fmaxf(rintf(r * inv_step), -127.0f), 127.0f);
+        r = fmaf(-cv, step, r);
+        step *= 1.0f / 254.0f;
+        inv_step *= 254.0f;
+        c[p][e >> 2] |= (static_cast<uint32_t>(static_cast<int>(cv)) & 0xffu) << (8 * (e & 3));
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < kQParts; ++p) q8[p * (D / 64) + j] = u32x4{c[p][0], c[p][1], c[p][2], c[p][3]};
+  }
+  return sq;
+}
+
+// K codes -> the bf16 K operands the bf16 path loads (codes are exact in bf16).
+template <int D>
+__device__ __forceinline__ void widen_k8(const RawBlock8<D>& raw, u32x4* k) {
 #pragma unroll
   for (int j = 0; j < D / 64; ++j) {
     const u32x2 k0 = i8x4_to_bf16x4(raw.k[j].x), k1 = i8x4_to_bf16x4(raw.k[j].y);
     const u32x2 k2 = i8x4_to_bf16x4(raw.k[j].z), k3 = i8x4_to_bf16x4(raw.k[j].w);
-    ops.k[2 * j] = u32x4{k0.x, k0.y, k1.x, k1.y};
-    ops.k[2 * j + 1] = u32x4{k2.x, k2.y, k3.x, k3.y};
-    ops.v[4 * j] = i8x4_to_bf16x4(raw.v[j].x);
-    ops.v[4 * j + 1] = i8x4_to_bf16x4(raw.v[j].y);
-    ops.v[4 * j + 2] = i8x4_to_bf16x4(raw.v[j].z);
-    ops.v[4 * j + 3] = i8x4_to_bf16x4(raw.v[j].w);
+    k[2 * j] = u32x4{k0.x, k0.y, k1.x, k1.y};
+    k[2 * j + 1] = u32x4{k2.x, k2.y, k3.x, k3.y};
   }
 }
 
-// consume_block for INT8 pools: score = k_scale * (q . code), and the V scale
-// of each key multiplies its probability (P'V = P (scale * code)); l keeps
-// the unscaled probabilities. Masked keys get a zero V scale so an unwritten
+// V codes -> the bf16 V^T operands the bf16 path loads.
+template <int D>
+__device__ __forceinline__ void widen_v8(const RawBlock8<D>& raw, u32x2* v) {
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) {
+    v[4 * j] = i8x4_to_bf16x4(raw.v[j].x);
+    v[4 * j + 1] = i8x4_to_bf16x4(raw.v[j].y);
+    v[4 * j + 2] = i8x4_to_bf16x4(raw.v[j].z);
+    v[4 * j + 3] = i8x4_to_bf16x4(raw.v[j].w);
+  }
+}
+
+// consume_block for INT8 pools: score = k_scale * (q . code) -- with kI8, the
+// dot product on the int8 matrix cores as sq * sum_p (c_p . code) / 254^p
+// (split_q8; qop then holds the split operands and sl2 already carries sq),
+// otherwise on the bf16 ones with the codes widened --, and the V scale of
+// each key multiplies its probability (P'V = P (scale * code)); l keeps the
+// unscaled probabilities. Masked keys get a zero V scale so an unwritten
 // slot's scale cannot reach O. P' goes to the matrix cores as two bf16 parts,
 // hi = bf16(P') and lo = bf16(P' - hi), in one v_mfma_f32_16x16x32_bf16 per
 // dim tile whose A operand holds the block's codes twice (codes are exact in
 // bf16): a single bf16 P' would carry a 2^-9 relative error on every term,
 // also on a row's dominant key, whose probability times an arbitrary scale
 // is no longer 1. The 32-deep product takes the cycles of the 16-deep one.
-template <int D>
+template <int D, bool kI8>
 __device__ __forceinline__ void consume_block8(const RawBlock8<D>& raw, const u32x4* qop, int first_key, int t,
                                                bool partial, float sl2, float& m_run, float& l_run, f32x4* o,
                                                int q4) {
-  constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   BlockOps<D> ops;
-  widen_block8<D>(raw, ops);
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  widen_v8<D>(raw, ops.v);
+  f32x4 s;
+  if constexpr (kI8) {
+    i32x4 sp[kQParts];
 #pragma unroll
-  for (int m = 0; m < KS; ++m) s = mfma_16x16x32(ops.k[m], qop[m], s);
+    for (int p = 0; p < kQParts; ++p) {
+      sp[p] = i32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < D / 64; ++j) sp[p] = mfma_i8_16x16x64(raw.k[j], qop[p * (D / 64) + j], sp[p]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float acc = static_cast<float>(sp[kQParts - 1][r]);
+#pragma unroll
+      for (int p = kQParts - 2; p >= 0; --p) acc = fmaf(acc, 1.0f / 254.0f, static_cast<float>(sp[p][r]));
+      s[r] = acc * raw.ks[r];
+    }
+  } else {
+    widen_k8<D>(raw, ops.k);
+    s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) s = mfma_16x16x32(ops.k[m], qop[m], s);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] *= raw.ks[r];
+  }
   float vs[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    s[r] *= raw.ks[r];
-    vs[r] = raw.vs[r];
-  }
+  for (int r = 0; r < 4; ++r) vs[r] = raw.vs[r];
   if (partial) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -260,10 +351,10 @@ __device__ __forceinline__ void load_buf(BlockBuf<D, kKv8>& b, const DecodeArgs&
   else load_block<D>(b.ops, a.k_pool, a.v_pool, base, q4, c16);
 }
 
-template <int D, bool kKv8>
+template <int D, bool kKv8, bool kI8>
 __device__ __forceinline__ void consume_buf(BlockBuf<D, kKv8>& b, const u32x4* qop, int first_key, int t,
                                             bool partial, float sl2, float& m_run, float& l_run, f32x4* o, int q4) {
-  if constexpr (kKv8) consume_block8<D>(b.raw, qop, first_key, t, partial, sl2, m_run, l_run, o, q4);
+  if constexpr (kKv8) consume_block8<D, kI8>(b.raw, qop, first_key, t, partial, sl2, m_run, l_run, o, q4);
   else consume_block<D>(b.ops, qop, first_key, t, partial, sl2, m_run, l_run, o, q4);
 }
 
@@ -512,6 +603,14 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
   };
 
   const float sl2 = a.geo.scale * kLog2e;
+  // INT8 full layers: Q split for the int8 matrix cores (split_q8), its step
+  // folded into the scale of this lane's head; done once the first blocks'
+  // loads are in flight. An SWA wave consumes one block, too few to repay
+  // the split: it widens its K codes instead.
+  constexpr bool kI8 = kKv8 && kFull;
+  u32x4 q8[kQParts * (D / 64)];
+  float sl2k = sl2;
+  const u32x4* qk = kI8 ? q8 : qop;
   float m_run = -INFINITY;  // running max of this head (log2 domain), same in all lane groups
   float l_run = 0.0f;       // partial sum over this lane's keys
   f32x4 o[DT];
@@ -572,13 +671,13 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
       if (i < last) {
         load_buf<D, kKv8>(A, a, base_of(i, 0), q4, c16);
         patch_new(A, i);
-        consume_buf<D, kKv8>(A, qop, kBlock * i, key_last, is_partial(i), sl2, m_run, l_run, o, q4);
+        consume_buf<D, kKv8, kI8>(A, qk, kBlock * i, key_last, is_partial(i), sl2k, m_run, l_run, o, q4);
       }
     } else {
       for (int i = first + wave; i < last; i += kWaves) {
         load_buf<D, kKv8>(A, a, base_of(i, 0), q4, c16);
         patch_new(A, i);
-        consume_buf<D, kKv8>(A, qop, kBlock * i, key_last, is_partial(i), sl2, m_run, l_run, o, q4);
+        consume_buf<D, kKv8, kI8>(A, qk, kBlock * i, key_last, is_partial(i), sl2k, m_run, l_run, o, q4);
       }
     }
   } else {
@@ -593,6 +692,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
     BlockBuf<D, kKv8> A, B;
     load_buf<D, kKv8>(A, a, base_a, q4, c16);
     load_buf<D, kKv8>(B, a, base_b, q4, c16);
+    if constexpr (kI8) sl2k = sl2 * split_q8<D>(qop, q8);
     int pg_a2 = page_of(ia + 2 * kStep), pg_b2 = page_of(ib + 2 * kStep);
     // Pairs (A, B) in a loop with a fixed trip count and no early exit, so the
     // loads in flight at the loop head are the same on every path; an odd last
@@ -600,13 +700,13 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
     const int nmine = (last > ia) ? (last - ia + kStep - 1) / kStep : 0;
     for (int k = 0; k + 1 < nmine; k += 2) {
       patch_new(A, ia);
-      if (base_a >= 0) consume_buf<D, kKv8>(A, qop, kBlock * ia, t, is_partial(ia), sl2, m_run, l_run, o, q4);
+      if (base_a >= 0) consume_buf<D, kKv8, kI8>(A, qk, kBlock * ia, t, is_partial(ia), sl2k, m_run, l_run, o, q4);
       ia += 2 * kStep;
       base_a = base_of(ia, pg_a2);
       load_buf<D, kKv8>(A, a, base_a, q4, c16);
       pg_a2 = page_of(ia + 2 * kStep);
       patch_new(B, ib);
-      if (base_b >= 0) consume_buf<D, kKv8>(B, qop, kBlock * ib, t, is_partial(ib), sl2, m_run, l_run, o, q4);
+      if (base_b >= 0) consume_buf<D, kKv8, kI8>(B, qk, kBlock * ib, t, is_partial(ib), sl2k, m_run, l_run, o, q4);
       ib += 2 * kStep;
       base_b = base_of(ib, pg_b2);
       load_buf<D, kKv8>(B, a, base_b, q4, c16);
@@ -614,7 +714,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 3 : 4) void dec
     }
     if (nmine & 1) {
       patch_new(A, ia);
-      if (base_a >= 0) consume_buf<D, kKv8>(A, qop, kBlock * ia, t, is_partial(ia), sl2, m_run, l_run, o, q4);
+      if (base_a >= 0) consume_buf<D, kKv8, kI8>(A, qk, kBlock * ia, t, is_partial(ia), sl2k, m_run, l_run, o, q4);
     }
   }
 
