@@ -17,9 +17,10 @@ Default run (prints ONE JSON line on stdout):
            call), timed with HIP events on the launch stream.
   verify, int8_kv, ragged, reuse
            the decode pools with 4 new tokens per sequence; the decode step
-           on INT8 pools; ragged long-context decode (24 sequences, 1K to 1M
-           cached tokens, split-K); prefix-reuse prefill (32 sequences,
-           window-safe reuse) -- each skippable with --no-<name>.
+           and that verify step on INT8 pools; ragged long-context decode (24
+           sequences, 1K to 1M cached tokens, split-K); prefix-reuse prefill
+           (32 sequences, window-safe reuse) -- each skippable with
+           --no-<name>.
   cpu_baseline  the fp64 oracle on a bounded sample of the decode step.
 
 Inputs are synthetic and resident in HBM before timing starts. Options select
@@ -56,7 +57,7 @@ def parse():
     p.add_argument("--restore-groups", type=int, default=4,
                    help="groups in the stack the restore workload pipelines (its pools are per group)")
     p.add_argument("--workload", choices=["decode", "reuse", "ragged", "chunked", "copy", "verify", "restore",
-                                          "decode_int8"],
+                                          "decode_int8", "verify_int8"],
                    default="decode",
                    help="copy: 2 GiB elementwise copy, the known-size kernel that scales HBM counters")
     p.add_argument("--prefill-passes", type=int, default=3)
@@ -513,26 +514,30 @@ def int8_quant_error(torch, synth, q8, args):
                       f"heads, against float32 attention over the unquantized bf16 K/V ({int(hist[0]) + 1} keys)"}
 
 
-def verify_layer_bytes(shape, kind, t0, nq):
+def verify_layer_bytes(shape, kind, t0, nq, kv8=False):
     """Algorithmic bytes of one multi-token verify call: the history keys the
     queries need (all t0 for full layers; the W-1 before t0 for SWA layers),
-    the new tokens' K/V read and appended, Q read, O (fp32) and LSE written."""
+    the new tokens' K/V read (bf16) and appended (in the pool's format), Q
+    read, O (fp32) and LSE written."""
     t0 = np.asarray(t0, dtype=np.int64)
     hist = t0 if kind == "full" else np.minimum(t0, shape.window - 1)
     b = len(t0)
     tok = kv_bytes_per_token(shape)
+    pool_tok = kv8_bytes_per_token(shape) if kv8 else tok
     q = b * nq * shape.num_q_heads * shape.head_dim * 2
     o = b * nq * shape.num_q_heads * shape.head_dim * 4
     l = b * nq * shape.num_q_heads * 4
-    return int(hist.sum()) * tok + 2 * b * nq * tok + q + o + l
+    return int(hist.sum()) * pool_tok + b * nq * (tok + pool_tok) + q + o + l
 
 
-def run_verify(torch, ha, grp, synth, args, device, nq=4):
-    """The decode workload's pools, one step verifying nq tokens per sequence
-    in every layer of the group, timed like the decode step (cold rotation
-    over ring copies, warm, eager); and the full-layer call alone."""
+def run_verify(torch, ha, grp, synth, args, device, nq=4, kv_dtype="bf16"):
+    """The decode workload's pools (bf16, or INT8 with kv_dtype="int8"), one
+    step verifying nq tokens per sequence in every layer of the group, timed
+    like the decode step (cold rotation over ring copies, warm, eager); and
+    the full-layer call alone."""
+    kv8 = kv_dtype == "int8"
     struct = synth.decode_structure()
-    copies, _ = build_copies(torch, ha, grp, synth, struct, args, device)
+    copies, _ = build_copies(torch, ha, grp, synth, struct, args, device, kv_dtype=kv_dtype)
     shape, group, _plan, data = copies[0]
     b = struct.batch
     hist = data["hist"].astype(np.int64)
@@ -551,13 +556,14 @@ def run_verify(torch, ha, grp, synth, args, device, nq=4):
     dt = t["cold_s"]
     full_i = [i for i, layer in enumerate(group.layers) if layer.kind == "full"][0]
     full_ms = float(t["call_ms"][full_i])
-    step_bytes = sum(verify_layer_bytes(shape, layer.kind, hist, nq) for layer in group.layers)
-    full_bytes = verify_layer_bytes(shape, "full", hist, nq)
+    step_bytes = sum(verify_layer_bytes(shape, layer.kind, hist, nq, kv8) for layer in group.layers)
+    full_bytes = verify_layer_bytes(shape, "full", hist, nq, kv8)
     value = step_bytes / dt / 1e9
-    log(f"[bench] verify step {dt * 1e3:.3f} ms, {value:.1f} GB/s, {b * nq / dt:.0f} tokens verified/s; "
-        f"full call {full_ms * 1e3:.1f} us ({full_bytes / full_ms / 1e6:.0f} GB/s)")
+    log(f"[bench] verify step ({kv_dtype} pools) {dt * 1e3:.3f} ms, {value:.1f} GB/s, "
+        f"{b * nq / dt:.0f} tokens verified/s; full call {full_ms * 1e3:.1f} us ({full_bytes / full_ms / 1e6:.0f} GB/s)")
     return {
-        "metric": "multi-token verify decode attn HBM GB/s (% peak), SWA:full 6:1",
+        "metric": ("multi-token verify decode attn HBM GB/s (% peak), SWA:full 6:1"
+                   + (", INT8 KV pools" if kv8 else "")),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -569,15 +575,17 @@ def run_verify(torch, ha, grp, synth, args, device, nq=4):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": (f"verify: {b} sequences x {int(hist[0])} cached tokens + {nq} new tokens each "
-                                f"(causal among them), one 6:1 group, Hq/Hkv/D {hq}/{hkv}/{d}"),
+                                f"(causal among them), one 6:1 group, Hq/Hkv/D {hq}/{hkv}/{d}"
+                                + (", INT8 pools (per-token scales)" if kv8 else "")),
                    "global_batch": b, "tokens_per_sequence": nq, "parallelism": "none (1 GPU)"},
         "pct_peak_hbm": round(100.0 * value / HBM_PEAK_GBS, 2),
         "tokens_verified_per_s": round(b * nq / dt, 1),
         **timing_fields(t, step_bytes),
         "roofline": {"bound": "hbm", "achieved": round(full_bytes / full_ms / 1e6, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(full_bytes / full_ms / 1e6 / HBM_PEAK_GBS, 4),
-                     "traffic": profile_traffic(VERIFY_PROFILE),
-                     "kernel": "hybrid_attn_verify, full layer (verify_kernel<128,full,bf16,2> + reduce)",
+                     "traffic": None if kv8 else profile_traffic(VERIFY_PROFILE),
+                     "kernel": (f"hybrid_attn_verify, full layer (verify_kernel<128,full,bf16,2,{kv_dtype}> "
+                                "+ reduce)"),
                      "bytes_per_launch": full_bytes},
     }
 
@@ -1134,8 +1142,9 @@ def main():
     if args.workload == "reuse":
         print(json.dumps(run_reuse(torch, ha, grp, synth, args, device)))
         return 0
-    if args.workload == "verify":
-        print(json.dumps(run_verify(torch, ha, grp, synth, args, device)))
+    if args.workload in ("verify", "verify_int8"):
+        kv_dtype = "int8" if args.workload == "verify_int8" else "bf16"
+        print(json.dumps(run_verify(torch, ha, grp, synth, args, device, kv_dtype=kv_dtype)))
         return 0
     if args.workload == "restore":
         print(json.dumps(run_restore(torch, ha, grp, synth, args, device)))
@@ -1230,6 +1239,13 @@ def main():
         if not args.no_quant_error:
             line["int8_kv"]["quant_error"] = int8_quant_error(torch, synth, q8, args)
         del q8
+        torch.cuda.empty_cache()
+        log("[bench] multi-token verify on INT8 pools")
+        v8 = run_verify(torch, ha, grp, synth, args, device, kv_dtype="int8")
+        line["int8_kv"]["verify"] = {k: v8[k] for k in ("value", "unit", "ms_per_step", "pct_peak_hbm",
+                                                        "tokens_verified_per_s")}
+        line["int8_kv"]["verify"]["full_call_gbs"] = v8["roofline"]["achieved"]
+        del v8
         torch.cuda.empty_cache()
     if args.workload == "decode" and not args.no_ragged:
         log("[bench] ragged long-context decode")

@@ -420,7 +420,6 @@ ha_status hybrid_attn_verify(const ha_shape* shape, const ha_kv_view* kv, const 
     return fail(HA_ERR_RANGE, "batch, max_kv_len and num_splits must be >= 0");
   if ((st = check_nq(geo, nq)) != HA_OK) return st;
   if ((st = check_view(kv, batch, geo)) != HA_OK) return st;
-  if (kv->kv_dtype != HA_KV_BF16) return fail(HA_ERR_UNSUPPORTED, "verify reads bf16 pools only");
   if ((st = check_dtype(in_dtype)) != HA_OK) return st;
   if (batch == 0) return ok();
   if (batch > 65535) return fail(HA_ERR_RANGE, "verify batch %d exceeds 65535", batch);
@@ -447,6 +446,9 @@ ha_status hybrid_attn_verify(const ha_shape* shape, const ha_kv_view* kv, const 
   a.k_new = k_new;
   a.v_new = v_new;
   a.in_f32 = in_dtype == HA_F32;
+  a.kv8 = kv->kv_dtype == HA_KV_INT8;
+  a.k_scale = kv->k_scale;
+  a.v_scale = kv->v_scale;
   a.out = out;
   a.lse = lse;
   a.split_blocks = ha::decode_split_blocks(full, geo.window, max_kv_len, batch, geo.hkv, num_splits);

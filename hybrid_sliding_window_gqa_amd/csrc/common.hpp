@@ -214,4 +214,86 @@ __device__ __forceinline__ float group4_sum(float v) {
   return a + b;
 }
 
+// ---- INT8 pool blocks (decode and verify) ----
+// The raw 16-byte units of one block as a lane (q4, c16) loads them (K: D/64
+// units holding two 32-channel slices each; V: D/64 units holding four
+// 16-channel tiles each) and the 4 K and 4 V scales of the lane's keys
+// 4*q4 .. 4*q4+3.
+template <int D>
+struct RawBlock8 {
+  u32x4 k[D / 64];
+  u32x4 v[D / 64];
+  f32x4 ks;
+  f32x4 vs;
+};
+
+// Loads one INT8 block at element offset `base` of the code pools (the
+// scales of its 16 tokens at base / D); base < 0 loads zeros without traffic.
+template <int D>
+__device__ __forceinline__ void load_block8(RawBlock8<D>& raw, const void* k_pool, const void* v_pool,
+                                            const float* k_scale, const float* v_scale, int64_t base, int lane) {
+  const bool ok = base >= 0;
+  const int64_t b0 = ok ? base : 0;
+  const uint32_t bytes = ok ? kBlock * D : 0;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const uint8_t*>(k_pool) + b0, bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const uint8_t*>(v_pool) + b0, bytes);
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) {
+    raw.k[j] = buf_load16_stream(rk, 16 * (64 * j + lane));
+    raw.v[j] = buf_load16_stream(rv, 16 * (64 * j + lane));
+  }
+  const uint32_t sbytes = ok ? kBlock * 4 : 0;
+  const __amdgpu_buffer_rsrc_t rks = make_rsrc(k_scale + b0 / D, sbytes);
+  const __amdgpu_buffer_rsrc_t rvs = make_rsrc(v_scale + b0 / D, sbytes);
+  raw.ks = __builtin_bit_cast(f32x4, buf_load16_stream(rks, 16 * (lane >> 4)));
+  raw.vs = __builtin_bit_cast(f32x4, buf_load16_stream(rvs, 16 * (lane >> 4)));
+}
+
+// K codes -> the bf16 K operands of the bf16 pools (codes are exact in bf16).
+template <int D>
+__device__ __forceinline__ void widen_k8(const RawBlock8<D>& raw, u32x4* k) {
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) {
+    const u32x2 k0 = i8x4_to_bf16x4(raw.k[j].x), k1 = i8x4_to_bf16x4(raw.k[j].y);
+    const u32x2 k2 = i8x4_to_bf16x4(raw.k[j].z), k3 = i8x4_to_bf16x4(raw.k[j].w);
+    k[2 * j] = u32x4{k0.x, k0.y, k1.x, k1.y};
+    k[2 * j + 1] = u32x4{k2.x, k2.y, k3.x, k3.y};
+  }
+}
+
+// V codes -> the bf16 V^T operands of the bf16 pools.
+template <int D>
+__device__ __forceinline__ void widen_v8(const RawBlock8<D>& raw, u32x2* v) {
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) {
+    v[4 * j] = i8x4_to_bf16x4(raw.v[j].x);
+    v[4 * j + 1] = i8x4_to_bf16x4(raw.v[j].y);
+    v[4 * j + 2] = i8x4_to_bf16x4(raw.v[j].z);
+    v[4 * j + 3] = i8x4_to_bf16x4(raw.v[j].w);
+  }
+}
+
+// The INT8 code of x against its row's scale, with append8_kernel's float32
+// operations (a zero scale, an all-zero row, gives code 0).
+__device__ __forceinline__ uint32_t code8(float x, float scale) {
+  return scale > 0.0f ? static_cast<uint32_t>(static_cast<int>(fminf(fmaxf(rintf(x / scale), -127.0f), 127.0f))) & 0xffu
+                      : 0u;
+}
+
+// P'^T V^T for one block of INT8 V codes (v: the widened codes): P' = P times
+// each key's V scale goes to the matrix cores as two bf16 parts, hi =
+// bf16(P') and lo = bf16(P' - hi), in one v_mfma_f32_16x16x32_bf16 per dim
+// tile whose A operand holds the codes twice (exact in bf16). A single bf16
+// P' would carry a 2^-9 relative error on every term, also on a row's
+// dominant key, whose probability times an arbitrary scale is not 1.
+template <int D>
+__device__ __forceinline__ void pv8(const u32x2* v, const float (&pv)[4], f32x4* o) {
+  const uint32_t h01 = pack_bf16x2(pv[0], pv[1]), h23 = pack_bf16x2(pv[2], pv[3]);
+  const uint32_t l01 = pack_bf16x2(pv[0] - bf16_bits_to_f32(h01 & 0xffffu), pv[1] - bf16_bits_to_f32(h01 >> 16));
+  const uint32_t l23 = pack_bf16x2(pv[2] - bf16_bits_to_f32(h23 & 0xffffu), pv[3] - bf16_bits_to_f32(h23 >> 16));
+  const u32x4 pb = {h01, h23, l01, l23};
+#pragma unroll
+  for (int d = 0; d < D / 16; ++d) o[d] = mfma_16x16x32(u32x4{v[d].x, v[d].y, v[d].x, v[d].y}, pb, o[d]);
+}
+
 }  // namespace ha

@@ -43,7 +43,7 @@
 // pool does not hold position t yet: the wave that consumes the block of
 // position t patches the token's K row and V column into its operand
 // registers after the block's load, and after consuming the block writes the
-// token into the pool (ring slot t mod W, or page t/16 at row t mod 16). No
+// token into the pool (ring slot t mod W, or the page of t at its token). No
 // other workgroup reads that slot in this launch, so the result equals
 // append-then-decode with one launch instead of two.
 #include <climits>
@@ -134,37 +134,6 @@ __device__ __forceinline__ void consume_block(BlockOps<D>& ops, const u32x4* qop
 // Slack of the INT8 path's exp2 reference (log2 units); see consume_block8.
 constexpr float kDecodeSlack = 8.0f;
 
-// INT8 pools: the raw 16-byte units of one block (K: D/64 units holding two
-// 32-channel slices each; V: D/64 units holding four 16-channel tiles each)
-// and the 4 K and 4 V scales of this lane's keys 4*q4 .. 4*q4+3.
-template <int D>
-struct RawBlock8 {
-  u32x4 k[D / 64];
-  u32x4 v[D / 64];
-  f32x4 ks;
-  f32x4 vs;
-};
-
-template <int D>
-__device__ __forceinline__ void load_block8(RawBlock8<D>& raw, const DecodeArgs& a, int64_t base, int q4, int c16) {
-  const bool ok = base >= 0;
-  const int64_t b0 = ok ? base : 0;
-  const uint32_t bytes = ok ? kBlock * D : 0;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const uint8_t*>(a.k_pool) + b0, bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const uint8_t*>(a.v_pool) + b0, bytes);
-  const int lane = 16 * q4 + c16;
-#pragma unroll
-  for (int j = 0; j < D / 64; ++j) {
-    raw.k[j] = buf_load16_stream(rk, 16 * (64 * j + lane));
-    raw.v[j] = buf_load16_stream(rv, 16 * (64 * j + lane));
-  }
-  const uint32_t sbytes = ok ? kBlock * 4 : 0;
-  const __amdgpu_buffer_rsrc_t rks = make_rsrc(a.k_scale + b0 / D, sbytes);
-  const __amdgpu_buffer_rsrc_t rvs = make_rsrc(a.v_scale + b0 / D, sbytes);
-  raw.ks = __builtin_bit_cast(f32x4, buf_load16_stream(rks, 16 * q4));
-  raw.vs = __builtin_bit_cast(f32x4, buf_load16_stream(rvs, 16 * q4));
-}
-
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ i32x4 mfma_i8_16x16x64(const u32x4& a, const u32x4& b, const i32x4& c) {
@@ -226,42 +195,14 @@ __device__ __forceinline__ float split_q8(const u32x4* qop, u32x4* q8) {
   return sq;
 }
 
-// K codes -> the bf16 K operands the bf16 path loads (codes are exact in bf16).
-template <int D>
-__device__ __forceinline__ void widen_k8(const RawBlock8<D>& raw, u32x4* k) {
-#pragma unroll
-  for (int j = 0; j < D / 64; ++j) {
-    const u32x2 k0 = i8x4_to_bf16x4(raw.k[j].x), k1 = i8x4_to_bf16x4(raw.k[j].y);
-    const u32x2 k2 = i8x4_to_bf16x4(raw.k[j].z), k3 = i8x4_to_bf16x4(raw.k[j].w);
-    k[2 * j] = u32x4{k0.x, k0.y, k1.x, k1.y};
-    k[2 * j + 1] = u32x4{k2.x, k2.y, k3.x, k3.y};
-  }
-}
-
-// V codes -> the bf16 V^T operands the bf16 path loads.
-template <int D>
-__device__ __forceinline__ void widen_v8(const RawBlock8<D>& raw, u32x2* v) {
-#pragma unroll
-  for (int j = 0; j < D / 64; ++j) {
-    v[4 * j] = i8x4_to_bf16x4(raw.v[j].x);
-    v[4 * j + 1] = i8x4_to_bf16x4(raw.v[j].y);
-    v[4 * j + 2] = i8x4_to_bf16x4(raw.v[j].z);
-    v[4 * j + 3] = i8x4_to_bf16x4(raw.v[j].w);
-  }
-}
-
 // consume_block for INT8 pools: score = k_scale * (q . code) -- with kI8, the
 // dot product on the int8 matrix cores as sq * sum_p (c_p . code) / 254^p
 // (split_q8; qop then holds the split operands and sl2 already carries sq),
 // otherwise on the bf16 ones with the codes widened --, and the V scale of
 // each key multiplies its probability (P'V = P (scale * code)); l keeps the
 // unscaled probabilities. Masked keys get a zero V scale so an unwritten
-// slot's scale cannot reach O. P' goes to the matrix cores as two bf16 parts,
-// hi = bf16(P') and lo = bf16(P' - hi), in one v_mfma_f32_16x16x32_bf16 per
-// dim tile whose A operand holds the block's codes twice (codes are exact in
-// bf16): a single bf16 P' would carry a 2^-9 relative error on every term,
-// also on a row's dominant key, whose probability times an arbitrary scale
-// is no longer 1. The 32-deep product takes the cycles of the 16-deep one.
+// slot's scale cannot reach O. P' goes to the matrix cores in two bf16 parts
+// (pv8); the 32-deep product takes the cycles of the 16-deep one.
 template <int D, bool kI8>
 __device__ __forceinline__ void consume_block8(const RawBlock8<D>& raw, const u32x4* qop, int first_key, int t,
                                                bool partial, float sl2, float& m_run, float& l_run, f32x4* o,
@@ -325,12 +266,7 @@ __device__ __forceinline__ void consume_block8(const RawBlock8<D>& raw, const u3
   float pv[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) pv[r] = p[r] * vs[r];
-  const uint32_t h01 = pack_bf16x2(pv[0], pv[1]), h23 = pack_bf16x2(pv[2], pv[3]);
-  const uint32_t l01 = pack_bf16x2(pv[0] - bf16_bits_to_f32(h01 & 0xffffu), pv[1] - bf16_bits_to_f32(h01 >> 16));
-  const uint32_t l23 = pack_bf16x2(pv[2] - bf16_bits_to_f32(h23 & 0xffffu), pv[3] - bf16_bits_to_f32(h23 >> 16));
-  const u32x4 pb = {h01, h23, l01, l23};
-#pragma unroll
-  for (int d = 0; d < DT; ++d) o[d] = mfma_16x16x32(u32x4{ops.v[d].x, ops.v[d].y, ops.v[d].x, ops.v[d].y}, pb, o[d]);
+  pv8<D>(ops.v, pv, o);
 }
 
 // One block's operands in the pool's format.
@@ -347,7 +283,7 @@ struct BlockBuf<D, true> {
 
 template <int D, bool kKv8>
 __device__ __forceinline__ void load_buf(BlockBuf<D, kKv8>& b, const DecodeArgs& a, int64_t base, int q4, int c16) {
-  if constexpr (kKv8) load_block8<D>(b.raw, a, base, q4, c16);
+  if constexpr (kKv8) load_block8<D>(b.raw, a.k_pool, a.v_pool, a.k_scale, a.v_scale, base, 16 * q4 + c16);
   else load_block<D>(b.ops, a.k_pool, a.v_pool, base, q4, c16);
 }
 
@@ -383,11 +319,6 @@ struct NewToken8 {
   float vs;
 };
 
-// The quantized code of x, exactly as append8_kernel computes it.
-__device__ __forceinline__ uint32_t code8(float x, float scale) {
-  return scale > 0.0f ? static_cast<uint32_t>(static_cast<int>(fminf(fmaxf(rintf(x / scale), -127.0f), 127.0f))) & 0xffu
-                      : 0u;
-}
 
 // The new token's operand pieces for the wave that owns its block: K chunk
 // (m, q4) of the token row (used by lanes c16 == row) and the V values of

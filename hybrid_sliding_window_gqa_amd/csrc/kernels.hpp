@@ -114,6 +114,9 @@ struct VerifyArgs {
   const void* k_new;      // [B][nq][Hkv][D]
   const void* v_new;
   bool in_f32;
+  bool kv8;               // INT8 pools: codes + per-token scales
+  float* k_scale;
+  float* v_scale;
   float* out;             // [B][nq][Hq][D]
   float* lse;             // [B][nq][Hq]
   int32_t splits;

@@ -28,6 +28,15 @@
 // writes the new tokens into the pool: nothing in the launch reads those
 // slots as keys (they are at or past t0, or, for the ring, read by this
 // workgroup only, before the barrier).
+//
+// INT8 pools (include/hybrid_attn.h): history blocks are loaded as codes and
+// scales and widened to the bf16 operands right before use; the K scale
+// multiplies the scores and the V scale each probability (P' in two bf16
+// parts, as in decode). The new tokens' block is quantized in registers with
+// the appends' arithmetic (row absmax butterflies over the lanes that hold a
+// K row or a V row), so they attend as the codes they are stored with; the
+// append after the merge quantizes them again, one 8-channel chunk per lane,
+// with the same operations.
 #include <cmath>
 
 #include "common.hpp"
@@ -65,6 +74,29 @@ __device__ __forceinline__ void vload_block(VBlock<D>& ops, const uint16_t* kp, 
   }
 }
 
+// One history block as loaded: bf16 operands, or INT8 codes and scales.
+template <int D, bool kKv8>
+struct VBuf;
+template <int D>
+struct VBuf<D, false> {
+  VBlock<D> ops;
+};
+template <int D>
+struct VBuf<D, true> {
+  RawBlock8<D> raw;
+};
+
+template <int D, bool kKv8>
+__device__ __forceinline__ void vload_buf(VBuf<D, kKv8>& b, const VerifyArgs& a, int64_t base, int lane) {
+  if constexpr (kKv8) load_block8<D>(b.raw, a.k_pool, a.v_pool, a.k_scale, a.v_scale, base, lane);
+  else vload_block<D>(b.ops, a.k_pool, a.v_pool, base, lane);
+}
+
+// bf16 bits of an INT8 code (exact).
+__device__ __forceinline__ uint32_t code_bf16(uint32_t code) {
+  return __float_as_uint(static_cast<float>(static_cast<int8_t>(code))) >> 16;
+}
+
 template <bool kF32>
 __device__ __forceinline__ uint32_t bf16_at(const void* src, int64_t elem) {
   if constexpr (kF32) return f32_to_bf16_bits(static_cast<const float*>(src)[elem]);
@@ -81,7 +113,7 @@ struct ColState {
 
 }  // namespace
 
-template <int D, bool kFull, bool kF32, int NG>
+template <int D, bool kFull, bool kF32, int NG, bool kKv8>
 __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs a) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
@@ -214,8 +246,8 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
   // merge. Elements past nq x D read past the buffer's end and get zeros.
   constexpr int kAppendRegs = 4;
   uint32_t app_k[kAppendRegs], app_v[kAppendRegs];
-  const bool app_pre = !kF32 && split == 0 && nq * D <= kAppendRegs * 64 * kVerifyWaves;
-  if constexpr (!kF32) {
+  const bool app_pre = !kF32 && !kKv8 && split == 0 && nq * D <= kAppendRegs * 64 * kVerifyWaves;
+  if constexpr (!kF32 && !kKv8) {
     if (app_pre) {
       const int64_t row0 = static_cast<int64_t>(b) * nq * hkv * D;
       const uint32_t bytes = static_cast<uint32_t>(nq * hkv * D * 2);
@@ -242,11 +274,18 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
   }
 
   // One block: keys at positions kp[r] (key 4 q4 + r; -1: no key), shared
-  // by every column group.
-  auto consume = [&](VBlock<D>& ops, const int (&kp)[4]) {
-    // zero V of keys that do not exist (their pool slots may hold anything);
-    // blocks whose keys all exist (every full history block) skip it
-    if (!__all(kp[0] >= 0 && kp[1] >= 0 && kp[2] >= 0 && kp[3] >= 0)) {
+  // by every column group. INT8 pools: ops holds the widened codes, ks / vs
+  // the keys' K and V scales (the K scale multiplies the scores, the V scale
+  // each probability, l sums the unscaled ones); a key that does not exist
+  // gets a zero V scale, so its slot's scale cannot reach O.
+  auto consume_ops = [&](VBlock<D>& ops, const int (&kp)[4], const float (&ks)[4], const float (&vs)[4]) {
+    float vsk[4];
+    if constexpr (kKv8) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vsk[r] = kp[r] >= 0 ? vs[r] : 0.0f;
+    } else if (!__all(kp[0] >= 0 && kp[1] >= 0 && kp[2] >= 0 && kp[3] >= 0)) {
+      // zero V of keys that do not exist (their pool slots may hold anything);
+      // blocks whose keys all exist (every full history block) skip it
       uint32_t keep[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) keep[r] = kp[r] >= 0 ? 0xffffu : 0u;
@@ -263,6 +302,10 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < KS; ++m) s = mfma_16x16x32(ops.k[m], qop[gr][m], s);
+      if constexpr (kKv8) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[r] *= ks[r];
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         bool ok = kp[r] >= 0 && kp[r] <= tcol[gr];
@@ -288,9 +331,29 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
 #pragma unroll
       for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s[r] * sl2 - m_use);
       cs.l_run += (p[0] + p[1]) + (p[2] + p[3]);
-      const u32x2 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+      if constexpr (kKv8) {
+        float pv[4];
 #pragma unroll
-      for (int d = 0; d < DT; ++d) cs.o[d] = mfma_16x16x16(ops.v[d], pb, cs.o[d]);
+        for (int r = 0; r < 4; ++r) pv[r] = p[r] * vsk[r];
+        pv8<D>(ops.v, pv, cs.o);
+      } else {
+        const u32x2 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+#pragma unroll
+        for (int d = 0; d < DT; ++d) cs.o[d] = mfma_16x16x16(ops.v[d], pb, cs.o[d]);
+      }
+    }
+  };
+  auto consume = [&](VBuf<D, kKv8>& buf, const int (&kp)[4]) {
+    if constexpr (kKv8) {
+      VBlock<D> ops;
+      widen_k8<D>(buf.raw, ops.k);
+      widen_v8<D>(buf.raw, ops.v);
+      const float ks[4] = {buf.raw.ks[0], buf.raw.ks[1], buf.raw.ks[2], buf.raw.ks[3]};
+      const float vs[4] = {buf.raw.vs[0], buf.raw.vs[1], buf.raw.vs[2], buf.raw.vs[3]};
+      consume_ops(ops, kp, ks, vs);
+    } else {
+      const float none[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      consume_ops(buf.ops, kp, none, none);
     }
   };
   auto hist_keys = [&](int i, int (&kp)[4]) {
@@ -354,9 +417,9 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
     int pg_a2 = 0, pg_b2 = 0;
     int64_t base_a = base_of(ia, page_of(ia));
     int64_t base_b = base_of(ib, page_of(ib));
-    VBlock<D> A, B;
-    vload_block<D>(A, a.k_pool, a.v_pool, base_a, lane);
-    vload_block<D>(B, a.k_pool, a.v_pool, base_b, lane);
+    VBuf<D, kKv8> A, B;
+    vload_buf<D, kKv8>(A, a, base_a, lane);
+    vload_buf<D, kKv8>(B, a, base_b, lane);
     pg_a2 = page_of(ia + 2 * kVerifyWaves);
     pg_b2 = page_of(ib + 2 * kVerifyWaves);
     if (has_new) {
@@ -372,6 +435,48 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
         else
           asm volatile("" : "+v"(vb[r][0]), "+v"(vb[r][1]), "+v"(vb[r][2]), "+v"(vb[r][3])::"memory");
       }
+      float ksn[4] = {0.0f, 0.0f, 0.0f, 0.0f}, vsn[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (kKv8) {
+        // INT8 pools: the new tokens attend as the codes and scales they are
+        // appended with, computed with append8_kernel's float32 operations.
+        // K row of token c16: the 4 lanes of column c16; V row of token
+        // 4 q4 + r: element r of the 16 lanes of row group q4.
+        float ka = 0.0f;
+#pragma unroll
+        for (int m = 0; m < KS; ++m) {
+          const uint32_t w4[4] = {N.k[m].x, N.k[m].y, N.k[m].z, N.k[m].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            ka = max_prop(ka, max_prop(fabsf(__uint_as_float(w4[j] << 16)), fabsf(__uint_as_float(w4[j] & 0xffff0000u))));
+        }
+        ka = max_prop(ka, __shfl_xor(ka, 16));
+        ka = max_prop(ka, __shfl_xor(ka, 32));
+        const float ks_tok = ka / 127.0f;
+#pragma unroll
+        for (int m = 0; m < KS; ++m) {
+          uint32_t w4[4] = {N.k[m].x, N.k[m].y, N.k[m].z, N.k[m].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t lo = code_bf16(code8(__uint_as_float(w4[j] << 16), ks_tok));
+            const uint32_t hi = code_bf16(code8(__uint_as_float(w4[j] & 0xffff0000u), ks_tok));
+            w4[j] = lo | (hi << 16);
+          }
+          N.k[m] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          ksn[r] = __shfl(ks_tok, 4 * q4 + r);   // key 4 q4 + r = token of column 4 q4 + r
+          float va = 0.0f;
+#pragma unroll
+          for (int d = 0; d < DT; ++d) va = max_prop(va, fabsf(__uint_as_float(static_cast<uint32_t>(vb[r][d]) << 16)));
+#pragma unroll
+          for (int mask = 1; mask < 16; mask <<= 1) va = max_prop(va, __shfl_xor(va, mask));
+          vsn[r] = va / 127.0f;
+#pragma unroll
+          for (int d = 0; d < DT; ++d)
+            vb[r][d] = static_cast<uint16_t>(code_bf16(code8(__uint_as_float(static_cast<uint32_t>(vb[r][d]) << 16), vsn[r])));
+        }
+      }
 #pragma unroll
       for (int d = 0; d < DT; ++d)
         N.v[d] = u32x2{static_cast<uint32_t>(vb[0][d]) | (static_cast<uint32_t>(vb[1][d]) << 16),
@@ -379,7 +484,7 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
       int kpn[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) kpn[r] = (4 * q4 + r < nq) ? t0 + 4 * q4 + r : -1;
-      consume(N, kpn);
+      consume_ops(N, kpn, ksn, vsn);
     }
     const int nmine = (last > ia) ? (last - ia + kVerifyWaves - 1) / kVerifyWaves : 0;
     int kp[4];
@@ -390,7 +495,7 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
       }
       ia += 2 * kVerifyWaves;
       base_a = base_of(ia, pg_a2);
-      vload_block<D>(A, a.k_pool, a.v_pool, base_a, lane);
+      vload_buf<D, kKv8>(A, a, base_a, lane);
       pg_a2 = page_of(ia + 2 * kVerifyWaves);
       if (base_b >= 0) {
         hist_keys(ib, kp);
@@ -398,7 +503,7 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
       }
       ib += 2 * kVerifyWaves;
       base_b = base_of(ib, pg_b2);
-      vload_block<D>(B, a.k_pool, a.v_pool, base_b, lane);
+      vload_buf<D, kKv8>(B, a, base_b, lane);
       pg_b2 = page_of(ib + 2 * kVerifyWaves);
     }
     if ((nmine & 1) && base_a >= 0) {
@@ -460,25 +565,86 @@ __global__ __launch_bounds__(64 * kVerifyWaves, 2) void verify_kernel(VerifyArgs
   }
 
   // Append the new tokens (split 0; every read of this workgroup is done).
-  auto append_elem = [&](int e, uint32_t kv, uint32_t vv) {
-    const int j = e / D;
-    const int dd = e - j * D;
+  // Pool block (element offset) and row of new token j, or false when it is
+  // not written (no valid page or ring, or a ring slot a later token of this
+  // call writes again).
+  auto new_slot = [&](int j, int64_t& blk, int& row) -> bool {
     const int p = t0 + j;
-    int64_t blk;
-    int row;
     if constexpr (kFull) {
       const int lb = p / kBlock;
       const int pg = (lb >> psh) < a.table_stride ? page_row[lb >> psh] : -1;
-      if (pg < 0 || pg >= a.num_blocks) return;
+      if (pg < 0 || pg >= a.num_blocks) return false;
       blk = page_block_offset(pg, g, hkv, lb & ((1 << psh) - 1), psh, kBlock * D);
       row = p % kBlock;
     } else {
-      if (ring < 0 || ring >= a.num_blocks) return;
-      if (j < nq - W) return;         // its slot is written again by a later token of this call
+      if (ring < 0 || ring >= a.num_blocks) return false;
+      if (j < nq - W) return false;
       const int s = p % W;
       blk = ((static_cast<int64_t>(ring) * hkv + g) * a.geo.ring + kBlock * (s / kBlock)) * D;
       row = s % kBlock;
     }
+    return true;
+  };
+  if constexpr (kKv8) {
+    // INT8 pools: append8_kernel's arithmetic, D/8 lanes per token row (one
+    // 8-channel chunk each), the row's absmax a butterfly over those lanes.
+    if (split == 0) {
+      constexpr int kChunks = D / 8;
+      constexpr int kRowsPerPass = 64 * kVerifyWaves / kChunks;
+      const int c = static_cast<int>(threadIdx.x) % kChunks;
+      for (int j = static_cast<int>(threadIdx.x) / kChunks; j < nq; j += kRowsPerPass) {
+        int64_t blk;
+        int row;
+        if (!new_slot(j, blk, row)) continue;   // uniform over the row's lanes
+        const int64_t src = ((static_cast<int64_t>(b) * nq + j) * hkv + g) * D + c * 8;
+        const u32x4 kraw = load8_as_bf16<kF32>(a.k_new, src);
+        const u32x4 vraw = load8_as_bf16<kF32>(a.v_new, src);
+        const uint32_t kw[4] = {kraw.x, kraw.y, kraw.z, kraw.w};
+        const uint32_t vw[4] = {vraw.x, vraw.y, vraw.z, vraw.w};
+        float kx[8], vx[8];
+        float ka = 0.0f, va = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kx[2 * e] = __uint_as_float(kw[e] << 16);
+          kx[2 * e + 1] = __uint_as_float(kw[e] & 0xffff0000u);
+          vx[2 * e] = __uint_as_float(vw[e] << 16);
+          vx[2 * e + 1] = __uint_as_float(vw[e] & 0xffff0000u);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ka = max_prop(ka, fabsf(kx[e]));
+          va = max_prop(va, fabsf(vx[e]));
+        }
+#pragma unroll
+        for (int mask = kChunks / 2; mask >= 1; mask >>= 1) {
+          ka = max_prop(ka, __shfl_xor(ka, mask));
+          va = max_prop(va, __shfl_xor(va, mask));
+        }
+        const float ks = ka / 127.0f;
+        const float vs = va / 127.0f;
+        uint8_t* kb = reinterpret_cast<uint8_t*>(a.k_pool_w) + blk;
+        uint8_t* vbk = reinterpret_cast<uint8_t*>(a.v_pool_w) + blk;
+        uint32_t kq[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kq[e >> 2] |= code8(kx[e], ks) << (8 * (e & 3));
+          vbk[v8_elem(row, c * 8 + e)] = static_cast<uint8_t>(code8(vx[e], vs));
+        }
+        *reinterpret_cast<u32x2*>(kb + k8_elem(row, c * 8)) = u32x2{kq[0], kq[1]};
+        if (c == 0) {
+          a.k_scale[blk / D + row] = ks;
+          a.v_scale[blk / D + row] = vs;
+        }
+      }
+    }
+    return;
+  }
+  auto append_elem = [&](int e, uint32_t kv, uint32_t vv) {
+    const int j = e / D;
+    const int dd = e - j * D;
+    int64_t blk;
+    int row;
+    if (!new_slot(j, blk, row)) return;
     a.k_pool_w[blk + k_elem(row, dd)] = static_cast<uint16_t>(kv);
     a.v_pool_w[blk + v_elem(row, dd)] = static_cast<uint16_t>(vv);
   };
@@ -536,8 +702,13 @@ int verify_column_groups(int nq, int group) { return (nq * group + 15) / 16; }
 template <int D, bool kFull, int NG>
 static void launch_verify_k(const VerifyArgs& a, dim3 grid, hipStream_t stream) {
   const dim3 block(64 * kVerifyWaves);
-  if (a.in_f32) hipLaunchKernelGGL((verify_kernel<D, kFull, true, NG>), grid, block, 0, stream, a);
-  else hipLaunchKernelGGL((verify_kernel<D, kFull, false, NG>), grid, block, 0, stream, a);
+  if (a.kv8) {
+    if (a.in_f32) hipLaunchKernelGGL((verify_kernel<D, kFull, true, NG, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((verify_kernel<D, kFull, false, NG, true>), grid, block, 0, stream, a);
+  } else {
+    if (a.in_f32) hipLaunchKernelGGL((verify_kernel<D, kFull, true, NG, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((verify_kernel<D, kFull, false, NG, false>), grid, block, 0, stream, a);
+  }
 }
 
 template <int D>

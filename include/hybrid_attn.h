@@ -146,9 +146,10 @@ typedef struct ha_shape {
  *            authoritative logical->physical index of the sequence ([YLY]).
  * kv_dtype selects bf16 pools (HA_KV_BF16, scales unused) or INT8 pools
  * (HA_KV_INT8: k_scale / v_scale required, layout above). INT8 pools are
- * written by the two append calls (and by hybrid_attn_decode's fused append,
- * which quantizes the token the same way) and read by hybrid_attn_decode;
- * prefill, verify and the pool reads reject them (HA_ERR_UNSUPPORTED). */
+ * written by the two append calls (and by the fused appends of
+ * hybrid_attn_decode and hybrid_attn_verify, which quantize the new tokens
+ * the same way) and read by hybrid_attn_decode and hybrid_attn_verify;
+ * prefill and the pool reads reject them (HA_ERR_UNSUPPORTED). */
 typedef struct ha_kv_view {
   int32_t kind;
   void* k;
@@ -250,10 +251,10 @@ ha_status hybrid_attn_prefill(const ha_shape* shape, const ha_kv_view* kv, const
  *   q [batch][Hq][D] in_dtype; out float32 [batch][Hq][D]; lse float32 [batch][Hq]
  *   k_new, v_new: the new token's K/V, [batch][Hkv][D] in_dtype, or both NULL.
  *     Given: the pool holds positions < t and the call also appends position
- *     t (ring slot t mod W, or page t/16 row t mod 16) -- the same pool and
- *     outputs as swa_ring_append / full_pool_append followed by this call
- *     with NULL, in one launch. NULL: position t must already be in the pool
- *     and the pool is only read.
+ *     t (ring slot t mod W, or page t / page_size at page token t mod
+ *     page_size) -- the same pool and outputs as swa_ring_append /
+ *     full_pool_append followed by this call with NULL, in one launch.
+ *     NULL: position t must already be in the pool and the pool is only read.
  *   num_splits: maximum key splits per sequence, 0 = automatic
  *   workspace: hybrid_attn_workspace_size(..., decode = 1) bytes. */
 ha_status hybrid_attn_decode(const ha_shape* shape, const ha_kv_view* kv, const int32_t* kv_len,
@@ -303,8 +304,12 @@ int32_t hybrid_attn_decode_splits(const ha_shape* shape, int32_t kind, int32_t b
  * nq; the pool holds positions < t0 and the tokens' K/V are given. Query
  * token i sees keys [0, t0 + i] (full) or [t0 + i - W + 1, t0 + i] (SWA):
  * causal among the new tokens. The call also appends the nq tokens (ring
- * slots p mod W, or page p/16 row p mod 16) after reading: pool and outputs
- * equal hybrid_attn_prefill over a chunk of nq tokens followed by the append.
+ * slots p mod W, or page p / page_size at page token p mod page_size) after
+ * reading: pool and outputs equal hybrid_attn_prefill over a chunk of nq
+ * tokens followed by the append. INT8 pools: the new tokens are quantized
+ * with the appends' arithmetic and attend, like the history, as the codes
+ * times the scales they are stored with; the pool afterwards equals the
+ * append of the nq tokens.
  * Full layers split the history over workgroups like hybrid_attn_decode.
  *   kv_len int32 [batch] device (kv_len[b] < nq: rows out = 0, lse = -inf,
  *     nothing appended);  max_kv_len >= every kv_len[b] (host)

@@ -238,11 +238,16 @@ def test_int8_view_errors(lib):
         assert decode_call(lib, s, bad) == status
         assert lib.full_pool_append(ctypes.byref(s), ctypes.byref(bad), FAKE, FAKE, 2, 10, FAKE, FAKE, 0,
                                     None) == status
-    # prefill and verify read bf16 pools only
+    # prefill reads bf16 pools only
     args = [FAKE, FAKE, 2, 10, 5, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, 1 << 30, None]
     assert lib.hybrid_attn_prefill(ctypes.byref(s), ctypes.byref(ring), *args) == _lib.HA_ERR_UNSUPPORTED
-    assert lib.hybrid_attn_verify(ctypes.byref(s), ctypes.byref(pages), FAKE, 2, 100, 4, FAKE, FAKE, FAKE, 0,
-                                  FAKE, FAKE, 0, FAKE, 1 << 30, None) == _lib.HA_ERR_UNSUPPORTED
+    # verify takes INT8 pools: validation reaches the NULL query (and a view
+    # without scales is refused first)
+    verify = lambda v, q: lib.hybrid_attn_verify(ctypes.byref(s), ctypes.byref(v), FAKE, 2, 100, 4, q, FAKE, FAKE,
+                                                  0, FAKE, FAKE, 0, FAKE, 1 << 30, None)
+    assert verify(pages, None) == _lib.HA_ERR_NULL
+    assert verify(ring, None) == _lib.HA_ERR_NULL
+    assert verify(int8(_lib.HA_FULL, ks=None), FAKE) == _lib.HA_ERR_NULL
     # the zero-initialised tail of a view is a bf16 pool
     assert HaKvView(_lib.HA_FULL, FAKE, FAKE, 8, FAKE, 4).kv_dtype == _lib.HA_KV_BF16
 

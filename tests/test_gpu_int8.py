@@ -284,3 +284,63 @@ def test_int8_quantization_error_at_long_context():
         print(f"[int8 quantization error] {n} keys: max|O - oracle(bf16 K/V)| {err_o:.3e}, "
               f"max|LSE - oracle| {err_l:.3e} (max|V| {v_max:.2f})", flush=True)
         assert err_o <= v_max / 127 and err_l <= 1e-2, (n, err_o, err_l)
+
+
+def oracle_rows8(q_rows, k_seq, v_seq, positions, kind, window):
+    """Oracle rows at `positions` over the dequantized K/V of k_seq / v_seq."""
+    qk, sk = quantize_rows(bf16_round(k_seq))
+    qv, sv = quantize_rows(bf16_round(v_seq))
+    kd = np.stack([dequantize_rows(qk[:, g], sk[:, g]) for g in range(qk.shape[1])], axis=1)
+    vd = np.stack([dequantize_rows(qv[:, g], sv[:, g]) for g in range(qv.shape[1])], axis=1)
+    return attend(q_rows, kd, vd, np.asarray(positions), kind, window)
+
+
+@pytest.mark.parametrize("kind", [ha.HA_SWA, ha.HA_FULL])
+@pytest.mark.parametrize("hq,hkv,d,window,nq,splits,src", [(64, 8, 128, 128, 4, 0, None),
+                                                            (64, 8, 128, 128, 1, 3, None),
+                                                            (8, 2, 64, 32, 8, 0, torch.float32),
+                                                            (8, 4, 128, 24, 16, 5, None),
+                                                            (8, 2, 64, 3, 4, 0, None)])
+def test_verify_over_int8_pools(kind, hq, hkv, d, window, nq, splits, src):
+    """Multi-token verify over INT8 pools: the nq new tokens are quantized as
+    append8 does and attend, like the history, as codes times scales, so the
+    rows match the oracle over the dequantized K/V of every position; the
+    pool afterwards holds exactly the codes and scales of appending all
+    tokens (bit-exact, including rows whose kv_len is below nq: nothing is
+    written for them, and their outputs are 0 with LSE -inf)."""
+    shape = ha.HeadShape(hq, hkv, d, window=window)
+    lens = [nq, nq + 1, 17, window + nq, 300, 2049, max(nq - 1, 0)]
+    gen = make_generator(hq + d + window + nq + splits)
+    k = [randn_bf16(gen, max(n, nq), hkv, d) for n in lens]
+    v = [randn_bf16(gen, max(n, nq), hkv, d) for n in lens]
+    q = [randn_bf16(gen, max(n, nq), hq, d) for n in lens]
+    hist = [max(n - nq, 0) for n in lens]
+    pool, view, _ = make_pools(shape, kind, lens, seed=nq)
+    ref_pool, ref_view, _ = make_pools(shape, kind, lens, seed=nq)
+    starts = [max(0, h - window) if kind == ha.HA_SWA else 0 for h in hist]
+    append_history(shape, view, list(zip(k, v)), starts, hist)
+    rows = lambda xs: torch.stack([x[h:h + nq] for x, h in zip(xs, hist)]).contiguous()
+    q_new, k_new, v_new = rows(q), rows(k), rows(v)
+    if src is not None:
+        q_new, k_new, v_new = q_new.to(src), k_new.to(src), v_new.to(src)
+    out, lse = ha.hybrid_attn_verify(shape, view, i32(lens), q_new, k_new, v_new, max(lens), num_splits=splits)
+    # reference pool: the history appended, then the nq tokens, by the append calls
+    full_ends = [n if n >= nq else 0 for n in lens]
+    append_history(shape, ref_view, list(zip(k, v)), starts, hist)
+    fn = ha.swa_ring_append if kind == ha.HA_SWA else ha.full_pool_append
+    live = [s for s, n in enumerate(lens) if n >= nq]
+    fn(shape, ref_view, i32(hist), i32(np.concatenate([[0], np.cumsum([nq if n >= nq else 0 for n in lens])])),
+       k_new[live].reshape(-1, hkv, d).contiguous(), v_new[live].reshape(-1, hkv, d).contiguous())
+    torch.cuda.synchronize()
+    kname = "swa" if kind == ha.HA_SWA else "full"
+    o, l = host(out), host(lse)
+    for s, n in enumerate(lens):
+        if n < nq:
+            assert np.all(o[s] == 0) and np.all(l[s] == -np.inf), f"row {s} (kv_len {n} < nq)"
+            continue
+        pos = np.arange(n - nq, n)
+        ref_o, ref_l = oracle_rows8(host(q[s][n - nq:n]), host(k[s][:n]), host(v[s][:n]), pos, kname, window)
+        assert_close(o[s], l[s], ref_o, ref_l, f"kind={kind} nq={nq} seq={s} len={n} full_end={full_ends[s]}")
+    assert torch.equal(pool.k, ref_pool.k) and torch.equal(pool.v, ref_pool.v)
+    assert torch.equal(pool.k_scale.view(torch.int32), ref_pool.k_scale.view(torch.int32))
+    assert torch.equal(pool.v_scale.view(torch.int32), ref_pool.v_scale.view(torch.int32))

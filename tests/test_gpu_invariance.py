@@ -73,7 +73,8 @@ def test_prefill_is_placement_invariant(kind):
 
 
 @pytest.mark.parametrize("kind", [ha.HA_SWA, ha.HA_FULL])
-def test_verify_is_placement_invariant(kind):
+@pytest.mark.parametrize("kv_dtype", ["bf16", "int8"])
+def test_verify_is_placement_invariant(kind, kv_dtype):
     nq = 4
     lens = [25, 700, 2049]
     seq = logical(lens, seed=31)
@@ -82,7 +83,7 @@ def test_verify_is_placement_invariant(kind):
     rows = lambda i: torch.stack([s[i][n - nq:n] for s, n in zip(seq, lens)]).contiguous()
     results = []
     for placement in PLACEMENTS[kind]:
-        pool, view = make_view(kind, dict(placement, lens=lens))
+        pool, view = make_view(kind, dict(placement, lens=lens), kv_dtype)
         append_history(SHAPE, view, seq, [0] * 3, [n - nq for n in lens])
         out, lse = ha.hybrid_attn_verify(SHAPE, view, i32(lens), q, rows(0), rows(1), max(lens), num_splits=3)
         torch.cuda.synchronize()

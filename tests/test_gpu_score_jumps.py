@@ -97,8 +97,8 @@ def test_decode_with_late_score_jumps(kind, kv_dtype, splits):
 
 
 @pytest.mark.parametrize("kind", [ha.HA_SWA, ha.HA_FULL])
-@pytest.mark.parametrize("nq,splits", [(4, 0), (2, 4)])
-def test_verify_with_late_score_jumps(kind, nq, splits):
+@pytest.mark.parametrize("nq,splits,kv_dtype", [(4, 0, "bf16"), (2, 4, "bf16"), (4, 0, "int8"), (2, 4, "int8")])
+def test_verify_with_late_score_jumps(kind, nq, splits, kv_dtype):
     shape = ha.HeadShape(64, 8, 128)
     gen = make_generator(29 + nq)
     hq, hkv, d = shape.num_q_heads, shape.num_kv_heads, shape.head_dim
@@ -108,7 +108,7 @@ def test_verify_with_late_score_jumps(kind, nq, splits):
     for s, n in enumerate(LENS):
         spike(k[s], n)
         q[s] = (q[s].float() * 6.0).to(torch.bfloat16)
-    view = pools(shape, kind, LENS)
+    view = pools(shape, kind, LENS, kv_dtype)
     hist = [n - nq for n in LENS]
     append_history(shape, view, list(zip(k, v)), [0] * len(LENS), hist)
     rows = lambda xs: torch.stack([x[h:h + nq] for x, h in zip(xs, hist)]).contiguous()
@@ -117,7 +117,11 @@ def test_verify_with_late_score_jumps(kind, nq, splits):
     torch.cuda.synchronize()
     kname = "swa" if kind == ha.HA_SWA else "full"
     for s, n in enumerate(LENS):
-        ref_o, ref_l = oracle_rows(host(q[s][n - nq:n]), host(k[s]), host(v[s]), np.arange(n - nq, n), kname,
-                                   shape.window)
+        pos = np.arange(n - nq, n)
+        if kv_dtype == "int8":
+            kd, vd = dequantized(k[s][:n]), dequantized(v[s][:n])
+            ref_o, ref_l = attend(host(q[s][n - nq:n]), kd, vd, pos, kname, shape.window)
+        else:
+            ref_o, ref_l = oracle_rows(host(q[s][n - nq:n]), host(k[s]), host(v[s]), pos, kname, shape.window)
         check_rows(host(out[s]), host(lse[s]), ref_o, ref_l, float(np.abs(host(v[s])).max()),
-                   f"kind={kname} nq={nq} splits={splits} len={n}")
+                   f"kind={kname} kv={kv_dtype} nq={nq} splits={splits} len={n}")
