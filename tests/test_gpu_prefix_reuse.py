@@ -54,9 +54,11 @@ def test_read_returns_what_was_appended():
     assert torch.equal(rvv.view(torch.int16), want_v.view(torch.int16))
 
 
+@pytest.mark.parametrize("page_size", [16, 64])
 @pytest.mark.parametrize("cached,new", [(300, 40), (256, 17), (45, 80)])
-def test_tree_driven_reuse_matches_the_oracle(cached, new):
-    shape = ha.HeadShape(16, 2, 128, window=W)
+def test_tree_driven_reuse_matches_the_oracle(cached, new, page_size):
+    ps = page_size
+    shape = ha.HeadShape(16, 2, 128, window=W, page_size=ps)
     total = cached + new
     gen = make_generator(cached + new)
     rng = np.random.default_rng(cached)
@@ -70,30 +72,30 @@ def test_tree_driven_reuse_matches_the_oracle(cached, new):
     rings = ha.SwaRingPool(shape, 4, "cuda", fill=float("nan"))
     pools = ha.FullPagePool(shape, npg, "cuda", fill=float("nan"))
     # request A: its K/V in ring 0 and its pages, then handed to the tree
-    pages_a = alloc.alloc(-(-cached // 16))
+    pages_a = alloc.alloc(-(-cached // ps))
     ring_a, table_a = rings.view(i32([0])), pools.view(i32([pages_a]))
     one = lambda n: i32([0, n])
     ha.swa_ring_append(shape, ring_a, i32([0]), one(cached), kv[ha.HA_SWA][0][:cached].contiguous(),
                        kv[ha.HA_SWA][1][:cached].contiguous())
     ha.full_pool_append(shape, table_a, i32([0]), one(cached), kv[ha.HA_FULL][0][:cached].contiguous(),
                         kv[ha.HA_FULL][1][:cached].contiguous())
-    tree = PrefixTree(W, 16)
+    tree = PrefixTree(W, ps)
     kept, ring_kept = tree.insert(tok_a, pages_a, ring_id=0, ring_len=cached, transfer=True)
     assert kept.all() and ring_kept
     snapshot = pools.k.clone(), pools.v.clone()
     # request B: what the tree lets it reuse
     r = tree.reuse(tok_b)
     assert r.matched == cached and r.length == cached        # the whole cached request, window-safe
-    assert r.shared_pages.tolist() == pages_a[: cached // 16]
+    assert r.shared_pages.tolist() == pages_a[: cached // ps]
     assert set(r.window_rings.tolist()) == {0}
     tree.lock(tok_b, r.length)
-    n_pages_b = -(-total // 16)
+    n_pages_b = -(-total // ps)
     own = alloc.alloc(n_pages_b - len(r.shared_pages))
     pages_b = r.shared_pages.tolist() + own
     ring_b, table_b = rings.view(i32([1])), pools.view(i32([pages_b]))
     L = r.length
     if r.cow_page >= 0:                                      # copy the partly shared page before writing to it
-        p0 = (L // 16) * 16
+        p0 = (L // ps) * ps
         ko = torch.empty(L - p0, 2, 128, dtype=torch.bfloat16, device="cuda")
         vo = torch.empty_like(ko)
         ha.full_pool_read(shape, table_a, i32([p0]), one(L - p0), ko, vo)
