@@ -577,10 +577,38 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
     }
     store_pos(0);
   }
+  // Full layers: does any history block of this workgroup's tiles lack a
+  // valid page (a hole in the page table, which the tiles then mask)? Only
+  // then do the tiles read the per-block flags from LDS; skipping that read
+  // made the chunked workload's full-layer call 1.5-4.8% faster (three
+  // rounds on one box). Each wave checks a share of the page ids and
+  // publishes the result before the barrier below.
+  __shared__ int sm_bad[kWaves];
+  if constexpr (kFull) {
+    bool bad = false;
+    const int hb0 = min(t_begin * kStageBlocks, hist_blocks);
+    const int hb1 = min(min(t_end, n_hist_tiles) * kStageBlocks, hist_blocks);
+    if (hb1 > hb0) {
+      const int p1 = ((hb1 - 1) >> a.geo.page_shift) + 1;
+      for (int p = (hb0 >> a.geo.page_shift) + tid; p < p1; p += 64 * kWaves) {
+        const int pg = page_row[p];
+        bad = bad || pg < 0 || pg >= a.num_blocks;
+      }
+    }
+    const bool wave_bad = __any(bad);
+    if (lane == 0) sm_bad[wave] = wave_bad ? 1 : 0;
+  }
   // Everything loaded so far (Q, first tile) is complete before the loop, so
   // the loop's only outstanding global loads are the next tile's staging.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  bool any_bad = false;
+  if constexpr (kFull) {
+    int acc = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) acc |= sm_bad[w];
+    any_bad = __builtin_amdgcn_readfirstlane(acc) != 0;
+  }
 
   for (int tile = t_begin; tile < t_end; ++tile) {
     const int buf = (tile - t_begin) & 1;
@@ -603,7 +631,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<kFull>(), kFull ? 1 : 2) void pre
     // Full history tiles: bit kb set = block kb of this compute tile has no valid page.
     int no_page_bits = 0;
     if constexpr (kFull) {
-      if (tile < n_hist_tiles) {
+      if (any_bad && tile < n_hist_tiles) {
         const int4 f = reinterpret_cast<const int4*>(sm.pos[buf])[sub];
         no_page_bits = __builtin_amdgcn_readfirstlane((f.x & 1) | ((f.y & 1) << 1) | ((f.z & 1) << 2) |
                                                       ((f.w & 1) << 3));
